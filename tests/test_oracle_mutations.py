@@ -1,0 +1,140 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at
+least one pin catches each of them.  This is how we know the pins constrain
+the oracle rather than echo it."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe as om
+from tests import pins
+
+_quantize, _pack, _permute = om.quantize, om.pack, om.permute
+
+
+def _fails(fn, *a, **kw):
+    try:
+        fn(*a, **kw)
+    except AssertionError:
+        return True
+    return False
+
+
+def _quantize_zero_from_max(w, bits, group=64):
+    # mistake: zero taken from the maximum instead of the minimum
+    w = np.asarray(w, np.float32)
+    N, K = w.shape
+    qmax = np.float32(2 ** bits - 1)
+    wg = w.reshape(N, K // group, group)
+    mn, mx = wg.min(2), wg.max(2)
+    s16 = ((mx - mn) / qmax).astype(np.float16)
+    s16 = np.where(s16 == 0, np.float16(1), s16)
+    z16 = (mx / s16.astype(np.float32)).astype(np.float16)
+    q = np.clip(np.rint(wg / s16.astype(np.float32)[..., None] + z16.astype(np.float32)[..., None]), 0, qmax)
+    return q.astype(np.uint8).reshape(N, K), s16, z16
+
+
+def _quantize_trunc(w, bits, group=64):
+    # mistake: truncation instead of round-to-nearest-even
+    q, s16, z16 = _quantize(w, bits, group)
+    N, K = q.shape
+    wg = np.asarray(w, np.float32).reshape(N, K // group, group)
+    v = wg / s16.astype(np.float32)[..., None] + z16.astype(np.float32)[..., None]
+    q2 = np.clip(np.floor(v), 0, 2 ** bits - 1).astype(np.uint8).reshape(N, K)
+    return q2, s16, z16
+
+
+def _pack_swapped_nibbles(q, bits):
+    if bits == 4:
+        q = np.asarray(q, np.uint8)
+        return (q[:, 1::2] | (q[:, 0::2] << 4)).astype(np.uint8)
+    return _pack(q, bits)
+
+
+def _dequant_plus_zero(q, s16, z16, group=64):
+    # mistake: sign of the zero flipped
+    N, K = q.shape
+    qf = q.astype(np.float32).reshape(N, K // group, group)
+    return ((qf + z16.astype(np.float32)[..., None]) * s16.astype(np.float32)[..., None]).reshape(N, K)
+
+
+def _select_last_index_wins(L, k):
+    # mistake: ties broken towards the higher expert index
+    L = np.asarray(L, np.float32)
+    E = L.shape[1]
+    order = np.argsort(-L[:, ::-1], axis=1, kind="stable")
+    return (E - 1 - order[:, :k]).astype(np.int32)
+
+
+def _weights_full_softmax_no_renorm(L, idx):
+    # mistake: softmax over all experts, not renormalised over the selected
+    L64 = np.asarray(L, np.float64)
+    p = np.exp(L64 - L64.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    return np.take_along_axis(p, idx.astype(np.int64), 1)
+
+
+def _permute_unstable(idx, E, S=0):
+    counts, offsets, srt, inv = _permute(idx, E, S)
+    srt = srt.copy()
+    for e in range(E + S):       # mistake: descending order inside an expert
+        srt[offsets[e]:offsets[e + 1]] = srt[offsets[e]:offsets[e + 1]][::-1]
+    inv = np.empty_like(srt)
+    inv[srt] = np.arange(srt.size)
+    return counts, offsets, srt, inv
+
+
+def _ffn_silu_on_up(x, wg, wu, wd):
+    x = np.asarray(x, np.float64)
+    g = x @ np.asarray(wg, np.float64).T
+    u = x @ np.asarray(wu, np.float64).T
+    return (g * om.silu(u)) @ np.asarray(wd, np.float64).T
+
+
+def _ffn_transposed_down(x, wg, wu, wd):
+    x = np.asarray(x, np.float64)
+    g = x @ np.asarray(wg, np.float64).T
+    u = x @ np.asarray(wu, np.float64).T
+    return (om.silu(g) * u) @ np.asarray(wd, np.float64).T[::-1]   # mistake: rows reversed
+
+
+def _combine_drop_shared(y, w, S=0):
+    # mistake: the shared experts' outputs are left out
+    T, kS, H = y.shape
+    out = np.zeros((T, H))
+    for j in range(kS - S):
+        out += w[:, j:j + 1] * y[:, j, :]
+    return out
+
+
+def _rmsnorm_no_eps(x_bf16, eps=1e-6, gamma=None):
+    x = om.bf16_to_f32(x_bf16).astype(np.float64)
+    return om.f32_to_bf16(x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True)))
+
+
+def _residual_no_block_rounding(x_bf16, moe_out):
+    return om.f32_to_bf16(om.bf16_to_f32(x_bf16).astype(np.float64) + np.asarray(moe_out, np.float64))
+
+
+MUTANTS = [
+    ("quantize", _quantize_zero_from_max, [pins.pin_quant_golden, lambda o: pins.pin_quant_error_bound(o, 4)]),
+    ("quantize", _quantize_trunc, [pins.pin_quant_golden, lambda o: pins.pin_quant_error_bound(o, 6)]),
+    ("pack", _pack_swapped_nibbles, [pins.pin_quant_golden]),
+    ("dequant", _dequant_plus_zero, [pins.pin_quant_golden, lambda o: pins.pin_quant_on_grid(o, 8)]),
+    ("select_topk", _select_last_index_wins, [pins.pin_routing_golden, pins.pin_topk_bruteforce]),
+    ("topk_weights", _weights_full_softmax_no_renorm, [pins.pin_routing_golden, pins.pin_weights]),
+    ("permute", _permute_unstable, [pins.pin_routing_golden, pins.pin_permute_bruteforce]),
+    ("expert_ffn", _ffn_silu_on_up, [pins.pin_layer_bruteforce, pins.pin_layer_special_cases]),
+    ("expert_ffn", _ffn_transposed_down, [pins.pin_layer_bruteforce, pins.pin_on_grid_layer]),
+    ("combine", _combine_drop_shared, [pins.pin_layer_bruteforce, pins.pin_layer_special_cases]),
+    ("rmsnorm_bf16", _rmsnorm_no_eps, [pins.pin_bf16_and_norm]),
+    ("residual_bf16", _residual_no_block_rounding, [pins.pin_bf16_and_norm]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,checks", MUTANTS,
+                         ids=[f"{m[0]}:{m[1].__name__}" for m in MUTANTS])
+def test_pins_catch_planted_mistake(monkeypatch, name, mutant, checks):
+    monkeypatch.setattr(om, name, mutant)
+    monkeypatch.setattr(oracle, name, mutant)
+    for check in checks:
+        assert _fails(check, oracle), f"pin {check} did not catch mutant {mutant.__name__}"
