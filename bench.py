@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantised MoE FFN layer's hot path on one MI355X.
+
+A step is one pass of the whole layer -- router logits, top-k routing,
+permutation, the expert FFN (decode grouped GEMV or prefill grouped GEMM)
+and the weighted combine -- over one batch of synthetic tokens whose inputs
+and weights are already resident in HBM.  The default workload is decode
+with a batch of 8 tokens on the 256-expert + 1-shared-expert, 4-bit layer.
+
+Cache-honest timing: successive steps use different copies of the layer's
+weights (R replicas at distinct addresses, R * layer size >> the 256 MB
+Infinity Cache) and different token batches, the way consecutive layers of
+a model would, so weight bytes come from HBM.  The steps are captured once
+in a HIP graph (one graph holds one step per replica) and replayed.
+
+Prints one JSON line (see the field list in the design notes).
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME:T]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+DEFAULT_WORKLOAD = "moe_h2048_e256_k8_s1_b4:8"
+
+
+def parse_workload(s):
+    name, _, T = s.partition(":")
+    w = synth.get_workload(name)
+    return w, int(T) if T else w.tokens[-1]
+
+
+def expert_bytes(w, bits):
+    """Algorithmic bytes of one expert: three I x H matrices of codes plus an
+    fp16 scale and zero per 64 weights."""
+    return 3 * w.I * w.H * (bits / 8 + 4 / 64)
+
+
+class Step:
+    """Preallocated buffers and the ctypes calls of one layer step."""
+
+    def __init__(self, bq, layer, wr, bias, x, T, ws):
+        import torch
+        self.bq, self.L, self.T = bq, layer, T
+        self.desc = layer.desc()
+        dev = x.device
+        E, S, k, H = layer.E, layer.S, layer.k, layer.H
+        A = T * (k + S)
+        self.x, self.wr, self.bias, self.ws = x, wr, bias, ws
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E + S, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
+        self.sorted = torch.empty(A, dtype=torch.int32, device=dev)
+        self.inverse = torch.empty(A, dtype=torch.int32, device=dev)
+        self.active = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
+        self.prefill = T > bq.DECODE_MAX_T
+        self.y = torch.empty((A, H), dtype=torch.bfloat16 if self.prefill else torch.float32, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def route_permute(self, s):
+        lib, p, L = self.bq.lib(), self.bq._p, self.L
+        self.bq._check(lib.moe_route_topk(p(self.x), p(self.wr), p(self.bias), self.T, L.H, L.E, L.k, p(self.logits),
+                                          p(self.idx), p(self.w), p(self.ws), self.ws.numel(), s))
+        self.bq._check(lib.moe_permute(p(self.idx), self.T, L.k, L.E, L.S, p(self.counts), p(self.offsets),
+                                       p(self.sorted), p(self.inverse), p(self.active), p(self.ws), self.ws.numel(), s))
+
+    def experts(self, s):
+        lib, p = self.bq.lib(), self.bq._p
+        d = ctypes.byref(self.desc)
+        if self.prefill:
+            self.bq._check(lib.moe_qgemm_prefill(d, p(self.x), self.T, p(self.counts), p(self.offsets),
+                                                 p(self.sorted), p(self.y), p(self.ws), self.ws.numel(), s))
+        else:
+            self.bq._check(lib.moe_qgemv_decode(d, p(self.x), self.T, p(self.offsets), p(self.sorted),
+                                                p(self.active), p(self.y), p(self.ws), self.ws.numel(), s))
+
+    def combine(self, s):
+        lib, p, L = self.bq.lib(), self.bq._p, self.L
+        self.bq._check(lib.moe_combine(p(self.y), 1 if self.prefill else 0, p(self.w), None, self.T, L.k, L.S, L.H,
+                                       p(self.out), s))
+
+    def run(self, s):
+        self.route_permute(s)
+        self.experts(s)
+        self.combine(s)
+
+
+def build_replicas(bq, w, R, device):
+    """Quantise the layer once on the device, then copy it to R - 1 more
+    places so consecutive steps never find their weights in a cache."""
+    import torch
+    from tests.gpu_util import gpu_layer
+    base = gpu_layer(w, device=device)
+    reps = [base]
+    for _ in range(R - 1):
+        cp = lambda qw: bq.QWeight(qw.q.clone(), qw.sz.clone(), qw.bits)
+        reps.append(bq.QuantLayer(base.H, base.I, base.E, base.S, base.k, cp(base.gate), cp(base.up), cp(base.down)))
+    torch.cuda.synchronize()
+    return reps
+
+
+def cpu_baseline(w, T, budget_s=20.0):
+    """The oracle as it stands, timed on this host's cores on a bounded
+    sample: whole-layer forwards of the same workload (routing, permutation,
+    dequantisation of the touched experts, FFN, combine), one batch at a
+    time until ~budget_s of CPU work.  Quantisation of the weights is the
+    oracle's load step and is not timed."""
+    import oracle
+    from tests.gpu_util import LazyExperts
+    from threadpoolctl import threadpool_info
+    wr = synth.router_weight_bf16(w)
+    bias = synth.router_bias(w)
+    experts = LazyExperts(w)
+    n_tok, t_total, n_runs = 0, 0.0, 0
+    b = 0
+    while t_total < budget_s and n_runs < 64:
+        x = synth.activations_bf16(w, T, batch=1000 + b)
+        L = oracle.router_logits(x, wr, bias)
+        for e in set(oracle.select_topk(L, w.k).reshape(-1).tolist()) | set(range(w.E, w.E + w.S)):
+            experts[e]            # quantise (load step, untimed)
+        layer = oracle.QuantLayer(w.H, w.I, w.E, w.k, w.S, experts)   # fresh dequant cache
+        t0 = time.perf_counter()
+        oracle.moe_layer(layer, x, wr, bias)
+        t_total += time.perf_counter() - t0
+        n_tok += T
+        n_runs += 1
+        b += 1
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"value": n_tok / t_total, "unit": "tokens/s", "cores": max(blas + [1]),
+            "kind": "oracle",
+            "sample": f"{n_runs} whole-layer forwards of {T} tokens ({n_tok} tokens, {t_total:.1f} s); "
+                      f"dequantisation of the routed experts included, weight quantisation excluded; "
+                      f"NumPy elementwise work single-threaded, BLAS threads as given in cores; "
+                      f"host has {len(os.sched_getaffinity(0))} usable cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--replicas", type=int, default=0, help="weight copies (0: enough for >= 2 GB)")
+    ap.add_argument("--batches", type=int, default=16)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU sharding is described in the design notes, not built)"}))
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_expert_amd as bq
+    from tests.gpu_util import bf16_tensor
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w, T = parse_workload(a.workload)
+    bits = w.bits
+    layer_bytes = expert_bytes(w, bits) * w.n_mats
+    R = a.replicas or max(2, min(16, math.ceil(2e9 / layer_bytes)))
+    t0 = time.time()
+    reps = build_replicas(bq, w, R, dev)
+    wr = bf16_tensor(synth.router_weight_bf16(w))
+    bias = synth.router_bias(w)
+    bias_t = None if bias is None else torch.from_numpy(bias).to(dev)
+    NB = a.batches
+    xs = [bf16_tensor(synth.activations_bf16(w, T, batch=b)) for b in range(NB)]
+    ws = [reps[0].workspace(T, device=dev) for _ in range(R)]
+    G = max(R, NB)    # steps per graph: every replica and batch once
+    steps = [Step(bq, reps[i % R], wr, bias_t, xs[i % NB], T, ws[i % R]) for i in range(G)]
+    print(f"# setup {time.time() - t0:.1f}s: {w.name} T={T} replicas={R} batches={NB} graph_steps={G}",
+          file=sys.stderr, flush=True)
+
+    s = torch.cuda.Stream()
+    sp = ctypes.c_void_p(s.cuda_stream)
+    with torch.cuda.stream(s):
+        for st in steps:          # eager warm pass (also loads code objects)
+            st.run(sp)
+    torch.cuda.synchronize()
+
+    # realised distinct experts per step -> algorithmic bytes of the expert kernels
+    distinct = [int((st.counts > 0).sum().item()) for st in steps]
+    alg_expert_bytes = float(np.mean(distinct)) * expert_bytes(w, bits) + T * w.H * 2
+    alg_layer_bytes = alg_expert_bytes + w.E * w.H * 2 + T * w.H * 2
+    flops = T * (w.k + w.S) * 6 * w.I * w.H + 2 * T * w.E * w.H
+
+    graph = None
+    if not a.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            for st in steps:
+                st.run(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+
+    def run_steps(n):
+        with torch.cuda.stream(s):
+            if graph is not None:
+                for _ in range(n // G):
+                    graph.replay()
+                for i in range(n % G):
+                    steps[i].run(sp)
+            else:
+                for i in range(n):
+                    steps[i % G].run(sp)
+
+    run_steps(a.warmup)
+    torch.cuda.synchronize()
+    K = max(G, (a.steps // G) * G)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(s)
+    run_steps(K)
+    ev1.record(s)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / K
+
+    # dominant kernel(s): the expert FFN call, timed alone with events on its stream
+    kev = []
+    with torch.cuda.stream(s):
+        for i in range(2 * G):
+            st = steps[i % G]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            st.route_permute(sp)
+            e0.record(s)
+            st.experts(sp)
+            e1.record(s)
+            st.combine(sp)
+            kev.append((e0, e1))
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in kev]))
+
+    prefill = T > bq.DECODE_MAX_T
+    if prefill:
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "moe_qgemm_prefill (gate/up + down grouped GEMM kernels)"}
+    else:
+        achieved = alg_expert_bytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "moe_qgemv_decode (gate/up + down grouped GEMV kernels)",
+                "alg_bytes_per_launch": round(alg_expert_bytes), "kernel_us": round(kern_ms * 1e3, 3)}
+
+    res = {
+        "metric": "MoE-layer tokens/s",
+        "value": round(T * K / (total_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"u{bits} codes x bf16 -> fp32" if not prefill else f"u{bits} codes -> bf16 MFMA, fp32 acc",
+        "data": "synthetic (seeded N(0,0.02) weights quantised on the GPU; N(0,1) bf16 tokens)",
+        "config": {"workload": w.name, "tokens": T, "hidden": w.H, "intermediate": w.I, "experts": w.E,
+                   "top_k": w.k, "shared": w.S, "bits": bits, "weight_replicas": R, "token_batches": NB,
+                   "hip_graph": graph is not None, "distinct_experts_per_step": round(float(np.mean(distinct)), 2),
+                   "layer_alg_bytes": round(alg_layer_bytes), "layer_GBps": round(alg_layer_bytes / (ms_per_step * 1e-3) / 1e9, 1)},
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, T, a.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

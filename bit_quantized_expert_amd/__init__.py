@@ -1,0 +1,319 @@
+"""Python binding of libmoeq: the forward pass of a group-quantised MoE FFN
+layer on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the layer runs in the HIP kernels
+of ``libmoeq.so`` (built by ``python -m bit_quantized_expert_amd.build``);
+PyTorch supplies device memory and the current stream.  Importing this
+package without the built library raises -- there is no fallback.
+
+Functions carry the names of the C entry points (see ``include/moeq.h``):
+``moe_quantize``, ``moe_unpack``, ``moe_route_topk``, ``moe_permute``,
+``moe_qgemv_decode``, ``moe_qgemm_prefill``, ``moe_combine``,
+``moe_rmsnorm``, ``moe_workspace_bytes``, ``moe_read_status``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoeq.so")
+
+MOEQ_Y_F32, MOEQ_Y_BF16 = 0, 1
+GROUP = 64
+
+_ERRORS = {-1: "invalid argument", -2: "unsupported", -3: "misaligned", -4: "workspace", -5: "HIP error"}
+
+
+class MoeqError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libmoeq error {code} ({_ERRORS.get(code, '?')}): {msg}")
+        self.code = code
+
+
+class _QWeight(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("sz", ctypes.c_void_p), ("bits", ctypes.c_int)]
+
+
+class _LayerDesc(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int), ("I", ctypes.c_int), ("E", ctypes.c_int), ("S", ctypes.c_int),
+                ("k", ctypes.c_int), ("gate", _QWeight), ("up", _QWeight), ("down", _QWeight)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoeq.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_quantized_expert_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, L64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_size_t
+        sig = {
+            "moe_workspace_bytes": (SZ, [P, I]),
+            "moe_last_error": (ctypes.c_char_p, []),
+            "moe_quantize": (I, [P, L64, I, I, P, P, P]),
+            "moe_unpack": (I, [P, L64, I, I, P, P]),
+            "moe_route_topk": (I, [P, P, P, I, I, I, I, P, P, P, P, SZ, P]),
+            "moe_permute": (I, [P, I, I, I, I, P, P, P, P, P, P, SZ, P]),
+            "moe_qgemv_decode": (I, [P, P, I, P, P, P, P, P, SZ, P]),
+            "moe_qgemm_prefill": (I, [P, P, I, P, P, P, P, P, SZ, P]),
+            "moe_combine": (I, [P, I, P, P, I, I, I, I, P, P]),
+            "moe_rmsnorm": (I, [P, P, I, I, ctypes.c_float, P, P]),
+            "moe_read_status": (I, [P, SZ, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+lib()   # fail at import time if the library is missing
+
+
+def _check(rc):
+    if rc != 0:
+        raise MoeqError(rc, lib().moe_last_error().decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtype=None, name="tensor"):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+# --------------------------------------------------------------------------
+# quantised weights
+# --------------------------------------------------------------------------
+@dataclass
+class QWeight:
+    """One projection of all experts: q [n_mats, N, K*bits/8] uint8 and
+    sz [n_mats, N, K/64] int32 (fp16 scale | fp16 zero << 16)."""
+    q: torch.Tensor
+    sz: torch.Tensor
+    bits: int
+
+    def desc(self):
+        return _QWeight(self.q.data_ptr(), self.sz.data_ptr(), self.bits)
+
+
+def moe_quantize(w: torch.Tensor, bits: int, out: Optional[QWeight] = None, stream=None) -> QWeight:
+    """Quantise fp32 weights [..., N, K] (device) along K in groups of 64."""
+    _dev(w, torch.float32, "w")
+    K = w.shape[-1]
+    rows = w.numel() // K
+    if out is None:
+        q = torch.empty(w.shape[:-1] + (K * bits // 8,), dtype=torch.uint8, device=w.device)
+        sz = torch.empty(w.shape[:-1] + (K // GROUP,), dtype=torch.int32, device=w.device)
+        out = QWeight(q, sz, bits)
+    _check(lib().moe_quantize(_p(w), rows, K, bits, _p(out.q), _p(out.sz), _stream(stream)))
+    return out
+
+
+def moe_unpack(q: torch.Tensor, K: int, bits: int, stream=None) -> torch.Tensor:
+    _dev(q, torch.uint8, "q")
+    rows = q.numel() // (K * bits // 8)
+    codes = torch.empty(q.shape[:-1] + (K,), dtype=torch.uint8, device=q.device)
+    _check(lib().moe_unpack(_p(q), rows, K, bits, _p(codes), _stream(stream)))
+    return codes
+
+
+@dataclass
+class QuantLayer:
+    """Quantised expert weights of one MoE layer resident in HBM."""
+    H: int
+    I: int
+    E: int
+    S: int
+    k: int
+    gate: QWeight
+    up: QWeight
+    down: QWeight
+
+    def desc(self) -> _LayerDesc:
+        return _LayerDesc(self.H, self.I, self.E, self.S, self.k, self.gate.desc(), self.up.desc(),
+                          self.down.desc())
+
+    def workspace_bytes(self, T_max: int) -> int:
+        return moe_workspace_bytes(self, T_max)
+
+    def workspace(self, T_max: int, device="cuda") -> torch.Tensor:
+        return torch.empty(max(256, self.workspace_bytes(T_max)), dtype=torch.uint8, device=device)
+
+
+def moe_workspace_bytes(layer: QuantLayer, T_max: int) -> int:
+    d = layer.desc()
+    n = lib().moe_workspace_bytes(ctypes.byref(d), T_max)
+    if n == 0:
+        raise MoeqError(-1, lib().moe_last_error().decode())
+    return n
+
+
+# --------------------------------------------------------------------------
+# the five steps
+# --------------------------------------------------------------------------
+def moe_route_topk(x: Optional[torch.Tensor], w_router: Optional[torch.Tensor], bias: Optional[torch.Tensor],
+                   E: int, k: int, logits: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                   stream=None):
+    """Router logits (or given fp32 logits when w_router is None), top-k ids
+    and renormalised weights.  Returns (logits [T,E] f32, idx [T,k] i32,
+    w [T,k] f32)."""
+    if w_router is not None:
+        _dev(x, torch.bfloat16, "x")
+        _dev(w_router, torch.bfloat16, "w_router")
+        T, H = x.shape
+        if logits is None:
+            logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    else:
+        _dev(logits, torch.float32, "logits")
+        T, H = logits.shape[0], 0
+    if bias is not None:
+        _dev(bias, torch.float32, "bias")
+    dev = logits.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check(lib().moe_route_topk(_p(x) if w_router is not None else None, _p(w_router), _p(bias), T, H, E, k,
+                                _p(logits), _p(idx), _p(w), _p(ws), 0 if ws is None else ws.numel(),
+                                _stream(stream)))
+    return logits, idx, w
+
+
+def permute_ws_bytes(A: int, n_experts: int) -> int:
+    nblk = (A + 1023) // 1024
+    return 256 + ((nblk * n_experts * 4 + 255) // 256) * 256
+
+
+def moe_permute(idx: torch.Tensor, E: int, S: int, ws: Optional[torch.Tensor] = None, stream=None):
+    """Group assignments by expert.  Returns (counts, offsets, sorted, inverse,
+    active) int32 device tensors."""
+    _dev(idx, torch.int32, "topk_idx")
+    T, k = idx.shape
+    A = T * (k + S)
+    dev = idx.device
+    counts = torch.empty(E + S, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
+    sorted_a = torch.empty(max(A, 1), dtype=torch.int32, device=dev)
+    inverse = torch.empty(max(A, 1), dtype=torch.int32, device=dev)
+    active = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(permute_ws_bytes(A, E + S), dtype=torch.uint8, device=dev)
+    _check(lib().moe_permute(_p(idx), T, k, E, S, _p(counts), _p(offsets), _p(sorted_a), _p(inverse), _p(active),
+                             _p(ws), ws.numel(), _stream(stream)))
+    return counts, offsets, sorted_a[:A], inverse[:A], active
+
+
+def moe_qgemv_decode(layer: QuantLayer, x: torch.Tensor, offsets, sorted_a, active, ws: torch.Tensor,
+                     y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _dev(x, torch.bfloat16, "x")
+    T = x.shape[0]
+    A = T * (layer.k + layer.S)
+    if y is None:
+        y = torch.empty((A, layer.H), dtype=torch.float32, device=x.device)
+    d = layer.desc()
+    _check(lib().moe_qgemv_decode(ctypes.byref(d), _p(x), T, _p(offsets), _p(sorted_a), _p(active), _p(y),
+                                  _p(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_qgemm_prefill(layer: QuantLayer, x: torch.Tensor, counts, offsets, sorted_a, ws: torch.Tensor,
+                      y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _dev(x, torch.bfloat16, "x")
+    T = x.shape[0]
+    A = T * (layer.k + layer.S)
+    if y is None:
+        y = torch.empty((A, layer.H), dtype=torch.bfloat16, device=x.device)
+    d = layer.desc()
+    _check(lib().moe_qgemm_prefill(ctypes.byref(d), _p(x), T, _p(counts), _p(offsets), _p(sorted_a), _p(y),
+                                   _p(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, k: int, S: int, residual: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _dev(y, None, "y")
+    dt = {torch.float32: MOEQ_Y_F32, torch.bfloat16: MOEQ_Y_BF16}[y.dtype]
+    T = topk_w.shape[0]
+    H = y.shape[-1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check(lib().moe_combine(_p(y), dt, _p(topk_w), _p(residual), T, k, S, H, _p(out), _stream(stream)))
+    return out
+
+
+def moe_rmsnorm(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _dev(x, torch.bfloat16, "x")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().moe_rmsnorm(_p(x), _p(gamma), T, H, eps, _p(out), _stream(stream)))
+    return out
+
+
+def moe_read_status(ws: torch.Tensor, stream=None) -> int:
+    n = ctypes.c_int(0)
+    _check(lib().moe_read_status(_p(ws), ws.numel(), ctypes.byref(n), _stream(stream)))
+    return n.value
+
+
+# --------------------------------------------------------------------------
+# the whole layer
+# --------------------------------------------------------------------------
+DECODE_MAX_T = 64
+
+
+class MoELayer:
+    """A quantised MoE FFN layer with its router, run by the five calls.
+
+    ``forward(x)`` picks the decode path (grouped GEMV) for T <= 64 tokens
+    and the prefill path (grouped GEMM) above -- separate code paths for the
+    two phases (Krasis update, "Overview")."""
+
+    def __init__(self, qlayer: QuantLayer, w_router: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                 T_max: int = 1):
+        self.q = qlayer
+        self.w_router = w_router
+        self.bias = bias
+        self.T_max = 0
+        self.ws = None
+        self.reserve(T_max)
+
+    def reserve(self, T_max: int):
+        if T_max > self.T_max:
+            self.ws = self.q.workspace(T_max, device=self.w_router.device)
+            self.T_max = T_max
+
+    def forward(self, x: torch.Tensor, residual: Optional[torch.Tensor] = None, stream=None, prefill=None):
+        T = x.shape[0]
+        self.reserve(T)
+        q = self.q
+        logits, idx, w = moe_route_topk(x, self.w_router, self.bias, q.E, q.k, ws=self.ws, stream=stream)
+        counts, offsets, sorted_a, inverse, active = moe_permute(idx, q.E, q.S, ws=self.ws, stream=stream)
+        use_prefill = T > DECODE_MAX_T if prefill is None else prefill
+        if use_prefill:
+            y = moe_qgemm_prefill(q, x, counts, offsets, sorted_a, self.ws, stream=stream)
+        else:
+            y = moe_qgemv_decode(q, x, offsets, sorted_a, active, self.ws, stream=stream)
+        out = moe_combine(y, w, q.k, q.S, residual=residual, stream=stream)
+        return dict(out=out, logits=logits, idx=idx, w=w, counts=counts, offsets=offsets, sorted=sorted_a,
+                    inverse=inverse, active=active, y=y)

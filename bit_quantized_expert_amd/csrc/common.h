@@ -1,0 +1,99 @@
+// Internal helpers shared by the libmoeq translation units: error reporting,
+// workspace layout and small device functions (bf16/fp16 conversion, wave
+// reductions).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "moeq.h"
+
+// --------------------------------------------------------------------------
+// host side: error reporting and validation
+// --------------------------------------------------------------------------
+namespace moeq {
+
+int set_error(int code, const char* fmt, ...);
+int check_launch(const char* what);   // hipGetLastError after a launch
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool bits_ok(int b) { return b == 4 || b == 6 || b == 8; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// bytes of one packed row of K codes
+__host__ __device__ inline size_t row_bytes(int K, int bits) { return (size_t)K * bits / 8; }
+
+// Workspace layout for a layer and a maximum batch.  All regions are
+// 256-byte aligned; `total` is what moe_workspace_bytes reports.
+struct WsLayout {
+  size_t status;     // int32 status words (n_bad ids ...)
+  size_t perm_hist;  // int32 [perm_blocks][E+S] block histograms
+  size_t h;          // decode: fp32 [A][I]; prefill: bf16 [A][I]
+  size_t sched;      // prefill: int32 tile schedule
+  size_t total;
+};
+constexpr int kPermBlock = 1024;          // assignments per permute block
+constexpr int kPrefillBM = 128;           // prefill token tile
+int perm_blocks(long A);
+long prefill_max_tiles(long A, int nexp);
+WsLayout ws_layout(int H, int I, int E, int S, int k, int T_max);
+int validate_layer(const moe_layer_desc* L);
+
+}  // namespace moeq
+
+// --------------------------------------------------------------------------
+// device side
+// --------------------------------------------------------------------------
+#define MOEQ_DEV __device__ __forceinline__
+
+MOEQ_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+MOEQ_DEV uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+MOEQ_DEV float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+MOEQ_DEV uint32_t f32_to_f16_bits(float f) {   // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <int CTRL>
+MOEQ_DEV float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of `span` lanes (span in {1,2,4,...,64}); every lane
+// of a group ends with the group's sum.  DPP within a row of 16 lanes,
+// ds_swizzle / bpermute across rows.
+MOEQ_DEV float group_sum(float v, int span) {
+  if (span >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  if (span >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  if (span >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
+  if (span >= 16) v += dpp_f<0x140>(v);  // row_mirror
+  if (span >= 32) v += __shfl_xor(v, 16);
+  if (span >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+MOEQ_DEV float wave_sum(float v) { return group_sum(v, 64); }
+
+MOEQ_DEV float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+MOEQ_DEV float wave_min(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+
+MOEQ_DEV float silu_f32(float g) { return g / (1.0f + __expf(-g)); }

@@ -1,0 +1,108 @@
+// Device view of the packed weight format: how one lane loads a "chunk" of a
+// packed row and turns its codes into bf16 pairs for v_dot2_f32_bf16.
+//
+// A chunk is the unit one lane loads with one vector load:
+//   4-bit: 16 bytes = 32 codes (dwordx4); a 64-group spans 2 chunks
+//   6-bit: 12 bytes = 16 codes (dwordx3); a 64-group spans 4 chunks
+//   8-bit: 16 bytes = 16 codes (dwordx4); a 64-group spans 4 chunks
+// Codes become bf16 values exactly: 4- and 6-bit codes are OR-ed into the
+// mantissa of bf16 128.0 (giving 128 + q, "OFFSET" = 128, one AND-OR per two
+// codes); 8-bit codes are converted through fp32 (OFFSET = 0).  The pair
+// order inside a chunk is fixed per bit width (pair_code); activations are
+// arranged in the same order so each dot2 multiplies matching elements.
+#pragma once
+#include "common.h"
+
+template <int BITS> struct Fmt;
+template <> struct Fmt<4> {
+  static constexpr int BYTES = 16, CODES = 32, PAIRS = 16, DW = 4, CHUNKS_PER_GROUP = 2;
+  static constexpr float OFFSET = 128.0f;
+};
+template <> struct Fmt<6> {
+  static constexpr int BYTES = 12, CODES = 16, PAIRS = 8, DW = 3, CHUNKS_PER_GROUP = 4;
+  static constexpr float OFFSET = 128.0f;
+};
+template <> struct Fmt<8> {
+  static constexpr int BYTES = 16, CODES = 16, PAIRS = 8, DW = 4, CHUNKS_PER_GROUP = 4;
+  static constexpr float OFFSET = 0.0f;
+};
+
+// Code index (within the chunk) in the low (half=0) or high (half=1) bf16 of pair p.
+template <int BITS> MOEQ_DEV constexpr int pair_code(int p, int half);
+template <> MOEQ_DEV constexpr int pair_code<4>(int p, int half) {
+  return 8 * (p >> 2) + (p & 3) + 4 * half;          // nibble i and i+4 of dword p/4
+}
+template <> MOEQ_DEV constexpr int pair_code<6>(int p, int half) {
+  // derived from the 6-bit field positions: see chunk_pairs<6>
+  constexpr int lo[8] = {0, 1, 5, 6, 10, 11, 2, 12};
+  constexpr int hi[8] = {3, 4, 8, 9, 13, 14, 7, 15};
+  return half ? hi[p] : lo[p];
+}
+template <> MOEQ_DEV constexpr int pair_code<8>(int p, int half) { return 2 * p + half; }
+
+typedef uint32_t moeq_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t moeq_u32x3 __attribute__((ext_vector_type(3)));
+
+template <int BITS>
+MOEQ_DEV void load_chunk(const uint8_t* __restrict__ p, uint32_t (&d)[Fmt<BITS>::DW]) {
+  if constexpr (Fmt<BITS>::DW == 4) {
+    moeq_u32x4 v = *reinterpret_cast<const moeq_u32x4*>(p);
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  } else {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    d[0] = q[0];
+    d[1] = q[1];
+    d[2] = q[2];
+  }
+}
+
+MOEQ_DEV uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) { return (a & m) | o; }
+
+template <int BITS>
+MOEQ_DEV void chunk_pairs(const uint32_t (&d)[Fmt<BITS>::DW], uint32_t (&P)[Fmt<BITS>::PAIRS]) {
+  constexpr uint32_t M = 0x43004300u;   // bf16 128.0 in both halves
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = d[j];
+      P[4 * j + 0] = and_or(w, 0x000F000Fu, M);
+      P[4 * j + 1] = and_or(w >> 4, 0x000F000Fu, M);
+      P[4 * j + 2] = and_or(w >> 8, 0x000F000Fu, M);
+      P[4 * j + 3] = and_or(w >> 12, 0x000F000Fu, M);
+    }
+  } else if constexpr (BITS == 6) {
+    // code c of the chunk sits at bits 6c..6c+5 of the 96-bit little-endian
+    // chunk.  e0/e1/e2 are 32-bit windows starting at codes 0, 5 and 10.
+    uint32_t e0 = d[0];
+    uint32_t e1 = __builtin_amdgcn_alignbit(d[1], d[0], 30);
+    uint32_t e2 = __builtin_amdgcn_alignbit(d[2], d[1], 28);
+    const uint32_t e[3] = {e0, e1, e2};
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      // codes at bits 0 and 18 -> halves 0 and 16
+      P[2 * i + 0] = and_or(e[i] >> 2, 0x003F0000u, and_or(e[i], 0x3Fu, M));
+      // codes at bits 6 and 24
+      P[2 * i + 1] = and_or(e[i] >> 8, 0x003F0000u, and_or(e[i] >> 6, 0x3Fu, M));
+    }
+    P[6] = and_or(e1 << 4, 0x003F0000u, and_or(e0 >> 12, 0x3Fu, M));     // codes 2, 7
+    P[7] = and_or(d[2] >> 10, 0x003F0000u, and_or(e2 >> 12, 0x3Fu, M));  // codes 12, 15
+  } else {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = d[j];
+      bf16x2 a = {(__bf16)(float)(w & 0xFFu), (__bf16)(float)((w >> 8) & 0xFFu)};
+      bf16x2 b = {(__bf16)(float)((w >> 16) & 0xFFu), (__bf16)(float)(w >> 24)};
+      P[2 * j + 0] = __builtin_bit_cast(uint32_t, a);
+      P[2 * j + 1] = __builtin_bit_cast(uint32_t, b);
+    }
+  }
+}
+
+typedef __bf16 moeq_bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + lo(a)*lo(b) + hi(a)*hi(b), fp32 accumulate (v_dot2_f32_bf16)
+MOEQ_DEV float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(moeq_bf16x2, a),
+                                         __builtin_bit_cast(moeq_bf16x2, b), acc, false);
+}

@@ -1,0 +1,115 @@
+// Group quantisation of fp32 weights into the packed format, and the unpack
+// test entry that runs the decode kernels' in-register unpacking.
+#include "format.h"
+
+using namespace moeq;
+
+// One wavefront per 64-value group: lane l holds value l of the group.
+// Min and max come from wave reductions; the code of every lane is then
+// packed by shuffles.  fp32 arithmetic with IEEE division and rint (ties to
+// even) so the codes equal any other IEEE fp32 evaluation of the same
+// formula bit for bit.
+template <int BITS>
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, long ngroups,
+                                                       uint8_t* __restrict__ q, uint32_t* __restrict__ sz) {
+  const int lane = threadIdx.x & 63;
+  const long stride = (long)gridDim.x * 4;
+  for (long g = (long)blockIdx.x * 4 + (threadIdx.x >> 6); g < ngroups; g += stride) {
+    const float v = w[g * 64 + lane];
+    const float mn = wave_min(v);
+    const float mx = wave_max(v);
+    const float qmax = (float)((1 << BITS) - 1);
+    const float s = (mx - mn) / qmax;
+    uint32_t s16 = f32_to_f16_bits(s);
+    const bool degenerate = (s16 & 0x7FFFu) == 0;
+    if (degenerate) s16 = 0x3C00u;                       // fp16 1.0
+    const float sf = f16_bits_to_f32(s16);
+    const uint32_t z16 = f32_to_f16_bits(-mn / sf);
+    const float zf = f16_bits_to_f32(z16);
+    float r = rintf(v / sf + zf);
+    r = fminf(fmaxf(r, 0.0f), qmax);
+    const uint32_t code = degenerate ? 0u : (uint32_t)r;
+    uint8_t* qg = q + g * (64 * BITS / 8);
+    if constexpr (BITS == 4) {
+      const uint32_t lo = __shfl(code, (2 * lane) & 63);
+      const uint32_t hi = __shfl(code, (2 * lane + 1) & 63);
+      if (lane < 32) qg[lane] = (uint8_t)(lo | (hi << 4));
+    } else if constexpr (BITS == 6) {
+      const uint32_t c0 = __shfl(code, (4 * lane + 0) & 63);
+      const uint32_t c1 = __shfl(code, (4 * lane + 1) & 63);
+      const uint32_t c2 = __shfl(code, (4 * lane + 2) & 63);
+      const uint32_t c3 = __shfl(code, (4 * lane + 3) & 63);
+      const uint32_t word = c0 | (c1 << 6) | (c2 << 12) | (c3 << 18);
+      if (lane < 16) {
+        qg[3 * lane + 0] = (uint8_t)(word & 0xFF);
+        qg[3 * lane + 1] = (uint8_t)((word >> 8) & 0xFF);
+        qg[3 * lane + 2] = (uint8_t)((word >> 16) & 0xFF);
+      }
+    } else {
+      qg[lane] = (uint8_t)code;
+    }
+    if (lane == 0) sz[g] = s16 | (z16 << 16);
+  }
+}
+
+// One thread per chunk: load, turn into bf16 pairs exactly as the decode
+// kernels do, and write the codes back in natural order.
+template <int BITS>
+__global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__ q, long nchunks,
+                                                     uint8_t* __restrict__ codes) {
+  using F = Fmt<BITS>;
+  for (long c = (long)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += (long)gridDim.x * blockDim.x) {
+    uint32_t d[F::DW];
+    load_chunk<BITS>(q + c * F::BYTES, d);
+    uint32_t P[F::PAIRS];
+    chunk_pairs<BITS>(d, P);
+    uint8_t* out = codes + c * F::CODES;
+#pragma unroll
+    for (int p = 0; p < F::PAIRS; ++p) {
+      out[pair_code<BITS>(p, 0)] = (uint8_t)(bf16_bits_to_f32(P[p] & 0xFFFFu) - F::OFFSET);
+      out[pair_code<BITS>(p, 1)] = (uint8_t)(bf16_bits_to_f32(P[p] >> 16) - F::OFFSET);
+    }
+  }
+}
+
+static int grid_for(long work, int per_block) {
+  long b = (work + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > 65536) b = 65536;
+  return (int)b;
+}
+
+extern "C" int moe_quantize(const float* w, long rows, int K, int bits, uint8_t* q, uint32_t* sz,
+                            hipStream_t stream) {
+  if (!w || !q || !sz) return set_error(MOEQ_ERR_INVALID_ARG, "moe_quantize: NULL pointer");
+  if (rows < 0 || K <= 0) return set_error(MOEQ_ERR_INVALID_ARG, "moe_quantize: rows=%ld K=%d", rows, K);
+  if (!bits_ok(bits)) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_quantize: bits=%d not in {4,6,8}", bits);
+  if (K % MOEQ_GROUP) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_quantize: K=%d not a multiple of 64", K);
+  if (!aligned16(w) || !aligned16(q)) return set_error(MOEQ_ERR_MISALIGNED, "moe_quantize: w and q must be 16-byte aligned");
+  if (((uintptr_t)sz & 3u) != 0) return set_error(MOEQ_ERR_MISALIGNED, "moe_quantize: sz must be 4-byte aligned");
+  const long ngroups = rows * (K / MOEQ_GROUP);
+  if (ngroups == 0) return MOEQ_OK;
+  const int grid = grid_for(ngroups, 4);
+  switch (bits) {
+    case 4: quantize_kernel<4><<<grid, 256, 0, stream>>>(w, ngroups, q, sz); break;
+    case 6: quantize_kernel<6><<<grid, 256, 0, stream>>>(w, ngroups, q, sz); break;
+    default: quantize_kernel<8><<<grid, 256, 0, stream>>>(w, ngroups, q, sz); break;
+  }
+  return check_launch("moe_quantize");
+}
+
+extern "C" int moe_unpack(const uint8_t* q, long rows, int K, int bits, uint8_t* codes, hipStream_t stream) {
+  if (!q || !codes) return set_error(MOEQ_ERR_INVALID_ARG, "moe_unpack: NULL pointer");
+  if (rows < 0 || K <= 0) return set_error(MOEQ_ERR_INVALID_ARG, "moe_unpack: rows=%ld K=%d", rows, K);
+  if (!bits_ok(bits)) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_unpack: bits=%d not in {4,6,8}", bits);
+  if (K % MOEQ_GROUP) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_unpack: K=%d not a multiple of 64", K);
+  if (!aligned16(q)) return set_error(MOEQ_ERR_MISALIGNED, "moe_unpack: q must be 16-byte aligned");
+  const long ncodes = rows * (long)K;
+  if (ncodes == 0) return MOEQ_OK;
+  switch (bits) {
+    case 4: unpack_kernel<4><<<grid_for(ncodes / 32, 256), 256, 0, stream>>>(q, ncodes / 32, codes); break;
+    case 6: unpack_kernel<6><<<grid_for(ncodes / 16, 256), 256, 0, stream>>>(q, ncodes / 16, codes); break;
+    default: unpack_kernel<8><<<grid_for(ncodes / 16, 256), 256, 0, stream>>>(q, ncodes / 16, codes); break;
+  }
+  return check_launch("moe_unpack");
+}

@@ -1,0 +1,195 @@
+/*
+ * moeq.h -- C ABI of libmoeq, the forward pass of a Mixture-of-Experts FFN
+ * layer whose expert weights are low-bit group-quantised, on AMD MI355X
+ * (gfx950).
+ *
+ * The layer: router logits -> top-k routing with renormalised softmax
+ * weights -> grouping of (token, expert) assignments by expert -> per expert
+ * a SwiGLU FFN, h = silu(Wg x) * (Wu x), y = Wd h, with weights dequantised
+ * on the fly as (q - z) * s -> routing-weighted combine.  Prefill and decode
+ * are separate code paths (Krasis update, "Overview"): decode is a grouped
+ * GEMV over only the routed experts' weights, prefill a grouped GEMM over
+ * expert-sorted tokens (Qwen-tin, "Memory layout and performance": a long
+ * prompt touches nearly every expert).  Expert weights are HQQ-style 4-, 6-
+ * or 8-bit codes (Krasis update, "Latest results (v1.0)").
+ *
+ * Conventions for every entry point
+ *   - Pointers marked "device" point to GPU memory that the caller allocated
+ *     and owns; the library keeps no pointer after the call returns.  It
+ *     allocates no memory: scratch space comes in through a caller-owned
+ *     workspace whose size moe_workspace_bytes() reports.
+ *   - All GPU work is enqueued on the caller's stream; no call synchronises
+ *     or copies data to the host, except moe_read_status().
+ *   - bf16 and fp16 values travel as uint16_t bit patterns.
+ *   - Arguments are validated on the host before anything is enqueued.  On
+ *     error nothing is enqueued, a negative MOEQ_ERR_* code is returned and
+ *     moe_last_error() (thread-local) describes the problem.  No exception
+ *     crosses the ABI and the library never aborts the process.
+ *   - Calls that share a workspace must not run concurrently.
+ *   - Weights/activations pointers (q, sz, x) must be 16-byte aligned.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+#define MOEQ_OK               0
+#define MOEQ_ERR_INVALID_ARG (-1)  /* null pointer, bad size, k > E, ...        */
+#define MOEQ_ERR_UNSUPPORTED (-2)  /* bits not in {4,6,8}, K not a multiple of 64, shape without a kernel */
+#define MOEQ_ERR_MISALIGNED  (-3)  /* a pointer that must be 16-byte aligned is not */
+#define MOEQ_ERR_WORKSPACE   (-4)  /* workspace missing or smaller than required */
+#define MOEQ_ERR_HIP         (-5)  /* a HIP runtime call failed (launch, memcpy) */
+
+#define MOEQ_GROUP 64              /* quantisation group along the input dim  */
+
+/* One quantised projection of all experts.  For a projection mapping K inputs
+ * to N outputs, expert e's weight is an N x K matrix stored row by row:
+ *   q  [n_mats][N][K*bits/8] bytes, the codes of each row packed along K:
+ *        4-bit: code 2i in the low nibble of byte i, 2i+1 in the high nibble;
+ *        6-bit: codes 4i..4i+3 form the 24-bit little-endian word
+ *               c0 | c1<<6 | c2<<12 | c3<<18 in bytes 3i..3i+2;
+ *        8-bit: one byte per code.
+ *   sz [n_mats][N][K/64] uint32: bits 0-15 the fp16 scale s, bits 16-31 the
+ *        fp16 zero z of one group of 64 consecutive inputs of a row.
+ * The dequantised weight is (q - z) * s, computed in fp32. */
+typedef struct moe_qweight {
+  const uint8_t*  q;    /* device */
+  const uint32_t* sz;   /* device */
+  int             bits; /* 4, 6 or 8 */
+} moe_qweight;
+
+/* One MoE layer: E routed experts (ids 0..E-1) and S always-on shared experts
+ * (ids E..E+S-1), each a SwiGLU FFN with hidden size H and intermediate size
+ * I; k experts are routed per token.  gate and up map H -> I (N = I, K = H),
+ * down maps I -> H (N = H, K = I); n_mats = E + S.  The three projections may
+ * use different bit widths.
+ * An assignment is one (token, slot) pair: a = t*(k+S) + j, where slots
+ * j < k are the token's routed experts in routing order and slots j >= k
+ * its shared experts (weight one). */
+typedef struct moe_layer_desc {
+  int H, I, E, S, k;
+  moe_qweight gate, up, down;
+} moe_layer_desc;
+
+/* Size in bytes of the workspace the calls below need for batches of up to
+ * T_max tokens of layer L (decode and prefill alike).  0 if L is invalid. */
+size_t moe_workspace_bytes(const moe_layer_desc* L, int T_max);
+
+/* Description of the last error raised on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Quantisation format (the step before the forward path)
+ * ------------------------------------------------------------------------ */
+
+/* Quantise fp32 weights w [rows][K] (device, rows = n_mats*N) into codes and
+ * fp16 scale/zero per group of 64 along K, min-max affine (the starting point
+ * of HQQ; Krasis update, "Latest updates", names HQQ 4/6/8-bit weights), in
+ * fp32 with IEEE division and round-to-nearest-even:
+ *   s16 = fp16(fp32(max - min) / (2^bits - 1)),  z16 = fp16(-min / s16),
+ *   q   = clamp(rint(w / s16 + z16), 0, 2^bits - 1).
+ * A group whose s16 is zero stores s16 = 1, z16 = fp16(-min), q = 0.
+ * Writes q [rows][K*bits/8] and sz [rows][K/64] (device, layout as in
+ * moe_qweight).  w must be 16-byte aligned; w must hold finite values. */
+int moe_quantize(const float* w, long rows, int K, int bits,
+                 uint8_t* q, uint32_t* sz, hipStream_t stream);
+
+/* Unpack codes q [rows][K*bits/8] (device) into one byte per code,
+ * codes [rows][K] (device).  It runs the same in-register unpacking the
+ * decode kernels use, so it tests their view of the format bit for bit. */
+int moe_unpack(const uint8_t* q, long rows, int K, int bits,
+               uint8_t* codes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The five steps of the forward pass
+ * ------------------------------------------------------------------------ */
+
+/* Router and top-k routing.
+ * If w_router (device, bf16 [E][H]) is non-NULL: logits[t][e] =
+ * fp32(sum_h x[t][h]*w_router[e][h]) + bias[e] (bias device fp32 [E], may be
+ * NULL), accumulated in fp32, written to logits (device fp32 [T][E]).
+ * If w_router is NULL, logits is read as given (bias must be NULL) and x may
+ * be NULL.  Then, per token, the k largest logits are selected -- larger
+ * first, equal values lower expert index first, -0.0 equal to +0.0 -- into
+ * topk_idx (device int32 [T][k]), and topk_w (device fp32 [T][k]) receives a
+ * softmax over the selected logits, i.e. the softmax over all experts kept on
+ * the selected k and renormalised (Qwen 3.8 Flash Next on an RTX 3060,
+ * introduction: top-10 of 512 experts).  Logits must not be NaN.
+ * 1 <= k <= E <= 1024; T >= 0 (T = 0 enqueues nothing). */
+int moe_route_topk(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                   int T, int H, int E, int k,
+                   float* logits, int32_t* topk_idx, float* topk_w,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Group the T*(k+S) assignments by expert: histogram, exclusive scan and a
+ * stable scatter.  Outputs (device int32):
+ *   counts  [E+S]    assignments per expert,
+ *   offsets [E+S+1]  exclusive prefix sum of counts,
+ *   sorted  [T*(k+S)] assignment ids grouped by expert, ascending within one,
+ *   inverse [T*(k+S)] position of each assignment in sorted,
+ *   active  [E+S+1]  active[0] = number of experts with counts > 0,
+ *                    active[1..] those expert ids, ascending.
+ * Shared-expert slots get ids E..E+S-1.  A routed id outside [0, E) is
+ * skipped (its assignment is missing from sorted, its inverse is -1) and
+ * counted; moe_read_status() reports the count.  Results are identical from
+ * run to run (no atomics decide an order). */
+int moe_permute(const int32_t* topk_idx, int T, int k, int E, int S,
+                int32_t* counts, int32_t* offsets, int32_t* sorted,
+                int32_t* inverse, int32_t* active,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Decode path (small T): for every assignment a, y[a] = Wd h with
+ * h = silu(Wg x_t) * (Wu x_t), t = a / (k+S), using expert sorted-order data
+ * from moe_permute.  Only the experts in `active` are read, each once per
+ * batch, as a grouped GEMV: codes are unpacked in registers and dot products
+ * accumulated in fp32 with the group scale/zero applied per group in fp32.
+ * y is device fp32 [T*(k+S)][H], rows in assignment order.  Intended for
+ * T <= 64; correct for any T. */
+int moe_qgemv_decode(const moe_layer_desc* L, const uint16_t* x, int T,
+                     const int32_t* offsets, const int32_t* sorted,
+                     const int32_t* active, float* y,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Prefill path (large T): the same y as moe_qgemv_decode, computed as a
+ * grouped GEMM over expert-sorted tokens on the bf16 matrix cores: weights
+ * are dequantised (fp32, then rounded to bf16) into LDS tiles, products
+ * accumulate in fp32, h is rounded to bf16 between the two GEMMs.  y is
+ * device bf16 [T*(k+S)][H], rows in assignment order. */
+int moe_qgemm_prefill(const moe_layer_desc* L, const uint16_t* x, int T,
+                      const int32_t* counts, const int32_t* offsets,
+                      const int32_t* sorted, uint16_t* y,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+#define MOEQ_Y_F32  0
+#define MOEQ_Y_BF16 1
+/* Weighted combine: out[t] = sum_{j<k} topk_w[t][j] * y[t*(k+S)+j]
+ *                          + sum_{j>=k} y[t*(k+S)+j],
+ * summed in fp32 in ascending j.  If residual (device bf16 [T][H]) is
+ * non-NULL, out[t] = bf16(residual[t] + bf16(sum)) instead of bf16(sum).
+ * y is device fp32 or bf16 (y_dtype) [T*(k+S)][H]; out device bf16 [T][H]
+ * (may alias residual). */
+int moe_combine(const void* y, int y_dtype, const float* topk_w,
+                const uint16_t* residual, int T, int k, int S, int H,
+                uint16_t* out, hipStream_t stream);
+
+/* RMSNorm of bf16 rows: out[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps) * g),
+ * g = gamma (device bf16 [H]) or 1 if gamma is NULL; fp32 arithmetic.
+ * x, out device bf16 [T][H]; may not alias. */
+int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, int T, int H, float eps,
+                uint16_t* out, hipStream_t stream);
+
+/* Synchronise `stream` and report the number of out-of-range expert ids the
+ * last moe_permute on this workspace skipped. */
+int moe_read_status(const void* ws, size_t ws_bytes, int* n_bad_ids, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEQ_H */

@@ -1,0 +1,72 @@
+"""Shared helpers of the GPU tests: build a layer's inputs from the seeded
+generator on both sides -- the HIP path quantises on the device, the oracle
+quantises the same fp32 draws on the CPU -- and compare results."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synth
+
+PROJ = {"gate": synth.T_GATE, "up": synth.T_UP, "down": synth.T_DOWN}
+
+
+def bf16_tensor(bits_u16: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def to_bits(t) -> np.ndarray:
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_layer(w: synth.Workload, layer: int = 0, bits=None, device="cuda", chunk=64):
+    """Quantise every expert's weights on the device (HIP path) from the
+    seeded fp32 draws, streaming ``chunk`` experts at a time."""
+    import torch
+    import bit_quantized_expert_amd as bq
+    bits = bits or w.bits
+    n = w.n_mats
+    projs = {}
+    for name, tid in PROJ.items():
+        N, K = (w.I, w.H) if name != "down" else (w.H, w.I)
+        q = torch.empty((n, N, K * bits // 8), dtype=torch.uint8, device=device)
+        sz = torch.empty((n, N, K // 64), dtype=torch.int32, device=device)
+        qw = bq.QWeight(q, sz, bits)
+        for e0 in range(0, n, chunk):
+            es = list(range(e0, min(n, e0 + chunk)))
+            host = synth.expert_weights_f32(w, layer, tid, es)
+            wd = torch.from_numpy(host).to(device)
+            part = bq.QWeight(q[e0:e0 + len(es)], sz[e0:e0 + len(es)], bits)
+            bq.moe_quantize(wd, bits, out=part)
+            del wd
+        projs[name] = qw
+    torch.cuda.synchronize()
+    return bq.QuantLayer(w.H, w.I, w.E, w.S, w.k, projs["gate"], projs["up"], projs["down"])
+
+
+class LazyExperts:
+    """Oracle-side experts: quantised by the oracle from the same fp32 draws,
+    built on first use."""
+
+    def __init__(self, w: synth.Workload, layer: int = 0, bits=None):
+        self.w, self.layer, self.bits = w, layer, bits or w.bits
+        self.cache = {}
+
+    def __getitem__(self, e):
+        if e not in self.cache:
+            self.cache[e] = {name: oracle.quantize(synth.expert_weight_f32(self.w, self.layer, tid, e), self.bits)
+                             for name, tid in PROJ.items()}
+        return self.cache[e]
+
+
+def oracle_layer(w: synth.Workload, layer: int = 0, bits=None) -> oracle.QuantLayer:
+    return oracle.QuantLayer(w.H, w.I, w.E, w.k, w.S, LazyExperts(w, layer, bits))
+
+
+def rel_err(gpu, ref) -> float:
+    """max |gpu - ref| / (max |ref| + 1e-6)"""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.max(np.abs(gpu - ref)) / (np.max(np.abs(ref)) + 1e-6)) if ref.size else 0.0

@@ -1,0 +1,147 @@
+"""GPU parity of the whole MoE layer (route -> permute -> decode or prefill
+expert FFN -> combine) against the oracle, through the C ABI.
+
+The oracle is routed from the GPU's fp32 logits (its selection on given
+logits is checked bit for bit elsewhere), and the GPU logits themselves are
+checked against the oracle's.  Layer outputs must satisfy
+max|gpu - oracle| / (max|oracle| + 1e-6) <= 2e-2 on the bf16 output; the
+decode path, which keeps fp32 arithmetic, is also held to fp32-class error (see DECODE_TOL).
+Full-size workloads compare sampled tokens (tokens are independent in a MoE
+layer, so the oracle's result for a token subset is exact)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import bf16_tensor, gpu_layer, oracle_layer, rel_err, to_bits
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+SPEC_TOL = 2e-2
+# the decode path keeps fp32 arithmetic: its fp32 expert outputs y agree with
+# the oracle to 1e-4, and the bf16 layer output to within one bf16 half-ulp
+# (2^-8 relative) plus that
+DECODE_TOL = 2.0 ** -8 + 1e-4
+DECODE_Y_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def bq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_expert_amd as m
+    return m
+
+
+_LAYERS = {}
+
+
+def layer_for(bq, name, bits=None):
+    key = (name, bits)
+    if key not in _LAYERS:
+        if len(_LAYERS) >= 2:     # keep device memory bounded
+            _LAYERS.clear()
+            torch.cuda.empty_cache()
+        w = synth.get_workload(name)
+        q = gpu_layer(w, bits=bits)
+        wr = bf16_tensor(synth.router_weight_bf16(w))
+        bias = synth.router_bias(w)
+        bt = None if bias is None else torch.from_numpy(bias).cuda()
+        _LAYERS[key] = (w, bq.MoELayer(q, wr, bt, T_max=1), oracle_layer(w, bits=bits))
+    return _LAYERS[key]
+
+
+def check_layer(bq, name, T, prefill, sample=None, bits=None, batch=0):
+    w, layer, olayer = layer_for(bq, name, bits)
+    x = synth.activations_bf16(w, T, batch=batch)
+    r = layer.forward(bf16_tensor(x), prefill=prefill)
+    torch.cuda.synchronize()
+    logits = r["logits"].cpu().numpy()
+    wr = synth.router_weight_bf16(w)
+    bias = synth.router_bias(w)
+    rows = np.arange(T) if sample is None else np.unique(np.linspace(0, T - 1, sample).astype(int))
+    ref_logits = oracle.router_logits(x[rows], wr, bias)
+    assert np.max(np.abs(logits[rows] - ref_logits)) <= 1e-5 * np.max(np.abs(ref_logits))
+    ref = oracle.moe_layer(olayer, x[rows], logits=logits[rows])
+    idx = r["idx"].cpu().numpy()
+    assert np.array_equal(idx[rows], ref["idx"])
+    wt = r["w"].cpu().numpy()
+    assert np.max(np.abs(wt[rows] - ref["w"]) / ref["w"]) <= 1e-5
+    out = oracle.bf16_to_f32(to_bits(r["out"]))[rows]
+    err = rel_err(out, ref["out"])
+    assert err <= SPEC_TOL, err
+    kS = w.k + w.S
+    y = r["y"]
+    y = (oracle.bf16_to_f32(to_bits(y)) if y.dtype == torch.bfloat16 else y.cpu().numpy())
+    ya = y.reshape(T, kS, w.H)[rows].reshape(-1, w.H)
+    yerr = rel_err(ya, ref["y"])
+    if not prefill:
+        assert err <= DECODE_TOL and yerr <= DECODE_Y_TOL, (err, yerr)
+    else:
+        assert yerr <= SPEC_TOL, yerr
+    return r, err, yerr
+
+
+DECODE_CASES = [("moe_h2048_e128_k8_b4", 1), ("moe_h2048_e128_k8_b4", 16), ("moe_h2048_e256_k8_s1_b4", 1),
+                ("moe_h2048_e256_k8_s1_b4", 4), ("moe_h2048_e256_k8_s1_b4", 8), ("moe_h4096_e512_k10_b4_hot", 1)]
+
+
+@pytest.mark.parametrize("name,T", DECODE_CASES)
+def test_decode_layer(bq, name, T):
+    print(f"decode {name} T={T}", flush=True)
+    check_layer(bq, name, T, prefill=False)
+
+
+@pytest.mark.parametrize("bits", [6, 8])
+@pytest.mark.parametrize("T", [1, 3, 16])
+def test_decode_layer_6_8_bit(bq, bits, T):
+    # the stacked workload's 6- and 8-bit layers use the 128-expert shapes
+    print(f"decode 128-expert {bits}-bit T={T}", flush=True)
+    check_layer(bq, "moe_h2048_e128_k8_b4", T, prefill=False, bits=bits, batch=bits)
+
+
+@pytest.mark.parametrize("T", [1, 100, 512])
+def test_prefill_layer_small(bq, T):
+    print(f"prefill 128-expert 6-bit zipf T={T}", flush=True)
+    check_layer(bq, "moe_h2048_e128_k8_b6_zipf", T, prefill=True)
+
+
+@pytest.mark.parametrize("T", [2048, 4096])
+def test_prefill_layer_sampled(bq, T):
+    print(f"prefill 128-expert 6-bit zipf T={T} (sampled)", flush=True)
+    check_layer(bq, "moe_h2048_e128_k8_b6_zipf", T, prefill=True, sample=48)
+
+
+def test_prefill_wide_sampled(bq):
+    print("prefill 512-expert hot T=8192 (sampled)", flush=True)
+    check_layer(bq, "moe_h4096_e512_k10_b4_hot", 8192, prefill=True, sample=24)
+
+
+@pytest.mark.parametrize("name,T", [("moe_h2048_e256_k8_s1_b4", 64), ("moe_h2048_e128_k8_b4", 33)])
+def test_decode_prefill_agree(bq, name, T):
+    """Cross-check (not a pin): both paths on the same batch."""
+    w, layer, _ = layer_for(bq, name)
+    x = bf16_tensor(synth.activations_bf16(w, T, batch=3))
+    a = oracle.bf16_to_f32(to_bits(layer.forward(x, prefill=False)["out"]))
+    b = oracle.bf16_to_f32(to_bits(layer.forward(x, prefill=True)["out"]))
+    assert rel_err(b, a) <= SPEC_TOL
+
+
+@pytest.mark.parametrize("prefill,T", [(False, 16), (True, 700)])
+def test_deterministic(bq, prefill, T):
+    w, layer, _ = layer_for(bq, "moe_h2048_e128_k8_b4")
+    x = bf16_tensor(synth.activations_bf16(w, T, batch=9))
+    a = layer.forward(x, prefill=prefill)
+    b = layer.forward(x, prefill=prefill)
+    for key in ("out", "idx", "sorted", "y"):
+        assert torch.equal(a[key].view(torch.uint8) if a[key].dtype == torch.bfloat16 else a[key],
+                           b[key].view(torch.uint8) if b[key].dtype == torch.bfloat16 else b[key]), key
+
+
+def test_empty_batch(bq):
+    w, layer, _ = layer_for(bq, "moe_h2048_e128_k8_b4")
+    x = torch.empty((0, w.H), dtype=torch.bfloat16, device="cuda")
+    for prefill in (False, True):
+        r = layer.forward(x, prefill=prefill)
+        assert r["out"].shape == (0, w.H)

@@ -1,0 +1,186 @@
+"""GPU parity of the integer and routing steps against the oracle, through
+the C ABI: quantisation codes and packing (bit-exact), unpacking (bit-exact),
+top-k ids on given logits (bit-exact), routing weights (<= 1e-5 relative),
+router logits, permutation (bit-exact), combine and RMSNorm."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import bf16_tensor, rel_err, to_bits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def bq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_expert_amd as m
+    return m
+
+
+def _sz_from_oracle(s16, z16):
+    return (s16.view(np.uint16).astype(np.uint32) | (z16.view(np.uint16).astype(np.uint32) << 16))
+
+
+def _weights(seed, shape):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    w2 = w.reshape(-1, 64)
+    special = [lambda g: 0.37,                                   # constant group
+               lambda g: np.linspace(-1, 1, 64),                 # exact end points
+               lambda g: g * 1e3,                                # wide range
+               lambda g: g * 1e-3,                               # narrow range: subnormal fp16 scale
+               lambda g: (rng.integers(0, 16, 64) - 7) * 2.0 ** -6]   # on a power-of-two grid
+    for i, f in enumerate(special[: len(w2)]):
+        w2[i] = f(w2[i])
+    return w
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+@pytest.mark.parametrize("shape", [(3, 64, 512), (2, 130, 192), (1, 1, 64)])
+def test_quantize_bitexact(bq, bits, shape):
+    w = _weights(bits * 7 + shape[1], shape)
+    qw = bq.moe_quantize(torch.from_numpy(w).cuda(), bits)
+    torch.cuda.synchronize()
+    q, s16, z16 = oracle.quantize(w.reshape(-1, shape[-1]), bits)
+    ref_packed = oracle.pack(q, bits)
+    got_packed = qw.q.cpu().numpy().reshape(ref_packed.shape)
+    assert np.array_equal(got_packed, ref_packed)
+    got_sz = qw.sz.cpu().numpy().view(np.uint32).reshape(s16.shape)
+    assert np.array_equal(got_sz, _sz_from_oracle(s16, z16))
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_unpack_bitexact(bq, bits):
+    rng = np.random.default_rng(bits)
+    K = 2048
+    packed = rng.integers(0, 256, (37, K * bits // 8), dtype=np.uint8)
+    packed[0, : 256] = np.arange(256, dtype=np.uint8)
+    got = bq.moe_unpack(torch.from_numpy(packed).cuda(), K, bits).cpu().numpy()
+    assert np.array_equal(got, oracle.unpack(packed, bits, K))
+
+
+@pytest.mark.parametrize("E,k,T", [(128, 8, 16), (256, 8, 8), (512, 10, 33), (6, 3, 5), (1024, 64, 3), (8, 8, 4)])
+def test_topk_on_given_logits_bitexact(bq, E, k, T):
+    w = synth.Workload("t", 99, 64, 64, E, k, 0, 4, (T,))
+    L = synth.direct_logits_f32(w, T)
+    Lt = torch.from_numpy(L).cuda()
+    _, idx, wt = bq.moe_route_topk(None, None, None, E, k, logits=Lt)
+    ref = oracle.select_topk(L, k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+    rw = oracle.topk_weights(L, ref)
+    assert np.max(np.abs(wt.cpu().numpy() - rw) / rw) <= 1e-5
+
+
+def test_topk_ties_bitexact(bq):
+    rng = np.random.default_rng(11)
+    L = rng.integers(-3, 4, (300, 96)).astype(np.float32)
+    L[:20] *= np.float32(0.0)            # rows of +-0.0 ties
+    L[20, :] = 1.0                        # all equal
+    Lt = torch.from_numpy(L).cuda()
+    for k in (1, 5, 96):
+        _, idx, _ = bq.moe_route_topk(None, None, None, 96, k, logits=Lt)
+        assert np.array_equal(idx.cpu().numpy(), oracle.select_topk(L, k))
+
+
+@pytest.mark.parametrize("T", [1, 16, 63, 64, 200, 4096])
+@pytest.mark.parametrize("wl", ["moe_h2048_e128_k8_b4", "moe_h4096_e512_k10_b4_hot"])
+def test_router_logits(bq, T, wl):
+    w = synth.get_workload(wl)
+    if T > 512 and w.H > 2048:
+        T = 1024
+    x = synth.activations_bf16(w, T, batch=5)
+    wr = synth.router_weight_bf16(w)
+    bias = synth.router_bias(w)
+    bt = None if bias is None else torch.from_numpy(bias).cuda()
+    logits, idx, wt = bq.moe_route_topk(bf16_tensor(x), bf16_tensor(wr), bt, w.E, w.k)
+    ref = oracle.router_logits(x, wr, bias)
+    got = logits.cpu().numpy()
+    assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
+    # selection on the GPU's own logits is bit-exact
+    assert np.array_equal(idx.cpu().numpy(), oracle.select_topk(got, w.k))
+
+
+@pytest.mark.parametrize("T,k,E,S", [(0, 8, 128, 0), (1, 8, 128, 0), (16, 8, 128, 0), (8, 8, 256, 1),
+                                     (113, 8, 128, 1), (128, 8, 128, 0), (4096, 8, 128, 0), (8192, 10, 512, 0),
+                                     (300, 4, 4000, 1), (2000, 2, 3, 0)])
+def test_permute_bitexact(bq, T, k, E, S):
+    rng = np.random.default_rng(T + E)
+    if T:
+        if E >= 2 * k:   # skewed: half the tokens prefer a few experts
+            idx = np.stack([rng.choice(E, k, replace=False, p=None) for _ in range(T)]).astype(np.int32)
+            idx[: T // 2, 0] = rng.integers(0, 3, T // 2)
+            for t in range(T // 2):      # keep ids distinct within a token
+                row = idx[t]
+                _, first = np.unique(row, return_index=True)
+                if len(first) < k:
+                    free = np.setdiff1d(np.arange(E), row)
+                    dup = np.setdiff1d(np.arange(k), first)
+                    row[dup] = free[: len(dup)]
+        else:
+            idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    else:
+        idx = np.zeros((0, k), np.int32)
+    it = torch.from_numpy(idx).cuda() if T else torch.zeros((0, k), dtype=torch.int32, device="cuda")
+    counts, offsets, srt, inv, active = bq.moe_permute(it, E, S)
+    c, o, s, i = oracle.permute(idx, E, S)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(srt.cpu().numpy(), s)
+    assert np.array_equal(inv.cpu().numpy(), i)
+    act = active.cpu().numpy()
+    nz = np.nonzero(c)[0]
+    assert act[0] == len(nz) and np.array_equal(act[1:1 + len(nz)], nz)
+
+
+def test_permute_counts_out_of_range_ids(bq):
+    idx = np.array([[0, 1], [5, 2], [-1, 3], [2, 9]], np.int32)   # 5, -1 and 9 are outside [0, 5)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    counts, offsets, srt, inv, active = bq.moe_permute(torch.from_numpy(idx).cuda(), 5, 0, ws=ws)
+    assert bq.moe_read_status(ws) == 3
+    assert counts.cpu().tolist() == [1, 1, 2, 1, 0]
+    assert srt.cpu().tolist()[:5] == [0, 1, 3, 6, 5]
+    assert inv.cpu().tolist() == [0, 1, -1, 2, -1, 4, 3, -1]
+
+
+@pytest.mark.parametrize("T,k,S,H,dtype", [(1, 8, 0, 2048, "f32"), (8, 8, 1, 2048, "f32"), (37, 10, 0, 4096, "bf16"),
+                                           (5, 3, 1, 64, "bf16")])
+def test_combine(bq, T, k, S, H, dtype):
+    rng = np.random.default_rng(T * H)
+    y = rng.standard_normal((T * (k + S), H)).astype(np.float32)
+    w = rng.random((T, k))
+    w = (w / w.sum(1, keepdims=True)).astype(np.float32)
+    if dtype == "bf16":
+        yb = oracle.f32_to_bf16(y)
+        y = oracle.bf16_to_f32(yb)
+        yt = bf16_tensor(yb)
+    else:
+        yt = torch.from_numpy(y).cuda()
+    out = bq.moe_combine(yt, torch.from_numpy(w).cuda(), k, S)
+    ref = oracle.combine(y.reshape(T, k + S, H).astype(np.float64), w.astype(np.float64), S)
+    got = oracle.bf16_to_f32(to_bits(out))
+    assert rel_err(got, ref) <= 2.0 ** -8
+    # with a residual: bf16(res + bf16(sum))
+    res = oracle.f32_to_bf16(rng.standard_normal((T, H)).astype(np.float32))
+    out2 = bq.moe_combine(yt, torch.from_numpy(w).cuda(), k, S, residual=bf16_tensor(res))
+    ref2 = oracle.bf16_to_f32(oracle.residual_bf16(res, ref))
+    got2 = oracle.bf16_to_f32(to_bits(out2))
+    assert np.max(np.abs(got2 - ref2)) <= 2.0 ** -7 * np.max(np.abs(ref2))
+
+
+def test_rmsnorm(bq):
+    rng = np.random.default_rng(3)
+    x = oracle.f32_to_bf16((rng.standard_normal((9, 2048)) * 3).astype(np.float32))
+    x[0] = oracle.f32_to_bf16(np.full(2048, 0.5, np.float32))
+    out = bq.moe_rmsnorm(bf16_tensor(x))
+    got = to_bits(out)
+    ref = oracle.rmsnorm_bf16(x)
+    # fp32 arithmetic vs fp64: at most one bf16 ulp apart
+    gd = oracle.bf16_to_f32(got).astype(np.float64)
+    rd = oracle.bf16_to_f32(ref).astype(np.float64)
+    assert np.all(np.abs(gd - rd) <= 2.0 ** -7 * np.abs(rd) + 1e-30)
+    assert np.array_equal(got[0], ref[0])
