@@ -70,11 +70,18 @@ class Step:
         self.inverse = torch.empty(A, dtype=torch.int32, device=dev)
         self.active = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
         self.prefill = T > bq.DECODE_MAX_T
+        self.fused = not self.prefill and bq.fused_route_ok(T, H, E, k, S)
         self.y = torch.empty((A, H), dtype=torch.bfloat16 if self.prefill else torch.float32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     def route_permute(self, s):
         lib, p, L = self.bq.lib(), self.bq._p, self.L
+        if self.fused:
+            self.bq._check(lib.moe_route_permute_decode(
+                p(self.x), p(self.wr), p(self.bias), self.T, L.H, L.E, L.k, L.S, p(self.logits), p(self.idx),
+                p(self.w), p(self.counts), p(self.offsets), p(self.sorted), p(self.inverse), p(self.active),
+                p(self.ws), self.ws.numel(), s))
+            return
         self.bq._check(lib.moe_route_topk(p(self.x), p(self.wr), p(self.bias), self.T, L.H, L.E, L.k, p(self.logits),
                                           p(self.idx), p(self.w), p(self.ws), self.ws.numel(), s))
         self.bq._check(lib.moe_permute(p(self.idx), self.T, L.k, L.E, L.S, p(self.counts), p(self.offsets),
@@ -99,6 +106,146 @@ class Step:
         self.route_permute(s)
         self.experts(s)
         self.combine(s)
+
+
+class StackStep:
+    """One token through every block of the stacked workload:
+    n = RMSNorm(x); route n; experts(n); x = bf16(x + bf16(combine))."""
+
+    def __init__(self, bq, layers, wrs, x, ws):
+        import torch
+        self.bq, self.layers, self.wrs, self.x, self.ws = bq, layers, wrs, x, ws
+        L0 = layers[0]
+        dev = x.device
+        self.n = torch.empty_like(x)
+        self.steps = [Step(bq, L, wr, None, self.n, x.shape[0], ws) for L, wr in zip(layers, wrs)]
+        for st in self.steps:      # every block adds into the residual stream x
+            st.out = x
+
+    def run(self, s):
+        lib, p = self.bq.lib(), self.bq._p
+        T, H = self.x.shape
+        for st in self.steps:
+            self.bq._check(lib.moe_rmsnorm(p(self.x), None, T, H, ctypes.c_float(1e-6), p(self.n), s))
+            st.route_permute(s)
+            st.experts(s)
+            L = st.L
+            self.bq._check(lib.moe_combine(p(st.y), 0, p(st.w), p(self.x), T, L.k, L.S, L.H, p(self.x), s))
+
+
+def build_stack(bq, w, device):
+    """All blocks of the stacked workload, each with its own weights and bit
+    width (quantised on the device)."""
+    import torch
+    from tests.gpu_util import bf16_tensor, gpu_layer
+    bits = synth.layer_bits(w)
+    layers, wrs = [], []
+    for l, b in enumerate(bits):
+        layers.append(gpu_layer(w, layer=l, bits=b, device=device))
+        wrs.append(bf16_tensor(synth.router_weight_bf16(w, layer=l), device=device))
+    torch.cuda.synchronize()
+    return layers, wrs, bits
+
+
+def main_stack(a, w, bq, dev):
+    """Stacked decode: 256 consecutive batch-1 tokens through all blocks,
+    one HIP graph per token step, timed end to end."""
+    import torch
+    from tests.gpu_util import bf16_tensor
+    t0 = time.time()
+    layers, wrs, bits = build_stack(bq, w, dev)
+    n_tok = w.steps
+    xs = torch.stack([bf16_tensor(synth.activations_bf16(w, 1, batch=b), device=dev) for b in range(n_tok)])
+    x = torch.empty((1, w.H), dtype=torch.bfloat16, device=dev)
+    ws = layers[0].workspace(1, device=dev)
+    st = StackStep(bq, layers, wrs, x, ws)
+    print(f"# setup {time.time() - t0:.1f}s: {w.name} layers={len(layers)} bits={bits}", file=sys.stderr, flush=True)
+    s = torch.cuda.Stream()
+    sp = ctypes.c_void_p(s.cuda_stream)
+    with torch.cuda.stream(s):
+        x.copy_(xs[0])
+        st.run(sp)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        st.run(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+
+    def tokens(n):
+        with torch.cuda.stream(s):
+            for i in range(n):
+                x.copy_(xs[i % n_tok])
+                graph.replay()
+
+    tokens(min(a.warmup, n_tok))
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(s)
+    tokens(n_tok)
+    ev1.record(s)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    per_tok = total_ms / n_tok
+    # algorithmic bytes per token: routed experts (realised, per layer) + routers + x, out
+    distinct = [int((ss.counts > 0).sum().item()) for ss in st.steps]
+    alg = sum(d * expert_bytes(w, b) for d, b in zip(distinct, bits)) + len(bits) * (w.E * w.H * 2 + 4 * w.H * 2)
+    # expert kernels alone: time one token's decode calls with events
+    kev = []
+    with torch.cuda.stream(s):
+        x.copy_(xs[0])
+        for ss in st.steps:
+            ss.route_permute(sp)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            ss.experts(sp)
+            e1.record(s)
+            kev.append((e0, e1))
+    torch.cuda.synchronize()
+    kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in kev)
+    exp_bytes = sum(d * expert_bytes(w, b) for d, b in zip(distinct, bits))
+    achieved = exp_bytes / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "MoE-layer tokens/s", "value": round(n_tok / (total_ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": n_tok, "warmup": a.warmup, "ms_per_step": round(per_tok, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u4/u6/u8 codes x bf16 -> fp32",
+        "data": "synthetic (seeded N(0,0.02) weights quantised on the GPU; N(0,1) bf16 states)",
+        "config": {"workload": w.name, "blocks": len(bits), "bits_per_block": bits, "tokens_per_step": 1,
+                   "hip_graph": True, "alg_bytes_per_token": round(alg),
+                   "GBps_per_token_stream": round(alg / (per_tok * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "moe_qgemv_decode (gate/up + down), summed over the 48 blocks of one token"},
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_stack(w, bits, a.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_stack(w, bits, budget_s):
+    import oracle
+    from tests.gpu_util import LazyExperts
+    from threadpoolctl import threadpool_info
+    n, t_total = 0, 0.0
+    experts = [LazyExperts(w, layer=l, bits=b) for l, b in enumerate(bits)]
+    wrs = [synth.router_weight_bf16(w, layer=l) for l in range(len(bits))]
+    while t_total < budget_s and n < 8:
+        x = synth.activations_bf16(w, 1, batch=2000 + n)
+        for l in range(len(bits)):          # quantise the touched experts first (untimed load step)
+            nrm = oracle.rmsnorm_bf16(x)
+            L = oracle.router_logits(nrm, wrs[l])
+            for e in oracle.select_topk(L, w.k)[0]:
+                experts[l][int(e)]
+            layer = oracle.QuantLayer(w.H, w.I, w.E, w.k, w.S, experts[l])
+            t0 = time.perf_counter()
+            out = oracle.moe_layer(layer, nrm, wrs[l])["out"]
+            x = oracle.residual_bf16(x, out)
+            t_total += time.perf_counter() - t0
+        n += 1
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"value": n / t_total, "unit": "tokens/s", "cores": max(blas + [1]), "kind": "oracle",
+            "sample": f"{n} tokens through all {len(bits)} blocks ({t_total:.1f} s of oracle time; the per-block "
+                      f"quantisation of the touched experts excluded)"}
 
 
 def build_replicas(bq, w, R, device):
@@ -175,6 +322,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w, T = parse_workload(a.workload)
+    if w.layers > 1:
+        return main_stack(a, w, bq, dev)
     bits = w.bits
     layer_bytes = expert_bytes(w, bits) * w.n_mats
     R = a.replicas or max(2, min(16, math.ceil(2e9 / layer_bytes)))

@@ -2,7 +2,7 @@
 layer on MI355X (gfx950).
 
 Argument marshalling only.  Every step of the layer runs in the HIP kernels
-of ``libmoeq.so`` (built by ``python -m bit_quantized_expert_amd.build``);
+of ``libmoeq.so`` (built by ``python bit_quantized_expert_amd/build.py``);
 PyTorch supplies device memory and the current stream.  Importing this
 package without the built library raises -- there is no fallback.
 
@@ -52,7 +52,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_quantized_expert_amd.build`")
+            raise ImportError(f"{LIB_PATH} is not built; run `python bit_quantized_expert_amd/build.py`")
         L = ctypes.CDLL(LIB_PATH)
         P, I, L64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_size_t
         sig = {
@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "moe_unpack": (I, [P, L64, I, I, P, P]),
             "moe_route_topk": (I, [P, P, P, I, I, I, I, P, P, P, P, SZ, P]),
             "moe_permute": (I, [P, I, I, I, I, P, P, P, P, P, P, SZ, P]),
+            "moe_route_permute_decode": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_qgemv_decode": (I, [P, P, I, P, P, P, P, P, SZ, P]),
             "moe_qgemm_prefill": (I, [P, P, I, P, P, P, P, P, SZ, P]),
             "moe_combine": (I, [P, I, P, P, I, I, I, I, P, P]),
@@ -158,7 +159,8 @@ class QuantLayer:
         return moe_workspace_bytes(self, T_max)
 
     def workspace(self, T_max: int, device="cuda") -> torch.Tensor:
-        return torch.empty(max(256, self.workspace_bytes(T_max)), dtype=torch.uint8, device=device)
+        # zero-filled: the library's control words start (and stay) at zero
+        return torch.zeros(max(256, self.workspace_bytes(T_max)), dtype=torch.uint8, device=device)
 
 
 def moe_workspace_bytes(layer: QuantLayer, T_max: int) -> int:
@@ -216,10 +218,37 @@ def moe_permute(idx: torch.Tensor, E: int, S: int, ws: Optional[torch.Tensor] = 
     inverse = torch.empty(max(A, 1), dtype=torch.int32, device=dev)
     active = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
     if ws is None:
-        ws = torch.empty(permute_ws_bytes(A, E + S), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(permute_ws_bytes(A, E + S), dtype=torch.uint8, device=dev)
     _check(lib().moe_permute(_p(idx), T, k, E, S, _p(counts), _p(offsets), _p(sorted_a), _p(inverse), _p(active),
                              _p(ws), ws.numel(), _stream(stream)))
     return counts, offsets, sorted_a[:A], inverse[:A], active
+
+
+def fused_route_ok(T: int, H: int, E: int, k: int, S: int) -> bool:
+    return T * (k + S) <= 1024 and E + S <= 1024 and k <= 64 and H % 512 == 0 and H <= 4096
+
+
+def moe_route_permute_decode(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor], E: int,
+                             k: int, S: int, ws: torch.Tensor, stream=None):
+    """moe_route_topk + moe_permute in one launch (decode batches).  Returns
+    (logits, idx, w, counts, offsets, sorted, inverse, active)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w_router, torch.bfloat16, "w_router")
+    T, H = x.shape
+    dev = x.device
+    A = T * (k + S)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E + S, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
+    sorted_a = torch.empty(max(A, 1), dtype=torch.int32, device=dev)
+    inverse = torch.empty(max(A, 1), dtype=torch.int32, device=dev)
+    active = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
+    _check(lib().moe_route_permute_decode(_p(x), _p(w_router), _p(bias), T, H, E, k, S, _p(logits), _p(idx),
+                                          _p(w), _p(counts), _p(offsets), _p(sorted_a), _p(inverse), _p(active),
+                                          _p(ws), ws.numel(), _stream(stream)))
+    return logits, idx, w, counts, offsets, sorted_a[:A], inverse[:A], active
 
 
 def moe_qgemv_decode(layer: QuantLayer, x: torch.Tensor, offsets, sorted_a, active, ws: torch.Tensor,
@@ -303,13 +332,20 @@ class MoELayer:
             self.ws = self.q.workspace(T_max, device=self.w_router.device)
             self.T_max = T_max
 
-    def forward(self, x: torch.Tensor, residual: Optional[torch.Tensor] = None, stream=None, prefill=None):
+    def forward(self, x: torch.Tensor, residual: Optional[torch.Tensor] = None, stream=None, prefill=None,
+                fused_route=None):
         T = x.shape[0]
         self.reserve(T)
         q = self.q
-        logits, idx, w = moe_route_topk(x, self.w_router, self.bias, q.E, q.k, ws=self.ws, stream=stream)
-        counts, offsets, sorted_a, inverse, active = moe_permute(idx, q.E, q.S, ws=self.ws, stream=stream)
         use_prefill = T > DECODE_MAX_T if prefill is None else prefill
+        if fused_route is None:
+            fused_route = not use_prefill and T > 0 and fused_route_ok(T, q.H, q.E, q.k, q.S)
+        if fused_route:
+            logits, idx, w, counts, offsets, sorted_a, inverse, active = moe_route_permute_decode(
+                x, self.w_router, self.bias, q.E, q.k, q.S, self.ws, stream=stream)
+        else:
+            logits, idx, w = moe_route_topk(x, self.w_router, self.bias, q.E, q.k, ws=self.ws, stream=stream)
+            counts, offsets, sorted_a, inverse, active = moe_permute(idx, q.E, q.S, ws=self.ws, stream=stream)
         if use_prefill:
             y = moe_qgemm_prefill(q, x, counts, offsets, sorted_a, self.ws, stream=stream)
         else:

@@ -1,6 +1,8 @@
 """Build libmoeq.so (the HIP kernels and their C ABI) for gfx950 with hipcc.
 
-    python -m bit_quantized_expert_amd.build [-j N] [--save-temps]
+    python bit_quantized_expert_amd/build.py [-j N] [--save-temps]
+
+(Run it by path: importing the package itself needs the built library.)
 
 Each ``csrc/*.hip`` is compiled to an object under ``_build/`` in parallel and
 the objects are linked into ``bit_quantized_expert_amd/libmoeq.so``.

@@ -87,6 +87,26 @@ MOEQ_DEV float group_sum(float v, int span) {
 
 MOEQ_DEV float wave_sum(float v) { return group_sum(v, 64); }
 
+template <int CTRL, int ROW_MASK>
+MOEQ_DEV float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                                  0xF, false));
+}
+
+// Sum over aligned groups of SPAN lanes (SPAN a power of two <= 64) with DPP
+// only -- no branches, no LDS permutes.  The group's sum is valid in the
+// group's last lane (lane % SPAN == SPAN - 1); other lanes hold partials.
+template <int SPAN>
+MOEQ_DEV float group_sum_last(float v) {
+  if constexpr (SPAN >= 2) v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  if constexpr (SPAN >= 4) v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  if constexpr (SPAN >= 8) v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+  if constexpr (SPAN >= 16) v = dpp_add<0x140, 0xF>(v);  // row_mirror: whole row of 16
+  if constexpr (SPAN >= 32) v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  if constexpr (SPAN >= 64) v = dpp_add<0x143, 0x8>(v);  // row_bcast:31 into row 3
+  return v;
+}
+
 MOEQ_DEV float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
@@ -96,4 +116,33 @@ MOEQ_DEV float wave_min(float v) {
   return v;
 }
 
-MOEQ_DEV float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (about
+// 1 ulp each); -g*log2(e) overflowing to +inf gives rcp(inf) = 0, i.e. 0.
+// Wave arg-max under the routing order (larger value first, then lower
+// index), DPP only; every lane returns the winner.  An empty lane carries
+// (-inf, INT_MAX).
+template <int CTRL, int ROW_MASK>
+MOEQ_DEV void argmax_step(float& v, int& e) {
+  const float ov = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                         false));
+  const int oe = __builtin_amdgcn_update_dpp(e, e, CTRL, ROW_MASK, 0xF, false);
+  const bool b = ov > v || (ov == v && oe < e);
+  v = b ? ov : v;
+  e = b ? oe : e;
+}
+
+MOEQ_DEV void wave_argmax(float& v, int& e) {
+  argmax_step<0xB1, 0xF>(v, e);
+  argmax_step<0x4E, 0xF>(v, e);
+  argmax_step<0x141, 0xF>(v, e);
+  argmax_step<0x140, 0xF>(v, e);
+  argmax_step<0x142, 0xA>(v, e);
+  argmax_step<0x143, 0x8>(v, e);
+  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  e = __builtin_amdgcn_readlane(e, 63);
+}
+
+MOEQ_DEV float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+}

@@ -20,13 +20,11 @@ bool geometry(int K, int bits, int& lpr, int& iter) {
   return iter >= 1 && iter <= 4;
 }
 
-// Rows per wave: a multiple of the rows one unrolled step of a wave covers,
-// grown while the grid would still hold at least 2048 blocks.
-int pick_rows_per_wave(int N, int lpr, long slots) {
-  const int step = (64 / lpr) * decode_detail::kUnroll;
-  int rows = step;
-  while (rows * 2 <= decode_detail::kMaxRowsPerWave && slots * ((long)N / (4L * rows * 2)) >= 2048) rows *= 2;
-  return rows;
+// Rows per wave: CH chunks per lane and matrix held in registers cover
+// CH / iter row steps of 64 / lpr rows (CH as in decode_impl.h).
+int rows_per_wave(int lpr, int iter, bool gateup) {
+  const int ch = gateup ? (iter == 1 ? 8 : (iter == 3 ? 3 : 4)) : (iter == 1 ? 8 : (iter == 3 ? 6 : 4));
+  return (ch / iter) * (64 / lpr);
 }
 
 }  // namespace
@@ -51,21 +49,23 @@ extern "C" int moe_qgemv_decode(const moe_layer_desc* L, const uint16_t* x, int 
   const WsLayout wl = ws_layout(L->H, L->I, L->E, L->S, L->k, T);
   if (!ws || ws_bytes < wl.total)
     return set_error(MOEQ_ERR_WORKSPACE, "moe_qgemv_decode: workspace of %zu bytes, need %zu", ws_bytes, wl.total);
-  float* h = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.h);
+  // h as two bf16 planes (hi, lo) of [A][I] in the down kernel's pair order
+  uint16_t* hh = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.h);
+  uint16_t* hl = hh + (size_t)T * (L->k + L->S) * L->I;
   const long A = (long)T * (L->k + L->S);
   const int slots = (int)(A < L->E + L->S ? A : L->E + L->S);   // upper bound on active experts
-  const int rpw1 = pick_rows_per_wave(L->I, lpr1, slots);
-  const int rpw2 = pick_rows_per_wave(L->H, lpr2, slots);
+  const int rpw1 = rows_per_wave(lpr1, it1, true);
+  const int rpw2 = rows_per_wave(lpr2, it2, false);
   switch (L->gate.bits) {
-    case 4: rc = decode_gateup_b4(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, h, stream); break;
-    case 6: rc = decode_gateup_b6(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, h, stream); break;
-    default: rc = decode_gateup_b8(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, h, stream); break;
+    case 4: rc = decode_gateup_b4(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, hh, hl, stream); break;
+    case 6: rc = decode_gateup_b6(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, hh, hl, stream); break;
+    default: rc = decode_gateup_b8(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, hh, hl, stream); break;
   }
   if (rc != MOEQ_OK) return rc;
   switch (L->down.bits) {
-    case 4: rc = decode_down_b4(L, h, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
-    case 6: rc = decode_down_b6(L, h, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
-    default: rc = decode_down_b8(L, h, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
+    case 4: rc = decode_down_b4(L, hh, hl, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
+    case 6: rc = decode_down_b6(L, hh, hl, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
+    default: rc = decode_down_b8(L, hh, hl, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
   }
   return rc;
 }

@@ -17,9 +17,12 @@
 //   * gate and up rows that share the input are read in the same pass and
 //     combined into h = silu(g) u (Raon-1-mini optimisation table:
 //     projections sharing an input run together);
-//   * rows are reduced across their LPR lanes with DPP; with ITER > 1 the
-//     per-chunk partial sums of a row are added up in a small per-wave LDS
-//     array, so only one chunk's activations occupy registers at a time.
+//   * a wave loads all of its weight chunks (CH per lane, CH/ITER row steps)
+//     into registers before anything else, so every weight load of the wave
+//     is in flight at once; token passes (up to two tokens each) then reuse
+//     those registers, so an expert's weights are read from HBM once however
+//     many of the batch's tokens it serves;
+//   * rows are reduced across their LPR lanes with DPP.
 // The down projection reads h in fp32, split into two bf16 terms (hi + lo),
 // so its dot products carry about 16 significant bits of h.
 //
@@ -33,8 +36,6 @@ namespace moeq {
 namespace decode_detail {
 
 constexpr int kMaxNT = 2;        // tokens per pass over the weights
-constexpr int kUnroll = 2;       // row steps whose loads are issued together
-constexpr int kMaxRowsPerWave = 64;
 
 // NT tokens' activation slices (bf16 rows of `ld` elements) for chunk `cpos`
 // as dot2 pairs in the format's pair order, with their fp32 sums.  Tokens
@@ -58,52 +59,75 @@ MOEQ_DEV void load_x_bf16(const uint16_t* __restrict__ x, const int (&rowidx)[NT
       for (int i = 0; i < F::CODES / 2; ++i) v[i] = 0u;
     }
     float s = 0.0f;
+    const uint32_t ones = 0x3F803F80u;   // bf16 (1, 1): dot2 with it sums a pair
 #pragma unroll
     for (int p = 0; p < F::PAIRS; ++p) {
       const int c0 = pair_code<BITS>(p, 0), c1 = pair_code<BITS>(p, 1);
       const uint32_t lo = (v[c0 >> 1] >> (16 * (c0 & 1))) & 0xFFFFu;
       const uint32_t hi = (v[c1 >> 1] >> (16 * (c1 & 1))) & 0xFFFFu;
       X[t][p] = lo | (hi << 16);
-      s += bf16_bits_to_f32(lo) + bf16_bits_to_f32(hi);
+      s = dot2_bf16(X[t][p], ones, s);
     }
     XS[t] = s;
   }
 }
 
-// Same for fp32 rows (the intermediate h): each value v is split into
-// hi = bf16(v) and lo = bf16(v - hi); XS is the fp32 sum of hi + lo.
+// The intermediate h of the down projection comes from the gate/up kernels
+// already split into two bf16 planes, hi = bf16(h) and lo = bf16(h - hi),
+// each stored in the down kernel's pair order (h_store_pos), so a chunk's
+// pairs load directly.  XS is the fp32 sum of hi + lo over the chunk.
 template <int BITS, int NT>
-MOEQ_DEV void load_x_f32(const float* __restrict__ x, int row0, int nt, int cpos,
-                         uint32_t (&XH)[NT][Fmt<BITS>::PAIRS], uint32_t (&XL)[NT][Fmt<BITS>::PAIRS],
-                         float (&XS)[NT], int ld) {
+MOEQ_DEV void load_h_pairs(const uint16_t* __restrict__ hh, const uint16_t* __restrict__ hl, int row0, int nt,
+                           int cpos, uint32_t (&XH)[NT][Fmt<BITS>::PAIRS], uint32_t (&XL)[NT][Fmt<BITS>::PAIRS],
+                           float (&XS)[NT], int ld) {
   using F = Fmt<BITS>;
+  const uint32_t ones = 0x3F803F80u;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float v[F::CODES];
     if (t < nt) {
-      const float* src = x + (size_t)(row0 + t) * ld + (size_t)cpos * F::CODES;
+      const size_t off = (size_t)(row0 + t) * ld + (size_t)cpos * F::CODES;
 #pragma unroll
-      for (int i = 0; i < F::CODES / 4; ++i) {
-        const float4 q = *reinterpret_cast<const float4*>(src + 4 * i);
-        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+      for (int i = 0; i < F::PAIRS / 4; ++i) {
+        const moeq_u32x4 a = *reinterpret_cast<const moeq_u32x4*>(hh + off + 8 * i);
+        const moeq_u32x4 b = *reinterpret_cast<const moeq_u32x4*>(hl + off + 8 * i);
+        XH[t][4 * i] = a.x; XH[t][4 * i + 1] = a.y; XH[t][4 * i + 2] = a.z; XH[t][4 * i + 3] = a.w;
+        XL[t][4 * i] = b.x; XL[t][4 * i + 1] = b.y; XL[t][4 * i + 2] = b.z; XL[t][4 * i + 3] = b.w;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < F::CODES; ++i) v[i] = 0.0f;
+      for (int p = 0; p < F::PAIRS; ++p) { XH[t][p] = 0u; XL[t][p] = 0u; }
     }
     float s = 0.0f;
 #pragma unroll
     for (int p = 0; p < F::PAIRS; ++p) {
-      const float a = v[pair_code<BITS>(p, 0)], b = v[pair_code<BITS>(p, 1)];
-      const uint32_t ah = f32_to_bf16_bits(a), bh = f32_to_bf16_bits(b);
-      const uint32_t al = f32_to_bf16_bits(a - bf16_bits_to_f32(ah));
-      const uint32_t bl = f32_to_bf16_bits(b - bf16_bits_to_f32(bh));
-      XH[t][p] = ah | (bh << 16);
-      XL[t][p] = al | (bl << 16);
-      s += (bf16_bits_to_f32(ah) + bf16_bits_to_f32(al)) + (bf16_bits_to_f32(bh) + bf16_bits_to_f32(bl));
+      s = dot2_bf16(XH[t][p], ones, s);
+      s = dot2_bf16(XL[t][p], ones, s);
     }
     XS[t] = s;
   }
+}
+
+// Where natural index i of a K = I row of h is stored for a down projection
+// at DBITS: chunk-major, and inside a chunk pair p's two halves at 2p, 2p+1
+// (the inverse of pair_code).  4-bit: code 8q + r sits in pair 4q + (r & 3),
+// half r >> 2.  8-bit: pairs are natural.  6-bit: a 16-entry nibble table.
+template <int DBITS>
+MOEQ_DEV int h_store_pos(int i) {
+  using F = Fmt<DBITS>;
+  const int c = i / F::CODES, j = i % F::CODES;
+  int pos;
+  if constexpr (DBITS == 4) {
+    pos = (j & ~7) + 2 * (j & 3) + ((j >> 2) & 1);
+  } else if constexpr (DBITS == 8) {
+    pos = j;
+  } else {
+    // position of code j: codes (0,3)->(0,1), (1,4)->(2,3), (5,8)->(4,5),
+    // (6,9)->(6,7), (10,13)->(8,9), (11,14)->(10,11), (2,7)->(12,13),
+    // (12,15)->(14,15)
+    constexpr uint64_t kPos = 0xFB9EA875D6431C20ull;   // nibble j = position of code j
+    pos = (int)((kPos >> (4 * j)) & 0xF);
+  }
+  return c * F::CODES + pos;
 }
 
 // Partial dot products of one row chunk against NT tokens with the group's
@@ -119,124 +143,156 @@ MOEQ_DEV void chunk_dot(const uint32_t (&d)[Fmt<BITS>::DW], uint32_t szw, const 
   const float zc = f16_bits_to_f32(szw >> 16) + F::OFFSET;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float a = 0.0f;
+    // four independent accumulation chains: the dot2 results are not
+    // waited on one after another
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int p = 0; p < F::PAIRS; ++p) {
-      a = dot2_bf16(P[p], X0[t][p], a);
-      if constexpr (NX == 2) a = dot2_bf16(P[p], X1[t][p], a);
+      a[p & 3] = dot2_bf16(P[p], X0[t][p], a[p & 3]);
+      if constexpr (NX == 2) a[p & 3] = dot2_bf16(P[p], X1[t][p], a[p & 3]);
     }
-    out[t] = fmaf(s, a - zc * XS[t], out[t]);
+    const float acc = (a[0] + a[1]) + (a[2] + a[3]);
+    out[t] = fmaf(s, acc - zc * XS[t], out[t]);
   }
 }
 
+// Empty register-only barrier (no instruction is emitted): makes the packed
+// weights look modified at the start of each token pass, so the compiler
+// re-derives the bf16 pairs per pass instead of keeping all of them live.
+template <int CH, int DW>
+MOEQ_DEV void opaque(uint32_t (&d)[CH][DW]) {
+#pragma unroll
+  for (int s = 0; s < CH; ++s)
+#pragma unroll
+    for (int j = 0; j < DW; ++j) asm volatile("" : "+v"(d[s][j]));
+}
+
+template <int ITER, int LPR>
 struct Geo {
-  int lpr, iter, rpw;   // lanes per row, chunks per lane, rows per wave step
-  int rg, cl;           // this lane's row within the step and chunk column
-  MOEQ_DEV Geo(int lpr_, int iter_) : lpr(lpr_), iter(iter_), rpw(64 / lpr_) {
+  static constexpr int iter = ITER;      // chunks per lane per row
+  static constexpr int lpr = LPR;        // lanes per row
+  static constexpr int rpw = 64 / LPR;   // rows per wave step
+  int rg, cl;           // this lane's row within a step and its chunk column
+  MOEQ_DEV Geo() {
     const int lane = threadIdx.x & 63;
-    rg = lane / lpr;
-    cl = lane % lpr;
+    rg = lane / LPR;
+    cl = lane % LPR;
   }
+  MOEQ_DEV bool writer() const { return cl == LPR - 1; }   // holds the row sum
+  // chunk s of this lane: row step s / iter, chunk column cl + lpr * (s % iter)
+  MOEQ_DEV int row_of(int s) const { return (s / ITER) * rpw + rg; }
+  MOEQ_DEV int cpos_of(int s) const { return cl + lpr * (s % ITER); }
 };
 
+constexpr int gateup_ch(int iter) { return iter == 1 ? 8 : (iter == 3 ? 3 : 4); }
+constexpr int down_ch(int iter) { return iter == 1 ? 8 : (iter == 3 ? 6 : 4); }
+
 // -------------------------------------------------------------------------
-// gate/up: h[p][i] = silu(Wg x_t)[i] * (Wu x_t)[i] for tokens p0..p0+nt
+// gate/up: h[p][i] = silu(Wg x_t)[i] * (Wu x_t)[i]
+// A wave owns CH/ITER row steps (CH chunks of gate and of up per lane).  All
+// of its weight chunks are loaded into registers first; then every pass over
+// up to kMaxNT of the expert's tokens reuses them, one chunk column (ITER)
+// of activations at a time.
 // -------------------------------------------------------------------------
-template <int BITS, int NT>
-MOEQ_DEV void gateup_rows(const uint8_t* __restrict__ gq, const uint32_t* __restrict__ gsz,
-                          const uint8_t* __restrict__ uq, const uint32_t* __restrict__ usz,
-                          const uint16_t* __restrict__ x, int H, int I, int kS, const int32_t* __restrict__ sorted,
-                          int e, int p0, int nt, int row_begin, int row_end, const Geo& g, float* part,
-                          float* __restrict__ h) {
+template <int BITS, int DBITS, int ITER, int LPR, int CH, int NT>
+MOEQ_DEV void gateup_pass(uint32_t (&dg)[CH][Fmt<BITS>::DW], uint32_t (&du)[CH][Fmt<BITS>::DW],
+                          const uint32_t (&sg)[CH], const uint32_t (&su)[CH], const uint16_t* __restrict__ x,
+                          int H, int I, int kS, const int32_t* __restrict__ sorted, int p0, int nt, int row0,
+                          int I_end, const Geo<ITER, LPR>& g, uint16_t* __restrict__ hh,
+                          uint16_t* __restrict__ hl) {
   using F = Fmt<BITS>;
+  opaque(dg);
+  opaque(du);
   int tok[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) tok[t] = t < nt ? sorted[p0 + t] / kS : 0;
-  const size_t rb = row_bytes(H, BITS), gpr = H / 64;
-  for (int it = 0; it < g.iter; ++it) {
-    const int cpos = g.cl + g.lpr * it;
+  float ag[CH][NT], au[CH][NT];
+#pragma unroll
+  for (int s = 0; s < CH; ++s)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) { ag[s][t] = 0.0f; au[s][t] = 0.0f; }
+#pragma unroll 1
+  for (int it = 0; it < ITER; ++it) {
     uint32_t X[NT][F::PAIRS];
     float XS[NT];
-    load_x_bf16<BITS, NT>(x, tok, nt, cpos, X, XS, H);
-    for (int r0 = row_begin; r0 < row_end; r0 += kUnroll * g.rpw) {
-      uint32_t dg[kUnroll][F::DW], du[kUnroll][F::DW], sg[kUnroll], su[kUnroll];
+    load_x_bf16<BITS, NT>(x, tok, nt, g.cl + g.lpr * it, X, XS, H);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (r0 + u * g.rpw < row_end) {
-          const size_t grow = (size_t)e * I + r0 + u * g.rpw + g.rg;
-          load_chunk<BITS>(gq + grow * rb + (size_t)cpos * F::BYTES, dg[u]);
-          load_chunk<BITS>(uq + grow * rb + (size_t)cpos * F::BYTES, du[u]);
-          sg[u] = gsz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
-          su[u] = usz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (r0 + u * g.rpw >= row_end) break;
-        const int row = r0 + u * g.rpw + g.rg;
-        float cg[NT], cu[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) { cg[t] = 0.0f; cu[t] = 0.0f; }
-        chunk_dot<BITS, NT, 1>(dg[u], sg[u], X, X, XS, cg);
-        chunk_dot<BITS, NT, 1>(du[u], su[u], X, X, XS, cu);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const float gv = group_sum(cg[t], g.lpr);
-          const float uv = group_sum(cu[t], g.lpr);
-          if (g.cl == 0 && t < nt) {
-            if (g.iter == 1) {
-              h[(size_t)(p0 + t) * I + row] = silu_f32(gv) * uv;
-            } else {
-              float* pp = part + 2 * (NT * (row - row_begin) + t);
-              if (it == 0) { pp[0] = gv; pp[1] = uv; }
-              else { pp[0] += gv; pp[1] += uv; }
-            }
-          }
-        }
+    for (int s = 0; s < CH; ++s) {
+      if (s % ITER == it) {
+        chunk_dot<BITS, NT, 1>(dg[s], sg[s], X, X, XS, ag[s]);
+        chunk_dot<BITS, NT, 1>(du[s], su[s], X, X, XS, au[s]);
       }
     }
   }
-  if (g.iter > 1) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int lane = threadIdx.x & 63;
-    for (int i = lane; i < (row_end - row_begin) * NT; i += 64) {
-      const int rl = i / NT, t = i % NT;
-      if (t < nt) h[(size_t)(p0 + t) * I + row_begin + rl] = silu_f32(part[2 * i]) * part[2 * i + 1];
+  // rows: chunks s = step*iter .. step*iter+iter-1 belong to row step `step`
+#pragma unroll
+  for (int s = 0; s < CH; ++s) {
+    if (s % ITER != 0) continue;
+    float gs[NT], us[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) { gs[t] = ag[s][t]; us[t] = au[s][t]; }
+#pragma unroll
+    for (int q = 1; q < CH; ++q)
+      if (q < ITER && s + q < CH) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) { gs[t] += ag[s + q][t]; us[t] += au[s + q][t]; }
+      }
+    const int row = row0 + g.row_of(s);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float gv = group_sum_last<LPR>(gs[t]);
+      const float uv = group_sum_last<LPR>(us[t]);
+      if (g.writer() && t < nt && row < I_end) {
+        const float hv = silu_f32(gv) * uv;
+        const uint32_t hb = f32_to_bf16_bits(hv);
+        const size_t o = (size_t)(p0 + t) * I + h_store_pos<DBITS>(row);
+        hh[o] = (uint16_t)hb;
+        hl[o] = (uint16_t)f32_to_bf16_bits(hv - bf16_bits_to_f32(hb));
+      }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
-template <int BITS>
-__global__ __launch_bounds__(256) void gateup_gemv_kernel(const uint8_t* __restrict__ gq, const uint32_t* __restrict__ gsz,
+template <int BITS, int DBITS, int ITER, int LPR>
+__global__ __launch_bounds__(256, 2) void gateup_gemv_kernel(const uint8_t* __restrict__ gq, const uint32_t* __restrict__ gsz,
                                                           const uint8_t* __restrict__ uq, const uint32_t* __restrict__ usz,
                                                           const uint16_t* __restrict__ x, int H, int I, int kS,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ sorted,
                                                           const int32_t* __restrict__ active, int tiles,
-                                                          int rows_per_wave, int lpr, int iter,
-                                                          float* __restrict__ h) {
-  __shared__ float part_all[4][2 * kMaxNT * kMaxRowsPerWave];
+                                                          uint16_t* __restrict__ hh, uint16_t* __restrict__ hl) {
+  using F = Fmt<BITS>;
+  constexpr int CH = gateup_ch(ITER);
   const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-  if (slot >= active[0]) return;
-  const int e = active[1 + slot];
-  const int pb = offsets[e], pe = offsets[e + 1];
+  const int n_active = active[0];
+  const int e = active[1 + slot];   // in bounds: slot < E + S; read before the check
+  if (slot >= n_active) return;
+  const Geo<ITER, LPR> g;
   const int wave = threadIdx.x >> 6;
-  const int row_begin = (tile * 4 + wave) * rows_per_wave;
-  const int row_end = min(I, row_begin + rows_per_wave);
-  if (row_begin >= I) return;
-  const Geo g(lpr, iter);
-  float* part = part_all[wave];
+  const int rows_w = (CH / ITER) * g.rpw;
+  const int row0 = (tile * 4 + wave) * rows_w;
+  if (row0 >= I) return;
+  const int I_end = min(I, row0 + rows_w);
+  const size_t rb = row_bytes(H, BITS), gpr = H / 64;
+  // all weight chunks of this wave first
+  uint32_t dg[CH][F::DW], du[CH][F::DW], sg[CH], su[CH];
+#pragma unroll
+  for (int s = 0; s < CH; ++s) {
+    const int row = min(row0 + g.row_of(s), I - 1);   // rows past I repeat the last row, never stored
+    const int cpos = g.cpos_of(s);
+    const size_t grow = (size_t)e * I + row;
+    load_chunk<BITS>(gq + grow * rb + (size_t)cpos * F::BYTES, dg[s]);
+    load_chunk<BITS>(uq + grow * rb + (size_t)cpos * F::BYTES, du[s]);
+    sg[s] = gsz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
+    su[s] = usz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
+  }
+  const int pb = offsets[e], pe = offsets[e + 1];
   for (int p0 = pb; p0 < pe;) {
     if (pe - p0 >= 2) {
-      gateup_rows<BITS, 2>(gq, gsz, uq, usz, x, H, I, kS, sorted, e, p0, 2, row_begin, row_end, g, part, h);
+      gateup_pass<BITS, DBITS, ITER, LPR, CH, 2>(dg, du, sg, su, x, H, I, kS, sorted, p0, 2, row0, I_end, g, hh, hl);
       p0 += 2;
     } else {
-      gateup_rows<BITS, 1>(gq, gsz, uq, usz, x, H, I, kS, sorted, e, p0, 1, row_begin, row_end, g, part, h);
+      gateup_pass<BITS, DBITS, ITER, LPR, CH, 1>(dg, du, sg, su, x, H, I, kS, sorted, p0, 1, row0, I_end, g, hh, hl);
       p0 += 1;
     }
   }
@@ -245,93 +301,88 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(const uint8_t* __restr
 // -------------------------------------------------------------------------
 // down: y[a][n] = (Wd h_p)[n] for the expert's assignments a = sorted[p]
 // -------------------------------------------------------------------------
-template <int BITS, int NT>
-MOEQ_DEV void down_rows(const uint8_t* __restrict__ dq, const uint32_t* __restrict__ dsz, const float* __restrict__ h,
-                        int H, int I, const int32_t* __restrict__ sorted, int e, int p0, int nt, int row_begin,
-                        int row_end, const Geo& g, float* part, float* __restrict__ y) {
+template <int BITS, int ITER, int LPR, int CH, int NT>
+MOEQ_DEV void down_pass(uint32_t (&d)[CH][Fmt<BITS>::DW], const uint32_t (&sw)[CH], const uint16_t* __restrict__ hh,
+                        const uint16_t* __restrict__ hl,
+                        int H, int I, const int32_t* __restrict__ sorted, int p0, int nt, int row0, int H_end,
+                        const Geo<ITER, LPR>& g, float* __restrict__ y) {
   using F = Fmt<BITS>;
+  opaque(d);
   int arow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) arow[t] = t < nt ? sorted[p0 + t] : 0;
-  const size_t rb = row_bytes(I, BITS), gpr = I / 64;
-  for (int it = 0; it < g.iter; ++it) {
-    const int cpos = g.cl + g.lpr * it;
+  float ac[CH][NT];
+#pragma unroll
+  for (int s = 0; s < CH; ++s)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ac[s][t] = 0.0f;
+#pragma unroll 1
+  for (int it = 0; it < ITER; ++it) {
     uint32_t XH[NT][F::PAIRS], XL[NT][F::PAIRS];
     float XS[NT];
-    load_x_f32<BITS, NT>(h, p0, nt, cpos, XH, XL, XS, I);
-    for (int r0 = row_begin; r0 < row_end; r0 += kUnroll * g.rpw) {
-      uint32_t d[kUnroll][F::DW], sw[kUnroll];
+    load_h_pairs<BITS, NT>(hh, hl, p0, nt, g.cl + g.lpr * it, XH, XL, XS, I);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (r0 + u * g.rpw < row_end) {
-          const size_t grow = (size_t)e * H + r0 + u * g.rpw + g.rg;
-          load_chunk<BITS>(dq + grow * rb + (size_t)cpos * F::BYTES, d[u]);
-          sw[u] = dsz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (r0 + u * g.rpw >= row_end) break;
-        const int row = r0 + u * g.rpw + g.rg;
-        float c[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) c[t] = 0.0f;
-        chunk_dot<BITS, NT, 2>(d[u], sw[u], XH, XL, XS, c);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const float v = group_sum(c[t], g.lpr);
-          if (g.cl == 0 && t < nt) {
-            if (g.iter == 1) {
-              y[(size_t)arow[t] * H + row] = v;
-            } else {
-              float* pp = part + NT * (row - row_begin) + t;
-              if (it == 0) *pp = v;
-              else *pp += v;
-            }
-          }
-        }
-      }
-    }
+    for (int s = 0; s < CH; ++s)
+      if (s % ITER == it) chunk_dot<BITS, NT, 2>(d[s], sw[s], XH, XL, XS, ac[s]);
   }
-  if (g.iter > 1) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int lane = threadIdx.x & 63;
-    for (int i = lane; i < (row_end - row_begin) * NT; i += 64) {
-      const int rl = i / NT, t = i % NT;
-      if (t < nt) y[(size_t)arow[t] * H + row_begin + rl] = part[i];
+#pragma unroll
+  for (int s = 0; s < CH; ++s) {
+    if (s % ITER != 0) continue;
+    float cs[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) cs[t] = ac[s][t];
+#pragma unroll
+    for (int q = 1; q < CH; ++q)
+      if (q < ITER && s + q < CH) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) cs[t] += ac[s + q][t];
+      }
+    const int row = row0 + g.row_of(s);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float v = group_sum_last<LPR>(cs[t]);
+      if (g.writer() && t < nt && row < H_end) y[(size_t)arow[t] * H + row] = v;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
-template <int BITS>
-__global__ __launch_bounds__(256) void down_gemv_kernel(const uint8_t* __restrict__ dq, const uint32_t* __restrict__ dsz,
-                                                        const float* __restrict__ h, int H, int I,
+template <int BITS, int ITER, int LPR>
+__global__ __launch_bounds__(256, 2) void down_gemv_kernel(const uint8_t* __restrict__ dq, const uint32_t* __restrict__ dsz,
+                                                        const uint16_t* __restrict__ hh, const uint16_t* __restrict__ hl,
+                                                        int H, int I,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ sorted,
                                                         const int32_t* __restrict__ active, int tiles,
-                                                        int rows_per_wave, int lpr, int iter, float* __restrict__ y) {
-  __shared__ float part_all[4][kMaxNT * kMaxRowsPerWave];
+                                                        float* __restrict__ y) {
+  using F = Fmt<BITS>;
+  constexpr int CH = down_ch(ITER);
   const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-  if (slot >= active[0]) return;
-  const int e = active[1 + slot];
-  const int pb = offsets[e], pe = offsets[e + 1];
+  const int n_active = active[0];
+  const int e = active[1 + slot];   // in bounds: slot < E + S; read before the check
+  if (slot >= n_active) return;
+  const Geo<ITER, LPR> g;
   const int wave = threadIdx.x >> 6;
-  const int row_begin = (tile * 4 + wave) * rows_per_wave;
-  const int row_end = min(H, row_begin + rows_per_wave);
-  if (row_begin >= H) return;
-  const Geo g(lpr, iter);
-  float* part = part_all[wave];
+  const int rows_w = (CH / ITER) * g.rpw;
+  const int row0 = (tile * 4 + wave) * rows_w;
+  if (row0 >= H) return;
+  const int H_end = min(H, row0 + rows_w);
+  const size_t rb = row_bytes(I, BITS), gpr = I / 64;
+  uint32_t d[CH][F::DW], sw[CH];
+#pragma unroll
+  for (int s = 0; s < CH; ++s) {
+    const int row = min(row0 + g.row_of(s), H - 1);
+    const int cpos = g.cpos_of(s);
+    const size_t grow = (size_t)e * H + row;
+    load_chunk<BITS>(dq + grow * rb + (size_t)cpos * F::BYTES, d[s]);
+    sw[s] = dsz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
+  }
+  const int pb = offsets[e], pe = offsets[e + 1];
   for (int p0 = pb; p0 < pe;) {
     if (pe - p0 >= 2) {
-      down_rows<BITS, 2>(dq, dsz, h, H, I, sorted, e, p0, 2, row_begin, row_end, g, part, y);
+      down_pass<BITS, ITER, LPR, CH, 2>(d, sw, hh, hl, H, I, sorted, p0, 2, row0, H_end, g, y);
       p0 += 2;
     } else {
-      down_rows<BITS, 1>(dq, dsz, h, H, I, sorted, e, p0, 1, row_begin, row_end, g, part, y);
+      down_pass<BITS, ITER, LPR, CH, 1>(d, sw, hh, hl, H, I, sorted, p0, 1, row0, H_end, g, y);
       p0 += 1;
     }
   }
@@ -343,11 +394,11 @@ __global__ __launch_bounds__(256) void down_gemv_kernel(const uint8_t* __restric
 #define MOEQ_DECODE_LAUNCHERS(B, SPEC)                                                                   \
   SPEC int decode_gateup_b##B(const moe_layer_desc* L, const uint16_t* x, const int32_t* offsets,        \
                               const int32_t* sorted, const int32_t* active, int slots, int rows_per_wave, \
-                              int lpr, int iter, float* h, hipStream_t s)
+                              int lpr, int iter, uint16_t* hh, uint16_t* hl, hipStream_t s)
 #define MOEQ_DOWN_LAUNCHER(B, SPEC)                                                                      \
-  SPEC int decode_down_b##B(const moe_layer_desc* L, const float* h, const int32_t* offsets,             \
-                            const int32_t* sorted, const int32_t* active, int slots, int rows_per_wave,   \
-                            int lpr, int iter, float* y, hipStream_t s)
+  SPEC int decode_down_b##B(const moe_layer_desc* L, const uint16_t* hh, const uint16_t* hl,             \
+                            const int32_t* offsets, const int32_t* sorted, const int32_t* active,        \
+                            int slots, int rows_per_wave, int lpr, int iter, float* y, hipStream_t s)
 
 MOEQ_DECODE_LAUNCHERS(4, );
 MOEQ_DECODE_LAUNCHERS(6, );
@@ -356,20 +407,37 @@ MOEQ_DOWN_LAUNCHER(4, );
 MOEQ_DOWN_LAUNCHER(6, );
 MOEQ_DOWN_LAUNCHER(8, );
 
+// (iter, lanes per row) combinations with a kernel: lpr is the largest power
+// of two <= 64 dividing the chunks per row, iter the rest (1..4).
+#define MOEQ_DEC_SWITCH(ITERV, LPRV, CALL, RC)                       \
+  switch (ITERV * 100 + LPRV) {                                      \
+    case 164: CALL(1, 64); break;                                    \
+    case 132: CALL(1, 32); break;                                    \
+    case 116: CALL(1, 16); break;                                    \
+    case 108: CALL(1, 8); break;                                     \
+    case 264: CALL(2, 64); break;                                    \
+    case 364: CALL(3, 64); break;                                    \
+    case 332: CALL(3, 32); break;                                    \
+    case 316: CALL(3, 16); break;                                    \
+    case 308: CALL(3, 8); break;                                     \
+    case 464: CALL(4, 64); break;                                    \
+    default: RC = set_error(MOEQ_ERR_UNSUPPORTED, "decode: no kernel for %d chunks x %d lanes", ITERV, LPRV); \
+  }
+
 #define MOEQ_DEFINE_DECODE(B)                                                                            \
   MOEQ_DECODE_LAUNCHERS(B, ) {                                                                           \
     const int tiles = (L->I + 4 * rows_per_wave - 1) / (4 * rows_per_wave);                              \
-    decode_detail::gateup_gemv_kernel<B><<<slots * tiles, 256, 0, s>>>(                                  \
-        L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, L->k + L->S, offsets, sorted, active,   \
-        tiles, rows_per_wave, lpr, iter, h);                                                             \
-    return check_launch("moe_qgemv_decode (gate/up)");                                                   \
+    const int grid = slots * tiles;                                                                      \
+    int rc = MOEQ_OK;                                                                                    \
+    MOEQ_DEC_SWITCH(iter, lpr, MOEQ_GATEUP_CALL, rc)                                                     \
+    return rc != MOEQ_OK ? rc : check_launch("moe_qgemv_decode (gate/up)");                              \
   }                                                                                                      \
   MOEQ_DOWN_LAUNCHER(B, ) {                                                                              \
     const int tiles = (L->H + 4 * rows_per_wave - 1) / (4 * rows_per_wave);                              \
-    decode_detail::down_gemv_kernel<B><<<slots * tiles, 256, 0, s>>>(L->down.q, L->down.sz, h, L->H, L->I, \
-                                                                     offsets, sorted, active, tiles,     \
-                                                                     rows_per_wave, lpr, iter, y);       \
-    return check_launch("moe_qgemv_decode (down)");                                                      \
+    const int grid = slots * tiles;                                                                      \
+    int rc = MOEQ_OK;                                                                                    \
+    MOEQ_DEC_SWITCH(iter, lpr, MOEQ_DOWN_CALL, rc)                                                       \
+    return rc != MOEQ_OK ? rc : check_launch("moe_qgemv_decode (down)");                                 \
   }
 
 }  // namespace moeq

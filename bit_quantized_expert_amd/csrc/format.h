@@ -58,9 +58,18 @@ MOEQ_DEV void load_chunk(const uint8_t* __restrict__ p, uint32_t (&d)[Fmt<BITS>:
 
 MOEQ_DEV uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) { return (a & m) | o; }
 
+// The bf16 128.0 pair lives in a VGPR (an empty asm makes it opaque) so that
+// v_and_or_b32 can take the mask from an SGPR and the OR operand from this
+// register: gfx9 VOP3 encodings read at most one scalar operand.
+MOEQ_DEV uint32_t magic_128_pair() {
+  uint32_t m = 0x43004300u;
+  asm volatile("" : "+v"(m));
+  return m;
+}
+
 template <int BITS>
 MOEQ_DEV void chunk_pairs(const uint32_t (&d)[Fmt<BITS>::DW], uint32_t (&P)[Fmt<BITS>::PAIRS]) {
-  constexpr uint32_t M = 0x43004300u;   // bf16 128.0 in both halves
+  const uint32_t M = magic_128_pair();   // bf16 128.0 in both halves
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

@@ -70,16 +70,14 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
       const int e = row0 + r;
 #pragma unroll
       for (int t = 0; t < kRouterTok; ++t) {
-        const float s = wave_sum(acc[r][t]);
-        if (lane == 0 && e < E && t < nt) logits[(size_t)(t0 + t) * E + e] = s + (bias ? bias[e] : 0.0f);
+        const float s = group_sum_last<64>(acc[r][t]);
+        if (lane == 63 && e < E && t < nt) logits[(size_t)(t0 + t) * E + e] = s + (bias ? bias[e] : 0.0f);
       }
     }
   }
 }
 
 // (value, index) ordering of the selection: larger value first, then lower index.
-MOEQ_DEV bool better(float v, int e, float bv, int be) { return v > bv || (v == bv && e < be); }
-
 constexpr int kMaxSlots = 16;   // E <= 64 * 16
 
 // One wavefront per token.  Lane l holds experts l, l+64, ...; k rounds of a
@@ -112,12 +110,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       const int e = lane + 64 * i;
       if (!((taken >> i) & 1u) && (be == 0x7FFFFFFF || v[i] > bv)) { bv = v[i]; be = e; }
     }
-    // wave arg-max
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oe = __shfl_xor(be, o);
-      if (oe != 0x7FFFFFFF && (be == 0x7FFFFFFF || better(ov, oe, bv, be))) { bv = ov; be = oe; }
-    }
+    wave_argmax(bv, be);   // DPP; every lane gets the winner
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
     if (j == 0) top0 = bv;
     const float ex = expf(bv - top0);

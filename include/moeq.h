@@ -79,7 +79,9 @@ typedef struct moe_layer_desc {
 } moe_layer_desc;
 
 /* Size in bytes of the workspace the calls below need for batches of up to
- * T_max tokens of layer L (decode and prefill alike).  0 if L is invalid. */
+ * T_max tokens of layer L (decode and prefill alike).  0 if L is invalid.
+ * The workspace must be zero-filled before its first use; the library keeps
+ * the control words it relies on at zero between calls. */
 size_t moe_workspace_bytes(const moe_layer_desc* L, int T_max);
 
 /* Description of the last error raised on this thread ("" if none). */
@@ -144,6 +146,22 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int S,
                 int32_t* counts, int32_t* offsets, int32_t* sorted,
                 int32_t* inverse, int32_t* active,
                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Decode-batch routing: the results of moe_route_topk (with router weights)
+ * followed by moe_permute, bit for bit, from two small launches tuned for
+ * latency: a router kernel with one wavefront per router row, then a single
+ * block that selects every token's top k and groups the assignments.
+ * Removing dependent small launches is the decode lever the pages report
+ * (Raon-1-mini on an RTX 5070 Ti, optimisation table).
+ * Limits: T*(k+S) <= 1024, E+S <= 1024, k <= 64, H in {512, 1024, 2048,
+ * 4096}; MOEQ_ERR_UNSUPPORTED otherwise.  ws: at least 256 bytes (its first
+ * word receives the bad-id count, always 0 here). */
+int moe_route_permute_decode(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                             int T, int H, int E, int k, int S,
+                             float* logits, int32_t* topk_idx, float* topk_w,
+                             int32_t* counts, int32_t* offsets, int32_t* sorted,
+                             int32_t* inverse, int32_t* active,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Decode path (small T): for every assignment a, y[a] = Wd h with
  * h = silu(Wg x_t) * (Wu x_t), t = a / (k+S), using expert sorted-order data

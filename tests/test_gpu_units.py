@@ -184,3 +184,34 @@ def test_rmsnorm(bq):
     rd = oracle.bf16_to_f32(ref).astype(np.float64)
     assert np.all(np.abs(gd - rd) <= 2.0 ** -7 * np.abs(rd) + 1e-30)
     assert np.array_equal(got[0], ref[0])
+
+
+@pytest.mark.parametrize("wl,T", [("moe_h2048_e128_k8_b4", 1), ("moe_h2048_e128_k8_b4", 16),
+                                  ("moe_h2048_e256_k8_s1_b4", 8), ("moe_h4096_e512_k10_b4_hot", 1),
+                                  ("moe_h4096_e512_k10_b4_hot", 13), ("moe_h2048_e128_k8_b6_zipf", 64)])
+def test_route_permute_decode_fused(bq, wl, T):
+    """The one-launch decode routing equals the oracle's routing on the GPU's
+    logits (bit for bit) and its logits match the oracle's; repeated calls on
+    one workspace keep working."""
+    w = synth.get_workload(wl)
+    wr = bf16_tensor(synth.router_weight_bf16(w))
+    bias = synth.router_bias(w)
+    bt = None if bias is None else torch.from_numpy(bias).cuda()
+    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        x = synth.activations_bf16(w, T, batch=20 + rep)
+        r = bq.moe_route_permute_decode(bf16_tensor(x), wr, bt, w.E, w.k, w.S, ws)
+        logits = r[0].cpu().numpy()
+        ref_l = oracle.router_logits(x, synth.router_weight_bf16(w), bias)
+        assert np.max(np.abs(logits - ref_l)) <= 1e-5 * np.max(np.abs(ref_l))
+        idx = oracle.select_topk(logits, w.k)
+        assert np.array_equal(r[1].cpu().numpy(), idx)
+        rw = oracle.topk_weights(logits, idx)
+        assert np.max(np.abs(r[2].cpu().numpy() - rw) / rw) <= 1e-5
+        c, o, s, i = oracle.permute(idx, w.E, w.S)
+        for got, ref in zip(r[3:7], (c, o, s, i)):
+            assert np.array_equal(got.cpu().numpy(), ref)
+        act = r[7].cpu().numpy()
+        nz = np.nonzero(c)[0]
+        assert act[0] == len(nz) and np.array_equal(act[1:1 + len(nz)], nz)
+    assert ws[0:4].cpu().numpy().view(np.int32)[0] == 0   # no bad ids
