@@ -34,6 +34,8 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "bit_quantized_expert_amd", "csrc")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 DEFAULT_WORKLOAD = "moe_h2048_e256_k8_s1_b4:8"
 
@@ -48,6 +50,53 @@ def expert_bytes(w, bits):
     """Algorithmic bytes of one expert: three I x H matrices of codes plus an
     fp16 scale and zero per 64 weights."""
     return 3 * w.I * w.H * (bits / 8 + 4 / 64)
+
+
+def kernel_sources_hash():
+    """sha256 over every HIP source of the library: a counter reading taken
+    on other sources no longer describes the kernels that run."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, T):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    counter reads for a plain copy of known size), or None when there is no
+    summary for this workload or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, f"pmc_{workload}_T{T}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            k, sep, v = line.partition("=")
+            if sep:
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_hash():
+        return None
+    try:
+        return round(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibrate(mib):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
 class Step:
@@ -308,12 +357,17 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (counter calibration)")
     a = ap.parse_args()
 
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the multi-GPU sharding is described in the design notes, not built)"}))
         sys.exit(2)
+
+    if a.copy_calibrate:
+        return copy_calibrate(a.copy_calibrate)
 
     import torch
     import bit_quantized_expert_amd as bq
@@ -401,14 +455,15 @@ def main():
 
     prefill = T > bq.DECODE_MAX_T
     if prefill:
-        achieved = flops / (kern_ms * 1e-3) / 1e12
+        achieved = (flops - 2 * T * w.E * w.H) / (kern_ms * 1e-3) / 1e12   # expert FFN flops only
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "moe_qgemm_prefill (gate/up + down grouped GEMM kernels)"}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(w.name, T),
+                "kernel": "moe_qgemm_prefill (gate/up + down grouped GEMM kernels)",
+                "alg_flops_per_launch": flops - 2 * T * w.E * w.H, "kernel_us": round(kern_ms * 1e3, 3)}
     else:
         achieved = alg_expert_bytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name, T),
                 "kernel": "moe_qgemv_decode (gate/up + down grouped GEMV kernels)",
                 "alg_bytes_per_launch": round(alg_expert_bytes), "kernel_us": round(kern_ms * 1e3, 3)}
 
