@@ -225,12 +225,12 @@ def moe_permute(idx: torch.Tensor, E: int, S: int, ws: Optional[torch.Tensor] = 
 
 
 def fused_route_ok(T: int, H: int, E: int, k: int, S: int) -> bool:
-    return T * (k + S) <= 1024 and E + S <= 1024 and k <= 64 and H % 512 == 0 and H <= 4096
+    return T * (k + S) <= 1024 and E + S <= 1024 and k <= 64 and H in (512, 1024, 2048, 4096)
 
 
 def moe_route_permute_decode(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor], E: int,
                              k: int, S: int, ws: torch.Tensor, stream=None):
-    """moe_route_topk + moe_permute in one launch (decode batches).  Returns
+    """moe_route_topk + moe_permute in two short launches (decode batches).  Returns
     (logits, idx, w, counts, offsets, sorted, inverse, active)."""
     _dev(x, torch.bfloat16, "x")
     _dev(w_router, torch.bfloat16, "w_router")

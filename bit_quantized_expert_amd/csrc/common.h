@@ -116,33 +116,63 @@ MOEQ_DEV float wave_min(float v) {
   return v;
 }
 
+template <int CTRL, int ROW_MASK>
+MOEQ_DEV float dpp_max(float v) {
+  const int ninf = __builtin_bit_cast(int, -INFINITY);   // rows the mask leaves out contribute -inf
+  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(ninf, __builtin_bit_cast(int, v), CTRL,
+                                                                       ROW_MASK, 0xF, false)));
+}
+
+// Wave maximum with DPP (NaN-ignoring like fmaxf), returned on every lane.
+MOEQ_DEV float wave_max_dpp(float v) {
+  v = dpp_max<0xB1, 0xF>(v);
+  v = dpp_max<0x4E, 0xF>(v);
+  v = dpp_max<0x141, 0xF>(v);
+  v = dpp_max<0x140, 0xF>(v);
+  v = dpp_max<0x142, 0xA>(v);
+  v = dpp_max<0x143, 0x8>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// One round of top-k selection over the candidates a wave holds: lane l,
+// slot i holds expert 64 i + l with value v[i]; bit i of `taken` marks slots
+// already chosen or past the last expert.  Returns the next expert in the
+// routing order (larger value first, ties to the lower index; NaN after every
+// number, in index order), the same on every lane, marks it taken on its
+// lane, and sets `best` to its value.  Branch-free apart from uniform scalar
+// tests: a DPP maximum, then one ballot per slot finds the lowest index that
+// holds it.
+template <int NS>
+MOEQ_DEV int wave_topk_next(const float (&v)[NS], uint64_t& taken, float& best) {
+  static_assert(NS <= 64, "at most 64 slots per lane");
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) m = ((taken >> i) & 1u) ? m : fmaxf(m, v[i]);
+  m = wave_max_dpp(m);
+  int slot = -1;
+  uint64_t hit = 0;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const uint64_t b = __ballot(!((taken >> i) & 1u) && v[i] == m);
+    if (slot < 0 && b) { slot = i; hit = b; }
+  }
+  best = m;
+  if (slot < 0) {   // only NaN left
+    best = __builtin_nanf("");
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const uint64_t b = __ballot(!((taken >> i) & 1u));
+      if (slot < 0 && b) { slot = i; hit = b; }
+    }
+  }
+  const int l = __builtin_ctzll(hit);
+  if (lane == l) taken |= 1ull << slot;
+  return 64 * slot + l;
+}
+
 // silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (about
 // 1 ulp each); -g*log2(e) overflowing to +inf gives rcp(inf) = 0, i.e. 0.
-// Wave arg-max under the routing order (larger value first, then lower
-// index), DPP only; every lane returns the winner.  An empty lane carries
-// (-inf, INT_MAX).
-template <int CTRL, int ROW_MASK>
-MOEQ_DEV void argmax_step(float& v, int& e) {
-  const float ov = __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
-                                         false));
-  const int oe = __builtin_amdgcn_update_dpp(e, e, CTRL, ROW_MASK, 0xF, false);
-  const bool b = ov > v || (ov == v && oe < e);
-  v = b ? ov : v;
-  e = b ? oe : e;
-}
-
-MOEQ_DEV void wave_argmax(float& v, int& e) {
-  argmax_step<0xB1, 0xF>(v, e);
-  argmax_step<0x4E, 0xF>(v, e);
-  argmax_step<0x141, 0xF>(v, e);
-  argmax_step<0x140, 0xF>(v, e);
-  argmax_step<0x142, 0xA>(v, e);
-  argmax_step<0x143, 0x8>(v, e);
-  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-  e = __builtin_amdgcn_readlane(e, 63);
-}
-
 MOEQ_DEV float silu_f32(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
 }

@@ -23,7 +23,7 @@ bool geometry(int K, int bits, int& lpr, int& iter) {
 // Rows per wave: CH chunks per lane and matrix held in registers cover
 // CH / iter row steps of 64 / lpr rows (CH as in decode_impl.h).
 int rows_per_wave(int lpr, int iter, bool gateup) {
-  const int ch = gateup ? (iter == 1 ? 8 : (iter == 3 ? 3 : 4)) : (iter == 1 ? 8 : (iter == 3 ? 6 : 4));
+  const int ch = gateup ? decode_detail::gateup_ch(iter) : decode_detail::down_ch(iter);
   return (ch / iter) * (64 / lpr);
 }
 
@@ -49,23 +49,22 @@ extern "C" int moe_qgemv_decode(const moe_layer_desc* L, const uint16_t* x, int 
   const WsLayout wl = ws_layout(L->H, L->I, L->E, L->S, L->k, T);
   if (!ws || ws_bytes < wl.total)
     return set_error(MOEQ_ERR_WORKSPACE, "moe_qgemv_decode: workspace of %zu bytes, need %zu", ws_bytes, wl.total);
-  // h as two bf16 planes (hi, lo) of [A][I] in the down kernel's pair order
+  // h: bf16 [A][I] in the down kernel's pair order
   uint16_t* hh = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.h);
-  uint16_t* hl = hh + (size_t)T * (L->k + L->S) * L->I;
   const long A = (long)T * (L->k + L->S);
   const int slots = (int)(A < L->E + L->S ? A : L->E + L->S);   // upper bound on active experts
   const int rpw1 = rows_per_wave(lpr1, it1, true);
   const int rpw2 = rows_per_wave(lpr2, it2, false);
   switch (L->gate.bits) {
-    case 4: rc = decode_gateup_b4(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, hh, hl, stream); break;
-    case 6: rc = decode_gateup_b6(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, hh, hl, stream); break;
-    default: rc = decode_gateup_b8(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, hh, hl, stream); break;
+    case 4: rc = decode_gateup_b4(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, hh, stream); break;
+    case 6: rc = decode_gateup_b6(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, hh, stream); break;
+    default: rc = decode_gateup_b8(L, x, offsets, sorted, active, slots, rpw1, lpr1, it1, hh, stream); break;
   }
   if (rc != MOEQ_OK) return rc;
   switch (L->down.bits) {
-    case 4: rc = decode_down_b4(L, hh, hl, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
-    case 6: rc = decode_down_b6(L, hh, hl, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
-    default: rc = decode_down_b8(L, hh, hl, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
+    case 4: rc = decode_down_b4(L, hh, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
+    case 6: rc = decode_down_b6(L, hh, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
+    default: rc = decode_down_b8(L, hh, offsets, sorted, active, slots, rpw2, lpr2, it2, y, stream); break;
   }
   return rc;
 }

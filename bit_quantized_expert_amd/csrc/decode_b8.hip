@@ -8,9 +8,9 @@
     default: decode_detail::gateup_gemv_kernel<8, 8, IT, LP><<<grid, 256, 0, s>>>(GATEUP_ARGS); break;    \
   }
 #define GATEUP_ARGS \
-  L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, L->k + L->S, offsets, sorted, active, tiles, hh, hl
+  L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, L->k + L->S, offsets, sorted, active, tiles, hh
 #define MOEQ_DOWN_CALL(IT, LP)                                                                            \
-  decode_detail::down_gemv_kernel<8, IT, LP><<<grid, 256, 0, s>>>(L->down.q, L->down.sz, hh, hl, L->H,  \
+  decode_detail::down_gemv_kernel<8, IT, LP><<<grid, 256, 0, s>>>(L->down.q, L->down.sz, hh, L->H,  \
                                                                    L->I, offsets, sorted, active, tiles, y)
 
 namespace moeq {

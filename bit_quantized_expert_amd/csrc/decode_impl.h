@@ -23,12 +23,15 @@
 //     those registers, so an expert's weights are read from HBM once however
 //     many of the batch's tokens it serves;
 //   * rows are reduced across their LPR lanes with DPP.
-// The down projection reads h in fp32, split into two bf16 terms (hi + lo),
-// so its dot products carry about 16 significant bits of h.
+// The intermediate h = silu(g) u goes to the down projection in bf16, as on
+// the prefill path.
 //
 // Grid: (expert slot, row tile).  Slots index the active-expert list built by
-// moe_permute; blocks whose slot is past its end exit at once, so the host
-// never needs the routing result.
+// moe_permute, walked from its end (shared experts, which serve every token,
+// come first, so the longest blocks start first); blocks whose slot is past
+// the list's end exit at once, so the host never needs the routing result.
+// A wave holds few rows so that several waves share each SIMD: while some
+// wait for their weights, others compute.
 #pragma once
 #include "format.h"
 
@@ -72,14 +75,12 @@ MOEQ_DEV void load_x_bf16(const uint16_t* __restrict__ x, const int (&rowidx)[NT
   }
 }
 
-// The intermediate h of the down projection comes from the gate/up kernels
-// already split into two bf16 planes, hi = bf16(h) and lo = bf16(h - hi),
-// each stored in the down kernel's pair order (h_store_pos), so a chunk's
-// pairs load directly.  XS is the fp32 sum of hi + lo over the chunk.
+// The intermediate h of the down projection comes from the gate/up kernel
+// as bf16, stored in the down kernel's pair order (h_store_pos), so a
+// chunk's pairs load directly.  XS is the fp32 sum of the chunk's h values.
 template <int BITS, int NT>
-MOEQ_DEV void load_h_pairs(const uint16_t* __restrict__ hh, const uint16_t* __restrict__ hl, int row0, int nt,
-                           int cpos, uint32_t (&XH)[NT][Fmt<BITS>::PAIRS], uint32_t (&XL)[NT][Fmt<BITS>::PAIRS],
-                           float (&XS)[NT], int ld) {
+MOEQ_DEV void load_h_pairs(const uint16_t* __restrict__ hh, int row0, int nt, int cpos,
+                           uint32_t (&XH)[NT][Fmt<BITS>::PAIRS], float (&XS)[NT], int ld) {
   using F = Fmt<BITS>;
   const uint32_t ones = 0x3F803F80u;
 #pragma unroll
@@ -89,20 +90,15 @@ MOEQ_DEV void load_h_pairs(const uint16_t* __restrict__ hh, const uint16_t* __re
 #pragma unroll
       for (int i = 0; i < F::PAIRS / 4; ++i) {
         const moeq_u32x4 a = *reinterpret_cast<const moeq_u32x4*>(hh + off + 8 * i);
-        const moeq_u32x4 b = *reinterpret_cast<const moeq_u32x4*>(hl + off + 8 * i);
         XH[t][4 * i] = a.x; XH[t][4 * i + 1] = a.y; XH[t][4 * i + 2] = a.z; XH[t][4 * i + 3] = a.w;
-        XL[t][4 * i] = b.x; XL[t][4 * i + 1] = b.y; XL[t][4 * i + 2] = b.z; XL[t][4 * i + 3] = b.w;
       }
     } else {
 #pragma unroll
-      for (int p = 0; p < F::PAIRS; ++p) { XH[t][p] = 0u; XL[t][p] = 0u; }
+      for (int p = 0; p < F::PAIRS; ++p) XH[t][p] = 0u;
     }
     float s = 0.0f;
 #pragma unroll
-    for (int p = 0; p < F::PAIRS; ++p) {
-      s = dot2_bf16(XH[t][p], ones, s);
-      s = dot2_bf16(XL[t][p], ones, s);
-    }
+    for (int p = 0; p < F::PAIRS; ++p) s = dot2_bf16(XH[t][p], ones, s);
     XS[t] = s;
   }
 }
@@ -132,10 +128,9 @@ MOEQ_DEV int h_store_pos(int i) {
 
 // Partial dot products of one row chunk against NT tokens with the group's
 // scale/zero applied: out[t] += s * (sum (off+q) x - (z+off) * sum x).
-// NX = 2 adds the second (lo) activation term.
-template <int BITS, int NT, int NX>
+template <int BITS, int NT>
 MOEQ_DEV void chunk_dot(const uint32_t (&d)[Fmt<BITS>::DW], uint32_t szw, const uint32_t (&X0)[NT][Fmt<BITS>::PAIRS],
-                        const uint32_t (&X1)[NT][Fmt<BITS>::PAIRS], const float (&XS)[NT], float (&out)[NT]) {
+                        const float (&XS)[NT], float (&out)[NT]) {
   using F = Fmt<BITS>;
   uint32_t P[F::PAIRS];
   chunk_pairs<BITS>(d, P);
@@ -149,7 +144,6 @@ MOEQ_DEV void chunk_dot(const uint32_t (&d)[Fmt<BITS>::DW], uint32_t szw, const 
 #pragma unroll
     for (int p = 0; p < F::PAIRS; ++p) {
       a[p & 3] = dot2_bf16(P[p], X0[t][p], a[p & 3]);
-      if constexpr (NX == 2) a[p & 3] = dot2_bf16(P[p], X1[t][p], a[p & 3]);
     }
     const float acc = (a[0] + a[1]) + (a[2] + a[3]);
     out[t] = fmaf(s, acc - zc * XS[t], out[t]);
@@ -184,8 +178,26 @@ struct Geo {
   MOEQ_DEV int cpos_of(int s) const { return cl + lpr * (s % ITER); }
 };
 
-constexpr int gateup_ch(int iter) { return iter == 1 ? 8 : (iter == 3 ? 3 : 4); }
-constexpr int down_ch(int iter) { return iter == 1 ? 8 : (iter == 3 ? 6 : 4); }
+#ifndef MOEQ_GU_CH1
+#define MOEQ_GU_CH1 2
+#endif
+#ifndef MOEQ_DN_CH1
+#define MOEQ_DN_CH1 4
+#endif
+#ifndef MOEQ_NT2_MAX_ITER
+#define MOEQ_NT2_MAX_ITER 1
+#endif
+#ifndef MOEQ_GU_WAVES
+#define MOEQ_GU_WAVES 4
+#endif
+#ifndef MOEQ_DN_WAVES
+#define MOEQ_DN_WAVES 4
+#endif
+// chunks per lane and matrix held in registers (a multiple of iter)
+constexpr int gateup_ch(int iter) { return iter == 1 ? MOEQ_GU_CH1 : iter; }
+constexpr int down_ch(int iter) { return iter == 1 ? MOEQ_DN_CH1 : (iter == 3 ? 3 : 4); }
+constexpr int kGateupWaves = MOEQ_GU_WAVES;   // minimum waves per SIMD the register budget allows
+constexpr int kDownWaves = MOEQ_DN_WAVES;
 
 // -------------------------------------------------------------------------
 // gate/up: h[p][i] = silu(Wg x_t)[i] * (Wu x_t)[i]
@@ -198,8 +210,7 @@ template <int BITS, int DBITS, int ITER, int LPR, int CH, int NT>
 MOEQ_DEV void gateup_pass(uint32_t (&dg)[CH][Fmt<BITS>::DW], uint32_t (&du)[CH][Fmt<BITS>::DW],
                           const uint32_t (&sg)[CH], const uint32_t (&su)[CH], const uint16_t* __restrict__ x,
                           int H, int I, int kS, const int32_t* __restrict__ sorted, int p0, int nt, int row0,
-                          int I_end, const Geo<ITER, LPR>& g, uint16_t* __restrict__ hh,
-                          uint16_t* __restrict__ hl) {
+                          int I_end, const Geo<ITER, LPR>& g, uint16_t* __restrict__ hh) {
   using F = Fmt<BITS>;
   opaque(dg);
   opaque(du);
@@ -219,8 +230,8 @@ MOEQ_DEV void gateup_pass(uint32_t (&dg)[CH][Fmt<BITS>::DW], uint32_t (&du)[CH][
 #pragma unroll
     for (int s = 0; s < CH; ++s) {
       if (s % ITER == it) {
-        chunk_dot<BITS, NT, 1>(dg[s], sg[s], X, X, XS, ag[s]);
-        chunk_dot<BITS, NT, 1>(du[s], su[s], X, X, XS, au[s]);
+        chunk_dot<BITS, NT>(dg[s], sg[s], X, XS, ag[s]);
+        chunk_dot<BITS, NT>(du[s], su[s], X, XS, au[s]);
       }
     }
   }
@@ -244,29 +255,26 @@ MOEQ_DEV void gateup_pass(uint32_t (&dg)[CH][Fmt<BITS>::DW], uint32_t (&du)[CH][
       const float uv = group_sum_last<LPR>(us[t]);
       if (g.writer() && t < nt && row < I_end) {
         const float hv = silu_f32(gv) * uv;
-        const uint32_t hb = f32_to_bf16_bits(hv);
-        const size_t o = (size_t)(p0 + t) * I + h_store_pos<DBITS>(row);
-        hh[o] = (uint16_t)hb;
-        hl[o] = (uint16_t)f32_to_bf16_bits(hv - bf16_bits_to_f32(hb));
+        hh[(size_t)(p0 + t) * I + h_store_pos<DBITS>(row)] = (uint16_t)f32_to_bf16_bits(hv);
       }
     }
   }
 }
 
 template <int BITS, int DBITS, int ITER, int LPR>
-__global__ __launch_bounds__(256, 2) void gateup_gemv_kernel(const uint8_t* __restrict__ gq, const uint32_t* __restrict__ gsz,
+__global__ __launch_bounds__(256, ITER <= 2 ? kGateupWaves : 2) void gateup_gemv_kernel(const uint8_t* __restrict__ gq, const uint32_t* __restrict__ gsz,
                                                           const uint8_t* __restrict__ uq, const uint32_t* __restrict__ usz,
                                                           const uint16_t* __restrict__ x, int H, int I, int kS,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ sorted,
                                                           const int32_t* __restrict__ active, int tiles,
-                                                          uint16_t* __restrict__ hh, uint16_t* __restrict__ hl) {
+                                                          uint16_t* __restrict__ hh) {
   using F = Fmt<BITS>;
   constexpr int CH = gateup_ch(ITER);
-  const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-  const int n_active = active[0];
-  const int e = active[1 + slot];   // in bounds: slot < E + S; read before the check
-  if (slot >= n_active) return;
+  const int n_active = min(active[0], (int)(gridDim.x / tiles));   // the grid has a block row per possible slot
+  const int slot = n_active - 1 - (int)(blockIdx.x / tiles), tile = blockIdx.x % tiles;
+  if (slot < 0) return;
+  const int e = active[1 + slot];
   const Geo<ITER, LPR> g;
   const int wave = threadIdx.x >> 6;
   const int rows_w = (CH / ITER) * g.rpw;
@@ -287,12 +295,13 @@ __global__ __launch_bounds__(256, 2) void gateup_gemv_kernel(const uint8_t* __re
     su[s] = usz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
   }
   const int pb = offsets[e], pe = offsets[e + 1];
+  constexpr bool NT2 = ITER <= MOEQ_NT2_MAX_ITER;
   for (int p0 = pb; p0 < pe;) {
-    if (pe - p0 >= 2) {
-      gateup_pass<BITS, DBITS, ITER, LPR, CH, 2>(dg, du, sg, su, x, H, I, kS, sorted, p0, 2, row0, I_end, g, hh, hl);
+    if (NT2 && pe - p0 >= 2) {
+      gateup_pass<BITS, DBITS, ITER, LPR, CH, 2>(dg, du, sg, su, x, H, I, kS, sorted, p0, 2, row0, I_end, g, hh);
       p0 += 2;
     } else {
-      gateup_pass<BITS, DBITS, ITER, LPR, CH, 1>(dg, du, sg, su, x, H, I, kS, sorted, p0, 1, row0, I_end, g, hh, hl);
+      gateup_pass<BITS, DBITS, ITER, LPR, CH, 1>(dg, du, sg, su, x, H, I, kS, sorted, p0, 1, row0, I_end, g, hh);
       p0 += 1;
     }
   }
@@ -303,7 +312,6 @@ __global__ __launch_bounds__(256, 2) void gateup_gemv_kernel(const uint8_t* __re
 // -------------------------------------------------------------------------
 template <int BITS, int ITER, int LPR, int CH, int NT>
 MOEQ_DEV void down_pass(uint32_t (&d)[CH][Fmt<BITS>::DW], const uint32_t (&sw)[CH], const uint16_t* __restrict__ hh,
-                        const uint16_t* __restrict__ hl,
                         int H, int I, const int32_t* __restrict__ sorted, int p0, int nt, int row0, int H_end,
                         const Geo<ITER, LPR>& g, float* __restrict__ y) {
   using F = Fmt<BITS>;
@@ -318,12 +326,12 @@ MOEQ_DEV void down_pass(uint32_t (&d)[CH][Fmt<BITS>::DW], const uint32_t (&sw)[C
     for (int t = 0; t < NT; ++t) ac[s][t] = 0.0f;
 #pragma unroll 1
   for (int it = 0; it < ITER; ++it) {
-    uint32_t XH[NT][F::PAIRS], XL[NT][F::PAIRS];
+    uint32_t XH[NT][F::PAIRS];
     float XS[NT];
-    load_h_pairs<BITS, NT>(hh, hl, p0, nt, g.cl + g.lpr * it, XH, XL, XS, I);
+    load_h_pairs<BITS, NT>(hh, p0, nt, g.cl + g.lpr * it, XH, XS, I);
 #pragma unroll
     for (int s = 0; s < CH; ++s)
-      if (s % ITER == it) chunk_dot<BITS, NT, 2>(d[s], sw[s], XH, XL, XS, ac[s]);
+      if (s % ITER == it) chunk_dot<BITS, NT>(d[s], sw[s], XH, XS, ac[s]);
   }
 #pragma unroll
   for (int s = 0; s < CH; ++s) {
@@ -347,19 +355,18 @@ MOEQ_DEV void down_pass(uint32_t (&d)[CH][Fmt<BITS>::DW], const uint32_t (&sw)[C
 }
 
 template <int BITS, int ITER, int LPR>
-__global__ __launch_bounds__(256, 2) void down_gemv_kernel(const uint8_t* __restrict__ dq, const uint32_t* __restrict__ dsz,
-                                                        const uint16_t* __restrict__ hh, const uint16_t* __restrict__ hl,
-                                                        int H, int I,
+__global__ __launch_bounds__(256, ITER <= 2 ? kDownWaves : 2) void down_gemv_kernel(const uint8_t* __restrict__ dq, const uint32_t* __restrict__ dsz,
+                                                        const uint16_t* __restrict__ hh, int H, int I,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ sorted,
                                                         const int32_t* __restrict__ active, int tiles,
                                                         float* __restrict__ y) {
   using F = Fmt<BITS>;
   constexpr int CH = down_ch(ITER);
-  const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-  const int n_active = active[0];
-  const int e = active[1 + slot];   // in bounds: slot < E + S; read before the check
-  if (slot >= n_active) return;
+  const int n_active = min(active[0], (int)(gridDim.x / tiles));   // the grid has a block row per possible slot
+  const int slot = n_active - 1 - (int)(blockIdx.x / tiles), tile = blockIdx.x % tiles;
+  if (slot < 0) return;
+  const int e = active[1 + slot];
   const Geo<ITER, LPR> g;
   const int wave = threadIdx.x >> 6;
   const int rows_w = (CH / ITER) * g.rpw;
@@ -377,12 +384,13 @@ __global__ __launch_bounds__(256, 2) void down_gemv_kernel(const uint8_t* __rest
     sw[s] = dsz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
   }
   const int pb = offsets[e], pe = offsets[e + 1];
+  constexpr bool NT2 = ITER <= MOEQ_NT2_MAX_ITER;
   for (int p0 = pb; p0 < pe;) {
-    if (pe - p0 >= 2) {
-      down_pass<BITS, ITER, LPR, CH, 2>(d, sw, hh, hl, H, I, sorted, p0, 2, row0, H_end, g, y);
+    if (NT2 && pe - p0 >= 2) {
+      down_pass<BITS, ITER, LPR, CH, 2>(d, sw, hh, H, I, sorted, p0, 2, row0, H_end, g, y);
       p0 += 2;
     } else {
-      down_pass<BITS, ITER, LPR, CH, 1>(d, sw, hh, hl, H, I, sorted, p0, 1, row0, H_end, g, y);
+      down_pass<BITS, ITER, LPR, CH, 1>(d, sw, hh, H, I, sorted, p0, 1, row0, H_end, g, y);
       p0 += 1;
     }
   }
@@ -394,9 +402,9 @@ __global__ __launch_bounds__(256, 2) void down_gemv_kernel(const uint8_t* __rest
 #define MOEQ_DECODE_LAUNCHERS(B, SPEC)                                                                   \
   SPEC int decode_gateup_b##B(const moe_layer_desc* L, const uint16_t* x, const int32_t* offsets,        \
                               const int32_t* sorted, const int32_t* active, int slots, int rows_per_wave, \
-                              int lpr, int iter, uint16_t* hh, uint16_t* hl, hipStream_t s)
+                              int lpr, int iter, uint16_t* hh, hipStream_t s)
 #define MOEQ_DOWN_LAUNCHER(B, SPEC)                                                                      \
-  SPEC int decode_down_b##B(const moe_layer_desc* L, const uint16_t* hh, const uint16_t* hl,             \
+  SPEC int decode_down_b##B(const moe_layer_desc* L, const uint16_t* hh,                                 \
                             const int32_t* offsets, const int32_t* sorted, const int32_t* active,        \
                             int slots, int rows_per_wave, int lpr, int iter, float* y, hipStream_t s)
 

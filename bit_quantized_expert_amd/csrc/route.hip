@@ -78,40 +78,32 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 }
 
 // (value, index) ordering of the selection: larger value first, then lower index.
-constexpr int kMaxSlots = 16;   // E <= 64 * 16
+constexpr int kMaxSlots = 64;   // E <= 64 * 64 candidates per wave
 
 // One wavefront per token.  Lane l holds experts l, l+64, ...; k rounds of a
 // wave arg-max, the owner lane then drops the winner from its candidates.
+template <int NS>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* L = logits + (size_t)t * E;
-  float v[kMaxSlots];
-  uint32_t taken = 0;
-  const int nslot = (E + 63) / 64;
+  float v[NS];
+  uint64_t taken = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i) {
+  for (int i = 0; i < NS; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (i < nslot && e < E) ? L[e] : 0.0f;
-    if (!(i < nslot && e < E)) taken |= 1u << i;
+    v[i] = e < E ? L[e] : -INFINITY;
+    if (e >= E) taken |= 1ull << i;
   }
   float top0 = 0.0f;
   float wsum = 0.0f;
   int32_t* idx_row = idx_out + (size_t)t * k;
   float* w_row = w_out + (size_t)t * k;
   for (int j = 0; j < k; ++j) {
-    // best remaining candidate of this lane (ascending index -> strict >)
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kMaxSlots; ++i) {
-      const int e = lane + 64 * i;
-      if (!((taken >> i) & 1u) && (be == 0x7FFFFFFF || v[i] > bv)) { bv = v[i]; be = e; }
-    }
-    wave_argmax(bv, be);   // DPP; every lane gets the winner
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    float bv;
+    const int be = wave_topk_next<NS>(v, taken, bv);   // the same on every lane
     if (j == 0) top0 = bv;
     const float ex = expf(bv - top0);
     wsum += ex;
@@ -152,6 +144,14 @@ extern "C" int moe_route_topk(const uint16_t* x, const uint16_t* w_router, const
       if (rc != MOEQ_OK) return rc;
     }
   }
-  topk_kernel<<<(T + 3) / 4, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+  const unsigned grid = (unsigned)((T + 3) / 4);
+  const int ns = (E + 63) / 64;
+  if (ns <= 1) topk_kernel<1><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+  else if (ns <= 2) topk_kernel<2><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+  else if (ns <= 4) topk_kernel<4><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+  else if (ns <= 8) topk_kernel<8><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+  else if (ns <= 16) topk_kernel<16><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+  else if (ns <= 32) topk_kernel<32><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+  else topk_kernel<64><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
   return check_launch("moe_route_topk (top-k)");
 }

@@ -23,6 +23,9 @@ constexpr int kMaxRowChunks = 8;                 // H <= 4096 (8 x 16 B per lane
 constexpr int kMaxA = 1024;
 constexpr int kMaxExp = 1024;
 
+// tokens whose activations are loaded together (at most 128 registers of them)
+constexpr int tok_group(int nch) { return nch <= 4 ? 8 : 4; }
+
 template <int NCH>
 __global__ __launch_bounds__(64) void router_rows_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ wr,
@@ -35,18 +38,30 @@ __global__ __launch_bounds__(64) void router_rows_kernel(const uint16_t* __restr
 #pragma unroll
   for (int i = 0; i < NCH; ++i) w4[i] = *reinterpret_cast<const moeq_u32x4*>(wr + (size_t)e * H + 8 * (lane + 64 * i));
   const float be = bias ? bias[e] : 0.0f;
-  for (int t = 0; t < T; ++t) {
-    float a = 0.0f;
+  constexpr int kTokGroup = tok_group(NCH);
+  for (int t0 = 0; t0 < T; t0 += kTokGroup) {
+    // every activation load of the group is issued before the first use
+    moeq_u32x4 xv[kTokGroup][NCH];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const moeq_u32x4 xv = *reinterpret_cast<const moeq_u32x4*>(x + (size_t)t * H + 8 * (lane + 64 * i));
-      a = dot2_bf16(w4[i].x, xv.x, a);
-      a = dot2_bf16(w4[i].y, xv.y, a);
-      a = dot2_bf16(w4[i].z, xv.z, a);
-      a = dot2_bf16(w4[i].w, xv.w, a);
+    for (int u = 0; u < kTokGroup; ++u) {
+      const int t = min(t0 + u, T - 1);   // past the end: repeat the last token, never stored
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+        xv[u][i] = *reinterpret_cast<const moeq_u32x4*>(x + (size_t)t * H + 8 * (lane + 64 * i));
     }
-    a = group_sum_last<64>(a);
-    if (lane == 63) logits[(size_t)t * E + e] = a + be;
+#pragma unroll
+    for (int u = 0; u < kTokGroup; ++u) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        a = dot2_bf16(w4[i].x, xv[u][i].x, a);
+        a = dot2_bf16(w4[i].y, xv[u][i].y, a);
+        a = dot2_bf16(w4[i].z, xv[u][i].z, a);
+        a = dot2_bf16(w4[i].w, xv[u][i].w, a);
+      }
+      a = group_sum_last<64>(a);
+      if (lane == 63 && t0 + u < T) logits[(size_t)(t0 + u) * E + e] = a + be;
+    }
   }
 }
 
@@ -71,7 +86,12 @@ MOEQ_DEV int block_excl_scan(int v, int* tmp, int& total) {
   return before + incl - v;
 }
 
-// NS = candidate slots per lane = ceil(E / 64)
+// NS = candidate slots per lane = ceil(E / 64).
+// Grouping by expert: a token's k experts are distinct, so the rank of
+// assignment (t, j) among the assignments of its expert e is the number of
+// earlier tokens that chose e.  For T <= 64 each expert keeps a 64-bit mask of
+// the tokens that chose it and the rank is a popcount; longer batches count
+// the earlier assignments directly.
 template <int NS>
 __global__ __launch_bounds__(kThreads) void select_group_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                                 int S, int32_t* __restrict__ topk_idx,
@@ -85,44 +105,44 @@ __global__ __launch_bounds__(kThreads) void select_group_kernel(const float* __r
   __shared__ int cnt[kMaxExp];
   __shared__ int offs[kMaxExp];
   __shared__ int tmp[kWaves];
-  __shared__ int sidx[kMaxA];
+  __shared__ unsigned int mlo[kMaxExp], mhi[kMaxExp];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kS = k + S, nexp = E + S, A = T * kS;
-  for (int ee = threadIdx.x; ee < nexp; ee += kThreads) cnt[ee] = 0;
+  const bool masks = T <= 64;
+  for (int ee = threadIdx.x; ee < nexp; ee += kThreads) { cnt[ee] = 0; mlo[ee] = 0u; mhi[ee] = 0u; }
+  __syncthreads();
   for (int t = wave; t < T; t += kWaves) {
     const float* L = logits + (size_t)t * E;
     float v[NS];
-    uint32_t taken = 0;
+    uint64_t taken = 0;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int ee = lane + 64 * i;
       v[i] = ee < E ? L[ee] : -INFINITY;
-      if (ee >= E) taken |= 1u << i;
+      if (ee >= E) taken |= 1ull << i;
     }
     float top0 = 0.0f, wsum = 0.0f, myw = 0.0f;
     for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < NS; ++i)
-        if (!((taken >> i) & 1u) && (bi == 0x7FFFFFFF || v[i] > bv)) { bv = v[i]; bi = lane + 64 * i; }
-      wave_argmax(bv, bi);
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      float bv;
+      const int bi = wave_topk_next<NS>(v, taken, bv);
       if (j == 0) top0 = bv;
       const float ex = __expf(bv - top0);
       wsum += ex;
-      if (lane == (j & 63)) { sidx[t * k + j] = bi; topk_idx[(size_t)t * k + j] = bi; }
+      if (lane == (j & 63)) {
+        sid[t * kS + j] = bi;
+        topk_idx[(size_t)t * k + j] = bi;
+        if (masks) atomicOr(t < 32 ? &mlo[bi] : &mhi[bi], 1u << (t & 31));
+        else atomicAdd(&cnt[bi], 1);
+      }
       if (lane == j) myw = ex;
     }
+    for (int j = lane; j < S; j += 64) sid[t * kS + k + j] = E + j;
     if (lane < k) topk_w[(size_t)t * k + lane] = myw / wsum;
   }
   __syncthreads();
-  for (int a = threadIdx.x; a < A; a += kThreads) {
-    const int t = a / kS, j = a - t * kS;
-    const int id = j < k ? sidx[t * k + j] : E + (j - k);
-    sid[a] = id;
-    atomicAdd(&cnt[id], 1);   // counts only: order-free
-  }
+  if (masks)
+    for (int ee = threadIdx.x; ee < E; ee += kThreads) cnt[ee] = __popc(mlo[ee]) + __popc(mhi[ee]);
+  for (int ee = E + threadIdx.x; ee < nexp; ee += kThreads) cnt[ee] = T;   // shared experts serve every token
   __syncthreads();
   const int per = (nexp + kThreads - 1) / kThreads;
   const int e0 = min(nexp, (int)threadIdx.x * per), e1 = min(nexp, e0 + per);
@@ -142,9 +162,21 @@ __global__ __launch_bounds__(kThreads) void select_group_kernel(const float* __r
   if (threadIdx.x == 0) { offsets[nexp] = total; active[0] = total_nz; status[0] = A - total; }
   __syncthreads();
   for (int a = threadIdx.x; a < A; a += kThreads) {
-    const int id = sid[a];
-    int r = 0;
-    for (int b = 0; b < a; ++b) r += (sid[b] == id);
+    const int t = a / kS, id = sid[a];
+    int r;
+    if (id >= E) {
+      r = t;
+    } else if (masks) {
+      const unsigned int lo = t >= 32 ? mlo[id] : (mlo[id] & ((1u << t) - 1u));
+      const unsigned int hi = t <= 32 ? 0u : (mhi[id] & ((1u << (t - 32)) - 1u));
+      r = __popc(lo) + __popc(hi);
+    } else {
+      // earlier tokens' assignments only: the token's own experts are distinct
+      r = 0;
+      const int b_end = t * kS;
+#pragma unroll 8
+      for (int b = 0; b < b_end; ++b) r += (sid[b] == id);
+    }
     const int p = offs[id] + r;
     sorted[p] = a;
     inverse[a] = p;

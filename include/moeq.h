@@ -124,7 +124,7 @@ int moe_unpack(const uint8_t* q, long rows, int K, int bits,
  * softmax over the selected logits, i.e. the softmax over all experts kept on
  * the selected k and renormalised (Qwen 3.8 Flash Next on an RTX 3060,
  * introduction: top-10 of 512 experts).  Logits must not be NaN.
- * 1 <= k <= E <= 1024; T >= 0 (T = 0 enqueues nothing). */
+ * 1 <= k <= E <= 4096; T >= 0 (T = 0 enqueues nothing). */
 int moe_route_topk(const uint16_t* x, const uint16_t* w_router, const float* bias,
                    int T, int H, int E, int k,
                    float* logits, int32_t* topk_idx, float* topk_w,
@@ -167,7 +167,8 @@ int moe_route_permute_decode(const uint16_t* x, const uint16_t* w_router, const 
  * h = silu(Wg x_t) * (Wu x_t), t = a / (k+S), using expert sorted-order data
  * from moe_permute.  Only the experts in `active` are read, each once per
  * batch, as a grouped GEMV: codes are unpacked in registers and dot products
- * accumulated in fp32 with the group scale/zero applied per group in fp32.
+ * accumulated in fp32 with the group scale/zero applied per group in fp32;
+ * h is rounded to bf16 between the two projections (as on the prefill path).
  * y is device fp32 [T*(k+S)][H], rows in assignment order.  Intended for
  * T <= 64; correct for any T. */
 int moe_qgemv_decode(const moe_layer_desc* L, const uint16_t* x, int T,

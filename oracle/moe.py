@@ -216,17 +216,22 @@ def silu(g):
     return g / (1.0 + np.exp(-g))
 
 
-def expert_ffn(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+def expert_ffn(x: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, h_bf16: bool = False) -> np.ndarray:
     """SwiGLU expert: h = silu(Wg x) * (Wu x); y = Wd h.  fp64.
 
     x [n, H]; wg, wu [I, H]; wd [H, I] (dequantised fp32 weights).  The
     activation sits on the gate; gate and up share the input x (Raon-1-mini
     on an RTX 5070 Ti, optimisation table: projections sharing an input).
+    With ``h_bf16`` the intermediate h is rounded to bf16 (nearest even)
+    before the down projection: the variant in which h is stored in bf16
+    between the two projections; everything else stays fp64.
     """
     x = np.asarray(x, dtype=np.float64)
     g = x @ np.asarray(wg, np.float64).T
     u = x @ np.asarray(wu, np.float64).T
     h = silu(g) * u
+    if h_bf16:
+        h = bf16_to_f32(f32_to_bf16(h)).astype(np.float64)
     return h @ np.asarray(wd, np.float64).T
 
 
@@ -266,14 +271,15 @@ class QuantLayer:
         return self._cache[e]
 
 
-def moe_layer(layer: QuantLayer, x_bf16: np.ndarray, wr_bf16=None, bias=None, logits=None):
+def moe_layer(layer: QuantLayer, x_bf16: np.ndarray, wr_bf16=None, bias=None, logits=None, h_bf16=False):
     """Forward pass of one MoE FFN layer, step by step.
 
     1. router logits (or given fp32 ``logits``), 2. top-k selection,
     3. renormalised softmax weights, 4. permutation of assignments to
     experts, 5. per-expert SwiGLU FFN over that expert's tokens,
     6. weighted combine.  Returns a dict of every intermediate; ``out`` is the
-    fp64 layer output [T, H] before any rounding to bf16.
+    fp64 layer output [T, H] before any rounding to bf16.  ``h_bf16`` as in
+    expert_ffn.
     """
     T = x_bf16.shape[0]
     k, E, S, H = layer.k, layer.E, layer.S, layer.H
@@ -292,7 +298,7 @@ def moe_layer(layer: QuantLayer, x_bf16: np.ndarray, wr_bf16=None, bias=None, lo
             continue
         a = sorted_a[lo:hi]
         wg, wu, wd = layer.dense(e)
-        y[a] = expert_ffn(x[a // kS], wg, wu, wd)
+        y[a] = expert_ffn(x[a // kS], wg, wu, wd, h_bf16)
     out = combine(y.reshape(T, kS, H), w, S)
     return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets,
                 sorted=sorted_a, inverse=inverse, y=y, out=out)

@@ -421,3 +421,25 @@ def pin_bf16_and_norm(o, seed=8):
     # 1 + 2^-8 is a tie that goes to even (1.0); 1 + 1.5 ulp goes to 1 + 2 ulp
     r = o.residual_bf16(one, np.array([[2.0 ** -8 + 2.0 ** -20, 2.0 ** -7 + 2.0 ** -8]]))
     assert o.bf16_to_f32(r)[0].tolist() == [1.0, 1.015625]
+
+
+def pin_ffn_bf16_h(o, seed=9):
+    """h_bf16 rounds h = silu(g) u to bf16 before the down projection: torch's
+    own silu and bf16 conversion of the same h give the same y, and the change
+    from the fp64 FFN stays within the rounding bound 2^-9 sum_i |Wd||h|."""
+    import torch
+    rng = np.random.default_rng(seed)
+    n, H, I = 5, 64, 48
+    x = rng.standard_normal((n, H))
+    wg, wu = (rng.standard_normal((I, H)) * 0.3).astype(np.float32), (rng.standard_normal((I, H)) * 0.3).astype(np.float32)
+    wd = (rng.standard_normal((H, I)) * 0.3).astype(np.float32)
+    xt = torch.tensor(x, dtype=torch.float64)
+    h = torch.nn.functional.silu(xt @ torch.tensor(wg, dtype=torch.float64).T) * (xt @ torch.tensor(wu, dtype=torch.float64).T)
+    hb = h.float().to(torch.bfloat16).double()
+    ref = (hb @ torch.tensor(wd, dtype=torch.float64).T).numpy()
+    got = o.expert_ffn(x, wg, wu, wd, h_bf16=True)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+    exact = o.expert_ffn(x, wg, wu, wd)
+    bound = 2.0 ** -9 * (np.abs(h.numpy()) @ np.abs(wd.astype(np.float64)).T)
+    assert np.all(np.abs(got - exact) <= bound * (1 + 1e-9))
+    assert not np.array_equal(got, exact)

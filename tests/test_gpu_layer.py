@@ -4,8 +4,10 @@ expert FFN -> combine) against the oracle, through the C ABI.
 The oracle is routed from the GPU's fp32 logits (its selection on given
 logits is checked bit for bit elsewhere), and the GPU logits themselves are
 checked against the oracle's.  Layer outputs must satisfy
-max|gpu - oracle| / (max|oracle| + 1e-6) <= 2e-2 on the bf16 output; the
-decode path, which keeps fp32 arithmetic, is also held to fp32-class error (see DECODE_TOL).
+max|gpu - oracle| / (max|oracle| + 1e-6) <= 2e-2 on the bf16 output against
+the fp64 oracle.  The decode path keeps fp32 arithmetic except for h, which
+it stores in bf16 between the projections; against the oracle variant that
+rounds h the same way it is also held to the tighter DECODE_TOL.
 Full-size workloads compare sampled tokens (tokens are independent in a MoE
 layer, so the oracle's result for a token subset is exact)."""
 import numpy as np
@@ -19,11 +21,15 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 SPEC_TOL = 2e-2
-# the decode path keeps fp32 arithmetic: its fp32 expert outputs y agree with
-# the oracle to 1e-4, and the bf16 layer output to within one bf16 half-ulp
-# (2^-8 relative) plus that
-DECODE_TOL = 2.0 ** -8 + 1e-4
-DECODE_Y_TOL = 1e-4
+# Against the oracle variant that rounds h to bf16 as the decode path does,
+# the only differences left are fp32 accumulation (~1e-6) and the h values
+# whose fp32 and fp64 results fall on opposite sides of a bf16 rounding
+# boundary: each such h moves by one bf16 ulp (2^-8 relative).  A few h in
+# 10^3 do (fp32 error ~1e-5 relative against a 2^-8 spacing), so y stays
+# within 2e-3 of max|y|, and the bf16 output within one bf16 half-ulp
+# (2^-8 relative) plus 1e-3.
+DECODE_TOL = 2.0 ** -8 + 1e-3
+DECODE_Y_TOL = 2e-3
 
 
 @pytest.fixture(scope="module")
@@ -77,7 +83,10 @@ def check_layer(bq, name, T, prefill, sample=None, bits=None, batch=0):
     ya = y.reshape(T, kS, w.H)[rows].reshape(-1, w.H)
     yerr = rel_err(ya, ref["y"])
     if not prefill:
-        assert err <= DECODE_TOL and yerr <= DECODE_Y_TOL, (err, yerr)
+        ref_b = oracle.moe_layer(olayer, x[rows], logits=logits[rows], h_bf16=True)
+        err_b, yerr_b = rel_err(out, ref_b["out"]), rel_err(ya, ref_b["y"])
+        assert err_b <= DECODE_TOL and yerr_b <= DECODE_Y_TOL, (err_b, yerr_b)
+        assert yerr <= SPEC_TOL, yerr
     else:
         assert yerr <= SPEC_TOL, yerr
     return r, err, yerr

@@ -64,7 +64,8 @@ def test_unpack_bitexact(bq, bits):
     assert np.array_equal(got, oracle.unpack(packed, bits, K))
 
 
-@pytest.mark.parametrize("E,k,T", [(128, 8, 16), (256, 8, 8), (512, 10, 33), (6, 3, 5), (1024, 64, 3), (8, 8, 4)])
+@pytest.mark.parametrize("E,k,T", [(128, 8, 16), (256, 8, 8), (512, 10, 33), (6, 3, 5), (1024, 64, 3), (8, 8, 4),
+                                   (2500, 8, 7), (4096, 16, 5)])
 def test_topk_on_given_logits_bitexact(bq, E, k, T):
     w = synth.Workload("t", 99, 64, 64, E, k, 0, 4, (T,))
     L = synth.direct_logits_f32(w, T)
@@ -81,6 +82,8 @@ def test_topk_ties_bitexact(bq):
     L = rng.integers(-3, 4, (300, 96)).astype(np.float32)
     L[:20] *= np.float32(0.0)            # rows of +-0.0 ties
     L[20, :] = 1.0                        # all equal
+    L[21, :] = -np.inf                    # all -inf: index order
+    L[22, ::2] = -np.inf
     Lt = torch.from_numpy(L).cuda()
     for k in (1, 5, 96):
         _, idx, _ = bq.moe_route_topk(None, None, None, 96, k, logits=Lt)
@@ -190,7 +193,7 @@ def test_rmsnorm(bq):
                                   ("moe_h2048_e256_k8_s1_b4", 8), ("moe_h4096_e512_k10_b4_hot", 1),
                                   ("moe_h4096_e512_k10_b4_hot", 13), ("moe_h2048_e128_k8_b6_zipf", 64)])
 def test_route_permute_decode_fused(bq, wl, T):
-    """The one-launch decode routing equals the oracle's routing on the GPU's
+    """The decode routing entry point (router + selection/grouping) equals the oracle's routing on the GPU's
     logits (bit for bit) and its logits match the oracle's; repeated calls on
     one workspace keep working."""
     w = synth.get_workload(wl)
@@ -215,3 +218,20 @@ def test_route_permute_decode_fused(bq, wl, T):
         nz = np.nonzero(c)[0]
         assert act[0] == len(nz) and np.array_equal(act[1:1 + len(nz)], nz)
     assert ws[0:4].cpu().numpy().view(np.int32)[0] == 0   # no bad ids
+
+
+@pytest.mark.parametrize("T", [33, 65, 300])
+def test_route_permute_decode_long_batch(bq, T):
+    """Batches past 64 tokens take the counting branch of the grouping (the
+    token masks cover 64 tokens); both branches give the oracle's permutation."""
+    w = synth.Workload("route_long", 88, 512, 64, 32, 2, 1, 4, (T,))
+    wr = bf16_tensor(synth.router_weight_bf16(w))
+    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    x = synth.activations_bf16(w, T)
+    r = bq.moe_route_permute_decode(bf16_tensor(x), wr, None, w.E, w.k, w.S, ws)
+    logits = r[0].cpu().numpy()
+    idx = oracle.select_topk(logits, w.k)
+    assert np.array_equal(r[1].cpu().numpy(), idx)
+    c, o, s, i = oracle.permute(idx, w.E, w.S)
+    for got, ref in zip(r[3:7], (c, o, s, i)):
+        assert np.array_equal(got.cpu().numpy(), ref)

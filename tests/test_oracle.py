@@ -54,3 +54,7 @@ def test_on_grid_layer():
 
 def test_bf16_and_norm():
     pins.pin_bf16_and_norm(oracle)
+
+
+def test_ffn_bf16_h():
+    pins.pin_ffn_bf16_h(oracle)

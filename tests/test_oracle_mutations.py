@@ -83,18 +83,28 @@ def _permute_unstable(idx, E, S=0):
     return counts, offsets, srt, inv
 
 
-def _ffn_silu_on_up(x, wg, wu, wd):
+def _ffn_silu_on_up(x, wg, wu, wd, h_bf16=False):
     x = np.asarray(x, np.float64)
     g = x @ np.asarray(wg, np.float64).T
     u = x @ np.asarray(wu, np.float64).T
     return (g * om.silu(u)) @ np.asarray(wd, np.float64).T
 
 
-def _ffn_transposed_down(x, wg, wu, wd):
+def _ffn_transposed_down(x, wg, wu, wd, h_bf16=False):
     x = np.asarray(x, np.float64)
     g = x @ np.asarray(wg, np.float64).T
     u = x @ np.asarray(wu, np.float64).T
     return (om.silu(g) * u) @ np.asarray(wd, np.float64).T[::-1]   # mistake: rows reversed
+
+
+def _ffn_rounds_up_not_h(x, wg, wu, wd, h_bf16=False):
+    # mistake: the bf16 rounding applied to the up projection instead of h
+    x = np.asarray(x, np.float64)
+    g = x @ np.asarray(wg, np.float64).T
+    u = x @ np.asarray(wu, np.float64).T
+    if h_bf16:
+        u = om.bf16_to_f32(om.f32_to_bf16(u)).astype(np.float64)
+    return (om.silu(g) * u) @ np.asarray(wd, np.float64).T
 
 
 def _combine_drop_shared(y, w, S=0):
@@ -125,6 +135,7 @@ MUTANTS = [
     ("permute", _permute_unstable, [pins.pin_routing_golden, pins.pin_permute_bruteforce]),
     ("expert_ffn", _ffn_silu_on_up, [pins.pin_layer_bruteforce, pins.pin_layer_special_cases]),
     ("expert_ffn", _ffn_transposed_down, [pins.pin_layer_bruteforce, pins.pin_on_grid_layer]),
+    ("expert_ffn", _ffn_rounds_up_not_h, [pins.pin_ffn_bf16_h]),
     ("combine", _combine_drop_shared, [pins.pin_layer_bruteforce, pins.pin_layer_special_cases]),
     ("rmsnorm_bf16", _rmsnorm_no_eps, [pins.pin_bf16_and_norm]),
     ("residual_bf16", _residual_no_block_rounding, [pins.pin_bf16_and_norm]),
