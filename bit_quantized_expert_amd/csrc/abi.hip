@@ -57,6 +57,10 @@ int validate_layer(const moe_layer_desc* L) {
   if (L->E + L->S > 4096) return set_error(MOEQ_ERR_UNSUPPORTED, "E+S=%d exceeds 4096", L->E + L->S);
   if (L->H % MOEQ_GROUP || L->I % MOEQ_GROUP)
     return set_error(MOEQ_ERR_UNSUPPORTED, "H=%d and I=%d must be multiples of %d", L->H, L->I, MOEQ_GROUP);
+  // kernels address one expert's matrix with 32-bit byte offsets
+  if ((long long)L->H * L->I >= (1LL << 31))
+    return set_error(MOEQ_ERR_UNSUPPORTED, "H*I=%lld: one expert matrix must stay below 2^31 weights",
+                     (long long)L->H * L->I);
   const moe_qweight* ws[3] = {&L->gate, &L->up, &L->down};
   const char* nm[3] = {"gate", "up", "down"};
   for (int i = 0; i < 3; ++i) {

@@ -48,6 +48,7 @@ int validate_layer(const moe_layer_desc* L);
 // device side
 // --------------------------------------------------------------------------
 #define MOEQ_DEV __device__ __forceinline__
+#define MOEQ_HD __host__ __device__ __forceinline__
 
 MOEQ_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

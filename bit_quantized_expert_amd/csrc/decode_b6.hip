@@ -1,17 +1,21 @@
 // Decode kernels instantiated for 6-bit weights (see decode_impl.h).
 #include "decode_impl.h"
 
-#define MOEQ_GATEUP_CALL(IT, LP)                                                                          \
-  switch (L->down.bits) {                                                                                 \
-    case 4: decode_detail::gateup_gemv_kernel<6, 4, IT, LP><<<grid, 256, 0, s>>>(GATEUP_ARGS); break;     \
-    case 6: decode_detail::gateup_gemv_kernel<6, 6, IT, LP><<<grid, 256, 0, s>>>(GATEUP_ARGS); break;     \
-    default: decode_detail::gateup_gemv_kernel<6, 8, IT, LP><<<grid, 256, 0, s>>>(GATEUP_ARGS); break;    \
+// one launch per (W, CW) shape that covers whole groups at this width
+#define MOEQ_LAUNCH_GU(W_, CW_)                                                                        \
+  if constexpr (CW_ % Fmt<6>::CHUNKS_PER_GROUP == 0 && CW_ / Fmt<6>::CHUNKS_PER_GROUP <= 8)           \
+  if (W == W_ && CW == CW_) {                                                                          \
+    decode_detail::gateup_rows_kernel<6, W_, CW_><<<grid, 64 * W_, 0, s>>>(                          \
+        L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, dg, offsets, sorted, active, hh);     \
+    launched = true;                                                                                   \
   }
-#define GATEUP_ARGS \
-  L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, L->k + L->S, offsets, sorted, active, tiles, hh
-#define MOEQ_DOWN_CALL(IT, LP)                                                                            \
-  decode_detail::down_gemv_kernel<6, IT, LP><<<grid, 256, 0, s>>>(L->down.q, L->down.sz, hh, L->H,  \
-                                                                   L->I, offsets, sorted, active, tiles, y)
+#define MOEQ_LAUNCH_DN(W_, CW_)                                                                        \
+  if constexpr (CW_ % Fmt<6>::CHUNKS_PER_GROUP == 0 && CW_ / Fmt<6>::CHUNKS_PER_GROUP <= 8)           \
+  if (W == W_ && CW == CW_) {                                                                          \
+    decode_detail::down_rows_kernel<6, W_, CW_><<<grid, 64 * W_, 0, s>>>(                            \
+        L->down.q, L->down.sz, hh, L->H, L->I, dg, offsets, sorted, active, y);                        \
+    launched = true;                                                                                   \
+  }
 
 namespace moeq {
 MOEQ_DEFINE_DECODE(6)

@@ -2,450 +2,483 @@
 //
 // Weight streaming is the whole cost at decode (Raon-1-mini on an RTX
 // 5070 Ti: the finished runtime streams weights at about two thirds of the
-// card's bandwidth), so the kernels are built around reading each routed
-// expert's packed rows exactly once, with full-width vector loads:
+// card's bandwidth), so the kernels read each routed expert's packed rows
+// exactly once, with full-width coalesced loads, and spend as few vector
+// instructions per byte as possible:
 //
-//   * a lane owns fixed "chunks" of a row (16 B for 4/8-bit, 12 B for 6-bit);
-//     LPR lanes cover ITER chunks of a row each, so the lane's slice of the
-//     activation vector is fixed for a pass and lives in registers as bf16
-//     pairs;
+//   * one lane owns one output row: a wavefront covers a tile of 64 rows and
+//     walks its share of the K chunks; the tiled weight layout (format.h)
+//     makes each chunk load of the wavefront one contiguous block, and no
+//     cross-lane reduction is needed per row;
+//   * the activations of a chunk are the same for all 64 rows, so they are
+//     read with scalar loads into SGPRs (the dot products take them as their
+//     scalar operand): no vector registers or vector memory traffic for x;
 //   * codes become bf16 (128 + q, or q for 8-bit) with one AND-OR per two
 //     codes and are multiplied by v_dot2_f32_bf16 with fp32 accumulation: the
-//     products are exact, and the group's scale and zero enter once per chunk
-//     in fp32:
+//     products are exact, and the group's scale and zero enter once per
+//     group in fp32:
 //         sum_i (q_i - z) s x_i = s * (sum_i (128+q_i) x_i - (z+128) sum_i x_i);
+//     the group sums of x come from one cooperative load per wavefront;
 //   * gate and up rows that share the input are read in the same pass and
 //     combined into h = silu(g) u (Raon-1-mini optimisation table:
 //     projections sharing an input run together);
-//   * a wave loads all of its weight chunks (CH per lane, CH/ITER row steps)
-//     into registers before anything else, so every weight load of the wave
-//     is in flight at once; token passes (up to two tokens each) then reuse
-//     those registers, so an expert's weights are read from HBM once however
-//     many of the batch's tokens it serves;
-//   * rows are reduced across their LPR lanes with DPP.
-// The intermediate h = silu(g) u goes to the down projection in bf16, as on
-// the prefill path.
+//   * the W wavefronts of a block split K; each keeps the loads of DEPTH
+//     chunks in flight while it computes one (a software pipeline), and their
+//     partial sums meet in LDS, added in a fixed order.
+// h goes to the down projection in bf16, as on the prefill path.
 //
-// Grid: (expert slot, row tile).  Slots index the active-expert list built by
-// moe_permute, walked from its end (shared experts, which serve every token,
-// come first, so the longest blocks start first); blocks whose slot is past
-// the list's end exit at once, so the host never needs the routing result.
-// A wave holds few rows so that several waves share each SIMD: while some
-// wait for their weights, others compute.
+// Grid: see DecodeGrid.  Blocks whose expert is not active exit at once, so
+// the host never needs the routing result.
 #pragma once
 #include "format.h"
 
 namespace moeq {
 namespace decode_detail {
 
-constexpr int kMaxNT = 2;        // tokens per pass over the weights
+constexpr int kDepth = 4;   // chunks whose loads are in flight per wavefront
+constexpr int kMaxNT = 2;   // tokens per pass
 
-// NT tokens' activation slices (bf16 rows of `ld` elements) for chunk `cpos`
-// as dot2 pairs in the format's pair order, with their fp32 sums.  Tokens
-// t >= nt get zeros.
-template <int BITS, int NT>
-MOEQ_DEV void load_x_bf16(const uint16_t* __restrict__ x, const int (&rowidx)[NT], int nt, int cpos,
-                          uint32_t (&X)[NT][Fmt<BITS>::PAIRS], float (&XS)[NT], int ld) {
-  using F = Fmt<BITS>;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    uint32_t v[F::CODES / 2];
-    if (t < nt) {
-      const uint16_t* src = x + (size_t)rowidx[t] * ld + (size_t)cpos * F::CODES;
-#pragma unroll
-      for (int i = 0; i < F::CODES / 8; ++i) {
-        const moeq_u32x4 q = *reinterpret_cast<const moeq_u32x4*>(src + 8 * i);
-        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < F::CODES / 2; ++i) v[i] = 0u;
-    }
-    float s = 0.0f;
-    const uint32_t ones = 0x3F803F80u;   // bf16 (1, 1): dot2 with it sums a pair
-#pragma unroll
-    for (int p = 0; p < F::PAIRS; ++p) {
-      const int c0 = pair_code<BITS>(p, 0), c1 = pair_code<BITS>(p, 1);
-      const uint32_t lo = (v[c0 >> 1] >> (16 * (c0 & 1))) & 0xFFFFu;
-      const uint32_t hi = (v[c1 >> 1] >> (16 * (c1 & 1))) & 0xFFFFu;
-      X[t][p] = lo | (hi << 16);
-      s = dot2_bf16(X[t][p], ones, s);
-    }
-    XS[t] = s;
-  }
-}
-
-// The intermediate h of the down projection comes from the gate/up kernel
-// as bf16, stored in the down kernel's pair order (h_store_pos), so a
-// chunk's pairs load directly.  XS is the fp32 sum of the chunk's h values.
-template <int BITS, int NT>
-MOEQ_DEV void load_h_pairs(const uint16_t* __restrict__ hh, int row0, int nt, int cpos,
-                           uint32_t (&XH)[NT][Fmt<BITS>::PAIRS], float (&XS)[NT], int ld) {
-  using F = Fmt<BITS>;
-  const uint32_t ones = 0x3F803F80u;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (t < nt) {
-      const size_t off = (size_t)(row0 + t) * ld + (size_t)cpos * F::CODES;
-#pragma unroll
-      for (int i = 0; i < F::PAIRS / 4; ++i) {
-        const moeq_u32x4 a = *reinterpret_cast<const moeq_u32x4*>(hh + off + 8 * i);
-        XH[t][4 * i] = a.x; XH[t][4 * i + 1] = a.y; XH[t][4 * i + 2] = a.z; XH[t][4 * i + 3] = a.w;
-      }
-    } else {
-#pragma unroll
-      for (int p = 0; p < F::PAIRS; ++p) XH[t][p] = 0u;
-    }
-    float s = 0.0f;
-#pragma unroll
-    for (int p = 0; p < F::PAIRS; ++p) s = dot2_bf16(XH[t][p], ones, s);
-    XS[t] = s;
-  }
-}
-
-// Where natural index i of a K = I row of h is stored for a down projection
-// at DBITS: chunk-major, and inside a chunk pair p's two halves at 2p, 2p+1
-// (the inverse of pair_code).  4-bit: code 8q + r sits in pair 4q + (r & 3),
-// half r >> 2.  8-bit: pairs are natural.  6-bit: a 16-entry nibble table.
-template <int DBITS>
-MOEQ_DEV int h_store_pos(int i) {
-  using F = Fmt<DBITS>;
-  const int c = i / F::CODES, j = i % F::CODES;
-  int pos;
-  if constexpr (DBITS == 4) {
-    pos = (j & ~7) + 2 * (j & 3) + ((j >> 2) & 1);
-  } else if constexpr (DBITS == 8) {
-    pos = j;
-  } else {
-    // position of code j: codes (0,3)->(0,1), (1,4)->(2,3), (5,8)->(4,5),
-    // (6,9)->(6,7), (10,13)->(8,9), (11,14)->(10,11), (2,7)->(12,13),
-    // (12,15)->(14,15)
-    constexpr uint64_t kPos = 0xFB9EA875D6431C20ull;   // nibble j = position of code j
-    pos = (int)((kPos >> (4 * j)) & 0xF);
-  }
-  return c * F::CODES + pos;
-}
-
-// Partial dot products of one row chunk against NT tokens with the group's
-// scale/zero applied: out[t] += s * (sum (off+q) x - (z+off) * sum x).
-template <int BITS, int NT>
-MOEQ_DEV void chunk_dot(const uint32_t (&d)[Fmt<BITS>::DW], uint32_t szw, const uint32_t (&X0)[NT][Fmt<BITS>::PAIRS],
-                        const float (&XS)[NT], float (&out)[NT]) {
-  using F = Fmt<BITS>;
-  uint32_t P[F::PAIRS];
-  chunk_pairs<BITS>(d, P);
-  const float s = f16_bits_to_f32(szw & 0xFFFFu);
-  const float zc = f16_bits_to_f32(szw >> 16) + F::OFFSET;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    // four independent accumulation chains: the dot2 results are not
-    // waited on one after another
-    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int p = 0; p < F::PAIRS; ++p) {
-      a[p & 3] = dot2_bf16(P[p], X0[t][p], a[p & 3]);
-    }
-    const float acc = (a[0] + a[1]) + (a[2] + a[3]);
-    out[t] = fmaf(s, acc - zc * XS[t], out[t]);
-  }
-}
-
-// Empty register-only barrier (no instruction is emitted): makes the packed
-// weights look modified at the start of each token pass, so the compiler
-// re-derives the bf16 pairs per pass instead of keeping all of them live.
-template <int CH, int DW>
-MOEQ_DEV void opaque(uint32_t (&d)[CH][DW]) {
-#pragma unroll
-  for (int s = 0; s < CH; ++s)
-#pragma unroll
-    for (int j = 0; j < DW; ++j) asm volatile("" : "+v"(d[s][j]));
-}
-
-template <int ITER, int LPR>
-struct Geo {
-  static constexpr int iter = ITER;      // chunks per lane per row
-  static constexpr int lpr = LPR;        // lanes per row
-  static constexpr int rpw = 64 / LPR;   // rows per wave step
-  int rg, cl;           // this lane's row within a step and its chunk column
-  MOEQ_DEV Geo() {
-    const int lane = threadIdx.x & 63;
-    rg = lane / LPR;
-    cl = lane % LPR;
-  }
-  MOEQ_DEV bool writer() const { return cl == LPR - 1; }   // holds the row sum
-  // chunk s of this lane: row step s / iter, chunk column cl + lpr * (s % iter)
-  MOEQ_DEV int row_of(int s) const { return (s / ITER) * rpw + rg; }
-  MOEQ_DEV int cpos_of(int s) const { return cl + lpr * (s % ITER); }
+// Block -> work mapping shared by both kernels.  The grid has two parts:
+//  * shared experts (every token uses them, so the host knows their load):
+//    one block per (shared expert, row tile, pair of tokens), laid out so
+//    that the blocks of one row tile land on the same XCD (blocks are dealt
+//    to the 8 XCDs round-robin) a few dispatches apart, so the weights they
+//    all read come from that XCD's L2 after the first;
+//  * routed experts: one block per (active routed expert, row tile), the
+//    expert's tokens taken in passes of up to two.
+struct DecodeGrid {
+  int E, S;            // routed and shared expert counts
+  int kS;              // assignments per token (k + S)
+  int tiles;           // 64-row tiles per expert
+  int shared_blocks;   // blocks in the shared part (a multiple of 8 * groups)
+  int groups;          // token pairs of a shared expert: ceil(T / 2)
 };
 
-#ifndef MOEQ_GU_CH1
-#define MOEQ_GU_CH1 2
-#endif
-#ifndef MOEQ_DN_CH1
-#define MOEQ_DN_CH1 4
-#endif
-#ifndef MOEQ_NT2_MAX_ITER
-#define MOEQ_NT2_MAX_ITER 1
-#endif
-#ifndef MOEQ_GU_WAVES
-#define MOEQ_GU_WAVES 4
-#endif
-#ifndef MOEQ_DN_WAVES
-#define MOEQ_DN_WAVES 4
-#endif
-// chunks per lane and matrix held in registers (a multiple of iter)
-constexpr int gateup_ch(int iter) { return iter == 1 ? MOEQ_GU_CH1 : iter; }
-constexpr int down_ch(int iter) { return iter == 1 ? MOEQ_DN_CH1 : (iter == 3 ? 3 : 4); }
-constexpr int kGateupWaves = MOEQ_GU_WAVES;   // minimum waves per SIMD the register budget allows
-constexpr int kDownWaves = MOEQ_DN_WAVES;
+// Decodes blockIdx.x.  Returns false for a block without work; otherwise
+// sets the expert, the row tile and, for a shared-expert block, its token
+// pair (-1 for a routed block: all of the expert's tokens).
+MOEQ_DEV bool block_work(const DecodeGrid& dg, const int32_t* __restrict__ active, int& e, int& tile, int& pair) {
+  const int b = (int)blockIdx.x;
+  if (b < dg.shared_blocks) {
+    const int span = 8 * dg.groups;
+    const int l = (b / span) * 8 + (b % 8);   // (shared expert, row tile)
+    if (l >= dg.S * dg.tiles) return false;
+    pair = (b % span) / 8;
+    e = dg.E + l / dg.tiles;
+    tile = l % dg.tiles;
+    return true;
+  }
+  const int r = b - dg.shared_blocks;
+  const int j = r / dg.tiles;
+  tile = r % dg.tiles;
+  pair = -1;
+  if (j >= active[0] - dg.S) return false;   // active: routed ids first, then the S shared ones
+  e = active[1 + j];
+  return e < dg.E;
+}
 
-// -------------------------------------------------------------------------
-// gate/up: h[p][i] = silu(Wg x_t)[i] * (Wu x_t)[i]
-// A wave owns CH/ITER row steps (CH chunks of gate and of up per lane).  All
-// of its weight chunks are loaded into registers first; then every pass over
-// up to kMaxNT of the expert's tokens reuses them, one chunk column (ITER)
-// of activations at a time.
-// -------------------------------------------------------------------------
-template <int BITS, int DBITS, int ITER, int LPR, int CH, int NT>
-MOEQ_DEV void gateup_pass(uint32_t (&dg)[CH][Fmt<BITS>::DW], uint32_t (&du)[CH][Fmt<BITS>::DW],
-                          const uint32_t (&sg)[CH], const uint32_t (&su)[CH], const uint16_t* __restrict__ x,
-                          int H, int I, int kS, const int32_t* __restrict__ sorted, int p0, int nt, int row0,
-                          int I_end, const Geo<ITER, LPR>& g, uint16_t* __restrict__ hh) {
+// Values the compiler cannot see are the same on every lane (they are: all
+// their inputs are wave-uniform), moved to scalar registers so that addresses
+// built from them stay scalar.  A load address is then a scalar base plus
+// one 32-bit lane offset (the global_load "saddr" form): no per-chunk
+// address occupies vector registers.
+MOEQ_DEV int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// global-memory pointer (address space 1): loads through it are global_load,
+// not flat loads
+typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+MOEQ_DEV gbytes uniform_ptr(const uint8_t* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<gbytes>(((uint64_t)hi << 32) | lo);
+}
+
+template <int BITS>
+MOEQ_DEV void load_chunk_g(gbytes p, uint32_t (&d)[Fmt<BITS>::DW]) {
+  typedef const __attribute__((address_space(1))) moeq_u32x4* g4;
+  if constexpr (Fmt<BITS>::DW == 4) {
+    const moeq_u32x4 v = *reinterpret_cast<g4>(p);
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  } else {
+    typedef const __attribute__((address_space(1))) moeq_u32x3* g3;
+    const moeq_u32x3 v = *reinterpret_cast<g3>(p);
+    d[0] = v.x; d[1] = v.y; d[2] = v.z;
+  }
+}
+MOEQ_DEV uint32_t load_word_g(gbytes p) { return *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(p); }
+
+// Loads in flight for one chunk of NM matrices: the chunk's codes and, on
+// the first chunk of a group, the group's scale/zero words.
+template <int BITS, int NM>
+struct ChunkBuf {
+  uint32_t q[NM][Fmt<BITS>::DW];
+  uint32_t sz[NM];
+};
+
+// One wavefront's work: rows tile*64 + lane of one expert's matrices,
+// chunks [c0, c0 + CW) of K.  Each load address is a scalar base (this
+// wavefront's first chunk) plus a 32-bit lane offset (the global_load
+// "saddr" form), so no per-chunk address occupies registers.
+template <int BITS, int NM>
+struct Stream {
   using F = Fmt<BITS>;
-  opaque(dg);
-  opaque(du);
-  int tok[NT];
+  gbytes q[NM];    // codes of chunk c0 of the tile (uniform)
+  gbytes sz[NM];   // scale/zero word of group c0 / CPG of the tile (uniform)
+  int c0;
+  // qe, sze: the expert's codes and scale/zero words; cpr, gpr: chunks and
+  // groups per row
+  MOEQ_DEV void init(const uint8_t* const (&qe)[NM], const uint32_t* const (&sze)[NM], int cpr, int gpr, int tile,
+                     int first) {
+    c0 = first;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) tok[t] = t < nt ? sorted[p0 + t] / kS : 0;
-  float ag[CH][NT], au[CH][NT];
-#pragma unroll
-  for (int s = 0; s < CH; ++s)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) { ag[s][t] = 0.0f; au[s][t] = 0.0f; }
-#pragma unroll 1
-  for (int it = 0; it < ITER; ++it) {
-    uint32_t X[NT][F::PAIRS];
-    float XS[NT];
-    load_x_bf16<BITS, NT>(x, tok, nt, g.cl + g.lpr * it, X, XS, H);
-#pragma unroll
-    for (int s = 0; s < CH; ++s) {
-      if (s % ITER == it) {
-        chunk_dot<BITS, NT>(dg[s], sg[s], X, XS, ag[s]);
-        chunk_dot<BITS, NT>(du[s], su[s], X, XS, au[s]);
-      }
+    for (int m = 0; m < NM; ++m) {
+      q[m] = uniform_ptr(qe[m] + ((size_t)tile * cpr + (size_t)c0) * (64 * F::BYTES));
+      sz[m] = uniform_ptr(reinterpret_cast<const uint8_t*>(
+          sze[m] + ((size_t)tile * gpr + (size_t)(c0 / F::CHUNKS_PER_GROUP)) * 64));
     }
   }
-  // rows: chunks s = step*iter .. step*iter+iter-1 belong to row step `step`
+  MOEQ_DEV void load(int c, ChunkBuf<BITS, NM>& b) const {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t off = lane * (uint32_t)F::BYTES + (uint32_t)c * (64u * F::BYTES);
 #pragma unroll
-  for (int s = 0; s < CH; ++s) {
-    if (s % ITER != 0) continue;
-    float gs[NT], us[NT];
+    for (int m = 0; m < NM; ++m) load_chunk_g<BITS>(q[m] + off, b.q[m]);
+    if (c % F::CHUNKS_PER_GROUP == 0) {   // c0 is a multiple of the group's chunks
+      const uint32_t so = lane * 4u + (uint32_t)(c / F::CHUNKS_PER_GROUP) * 256u;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) { gs[t] = ag[s][t]; us[t] = au[s][t]; }
-#pragma unroll
-    for (int q = 1; q < CH; ++q)
-      if (q < ITER && s + q < CH) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) { gs[t] += ag[s + q][t]; us[t] += au[s + q][t]; }
-      }
-    const int row = row0 + g.row_of(s);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float gv = group_sum_last<LPR>(gs[t]);
-      const float uv = group_sum_last<LPR>(us[t]);
-      if (g.writer() && t < nt && row < I_end) {
-        const float hv = silu_f32(gv) * uv;
-        hh[(size_t)(p0 + t) * I + h_store_pos<DBITS>(row)] = (uint16_t)f32_to_bf16_bits(hv);
-      }
+      for (int m = 0; m < NM; ++m) b.sz[m] = load_word_g(sz[m] + so);
     }
+  }
+};
+
+// keeps the compiler from moving instructions across a pipeline stage
+MOEQ_DEV void stage_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Sums of x over the wavefront's NG groups [g0, g0 + NG) for up to two token
+// rows, computed cooperatively (lane 8 g + j adds x values 8 j .. 8 j + 7 of
+// group g); the sum of group g ends in lane 8 g + 7.
+template <int NG>
+MOEQ_DEV void group_sums(const uint16_t* const (&xr)[kMaxNT], int nt, int g0, float (&xs)[kMaxNT]) {
+  static_assert(NG >= 1 && NG <= 8, "at most 8 groups per wavefront");
+  const int lane = threadIdx.x & 63;
+  const uint32_t ones = 0x3F803F80u;   // bf16 (1, 1): dot2 with it sums a pair
+  const int off = g0 * 64 + 8 * (lane < 8 * NG ? lane : 0);
+#pragma unroll
+  for (int t = 0; t < kMaxNT; ++t) {
+    float s = 0.0f;
+    if (t < nt) {
+      const moeq_u32x4 v = *reinterpret_cast<const moeq_u32x4*>(xr[t] + off);
+      s = dot2_bf16(v.x, ones, s);
+      s = dot2_bf16(v.y, ones, s);
+      s = dot2_bf16(v.z, ones, s);
+      s = dot2_bf16(v.w, ones, s);
+    }
+    xs[t] = group_sum_last<8>(s);
   }
 }
 
-template <int BITS, int DBITS, int ITER, int LPR>
-__global__ __launch_bounds__(256, ITER <= 2 ? kGateupWaves : 2) void gateup_gemv_kernel(const uint8_t* __restrict__ gq, const uint32_t* __restrict__ gsz,
-                                                          const uint8_t* __restrict__ uq, const uint32_t* __restrict__ usz,
-                                                          const uint16_t* __restrict__ x, int H, int I, int kS,
-                                                          const int32_t* __restrict__ offsets,
-                                                          const int32_t* __restrict__ sorted,
-                                                          const int32_t* __restrict__ active, int tiles,
-                                                          uint16_t* __restrict__ hh) {
-  using F = Fmt<BITS>;
-  constexpr int CH = gateup_ch(ITER);
-  const int n_active = min(active[0], (int)(gridDim.x / tiles));   // the grid has a block row per possible slot
-  const int slot = n_active - 1 - (int)(blockIdx.x / tiles), tile = blockIdx.x % tiles;
-  if (slot < 0) return;
-  const int e = active[1 + slot];
-  const Geo<ITER, LPR> g;
-  const int wave = threadIdx.x >> 6;
-  const int rows_w = (CH / ITER) * g.rpw;
-  const int row0 = (tile * 4 + wave) * rows_w;
-  if (row0 >= I) return;
-  const int I_end = min(I, row0 + rows_w);
-  const size_t rb = row_bytes(H, BITS), gpr = H / 64;
-  // all weight chunks of this wave first
-  uint32_t dg[CH][F::DW], du[CH][F::DW], sg[CH], su[CH];
-#pragma unroll
-  for (int s = 0; s < CH; ++s) {
-    const int row = min(row0 + g.row_of(s), I - 1);   // rows past I repeat the last row, never stored
-    const int cpos = g.cpos_of(s);
-    const size_t grow = (size_t)e * I + row;
-    load_chunk<BITS>(gq + grow * rb + (size_t)cpos * F::BYTES, dg[s]);
-    load_chunk<BITS>(uq + grow * rb + (size_t)cpos * F::BYTES, du[s]);
-    sg[s] = gsz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
-    su[s] = usz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
-  }
-  const int pb = offsets[e], pe = offsets[e + 1];
-  constexpr bool NT2 = ITER <= MOEQ_NT2_MAX_ITER;
-  for (int p0 = pb; p0 < pe;) {
-    if (NT2 && pe - p0 >= 2) {
-      gateup_pass<BITS, DBITS, ITER, LPR, CH, 2>(dg, du, sg, su, x, H, I, kS, sorted, p0, 2, row0, I_end, g, hh);
-      p0 += 2;
-    } else {
-      gateup_pass<BITS, DBITS, ITER, LPR, CH, 1>(dg, du, sg, su, x, H, I, kS, sorted, p0, 1, row0, I_end, g, hh);
-      p0 += 1;
-    }
-  }
+MOEQ_DEV float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-// -------------------------------------------------------------------------
-// down: y[a][n] = (Wd h_p)[n] for the expert's assignments a = sorted[p]
-// -------------------------------------------------------------------------
-template <int BITS, int ITER, int LPR, int CH, int NT>
-MOEQ_DEV void down_pass(uint32_t (&d)[CH][Fmt<BITS>::DW], const uint32_t (&sw)[CH], const uint16_t* __restrict__ hh,
-                        int H, int I, const int32_t* __restrict__ sorted, int p0, int nt, int row0, int H_end,
-                        const Geo<ITER, LPR>& g, float* __restrict__ y) {
+// Largest divisor of cw that is at most lim (at least 1).
+constexpr int x_group(int cw, int lim) {
+  int g = 1;
+  for (int d = 1; d <= cw && d <= lim; ++d)
+    if (cw % d == 0) g = d;
+  return g;
+}
+
+// The wavefront's part of the dot products of its 64 rows with NT token rows
+// xr[t] (bf16, read as scalars), for NM matrices: out[m][t].  The loads of
+// chunks [0, D) are already in buf.
+template <int BITS, int NM, int NT, int CW, int D>
+MOEQ_DEV void stream_rows(const Stream<BITS, NM>& st, ChunkBuf<BITS, NM> (&buf)[D],
+                          const uint16_t* const (&xr)[kMaxNT], const float (&xs)[kMaxNT], float (&out)[NM][kMaxNT]) {
   using F = Fmt<BITS>;
-  opaque(d);
-  int arow[NT];
+  constexpr int CPG = F::CHUNKS_PER_GROUP;
+  static_assert(CW % CPG == 0, "a wavefront covers whole groups");
+  float acc[NM][NT][2];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) arow[t] = t < nt ? sorted[p0 + t] : 0;
-  float ac[CH][NT];
+  for (int m = 0; m < NM; ++m) {
 #pragma unroll
-  for (int s = 0; s < CH; ++s)
+    for (int t = 0; t < kMaxNT; ++t) out[m][t] = 0.0f;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) ac[s][t] = 0.0f;
-#pragma unroll 1
-  for (int it = 0; it < ITER; ++it) {
-    uint32_t XH[NT][F::PAIRS];
-    float XS[NT];
-    load_h_pairs<BITS, NT>(hh, p0, nt, g.cl + g.lpr * it, XH, XS, I);
-#pragma unroll
-    for (int s = 0; s < CH; ++s)
-      if (s % ITER == it) chunk_dot<BITS, NT>(d[s], sw[s], XH, XS, ac[s]);
+    for (int t = 0; t < NT; ++t) { acc[m][t][0] = 0.0f; acc[m][t][1] = 0.0f; }
   }
+  float s[NM], zc[NM];
+  // Activations: the same for every lane, read with scalar loads into
+  // SGPRs, XG chunks at a time (64 SGPRs), so one load latency covers XG
+  // chunks.
+  constexpr int XG = x_group(CW, 64 / F::PAIRS / NT);   // chunks per x load group
+  uint32_t X[XG][NT][F::PAIRS];
 #pragma unroll
-  for (int s = 0; s < CH; ++s) {
-    if (s % ITER != 0) continue;
-    float cs[NT];
+  for (int c = 0; c < CW; ++c) {
+    ChunkBuf<BITS, NM>& b = buf[c % D];
+    if (c % XG == 0) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) cs[t] = ac[s][t];
+      for (int g = 0; g < XG; ++g)
 #pragma unroll
-    for (int q = 1; q < CH; ++q)
-      if (q < ITER && s + q < CH) {
+        for (int t = 0; t < NT; ++t) {
+          const uint32_t* xp = reinterpret_cast<const uint32_t*>(xr[t] + (size_t)(st.c0 + c + g) * F::CODES);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) cs[t] += ac[s + q][t];
+          for (int p = 0; p < F::PAIRS; ++p) X[g][t][p] = xp[p];
+        }
+    }
+    if (c % CPG == 0) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        s[m] = f16_bits_to_f32(b.sz[m] & 0xFFFFu);
+        zc[m] = f16_bits_to_f32(b.sz[m] >> 16) + F::OFFSET;
       }
-    const int row = row0 + g.row_of(s);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float v = group_sum_last<LPR>(cs[t]);
-      if (g.writer() && t < nt && row < H_end) y[(size_t)arow[t] * H + row] = v;
     }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      // the chunk's codes are taken here, where they are needed: nothing
+      // derived from them is computed (and kept live) earlier
+#pragma unroll
+      for (int j = 0; j < F::DW; ++j) asm volatile("" : "+v"(b.q[m][j]));
+      uint32_t P[F::PAIRS];
+      chunk_pairs<BITS>(b.q[m], P);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int p = 0; p < F::PAIRS; ++p) acc[m][t][p & 1] = dot2_bf16(P[p], X[c % XG][t][p], acc[m][t][p & 1]);
+      stage_fence();   // one matrix's unpacked pairs live at a time
+    }
+    if (c + D < CW) st.load(c + D, b);
+    if (c % CPG == CPG - 1) {   // group complete: apply its scale and zero
+      const int gl = c / CPG;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float x_sum = lane_value(xs[t], 8 * gl + 7);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          out[m][t] = fmaf(s[m], (acc[m][t][0] + acc[m][t][1]) - zc[m] * x_sum, out[m][t]);
+          acc[m][t][0] = 0.0f;
+          acc[m][t][1] = 0.0f;
+        }
+      }
+    }
+    stage_fence();
   }
 }
 
-template <int BITS, int ITER, int LPR>
-__global__ __launch_bounds__(256, ITER <= 2 ? kDownWaves : 2) void down_gemv_kernel(const uint8_t* __restrict__ dq, const uint32_t* __restrict__ dsz,
-                                                        const uint16_t* __restrict__ hh, int H, int I,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ sorted,
-                                                        const int32_t* __restrict__ active, int tiles,
-                                                        float* __restrict__ y) {
-  using F = Fmt<BITS>;
-  constexpr int CH = down_ch(ITER);
-  const int n_active = min(active[0], (int)(gridDim.x / tiles));   // the grid has a block row per possible slot
-  const int slot = n_active - 1 - (int)(blockIdx.x / tiles), tile = blockIdx.x % tiles;
-  if (slot < 0) return;
-  const int e = active[1 + slot];
-  const Geo<ITER, LPR> g;
-  const int wave = threadIdx.x >> 6;
-  const int rows_w = (CH / ITER) * g.rpw;
-  const int row0 = (tile * 4 + wave) * rows_w;
-  if (row0 >= H) return;
-  const int H_end = min(H, row0 + rows_w);
-  const size_t rb = row_bytes(I, BITS), gpr = I / 64;
-  uint32_t d[CH][F::DW], sw[CH];
+// Partial sums of the block's W wavefronts: v[w][m][t][row].
+template <int W, int NM>
+struct Partials {
+  float v[W][NM][kMaxNT][64];
+};
+
+// One pass over the block's rows for the tokens of rows xr (nt of them):
+// every wavefront streams its chunks, then the partials are added in
+// wavefront order; wavefront t < nt ends with the sums of token t for its
+// lane's row in tot[m].
+template <int BITS, int NM, int W, int CW>
+MOEQ_DEV void block_pass(const Stream<BITS, NM>& st, ChunkBuf<BITS, NM> (&buf)[CW < kDepth ? CW : kDepth],
+                         const uint16_t* const (&xr)[kMaxNT], int nt, Partials<W, NM>& part, float (&tot)[NM]) {
+  constexpr int CPG = Fmt<BITS>::CHUNKS_PER_GROUP;
+  constexpr int D = CW < kDepth ? CW : kDepth;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index is uniform
+  float xs[kMaxNT];
+  group_sums<CW / CPG>(xr, nt, st.c0 / CPG, xs);
+  stage_fence();
+  float out[NM][kMaxNT];
+  if (nt == 2) stream_rows<BITS, NM, 2, CW, D>(st, buf, xr, xs, out);
+  else stream_rows<BITS, NM, 1, CW, D>(st, buf, xr, xs, out);
 #pragma unroll
-  for (int s = 0; s < CH; ++s) {
-    const int row = min(row0 + g.row_of(s), H - 1);
-    const int cpos = g.cpos_of(s);
-    const size_t grow = (size_t)e * H + row;
-    load_chunk<BITS>(dq + grow * rb + (size_t)cpos * F::BYTES, d[s]);
-    sw[s] = dsz[grow * gpr + cpos / F::CHUNKS_PER_GROUP];
-  }
-  const int pb = offsets[e], pe = offsets[e + 1];
-  constexpr bool NT2 = ITER <= MOEQ_NT2_MAX_ITER;
-  for (int p0 = pb; p0 < pe;) {
-    if (NT2 && pe - p0 >= 2) {
-      down_pass<BITS, ITER, LPR, CH, 2>(d, sw, hh, H, I, sorted, p0, 2, row0, H_end, g, y);
-      p0 += 2;
-    } else {
-      down_pass<BITS, ITER, LPR, CH, 1>(d, sw, hh, H, I, sorted, p0, 1, row0, H_end, g, y);
-      p0 += 1;
-    }
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < kMaxNT; ++t) part.v[wave][m][t][lane] = out[m][t];
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    float v = 0.0f;
+    if (wave < nt)
+#pragma unroll
+      for (int w = 0; w < W; ++w) v += part.v[w][m][wave][lane];
+    tot[m] = v;
   }
 }
+
+// -------------------------------------------------------------------------
+// gate/up: h[p][i] = bf16(silu(Wg x_t)[i] * (Wu x_t)[i]) for the expert's
+// sorted positions p (token t = sorted[p] / (k+S)); h is [A][I] bf16.
+// -------------------------------------------------------------------------
+template <int BITS, int W, int CW>
+__global__ __launch_bounds__(64 * W, 4) void gateup_rows_kernel(const uint8_t* __restrict__ gq,
+                                                                const uint32_t* __restrict__ gsz,
+                                                                const uint8_t* __restrict__ uq,
+                                                                const uint32_t* __restrict__ usz,
+                                                                const uint16_t* __restrict__ x, int H, int I,
+                                                                DecodeGrid dg, const int32_t* __restrict__ offsets,
+                                                                const int32_t* __restrict__ sorted,
+                                                                const int32_t* __restrict__ active,
+                                                                uint16_t* __restrict__ hh) {
+  using F = Fmt<BITS>;
+  constexpr int D = CW < kDepth ? CW : kDepth;
+  __shared__ Partials<W, 2> part;
+  int e, tile, pair;
+  if (!block_work(dg, active, e, tile, pair)) return;
+  e = uniform(e);
+  tile = uniform(tile);
+  pair = uniform(pair);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index is uniform
+  Stream<BITS, 2> st;
+  {
+    const size_t ebytes = (size_t)I * row_bytes(H, BITS), ewords = (size_t)I * (H / 64);
+    const uint8_t* const qe[2] = {gq + e * ebytes, uq + e * ebytes};
+    const uint32_t* const sze[2] = {gsz + e * ewords, usz + e * ewords};
+    st.init(qe, sze, H / F::CODES, H / 64, tile, wave * CW);
+  }
+  ChunkBuf<BITS, 2> buf[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) st.load(c, buf[c]);   // before the token lookups
+  stage_fence();
+  int pb = uniform(offsets[e]), pe = uniform(offsets[e + 1]);
+  if (pair >= 0) {
+    pb += 2 * pair;
+    pe = min(pe, pb + 2);
+  }
+  const int row = tile * 64 + lane;
+  // The first pass uses the loads issued above; later passes (experts with
+  // more than two tokens) reload into buffers of their own, so no buffer is
+  // carried around the loop (that would force a wait for every load in
+  // flight before the loop).
+  auto pass = [&](int p0, ChunkBuf<BITS, 2> (&b)[D]) {
+    const int nt = min(kMaxNT, pe - p0);
+    const int t0 = uniform(sorted[p0] / dg.kS);
+    const int t1 = nt > 1 ? uniform(sorted[p0 + 1] / dg.kS) : t0;
+    const uint16_t* const xr[kMaxNT] = {x + (size_t)t0 * H, x + (size_t)t1 * H};
+    float tot[2];
+    block_pass<BITS, 2, W, CW>(st, b, xr, nt, part, tot);
+    if (wave < nt) hh[(size_t)(p0 + wave) * I + row] = (uint16_t)f32_to_bf16_bits(silu_f32(tot[0]) * tot[1]);
+  };
+  if (pb >= pe) return;
+  pass(pb, buf);
+  for (int p0 = pb + kMaxNT; p0 < pe; p0 += kMaxNT) {
+    __syncthreads();   // the previous pass's partials have been read
+    ChunkBuf<BITS, 2> lb[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) st.load(c, lb[c]);
+    stage_fence();
+    pass(p0, lb);
+  }
+}
+
+// -------------------------------------------------------------------------
+// down: y[a][n] = (Wd h_p)[n] for the expert's sorted positions p and their
+// assignments a = sorted[p]; y is [A][H] fp32.
+// -------------------------------------------------------------------------
+template <int BITS, int W, int CW>
+__global__ __launch_bounds__(64 * W, 4) void down_rows_kernel(const uint8_t* __restrict__ dq,
+                                                              const uint32_t* __restrict__ dsz,
+                                                              const uint16_t* __restrict__ hh, int H, int I,
+                                                              DecodeGrid dg, const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ sorted,
+                                                              const int32_t* __restrict__ active,
+                                                              float* __restrict__ y) {
+  using F = Fmt<BITS>;
+  constexpr int D = CW < kDepth ? CW : kDepth;
+  __shared__ Partials<W, 1> part;
+  int e, tile, pair;
+  if (!block_work(dg, active, e, tile, pair)) return;
+  e = uniform(e);
+  tile = uniform(tile);
+  pair = uniform(pair);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index is uniform
+  Stream<BITS, 1> st;
+  {
+    const uint8_t* const qe[1] = {dq + e * ((size_t)H * row_bytes(I, BITS))};
+    const uint32_t* const sze[1] = {dsz + e * ((size_t)H * (I / 64))};
+    st.init(qe, sze, I / F::CODES, I / 64, tile, wave * CW);
+  }
+  ChunkBuf<BITS, 1> buf[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) st.load(c, buf[c]);   // before the token lookups
+  stage_fence();
+  int pb = uniform(offsets[e]), pe = uniform(offsets[e + 1]);
+  if (pair >= 0) {
+    pb += 2 * pair;
+    pe = min(pe, pb + 2);
+  }
+  const int row = tile * 64 + lane;
+  auto pass = [&](int p0, ChunkBuf<BITS, 1> (&b)[D]) {   // as in the gate/up kernel
+    const int nt = min(kMaxNT, pe - p0);
+    const uint16_t* const xr[kMaxNT] = {hh + (size_t)p0 * I, hh + (size_t)(p0 + (nt > 1 ? 1 : 0)) * I};
+    float tot[1];
+    block_pass<BITS, 1, W, CW>(st, b, xr, nt, part, tot);
+    if (wave < nt) y[(size_t)sorted[p0 + wave] * H + row] = tot[0];
+  };
+  if (pb >= pe) return;
+  pass(pb, buf);
+  for (int p0 = pb + kMaxNT; p0 < pe; p0 += kMaxNT) {
+    __syncthreads();
+    ChunkBuf<BITS, 1> lb[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) st.load(c, lb[c]);
+    stage_fence();
+    pass(p0, lb);
+  }
+}
+
+// (W, CW) shapes with a kernel: W wavefronts per block, CW chunks each.
+#define MOEQ_DECODE_SHAPES(X)                                                                            \
+  X(2, 2) X(2, 4) X(2, 8) X(2, 16) X(4, 2) X(4, 4) X(4, 6) X(4, 8) X(4, 12) X(4, 16) X(8, 2) X(8, 4)      \
+  X(8, 8) X(8, 16) X(16, 4) X(16, 8) X(16, 16)
+constexpr int kShapes[][2] = {{2, 2}, {2, 4}, {2, 8}, {2, 16}, {4, 2}, {4, 4}, {4, 6}, {4, 8}, {4, 12},
+                              {4, 16}, {8, 2}, {8, 4}, {8, 8}, {8, 16}, {16, 4}, {16, 8}, {16, 16}};
 
 }  // namespace decode_detail
 
+// Grid of the decode kernels for N output rows per expert (see
+// decode_detail::DecodeGrid); returns the block count.
+inline int decode_grid(const moe_layer_desc* L, int T, int N, decode_detail::DecodeGrid& dg) {
+  dg.E = L->E;
+  dg.S = L->S;
+  dg.kS = L->k + L->S;
+  dg.tiles = N / 64;
+  dg.groups = (T + 1) / 2;
+  dg.shared_blocks = L->S > 0 ? (L->S * dg.tiles + 7) / 8 * 8 * dg.groups : 0;
+  const long routed = (long)T * L->k < L->E ? (long)T * L->k : L->E;   // upper bound on active routed experts
+  return dg.shared_blocks + (int)routed * dg.tiles;
+}
+
 // Per-bit-width launchers (one translation unit each, decode_b{4,6,8}.hip).
-#define MOEQ_DECODE_LAUNCHERS(B, SPEC)                                                                   \
-  SPEC int decode_gateup_b##B(const moe_layer_desc* L, const uint16_t* x, const int32_t* offsets,        \
-                              const int32_t* sorted, const int32_t* active, int slots, int rows_per_wave, \
-                              int lpr, int iter, uint16_t* hh, hipStream_t s)
-#define MOEQ_DOWN_LAUNCHER(B, SPEC)                                                                      \
-  SPEC int decode_down_b##B(const moe_layer_desc* L, const uint16_t* hh,                                 \
-                            const int32_t* offsets, const int32_t* sorted, const int32_t* active,        \
-                            int slots, int rows_per_wave, int lpr, int iter, float* y, hipStream_t s)
+#define MOEQ_DECODE_LAUNCHERS(B)                                                                          \
+  int decode_gateup_b##B(const moe_layer_desc* L, const uint16_t* x, const int32_t* offsets,              \
+                         const int32_t* sorted, const int32_t* active, int T, int W, int CW, uint16_t* hh,  \
+                         hipStream_t s);                                                                  \
+  int decode_down_b##B(const moe_layer_desc* L, const uint16_t* hh, const int32_t* offsets,               \
+                       const int32_t* sorted, const int32_t* active, int T, int W, int CW, float* y,      \
+                       hipStream_t s)
 
-MOEQ_DECODE_LAUNCHERS(4, );
-MOEQ_DECODE_LAUNCHERS(6, );
-MOEQ_DECODE_LAUNCHERS(8, );
-MOEQ_DOWN_LAUNCHER(4, );
-MOEQ_DOWN_LAUNCHER(6, );
-MOEQ_DOWN_LAUNCHER(8, );
+MOEQ_DECODE_LAUNCHERS(4);
+MOEQ_DECODE_LAUNCHERS(6);
+MOEQ_DECODE_LAUNCHERS(8);
 
-// (iter, lanes per row) combinations with a kernel: lpr is the largest power
-// of two <= 64 dividing the chunks per row, iter the rest (1..4).
-#define MOEQ_DEC_SWITCH(ITERV, LPRV, CALL, RC)                       \
-  switch (ITERV * 100 + LPRV) {                                      \
-    case 164: CALL(1, 64); break;                                    \
-    case 132: CALL(1, 32); break;                                    \
-    case 116: CALL(1, 16); break;                                    \
-    case 108: CALL(1, 8); break;                                     \
-    case 264: CALL(2, 64); break;                                    \
-    case 364: CALL(3, 64); break;                                    \
-    case 332: CALL(3, 32); break;                                    \
-    case 316: CALL(3, 16); break;                                    \
-    case 308: CALL(3, 8); break;                                     \
-    case 464: CALL(4, 64); break;                                    \
-    default: RC = set_error(MOEQ_ERR_UNSUPPORTED, "decode: no kernel for %d chunks x %d lanes", ITERV, LPRV); \
-  }
-
-#define MOEQ_DEFINE_DECODE(B)                                                                            \
-  MOEQ_DECODE_LAUNCHERS(B, ) {                                                                           \
-    const int tiles = (L->I + 4 * rows_per_wave - 1) / (4 * rows_per_wave);                              \
-    const int grid = slots * tiles;                                                                      \
-    int rc = MOEQ_OK;                                                                                    \
-    MOEQ_DEC_SWITCH(iter, lpr, MOEQ_GATEUP_CALL, rc)                                                     \
-    return rc != MOEQ_OK ? rc : check_launch("moe_qgemv_decode (gate/up)");                              \
-  }                                                                                                      \
-  MOEQ_DOWN_LAUNCHER(B, ) {                                                                              \
-    const int tiles = (L->H + 4 * rows_per_wave - 1) / (4 * rows_per_wave);                              \
-    const int grid = slots * tiles;                                                                      \
-    int rc = MOEQ_OK;                                                                                    \
-    MOEQ_DEC_SWITCH(iter, lpr, MOEQ_DOWN_CALL, rc)                                                       \
-    return rc != MOEQ_OK ? rc : check_launch("moe_qgemv_decode (down)");                                 \
+#define MOEQ_DEFINE_DECODE(B)                                                                             \
+  int decode_gateup_b##B(const moe_layer_desc* L, const uint16_t* x, const int32_t* offsets,              \
+                         const int32_t* sorted, const int32_t* active, int T, int W, int CW, uint16_t* hh,  \
+                         hipStream_t s) {                                                                 \
+    decode_detail::DecodeGrid dg;                                                                         \
+    const int grid = decode_grid(L, T, L->I, dg);                                                         \
+    if (grid == 0) return MOEQ_OK;                                                                        \
+    bool launched = false;                                                                                \
+    MOEQ_DECODE_SHAPES(MOEQ_LAUNCH_GU)                                                                    \
+    if (!launched) return set_error(MOEQ_ERR_UNSUPPORTED, "decode: no gate/up kernel for W=%d CW=%d", W, CW); \
+    return check_launch("moe_qgemv_decode (gate/up)");                                                    \
+  }                                                                                                       \
+  int decode_down_b##B(const moe_layer_desc* L, const uint16_t* hh, const int32_t* offsets,               \
+                       const int32_t* sorted, const int32_t* active, int T, int W, int CW, float* y,      \
+                       hipStream_t s) {                                                                   \
+    decode_detail::DecodeGrid dg;                                                                         \
+    const int grid = decode_grid(L, T, L->H, dg);                                                         \
+    if (grid == 0) return MOEQ_OK;                                                                        \
+    bool launched = false;                                                                                \
+    MOEQ_DECODE_SHAPES(MOEQ_LAUNCH_DN)                                                                    \
+    if (!launched) return set_error(MOEQ_ERR_UNSUPPORTED, "decode: no down kernel for W=%d CW=%d", W, CW); \
+    return check_launch("moe_qgemv_decode (down)");                                                       \
   }
 
 }  // namespace moeq

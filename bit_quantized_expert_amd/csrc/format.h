@@ -1,15 +1,27 @@
-// Device view of the packed weight format: how one lane loads a "chunk" of a
-// packed row and turns its codes into bf16 pairs for v_dot2_f32_bf16.
+// Device view of the packed weight format: where a code lives in memory and
+// how one lane turns a "chunk" of codes into bf16 pairs for v_dot2_f32_bf16.
 //
 // A chunk is the unit one lane loads with one vector load:
 //   4-bit: 16 bytes = 32 codes (dwordx4); a 64-group spans 2 chunks
 //   6-bit: 12 bytes = 16 codes (dwordx3); a 64-group spans 4 chunks
 //   8-bit: 16 bytes = 16 codes (dwordx4); a 64-group spans 4 chunks
+//
+// Layout in memory (per projection, all experts' rows r = 0 .. n_mats*N-1):
+// rows come in tiles of 64, and inside a tile chunk-major: chunk c of row r
+// starts at byte ((r / 64) * CPR + c) * 64 * BYTES + (r % 64) * BYTES, CPR =
+// K / CODES.  A wavefront whose lane l handles row 64 t + l thus reads one
+// contiguous 64 * BYTES block per chunk.  The scale/zero word of group g of
+// row r sits at index ((r / 64) * GPR + g) * 64 + r % 64, GPR = K / 64.
+//
+// Inside a chunk the codes sit in "fields" (4-bit: nibble n = byte n/2, low
+// nibble first; 6-bit: bits 6n..6n+5 of the little-endian chunk; 8-bit:
+// byte n) in an order chosen so that the in-register unpacking below yields
+// the bf16 pairs (code 2p, code 2p+1) with one AND-OR per pair: field_code()
+// gives the code held by field n.
+//
 // Codes become bf16 values exactly: 4- and 6-bit codes are OR-ed into the
-// mantissa of bf16 128.0 (giving 128 + q, "OFFSET" = 128, one AND-OR per two
-// codes); 8-bit codes are converted through fp32 (OFFSET = 0).  The pair
-// order inside a chunk is fixed per bit width (pair_code); activations are
-// arranged in the same order so each dot2 multiplies matching elements.
+// mantissa of bf16 128.0 (giving 128 + q, "OFFSET" = 128); 8-bit codes are
+// converted through fp32 (OFFSET = 0).
 #pragma once
 #include "common.h"
 
@@ -27,18 +39,35 @@ template <> struct Fmt<8> {
   static constexpr float OFFSET = 0.0f;
 };
 
-// Code index (within the chunk) in the low (half=0) or high (half=1) bf16 of pair p.
-template <int BITS> MOEQ_DEV constexpr int pair_code(int p, int half);
-template <> MOEQ_DEV constexpr int pair_code<4>(int p, int half) {
-  return 8 * (p >> 2) + (p & 3) + 4 * half;          // nibble i and i+4 of dword p/4
+// Code index (within the chunk) in the low (half=0) or high (half=1) bf16 of
+// pair p: natural for every width (the field order makes it so).
+template <int BITS>
+MOEQ_DEV constexpr int pair_code(int p, int half) { return 2 * p + half; }
+
+// Code held by field n of a chunk.  4-bit: nibbles 8d + j and 8d + 4 + j
+// (j < 4) of dword d hold codes 8d + 2j and 8d + 2j + 1, so (w >> 4j) &
+// 0x000F000F of that dword is pair 4d + j.  6-bit: the fields chunk_pairs<6>
+// combines into pair p are (lo[p], hi[p]) = (0,3) (1,4) (5,8) (6,9) (10,13)
+// (11,14) (2,7) (12,15); they hold codes 2p and 2p + 1.  8-bit: natural.
+template <int BITS>
+MOEQ_HD constexpr int field_code(int n) {
+  if constexpr (BITS == 4) {
+    return 8 * (n >> 3) + 2 * (n & 3) + ((n >> 2) & 1);
+  } else if constexpr (BITS == 6) {
+    // nibble n: code of field n = 0, 2, 12, 1, 3, 4, 6, 13, 5, 7, 8, 10, 14, 9, 11, 15
+    return (int)((0xFB9EA875D6431C20ull >> (4 * n)) & 0xF);
+  } else {
+    return n;
+  }
 }
-template <> MOEQ_DEV constexpr int pair_code<6>(int p, int half) {
-  // derived from the 6-bit field positions: see chunk_pairs<6>
-  constexpr int lo[8] = {0, 1, 5, 6, 10, 11, 2, 12};
-  constexpr int hi[8] = {3, 4, 8, 9, 13, 14, 7, 15};
-  return half ? hi[p] : lo[p];
+
+// Byte offset of chunk c of row r, and index of the scale/zero word of
+// group g of row r, in the tiled layout (cpr chunks and gpr groups per row).
+template <int BITS>
+MOEQ_HD size_t chunk_offset(size_t r, size_t c, size_t cpr) {
+  return ((r >> 6) * cpr + c) * (64 * (size_t)Fmt<BITS>::BYTES) + (r & 63) * (size_t)Fmt<BITS>::BYTES;
 }
-template <> MOEQ_DEV constexpr int pair_code<8>(int p, int half) { return 2 * p + half; }
+MOEQ_HD size_t sz_index(size_t r, size_t g, size_t gpr) { return ((r >> 6) * gpr + g) * 64 + (r & 63); }
 
 typedef uint32_t moeq_u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t moeq_u32x3 __attribute__((ext_vector_type(3)));

@@ -105,18 +105,22 @@ struct QuantStage {
   static_assert(N >= 1 && ROWS * CPG % 256 == 0, "tile too small");
   uint32_t d[N][F::DW];
   uint32_t sz[N];
-  // row(r) returns (packed row base, sz row base) of tile row r
+  // row(r, q, s, grow) gives the projection's code and scale/zero arrays
+  // and the row index (over all experts) of tile row r; the K-slice
+  // [k0, k0 + 64) is group k0 / 64 (tiled layout, format.h)
   template <class RowPtr>
-  MOEQ_DEV void load(RowPtr row, int k0) {
+  MOEQ_DEV void load(RowPtr row, int k0, int K) {
+    const size_t cpr = (size_t)(K / F::CODES), gpr = (size_t)(K / 64);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       const int c = threadIdx.x + 256 * j;
       const int r = c / CPG, ch = c % CPG;
       const uint8_t* q;
       const uint32_t* s;
-      row(r, q, s);
-      load_chunk<BITS>(q + (size_t)(k0 / 64) * (64 * BITS / 8) + ch * F::BYTES, d[j]);
-      sz[j] = s[k0 / 64];
+      size_t grow;
+      row(r, q, s, grow);
+      load_chunk<BITS>(q + chunk_offset<BITS>(grow, (size_t)(k0 / 64) * CPG + ch, cpr), d[j]);
+      sz[j] = s[sz_index(grow, (size_t)(k0 / 64), gpr)];
     }
   }
   MOEQ_DEV void store(uint16_t* lds) const {
@@ -142,20 +146,20 @@ struct QuantStage {
             moeq_u32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
     }
   }
-  // codes of one chunk in natural order
+  // codes of one chunk in natural order (field n holds code field_code(n))
   static MOEQ_DEV void unpack_codes(const uint32_t (&w)[F::DW], uint32_t (&c)[F::CODES]) {
     if constexpr (BITS == 4) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int n = 0; n < 8; ++n) c[8 * j + n] = (w[j] >> (4 * n)) & 0xFu;
+        for (int n = 0; n < 8; ++n) c[field_code<4>(8 * j + n)] = (w[j] >> (4 * n)) & 0xFu;
     } else if constexpr (BITS == 6) {
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
         const int b = 6 * n, dw = b >> 5, sh = b & 31;
         uint32_t v = w[dw] >> sh;
         if (sh > 26) v |= w[dw + 1] << (32 - sh);
-        c[n] = v & 0x3Fu;
+        c[field_code<6>(n)] = v & 0x3Fu;
       }
     } else {
 #pragma unroll

@@ -75,12 +75,11 @@ __global__ __launch_bounds__(256) void gateup_kernel(const uint8_t* __restrict__
     const int r = (threadIdx.x >> 3) + 32 * j;
     arow[j] = r < rows ? x + (size_t)(sorted[base + r] / kS) * H : nullptr;
   }
-  const size_t rb = row_bytes(H, BITS), gpr = H / 64;
-  auto brow = [&](int rr, const uint8_t*& q, const uint32_t*& s) {
+  auto brow = [&](int rr, const uint8_t*& q, const uint32_t*& s, size_t& row) {
     const int blk = rr >> 5, f = n0 + 32 * (blk >> 1) + (rr & 31);
-    const size_t row = (size_t)e * I + f;
-    if (blk & 1) { q = uq + row * rb; s = usz + row * gpr; }
-    else { q = gq + row * rb; s = gsz + row * gpr; }
+    row = (size_t)e * I + f;
+    if (blk & 1) { q = uq; s = usz; }
+    else { q = gq; s = gsz; }
   };
   RowStage<BM> sa;
   QuantStage<BITS, 256> sb;
@@ -88,13 +87,13 @@ __global__ __launch_bounds__(256) void gateup_kernel(const uint8_t* __restrict__
   WaveAcc<2, 4> acc;
   acc.zero();
   sa.load(asrc, 0);
-  sb.load(brow, 0);
+  sb.load(brow, 0, H);
   sa.store(As);
   sb.store(Bs);
   __syncthreads();
   for (int k0 = 0; k0 < H; k0 += kBK) {
     const bool more = k0 + kBK < H;
-    if (more) { sa.load(asrc, k0 + kBK); sb.load(brow, k0 + kBK); }
+    if (more) { sa.load(asrc, k0 + kBK); sb.load(brow, k0 + kBK, H); }
     mfma_slice<2, 4>(As, Bs, 64 * wm, 128 * wn, lane, acc);
     __syncthreads();
     if (more) { sa.store(As); sb.store(Bs); }
@@ -132,25 +131,24 @@ __global__ __launch_bounds__(256) void down_kernel(const uint8_t* __restrict__ d
   const int base = offsets[e] + mt * BM;
   const int rows = min(BM, counts[e] - mt * BM);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  const size_t rb = row_bytes(I, BITS), gpr = I / 64;
   auto asrc = [&](int, int r) -> const uint16_t* { return r < rows ? h + (size_t)(base + r) * I : nullptr; };
-  auto brow = [&](int rr, const uint8_t*& q, const uint32_t*& s) {
-    const size_t row = (size_t)e * H + n0 + rr;
-    q = dq + row * rb;
-    s = dsz + row * gpr;
+  auto brow = [&](int rr, const uint8_t*& q, const uint32_t*& s, size_t& row) {
+    row = (size_t)e * H + n0 + rr;
+    q = dq;
+    s = dsz;
   };
   RowStage<BM> sa;
   QuantStage<BITS, 128> sb;
   WaveAcc<2, 2> acc;
   acc.zero();
   sa.load(asrc, 0);
-  sb.load(brow, 0);
+  sb.load(brow, 0, I);
   sa.store(As);
   sb.store(Bs);
   __syncthreads();
   for (int k0 = 0; k0 < I; k0 += kBK) {
     const bool more = k0 + kBK < I;
-    if (more) { sa.load(asrc, k0 + kBK); sb.load(brow, k0 + kBK); }
+    if (more) { sa.load(asrc, k0 + kBK); sb.load(brow, k0 + kBK, I); }
     mfma_slice<2, 2>(As, Bs, 64 * wm, 64 * wn, lane, acc);
     __syncthreads();
     if (more) { sa.store(As); sb.store(Bs); }

@@ -6,14 +6,16 @@ using namespace moeq;
 
 // One wavefront per 64-value group: lane l holds value l of the group.
 // Min and max come from wave reductions; the code of every lane is then
-// packed by shuffles.  fp32 arithmetic with IEEE division and rint (ties to
-// even) so the codes equal any other IEEE fp32 evaluation of the same
-// formula bit for bit.
+// packed into the tiled field order (format.h) by shuffles.  fp32
+// arithmetic with IEEE division and rint (ties to even) so the codes equal
+// any other IEEE fp32 evaluation of the same formula bit for bit.
 template <int BITS>
-__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, long ngroups,
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, long ngroups, int gpr,
                                                        uint8_t* __restrict__ q, uint32_t* __restrict__ sz) {
+  using F = Fmt<BITS>;
   const int lane = threadIdx.x & 63;
   const long stride = (long)gridDim.x * 4;
+  const int cpr = gpr * F::CHUNKS_PER_GROUP;
   for (long g = (long)blockIdx.x * 4 + (threadIdx.x >> 6); g < ngroups; g += stride) {
     const float v = w[g * 64 + lane];
     const float mn = wave_min(v);
@@ -29,41 +31,48 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     float r = rintf(v / sf + zf);
     r = fminf(fmaxf(r, 0.0f), qmax);
     const uint32_t code = degenerate ? 0u : (uint32_t)r;
-    uint8_t* qg = q + g * (64 * BITS / 8);
+    const long row = g / gpr;
+    const int gi = (int)(g % gpr);
     if constexpr (BITS == 4) {
-      const uint32_t lo = __shfl(code, (2 * lane) & 63);
-      const uint32_t hi = __shfl(code, (2 * lane + 1) & 63);
-      if (lane < 32) qg[lane] = (uint8_t)(lo | (hi << 4));
+      // lanes 0..31: byte b of chunk k (32 codes) holds fields 2b, 2b+1
+      const int k = (lane >> 4) & 1, b = lane & 15;
+      const uint32_t lo = __shfl(code, 32 * k + field_code<4>(2 * b));
+      const uint32_t hi = __shfl(code, 32 * k + field_code<4>(2 * b + 1));
+      if (lane < 32) q[chunk_offset<4>(row, 2 * gi + k, cpr) + b] = (uint8_t)(lo | (hi << 4));
     } else if constexpr (BITS == 6) {
-      const uint32_t c0 = __shfl(code, (4 * lane + 0) & 63);
-      const uint32_t c1 = __shfl(code, (4 * lane + 1) & 63);
-      const uint32_t c2 = __shfl(code, (4 * lane + 2) & 63);
-      const uint32_t c3 = __shfl(code, (4 * lane + 3) & 63);
-      const uint32_t word = c0 | (c1 << 6) | (c2 << 12) | (c3 << 18);
+      // lanes 0..15: 24-bit word i of chunk k holds fields 4i..4i+3
+      const int k = (lane >> 2) & 3, i = lane & 3;
+      uint32_t word = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) word |= __shfl(code, 16 * k + field_code<6>(4 * i + m)) << (6 * m);
       if (lane < 16) {
-        qg[3 * lane + 0] = (uint8_t)(word & 0xFF);
-        qg[3 * lane + 1] = (uint8_t)((word >> 8) & 0xFF);
-        qg[3 * lane + 2] = (uint8_t)((word >> 16) & 0xFF);
+        uint8_t* dst = q + chunk_offset<6>(row, 4 * gi + k, cpr) + 3 * i;
+        dst[0] = (uint8_t)(word & 0xFF);
+        dst[1] = (uint8_t)((word >> 8) & 0xFF);
+        dst[2] = (uint8_t)((word >> 16) & 0xFF);
       }
     } else {
-      qg[lane] = (uint8_t)code;
+      q[chunk_offset<8>(row, 4 * gi + (lane >> 4), cpr) + (lane & 15)] = (uint8_t)code;
     }
-    if (lane == 0) sz[g] = s16 | (z16 << 16);
+    if (lane == 0) sz[sz_index(row, gi, gpr)] = s16 | (z16 << 16);
   }
 }
 
-// One thread per chunk: load, turn into bf16 pairs exactly as the decode
-// kernels do, and write the codes back in natural order.
+// One thread per chunk (in memory order): load, turn into bf16 pairs exactly
+// as the decode kernels do, and write the codes back in natural order.
 template <int BITS>
-__global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__ q, long nchunks,
+__global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__ q, long nchunks, int cpr, int K,
                                                      uint8_t* __restrict__ codes) {
   using F = Fmt<BITS>;
-  for (long c = (long)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += (long)gridDim.x * blockDim.x) {
+  for (long m = (long)blockIdx.x * blockDim.x + threadIdx.x; m < nchunks; m += (long)gridDim.x * blockDim.x) {
+    const long tile = m / (64L * cpr), rem = m % (64L * cpr);
+    const long row = tile * 64 + rem % 64;
+    const long c = rem / 64;
     uint32_t d[F::DW];
-    load_chunk<BITS>(q + c * F::BYTES, d);
+    load_chunk<BITS>(q + m * F::BYTES, d);
     uint32_t P[F::PAIRS];
     chunk_pairs<BITS>(d, P);
-    uint8_t* out = codes + c * F::CODES;
+    uint8_t* out = codes + row * K + c * F::CODES;
 #pragma unroll
     for (int p = 0; p < F::PAIRS; ++p) {
       out[pair_code<BITS>(p, 0)] = (uint8_t)(bf16_bits_to_f32(P[p] & 0xFFFFu) - F::OFFSET);
@@ -85,15 +94,16 @@ extern "C" int moe_quantize(const float* w, long rows, int K, int bits, uint8_t*
   if (rows < 0 || K <= 0) return set_error(MOEQ_ERR_INVALID_ARG, "moe_quantize: rows=%ld K=%d", rows, K);
   if (!bits_ok(bits)) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_quantize: bits=%d not in {4,6,8}", bits);
   if (K % MOEQ_GROUP) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_quantize: K=%d not a multiple of 64", K);
+  if (rows % 64) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_quantize: rows=%ld not a multiple of 64", rows);
   if (!aligned16(w) || !aligned16(q)) return set_error(MOEQ_ERR_MISALIGNED, "moe_quantize: w and q must be 16-byte aligned");
   if (((uintptr_t)sz & 3u) != 0) return set_error(MOEQ_ERR_MISALIGNED, "moe_quantize: sz must be 4-byte aligned");
   const long ngroups = rows * (K / MOEQ_GROUP);
   if (ngroups == 0) return MOEQ_OK;
   const int grid = grid_for(ngroups, 4);
   switch (bits) {
-    case 4: quantize_kernel<4><<<grid, 256, 0, stream>>>(w, ngroups, q, sz); break;
-    case 6: quantize_kernel<6><<<grid, 256, 0, stream>>>(w, ngroups, q, sz); break;
-    default: quantize_kernel<8><<<grid, 256, 0, stream>>>(w, ngroups, q, sz); break;
+    case 4: quantize_kernel<4><<<grid, 256, 0, stream>>>(w, ngroups, K / 64, q, sz); break;
+    case 6: quantize_kernel<6><<<grid, 256, 0, stream>>>(w, ngroups, K / 64, q, sz); break;
+    default: quantize_kernel<8><<<grid, 256, 0, stream>>>(w, ngroups, K / 64, q, sz); break;
   }
   return check_launch("moe_quantize");
 }
@@ -103,13 +113,14 @@ extern "C" int moe_unpack(const uint8_t* q, long rows, int K, int bits, uint8_t*
   if (rows < 0 || K <= 0) return set_error(MOEQ_ERR_INVALID_ARG, "moe_unpack: rows=%ld K=%d", rows, K);
   if (!bits_ok(bits)) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_unpack: bits=%d not in {4,6,8}", bits);
   if (K % MOEQ_GROUP) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_unpack: K=%d not a multiple of 64", K);
+  if (rows % 64) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_unpack: rows=%ld not a multiple of 64", rows);
   if (!aligned16(q)) return set_error(MOEQ_ERR_MISALIGNED, "moe_unpack: q must be 16-byte aligned");
   const long ncodes = rows * (long)K;
   if (ncodes == 0) return MOEQ_OK;
   switch (bits) {
-    case 4: unpack_kernel<4><<<grid_for(ncodes / 32, 256), 256, 0, stream>>>(q, ncodes / 32, codes); break;
-    case 6: unpack_kernel<6><<<grid_for(ncodes / 16, 256), 256, 0, stream>>>(q, ncodes / 16, codes); break;
-    default: unpack_kernel<8><<<grid_for(ncodes / 16, 256), 256, 0, stream>>>(q, ncodes / 16, codes); break;
+    case 4: unpack_kernel<4><<<grid_for(ncodes / 32, 256), 256, 0, stream>>>(q, ncodes / 32, K / 32, K, codes); break;
+    case 6: unpack_kernel<6><<<grid_for(ncodes / 16, 256), 256, 0, stream>>>(q, ncodes / 16, K / 16, K, codes); break;
+    default: unpack_kernel<8><<<grid_for(ncodes / 16, 256), 256, 0, stream>>>(q, ncodes / 16, K / 16, K, codes); break;
   }
   return check_launch("moe_unpack");
 }

@@ -50,15 +50,26 @@ typedef struct ihipStream_t* hipStream_t;
 #define MOEQ_GROUP 64              /* quantisation group along the input dim  */
 
 /* One quantised projection of all experts.  For a projection mapping K inputs
- * to N outputs, expert e's weight is an N x K matrix stored row by row:
- *   q  [n_mats][N][K*bits/8] bytes, the codes of each row packed along K:
- *        4-bit: code 2i in the low nibble of byte i, 2i+1 in the high nibble;
- *        6-bit: codes 4i..4i+3 form the 24-bit little-endian word
- *               c0 | c1<<6 | c2<<12 | c3<<18 in bytes 3i..3i+2;
- *        8-bit: one byte per code.
- *   sz [n_mats][N][K/64] uint32: bits 0-15 the fp16 scale s, bits 16-31 the
- *        fp16 zero z of one group of 64 consecutive inputs of a row.
- * The dequantised weight is (q - z) * s, computed in fp32. */
+ * to N outputs (N a multiple of 64), expert e's weight is an N x K matrix; the
+ * rows r = e*N + n of all experts are stored together:
+ *   q  bytes, K*bits/8 per row as in plain packing, laid out in tiles of 64
+ *      rows.  A "chunk" is 32 codes in 16 bytes (4-bit), 16 codes in 12 bytes
+ *      (6-bit) or 16 codes in 16 bytes (8-bit); chunk c of row r starts at
+ *      byte ((r / 64) * CPR + c) * 64 * BYTES + (r % 64) * BYTES, CPR =
+ *      K / codes-per-chunk, BYTES = bytes per chunk.  Inside a chunk, field n
+ *      (4-bit: nibble n = low nibble of byte n/2 for even n, high for odd;
+ *      6-bit: bits 6n..6n+5 of the 96-bit little-endian chunk; 8-bit: byte
+ *      n) holds code F(n) of the chunk:
+ *        4-bit: F(n) = 8*(n/8) + 2*(n%4) + (n/4)%2
+ *        6-bit: F(0..15) = 0 2 12 1 3 4 6 13 5 7 8 10 14 9 11 15
+ *        8-bit: F(n) = n
+ *   sz uint32 words: bits 0-15 the fp16 scale s, bits 16-31 the fp16 zero z
+ *      of group g (64 consecutive inputs) of row r, at word
+ *      ((r / 64) * (K / 64) + g) * 64 + r % 64.
+ * A wavefront whose lane l handles row 64 t + l thus reads every chunk as one
+ * contiguous block, and the field order turns every two consecutive codes
+ * into a bf16 pair with one AND-OR.  moe_quantize writes this layout and
+ * moe_unpack reads it.  The dequantised weight is (q - z) * s, in fp32. */
 typedef struct moe_qweight {
   const uint8_t*  q;    /* device */
   const uint32_t* sz;   /* device */
@@ -72,7 +83,9 @@ typedef struct moe_qweight {
  * use different bit widths.
  * An assignment is one (token, slot) pair: a = t*(k+S) + j, where slots
  * j < k are the token's routed experts in routing order and slots j >= k
- * its shared experts (weight one). */
+ * its shared experts (weight one).
+ * Every call taking a descriptor requires H and I multiples of 64,
+ * E + S <= 4096 and H * I < 2^31 (MOEQ_ERR_UNSUPPORTED otherwise). */
 typedef struct moe_layer_desc {
   int H, I, E, S, k;
   moe_qweight gate, up, down;
@@ -98,13 +111,15 @@ const char* moe_last_error(void);
  *   s16 = fp16(fp32(max - min) / (2^bits - 1)),  z16 = fp16(-min / s16),
  *   q   = clamp(rint(w / s16 + z16), 0, 2^bits - 1).
  * A group whose s16 is zero stores s16 = 1, z16 = fp16(-min), q = 0.
- * Writes q [rows][K*bits/8] and sz [rows][K/64] (device, layout as in
- * moe_qweight).  w must be 16-byte aligned; w must hold finite values. */
+ * Writes q (rows*K*bits/8 bytes) and sz (rows*K/64 words) in the layout of
+ * moe_qweight (device); rows must be a multiple of 64.  w must be 16-byte
+ * aligned; w must hold finite values. */
 int moe_quantize(const float* w, long rows, int K, int bits,
                  uint8_t* q, uint32_t* sz, hipStream_t stream);
 
-/* Unpack codes q [rows][K*bits/8] (device) into one byte per code,
- * codes [rows][K] (device).  It runs the same in-register unpacking the
+/* Unpack codes q (rows*K*bits/8 bytes in the layout of moe_qweight, rows a
+ * multiple of 64, device) into one byte per code, codes [rows][K] (device,
+ * natural order).  It runs the same in-register unpacking the
  * decode kernels use, so it tests their view of the format bit for bit. */
 int moe_unpack(const uint8_t* q, long rows, int K, int bits,
                uint8_t* codes, hipStream_t stream);

@@ -65,6 +65,45 @@ def oracle_layer(w: synth.Workload, layer: int = 0, bits=None) -> oracle.QuantLa
     return oracle.QuantLayer(w.H, w.I, w.E, w.k, w.S, LazyExperts(w, layer, bits))
 
 
+# The device byte layout of packed codes (include/moeq.h, moe_qweight): in
+# each chunk (32 codes at 4-bit, 16 at 6/8-bit) field n holds code
+# FIELD_CODE[bits][n]; rows are tiled by 64, chunk-major inside a tile.
+CHUNK_CODES = {4: 32, 6: 16, 8: 16}
+FIELD_CODE = {4: [8 * (n >> 3) + 2 * (n & 3) + ((n >> 2) & 1) for n in range(32)],
+              6: [0, 2, 12, 1, 3, 4, 6, 13, 5, 7, 8, 10, 14, 9, 11, 15],
+              8: list(range(16))}
+
+
+def device_packed(q: np.ndarray, bits: int) -> np.ndarray:
+    """Device bytes of codes q [rows][K]: the oracle's packing of the
+    field-ordered codes, re-laid out in 64-row tiles (flat uint8)."""
+    rows, K = q.shape
+    c = CHUNK_CODES[bits]
+    cpr = K // c
+    fields = np.asarray(q).reshape(rows, cpr, c)[:, :, FIELD_CODE[bits]].reshape(rows, K)
+    packed = oracle.pack(fields, bits)
+    nb = c * bits // 8
+    return packed.reshape(rows // 64, 64, cpr, nb).transpose(0, 2, 1, 3).reshape(-1)
+
+
+def device_codes(dev_bytes: np.ndarray, rows: int, K: int, bits: int) -> np.ndarray:
+    """Inverse of device_packed: natural codes [rows][K] of device bytes."""
+    c = CHUNK_CODES[bits]
+    cpr = K // c
+    nb = c * bits // 8
+    rowmajor = np.asarray(dev_bytes).reshape(rows // 64, cpr, 64, nb).transpose(0, 2, 1, 3).reshape(rows, -1)
+    fields = oracle.unpack(rowmajor, bits, K).reshape(rows, cpr, c)
+    codes = np.empty_like(fields)
+    codes[:, :, FIELD_CODE[bits]] = fields
+    return codes.reshape(rows, K)
+
+
+def device_sz(words: np.ndarray) -> np.ndarray:
+    """Device order of scale/zero words [rows][K/64] (flat uint32)."""
+    rows, gpr = words.shape
+    return np.asarray(words).reshape(rows // 64, 64, gpr).transpose(0, 2, 1).reshape(-1)
+
+
 def rel_err(gpu, ref) -> float:
     """max |gpu - ref| / (max |ref| + 1e-6)"""
     gpu = np.asarray(gpu, np.float64)

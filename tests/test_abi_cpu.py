@@ -51,7 +51,8 @@ def test_host_validation(bq):
     assert L.moe_quantize(None, 4, 64, 4, ok, ok, None) == -1
     assert L.moe_quantize(ok, 4, 64, 5, ok, ok, None) == -2 and "bits" in _err(L)
     assert L.moe_quantize(ok, 4, 96, 4, ok, ok, None) == -2
-    assert L.moe_quantize(mis, 4, 64, 4, ok, ok, None) == -3
+    assert L.moe_quantize(ok, 4, 64, 4, ok, ok, None) == -2 and "multiple of 64" in _err(L)   # rows % 64
+    assert L.moe_quantize(mis, 64, 64, 4, ok, ok, None) == -3
     assert L.moe_unpack(ok, 4, 64, 7, ok, None) == -2
     # routing
     assert L.moe_route_topk(ok, ok, None, 4, 64, 8, 9, ok, ok, ok, None, 0, None) == -1    # k > E

