@@ -77,23 +77,6 @@ MOEQ_DEV bool block_work(const DecodeGrid& dg, const int32_t* __restrict__ activ
   return e < dg.E;
 }
 
-// Values the compiler cannot see are the same on every lane (they are: all
-// their inputs are wave-uniform), moved to scalar registers so that addresses
-// built from them stay scalar.  A load address is then a scalar base plus
-// one 32-bit lane offset (the global_load "saddr" form): no per-chunk
-// address occupies vector registers.
-MOEQ_DEV int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// global-memory pointer (address space 1): loads through it are global_load,
-// not flat loads
-typedef const __attribute__((address_space(1))) uint8_t* gbytes;
-MOEQ_DEV gbytes uniform_ptr(const uint8_t* p) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return reinterpret_cast<gbytes>(((uint64_t)hi << 32) | lo);
-}
-
 template <int BITS>
 MOEQ_DEV void load_chunk_g(gbytes p, uint32_t (&d)[Fmt<BITS>::DW]) {
   typedef const __attribute__((address_space(1))) moeq_u32x4* g4;
@@ -106,7 +89,6 @@ MOEQ_DEV void load_chunk_g(gbytes p, uint32_t (&d)[Fmt<BITS>::DW]) {
     d[0] = v.x; d[1] = v.y; d[2] = v.z;
   }
 }
-MOEQ_DEV uint32_t load_word_g(gbytes p) { return *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(p); }
 
 // Loads in flight for one chunk of NM matrices: the chunk's codes and, on
 // the first chunk of a group, the group's scale/zero words.

@@ -85,6 +85,25 @@ MOEQ_DEV void load_chunk(const uint8_t* __restrict__ p, uint32_t (&d)[Fmt<BITS>:
   }
 }
 
+// Values the compiler cannot see are the same on every lane (they are: all
+// their inputs are wave-uniform), moved to scalar registers so that addresses
+// built from them stay scalar.  A load address is then a scalar base plus
+// one 32-bit lane offset (the global_load "saddr" form): no per-chunk
+// address occupies vector registers.
+MOEQ_DEV int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// global-memory pointer (address space 1): loads through it are global_load,
+// not flat loads
+typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+MOEQ_DEV gbytes uniform_ptr(const uint8_t* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<gbytes>(((uint64_t)hi << 32) | lo);
+}
+
+MOEQ_DEV uint32_t load_word_g(gbytes p) { return *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(p); }
+
 MOEQ_DEV uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) { return (a & m) | o; }
 
 // The bf16 128.0 pair lives in a VGPR (an empty asm makes it opaque) so that
@@ -94,6 +113,26 @@ MOEQ_DEV uint32_t magic_128_pair() {
   uint32_t m = 0x43004300u;
   asm volatile("" : "+v"(m));
   return m;
+}
+
+// 6-bit chunk -> the 8 pairs (code 2p, code 2p+1), each code OR-ed into the
+// low mantissa bits of the 16-bit float pair M (bf16 128.0 or fp16 1024.0).
+MOEQ_DEV void pairs6(const uint32_t (&d)[3], uint32_t M, uint32_t (&P)[8]) {
+  // code c of the chunk sits at bits 6c..6c+5 of the 96-bit little-endian
+  // chunk.  e0/e1/e2 are 32-bit windows starting at codes 0, 5 and 10.
+  uint32_t e0 = d[0];
+  uint32_t e1 = __builtin_amdgcn_alignbit(d[1], d[0], 30);
+  uint32_t e2 = __builtin_amdgcn_alignbit(d[2], d[1], 28);
+  const uint32_t e[3] = {e0, e1, e2};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    // codes at bits 0 and 18 -> halves 0 and 16
+    P[2 * i + 0] = and_or(e[i] >> 2, 0x003F0000u, and_or(e[i], 0x3Fu, M));
+    // codes at bits 6 and 24
+    P[2 * i + 1] = and_or(e[i] >> 8, 0x003F0000u, and_or(e[i] >> 6, 0x3Fu, M));
+  }
+  P[6] = and_or(e1 << 4, 0x003F0000u, and_or(e0 >> 12, 0x3Fu, M));     // codes 2, 7
+  P[7] = and_or(d[2] >> 10, 0x003F0000u, and_or(e2 >> 12, 0x3Fu, M));  // codes 12, 15
 }
 
 template <int BITS>
@@ -109,21 +148,7 @@ MOEQ_DEV void chunk_pairs(const uint32_t (&d)[Fmt<BITS>::DW], uint32_t (&P)[Fmt<
       P[4 * j + 3] = and_or(w >> 12, 0x000F000Fu, M);
     }
   } else if constexpr (BITS == 6) {
-    // code c of the chunk sits at bits 6c..6c+5 of the 96-bit little-endian
-    // chunk.  e0/e1/e2 are 32-bit windows starting at codes 0, 5 and 10.
-    uint32_t e0 = d[0];
-    uint32_t e1 = __builtin_amdgcn_alignbit(d[1], d[0], 30);
-    uint32_t e2 = __builtin_amdgcn_alignbit(d[2], d[1], 28);
-    const uint32_t e[3] = {e0, e1, e2};
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      // codes at bits 0 and 18 -> halves 0 and 16
-      P[2 * i + 0] = and_or(e[i] >> 2, 0x003F0000u, and_or(e[i], 0x3Fu, M));
-      // codes at bits 6 and 24
-      P[2 * i + 1] = and_or(e[i] >> 8, 0x003F0000u, and_or(e[i] >> 6, 0x3Fu, M));
-    }
-    P[6] = and_or(e1 << 4, 0x003F0000u, and_or(e0 >> 12, 0x3Fu, M));     // codes 2, 7
-    P[7] = and_or(d[2] >> 10, 0x003F0000u, and_or(e2 >> 12, 0x3Fu, M));  // codes 12, 15
+    pairs6(d, M, P);
   } else {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll

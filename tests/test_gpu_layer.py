@@ -88,6 +88,7 @@ def check_layer(bq, name, T, prefill, sample=None, bits=None, batch=0):
         assert err_b <= DECODE_TOL and yerr_b <= DECODE_Y_TOL, (err_b, yerr_b)
         assert yerr <= SPEC_TOL, yerr
     else:
+        print(f"  out err {err:.3e} y err {yerr:.3e}", flush=True)
         assert yerr <= SPEC_TOL, yerr
     return r, err, yerr
 
@@ -114,6 +115,13 @@ def test_decode_layer_6_8_bit(bq, bits, T):
 def test_prefill_layer_small(bq, T):
     print(f"prefill 128-expert 6-bit zipf T={T}", flush=True)
     check_layer(bq, "moe_h2048_e128_k8_b6_zipf", T, prefill=True)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("T", [70, 300])
+def test_prefill_layer_4_8_bit(bq, bits, T):
+    print(f"prefill 128-expert {bits}-bit T={T}", flush=True)
+    check_layer(bq, "moe_h2048_e128_k8_b4", T, prefill=True, bits=bits, batch=bits)
 
 
 @pytest.mark.parametrize("T", [2048, 4096])
