@@ -45,9 +45,33 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Sources whose kernels count their own outstanding loads (explicit
+# s_waitcnt vmcnt(N) on global -> LDS loads): scratch traffic would add
+# vector-memory operations the counts do not know about, so these must
+# compile without any scratch use.
+NO_SCRATCH = {"prefill.hip"}
+
+
+def _check_no_scratch(src, out):
+    import re
+    bad = []
+    name = None
+    for line in out.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) != 0:
+            bad.append(name)
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch memory (register spills): {bad}")
+
+
 def _compile(src, save_temps=False):
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
     cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    if os.path.basename(src) in NO_SCRATCH:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     if save_temps:
         cmd.insert(1, "--save-temps")
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
@@ -55,6 +79,11 @@ def _compile(src, save_temps=False):
                     if "packed-fp32-ops" not in l)   # host pass does not know the feature
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{out}")
+    if os.path.basename(src) in NO_SCRATCH:
+        _check_no_scratch(src, out)
+        import re
+        out = "\n".join(l for l in out.splitlines()
+                        if "remark:" not in l and not re.match(r"^\s*\d*\s*\|", l))
     return obj, out
 
 

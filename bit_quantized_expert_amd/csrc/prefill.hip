@@ -15,38 +15,60 @@
 // token tile.
 #include "gemm_bf16.h"
 
+#include <type_traits>
+
 using namespace moeq;
 
 namespace {
 
 constexpr int BM = kPrefillBM;   // 128 tokens per tile
 
-// sched[0] = number of work items; sched[2 + 2i], sched[3 + 2i] = (expert, token tile)
+// sched[0] = number of work items; sched[2 + 2i], sched[3 + 2i] = (expert, token tile).
+// Work items are listed by the number of 32-row M-tiles they fill, most
+// first (full tiles, then partial ones from the largest down), so that
+// blocks dealt out last are the short ones and fill the tail of the launch.
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ counts, int nexp,
                                                         int32_t* __restrict__ sched) {
+  constexpr int NBK = BM / 32;   // buckets: 1 .. NBK M-tiles
   __shared__ int part[1024];
+  __shared__ int total[NBK + 1];
   const int tid = threadIdx.x;
   const int per = (nexp + 1023) / 1024;
   const int e0 = min(nexp, tid * per), e1 = min(nexp, e0 + per);
-  int mine = 0;
-  for (int e = e0; e < e1; ++e) mine += (counts[e] + BM - 1) / BM;
-  part[tid] = mine;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {   // inclusive Hillis-Steele scan
-    const int v = tid >= o ? part[tid - o] : 0;
+  auto mtiles = [](int c, int m) { return (min(BM, c - m * BM) + 31) / 32; };
+  int pos[NBK + 1];
+  for (int bk = NBK; bk >= 1; --bk) {   // exclusive scan of this thread's tiles in bucket bk
+    int mine = 0;
+    for (int e = e0; e < e1; ++e) {
+      const int c = counts[e], nt = (c + BM - 1) / BM;
+      for (int m = 0; m < nt; ++m) mine += mtiles(c, m) == bk;
+    }
+    part[tid] = mine;
     __syncthreads();
-    part[tid] += v;
+    for (int o = 1; o < 1024; o <<= 1) {   // inclusive Hillis-Steele scan
+      const int v = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    pos[bk] = part[tid] - mine;
+    if (tid == 1023) total[bk] = part[1023];
     __syncthreads();
   }
-  int pos = part[tid] - mine;
+  int start = 0;
+  for (int bk = NBK; bk >= 1; --bk) {
+    pos[bk] += start;
+    start += total[bk];
+  }
   for (int e = e0; e < e1; ++e) {
-    const int nt = (counts[e] + BM - 1) / BM;
-    for (int m = 0; m < nt; ++m, ++pos) {
-      sched[2 + 2 * pos] = e;
-      sched[3 + 2 * pos] = m;
+    const int c = counts[e], nt = (c + BM - 1) / BM;
+    for (int m = 0; m < nt; ++m) {
+      const int p = pos[mtiles(c, m)]++;
+      sched[2 + 2 * p] = e;
+      sched[3 + 2 * p] = m;
     }
   }
-  if (tid == 1023) sched[0] = part[1023];
+  if (tid == 0) sched[0] = start;
 }
 
 // ---------------------------------------------------------------------------
@@ -72,54 +94,91 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
 
 MOEQ_DEV int step_k(int st, int h) { return 32 * (st >> 1) + 16 * h + 8 * (st & 1); }
 
-// One weight row (B column) of one expert matrix, as this lane reads it:
-// the uniform base of the expert's rows plus 32-bit lane offsets, so the
-// loads take the scalar-base ("saddr") form.
+// One global -> LDS load of 4, 12 or 16 bytes per lane: lane l's data lands
+// at lds + 16 l (+ 4 l for 4 bytes); the LDS address must be the same on
+// every lane.  Plain functions rather than template members, so that each
+// builtin is seen once.
+MOEQ_DEV void load_lds_16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+MOEQ_DEV void load_lds_12(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 12, 0, 0);
+}
+MOEQ_DEV void load_lds_4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// The codes of a wavefront's two B columns (32 weight rows each) for one
+// slice, and those rows' scale/zero words, moved global -> LDS by the
+// wavefront itself (no other wavefront reads them).  One wavefront's stage
+// in LDS:
+//   column c = 0, 1: NI loads of 64 lanes x 16 bytes; load j, lane L holds
+//   the chunk row (chunk 2j + L / 32 of the slice, row L % 32): the whole
+//   16 bytes at 4 and 8 bits, 12 of the 16 at 6 bits;
+//   then the 64 scale/zero words, [column][row].
 template <int BITS>
-struct BCol {
+struct BDma {
   using F = Fmt<BITS>;
-  static constexpr uint32_t QSLICE = 64 * 64 * BITS / 8;   // code bytes of one slice of a 64-row tile
-  gbytes q, sz;        // uniform: the expert's first code byte and scale/zero word
-  uint32_t qo, so;     // this lane's byte offsets at slice 0
-  // m: the matrix (codes, scale/zero words); e, N: expert and rows per
-  // expert; r: the row within the expert; K: row length
-  MOEQ_DEV void init(const uint8_t* mq, const uint32_t* msz, int e, int N, int r, int K, int h) {
+  static constexpr int NI = BITS == 4 ? 1 : 2;             // loads per column per slice
+  static constexpr int COL = NI * 1024;                    // LDS bytes per column
+  static constexpr int STAGE = 2 * COL + 256;              // LDS bytes per wavefront per slice
+  static constexpr int LOADS = 2 * NI + 1;                 // vector-memory loads per slice
+  static constexpr size_t QSLICE = 64 * 64 * BITS / 8;     // code bytes of one slice of a 64-row tile
+  const uint8_t* src[2][NI];   // this lane's code source at slice 0
+  const uint32_t* szsrc;       // this lane's scale/zero source at slice 0 (column lane / 32)
+  // q, szm: the columns' matrices; row[c]: the first of column c's 32 rows
+  // (over all experts' rows, a multiple of 32); K: row length
+  MOEQ_DEV void init(const uint8_t* const (&q)[2], const uint32_t* const (&szm)[2], const size_t (&row)[2], int K) {
+    const int lane = threadIdx.x & 63;
     const size_t cpr = (size_t)(K / F::CODES), gpr = (size_t)(K / 64);
-    const size_t row0 = (size_t)e * N;   // a multiple of 64: offsets below split exactly
-    q = uniform_ptr(mq + chunk_offset<BITS>(row0, 0, cpr));
-    sz = uniform_ptr(reinterpret_cast<const uint8_t*>(msz + sz_index(row0, 0, gpr)));
-    qo = (uint32_t)chunk_offset<BITS>((size_t)r, 0, cpr) + (BITS == 4 ? 8u * h : (uint32_t)h * 64u * F::BYTES);
-    so = (uint32_t)sz_index((size_t)r, 0, gpr) * 4u;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        src[c][j] = q[c] + chunk_offset<BITS>(row[c] + (lane & 31), (size_t)(2 * j + (lane >> 5)), cpr);
+    const int c = lane >> 5;
+    szsrc = szm[c] + sz_index(row[c] + (lane & 31), 0, gpr);
+  }
+  MOEQ_DEV void issue(int s, uint8_t* stage) const {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const uint8_t* g = src[c][j] + (size_t)s * QSLICE;
+        if constexpr (BITS == 6) load_lds_12(g, stage + c * COL + 1024 * j);
+        else load_lds_16(g, stage + c * COL + 1024 * j);
+      }
+    load_lds_4(szsrc + (size_t)s * 64, stage + 2 * COL);
   }
 };
 
 // This lane's codes of one B column for one slice, and the group's
-// scale/zero word.
+// scale/zero word, read from the wavefront's LDS stage.
+//   4-bit: dwords 2h, 2h + 1 of chunks 0 and 1 -> d[2j], d[2j + 1];
+//   6-, 8-bit: chunks h and h + 2 whole -> d[NW/2 j ..].
 template <int BITS>
 struct SliceCodes {
   static constexpr int NW = BITS == 4 ? 4 : (BITS == 6 ? 6 : 8);
   uint32_t d[NW];
   uint32_t sz;
-  MOEQ_DEV void load(const BCol<BITS>& b, int s) {
+  MOEQ_DEV void read(const uint8_t* stage, int c) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    typedef const __attribute__((address_space(1))) u32x2* g2;
-    typedef const __attribute__((address_space(1))) moeq_u32x3* g3;
-    typedef const __attribute__((address_space(1))) moeq_u32x4* g4;
-    const gbytes qs = b.q + (size_t)s * BCol<BITS>::QSLICE + b.qo;
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+    const uint8_t* col = stage + c * BDma<BITS>::COL;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      if constexpr (BITS == 4) {   // dwords 2h, 2h + 1 of chunk j
-        const u32x2 v = *reinterpret_cast<g2>(qs + 1024 * j);
+      if constexpr (BITS == 4) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(col + 512 * j + 16 * r + 8 * h);
         d[2 * j] = v.x; d[2 * j + 1] = v.y;
-      } else if constexpr (BITS == 6) {   // chunk h + 2j
-        const moeq_u32x3 v = *reinterpret_cast<g3>(qs + 1536 * j);
+      } else if constexpr (BITS == 6) {
+        const moeq_u32x3 v = *reinterpret_cast<const moeq_u32x3*>(col + 1024 * j + 16 * (32 * h + r));
         d[3 * j] = v.x; d[3 * j + 1] = v.y; d[3 * j + 2] = v.z;
       } else {
-        const moeq_u32x4 v = *reinterpret_cast<g4>(qs + 2048 * j);
+        const moeq_u32x4 v = *reinterpret_cast<const moeq_u32x4*>(col + 1024 * j + 16 * (32 * h + r));
         d[4 * j] = v.x; d[4 * j + 1] = v.y; d[4 * j + 2] = v.z; d[4 * j + 3] = v.w;
       }
     }
-    sz = load_word_g(b.sz + (size_t)s * 256 + b.so);
+    sz = *reinterpret_cast<const uint32_t*>(stage + 2 * BDma<BITS>::COL + 4 * (32 * c + r));
   }
 };
 
@@ -237,13 +296,6 @@ struct ATile {
 // Slot t of row r holds the row's 16-byte part t ^ (r % 8): the MFMA operand
 // reads of 8 consecutive rows at one k then hit 8 different slots, i.e.
 // every LDS bank once.
-// One 16-byte global -> LDS load per lane: lane l's data lands at
-// lds + 16 l (the LDS address must be the same on every lane).  A plain
-// function rather than a template member, so that the builtin is seen once.
-MOEQ_DEV void load_lds_16(const uint16_t* g, uint16_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-
 template <int BM>
 struct ADma {
   static constexpr int N = BM / 32;   // pieces per wavefront per slice
@@ -284,96 +336,159 @@ MOEQ_DEV void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The K loop shared by both kernels: acc[i][c] += A rows 32i .. 32i + 31 of
-// the tile times B column c of this lane, over ns slices.  Three LDS tiles
-// and three slices of codes in registers: slice s is computed while the
-// loads of slices s + 1 and s + 2 are in flight.
+// LDS stages of the token-row tiles (NA) and of the code slices (NB) per
+// bit width: three of each where they fit two blocks per CU into the
+// 160 KB of LDS, else two.
+template <int BITS> struct Stages { static constexpr int NA = BITS == 4 ? 3 : 2, NB = BITS == 4 ? 3 : 2; };
+
 template <int BITS, int BM>
+constexpr int lds_bytes() {
+  return Stages<BITS>::NA * BM * 64 * 2 + Stages<BITS>::NB * 4 * BDma<BITS>::STAGE;
+}
+
+// The K loop shared by both kernels: acc[i][c] += A rows 32i .. 32i + 31 of
+// the tile times B column c of this lane, over ns slices.  Slice s is
+// computed while the loads of the next NA - 1 token-row tiles and NB - 1
+// code slices are in flight; all of them go global -> LDS without
+// registers, so the only waits for them are the explicit wait_vmcnt ones.
+template <int BITS, int BM, int MTA>
 struct Mainloop {
-  static constexpr int MT = BM / 32;
-  static constexpr int TILE = BM * 64;                 // elements of one LDS tile
-  static constexpr int LOADS = ADma<BM>::N + 6;        // loads per slice: A pieces, 2 x (2 code + 1 word)
+  static constexpr int MT = BM / 32;   // M-tiles of the LDS tile; MTA of them hold rows
+  static constexpr int NA = Stages<BITS>::NA, NB = Stages<BITS>::NB;
+  static constexpr int ATILE = BM * 64 * 2;              // bytes of one token-row tile
+  static constexpr int LA = ADma<BM>::N, LB = BDma<BITS>::LOADS;
+  // loads issued after those of slice s + 1 when slice s ends (each slice
+  // issues token rows, then codes; see run())
+  static constexpr int WAIT = (NA == 3 && NB == 3) ? LA + LB : (NA == 2 && NB == 3) ? LB : 0;
+  static_assert(NA == 2 || NB == 3, "stage combination");
+  // the next slice's first B operands are dequantised during the last
+  // MFMA step of this one, except at 6 bits where the unpacking needs the
+  // registers (there they are dequantised when the slice starts)
+  static constexpr bool EARLY_DQ = BITS != 6;
   const ADma<BM>& ad;
-  const BCol<BITS>& b0;
-  const BCol<BITS>& b1;
+  const BDma<BITS>& bd;
   int ns;
   f32x16_t (&acc)[MT][2];
-  uint16_t* As;
-  int hh;
-  int aoff[4];   // element offset of this lane's A operand (M-tile 0) at each step
+  uint8_t* lds;   // NA token-row tiles, then NB x 4 wavefront code stages
+  int hh, wv;
+  int aoff[4];    // byte offset of this lane's A operand (M-tile 0) at each step
 
-  MOEQ_DEV Mainloop(const ADma<BM>& ad_, const BCol<BITS>& b0_, const BCol<BITS>& b1_, int ns_,
-                    f32x16_t (&acc_)[MT][2], uint16_t* As_)
-      : ad(ad_), b0(b0_), b1(b1_), ns(ns_), acc(acc_), As(As_) {
+  MOEQ_DEV Mainloop(const ADma<BM>& ad_, const BDma<BITS>& bd_, int ns_, f32x16_t (&acc_)[MT][2], uint8_t* lds_)
+      : ad(ad_), bd(bd_), ns(ns_), acc(acc_), lds(lds_) {
     const int lane = threadIdx.x & 63;
     hh = lane >> 5;
+    wv = uniform(threadIdx.x >> 6);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) aoff[st] = (lane & 31) * 64 + 8 * ((step_k(st, hh) >> 3) ^ (lane & 7));
+    for (int st = 0; st < 4; ++st) aoff[st] = 2 * ((lane & 31) * 64 + 8 * ((step_k(st, hh) >> 3) ^ (lane & 7)));
+  }
+  MOEQ_DEV uint16_t* a_tile(int t) const { return reinterpret_cast<uint16_t*>(lds + ATILE * t); }
+  MOEQ_DEV uint8_t* b_stage(int t) const { return lds + NA * ATILE + (4 * t + wv) * BDma<BITS>::STAGE; }
+
+  // the loads of what slice t will compute; past the end the last slice
+  // again (its data goes unused), so that the count of loads in flight
+  // never depends on t
+  MOEQ_DEV void issue_a(int t) const { ad.issue(min(t, ns - 1), a_tile(t % NA)); }
+  MOEQ_DEV void issue_b(int t) const { bd.issue(min(t, ns - 1), b_stage(t % NB)); }
+
+  // A slice's codes read from LDS, with the B operands of its first MFMA
+  // step already dequantised
+  struct Ready {
+    SliceCodes<BITS> cur[2];
+    GroupDq g[2];
+    bf16x8_t w[2];
+  };
+  MOEQ_DEV void prepare(int s, Ready& r) const {
+    r.cur[0].read(b_stage(s % NB), 0);
+    r.cur[1].read(b_stage(s % NB), 1);
+    if constexpr (EARLY_DQ) dequant_first(r);
+  }
+  MOEQ_DEV static void dequant_first(Ready& r) {
+    r.g[0] = group_dq<BITS>(r.cur[0].sz);
+    r.g[1] = group_dq<BITS>(r.cur[1].sz);
+    r.w[0] = dequant_step<BITS>(r.cur[0], r.g[0], 0);
+    r.w[1] = dequant_step<BITS>(r.cur[1], r.g[1], 0);
   }
 
   MOEQ_DEV void run() {
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MTA; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) { acc[i][0][r] = 0.0f; acc[i][1][r] = 0.0f; }
-    SliceCodes<BITS> c[3][2];   // ring: slices s, s + 1, s + 2
     __builtin_amdgcn_sched_barrier(0);
-    ad.issue(0, As);
-    c[0][0].load(b0, 0);
-    c[0][1].load(b1, 0);
-    const int s1 = min(1, ns - 1);
-    ad.issue(s1, As + TILE);
-    c[1][0].load(b0, s1);
-    c[1][1].load(b1, s1);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int s = 0; s < ns; s += 3) {
-      slice(s, c[0], c[2]);
-      if (s + 1 < ns) slice(s + 1, c[1], c[0]);
-      if (s + 2 < ns) slice(s + 2, c[2], c[1]);
+    // what slices -2 and -1 would have issued
+#pragma unroll
+    for (int t = -2; t < 0; ++t) {
+      if (t + NA - 1 >= 0) issue_a(t + NA - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + NB - 1 >= 0) issue_b(t + NB - 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    wait_vmcnt<WAIT>();
+    Ready r;
+    prepare(0, r);
+    tile_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < ns; ++s) {
+      issue_a(s + NA - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_b(s + NB - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      slice(s, r);
+      // every wave's token-row tile s + 1 is in LDS; tile s is no longer read
+      tile_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the loads issued past the last slice still write LDS: let them land
+    // before the caller reuses it
+    wait_vmcnt<0>();
+    tile_barrier();
   }
 
-  MOEQ_DEV void slice(int s, const SliceCodes<BITS> (&cur)[2], SliceCodes<BITS> (&ahead)[2]) {
-    // this wave's loads of slice s are done once only the next slice's
-    // remain (every slice issues the same loads, see below)
-    wait_vmcnt<LOADS>();
-    tile_barrier();   // every wave's tile s is in LDS; tile s - 1 is no longer read
-    __builtin_amdgcn_sched_barrier(0);
-    // the loads of slice s + 2; past the end, the last slice again (its
-    // data goes unused) so that the count of loads in flight never depends
-    // on s
-    const int sn = min(s + 2, ns - 1);
-    ad.issue(sn, As + TILE * ((s + 2) % 3));
-    ahead[0].load(b0, sn);
-    ahead[1].load(b1, sn);
-    __builtin_amdgcn_sched_barrier(0);
-    const uint16_t* A = As + TILE * (s % 3);
-    const GroupDq g0 = group_dq<BITS>(cur[0].sz), g1 = group_dq<BITS>(cur[1].sz);
-    // software pipeline over the 4 MFMA steps: the weights of step st + 1
-    // are dequantised while the matrix cores run step st, the vector and
-    // matrix instructions interleaved (a few VALU per MFMA)
-    bf16x8_t w0 = dequant_step<BITS>(cur[0], g0, 0), w1 = dequant_step<BITS>(cur[1], g1, 0);
+  // Slice s from r; on return r holds slice s + 1 (its codes are this
+  // wave's own loads, so they are read before the barrier, while the last
+  // MFMAs of slice s run).  Past the last slice r reads the repeated last
+  // slice, which goes unused.
+  MOEQ_DEV void slice(int s, Ready& r) {
+    const uint8_t* A = reinterpret_cast<const uint8_t*>(a_tile(s % NA));
+    if constexpr (!EARLY_DQ) dequant_first(r);
+    const SliceCodes<BITS> cur[2] = {r.cur[0], r.cur[1]};
+    const GroupDq g0 = r.g[0], g1 = r.g[1];
+    // software pipeline over the 4 MFMA steps: the A operands and the
+    // weights of step st + 1 are fetched and dequantised while the matrix
+    // cores run step st, vector and matrix instructions interleaved
+    bf16x8_t w0 = r.w[0], w1 = r.w[1];
+    bf16x8_t a[MTA];
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(A + 4096 * i + aoff[0]);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8_t a[MT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(A + 2048 * i + aoff[st]);
-      bf16x8_t n0 = w0, n1 = w1;
+      bf16x8_t an[MTA], n0 = w0, n1 = w1;
       if (st < 3) {
+#pragma unroll
+        for (int i = 0; i < MTA; ++i) an[i] = *reinterpret_cast<const bf16x8_t*>(A + 4096 * i + aoff[st + 1]);
         n0 = dequant_step<BITS>(cur[0], g0, st + 1);
         n1 = dequant_step<BITS>(cur[1], g1, st + 1);
+      } else {
+        // this wave's loads of slice s + 1 are complete once WAIT remain
+        wait_vmcnt<WAIT>();
+        prepare(s + 1, r);
       }
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
+      for (int i = 0; i < MTA; ++i) {
         acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], w0, acc[i][0], 0, 0, 0);
         acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], w1, acc[i][1], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);   // the A reads first
+      if (st < 3) __builtin_amdgcn_sched_group_barrier(0x100, MTA, 0);   // LDS reads first
+      else __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * MT; ++i) {
+      for (int i = 0; i < 2 * MTA; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to 5 VALU
+      }
+      if (st < 3) {
+#pragma unroll
+        for (int i = 0; i < MTA; ++i) a[i] = an[i];
       }
       w0 = n0;
       w1 = n1;
@@ -393,6 +508,27 @@ MOEQ_DEV void block_tile(int nft, int& w, int& ft) {
   ft = slot % nft;
 }
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// Epilogue staging: the block's output tile goes through LDS as rows of
+// bf16 (stride PITCH bytes) so that it leaves in 16-byte stores.
+template <int COLS>
+struct OutTile {
+  static constexpr int PITCH = COLS * 2 + 16;
+  static constexpr int BYTES = 128 * PITCH;
+};
+
+// Runs fn(std::integral_constant<int, MTA>) for MTA = the M-tiles holding rows.
+template <class Fn>
+MOEQ_DEV void with_mtiles(int rows, Fn&& fn) {
+  switch ((rows + 31) / 32) {
+    case 1: fn(std::integral_constant<int, 1>()); break;
+    case 2: fn(std::integral_constant<int, 2>()); break;
+    case 3: fn(std::integral_constant<int, 3>()); break;
+    default: fn(std::integral_constant<int, 4>()); break;
+  }
+}
+
 // gate/up: per (expert, BM-token tile, 128 features of I): h = silu(x Wg^T) *
 // (x Wu^T) rounded to bf16, rows in expert-sorted order.  Wavefront wv owns
 // features 32 wv .. 32 wv + 31 of the tile, of both gate and up.
@@ -407,8 +543,9 @@ __global__ __launch_bounds__(256, 2) void mfma_gateup_kernel(const uint8_t* __re
                                                              const int32_t* __restrict__ sorted,
                                                              const int32_t* __restrict__ sched,
                                                              uint16_t* __restrict__ h) {
-  constexpr int MT = BM / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t As[3][BM * 64];
+  static_assert(BM == 128, "tile");
+  using Out = OutTile<128>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[cmax(lds_bytes<BITS, BM>(), Out::BYTES)];
   int wi, ft;
   block_tile(I / 128, wi, ft);
   if (wi >= sched[0]) return;
@@ -417,7 +554,6 @@ __global__ __launch_bounds__(256, 2) void mfma_gateup_kernel(const uint8_t* __re
   const int rows = min(BM, counts[e] - mt * BM);
   const int lane = threadIdx.x & 63, hh = lane >> 5;
   const int wv = uniform(threadIdx.x >> 6);
-  const int f = ft * 128 + 32 * wv + (lane & 31);   // this lane's feature (B column)
   ADma<BM> ad;
   {
     const uint16_t* rowp[ADma<BM>::N];
@@ -426,18 +562,36 @@ __global__ __launch_bounds__(256, 2) void mfma_gateup_kernel(const uint8_t* __re
       rowp[j] = x + (size_t)(sorted[base + min(ADma<BM>::row_of(j), rows - 1)] / kS) * H;
     ad.init(rowp);
   }
-  BCol<BITS> bg, bu;
-  bg.init(gq, gsz, e, I, f, H, hh);
-  bu.init(uq, usz, e, I, f, H, hh);
-  f32x16_t acc[MT][2];
-  Mainloop<BITS, BM>(ad, bg, bu, H / 64, acc, &As[0][0]).run();
+  BDma<BITS> bd;
+  {
+    const uint8_t* const q[2] = {gq, uq};
+    const uint32_t* const sz[2] = {gsz, usz};
+    const size_t row0 = (size_t)e * I + ft * 128 + 32 * wv;   // gate and up rows of this wavefront
+    const size_t row[2] = {row0, row0};
+    bd.init(q, sz, row, H);
+  }
+  with_mtiles(rows, [&](auto mta) {
+    constexpr int MTA = decltype(mta)::value;
+    f32x16_t acc[BM / 32][2];
+    Mainloop<BITS, BM, MTA>(ad, bd, H / 64, acc, lds).run();
+    // h tile -> LDS: lane (l % 32, half hh) holds column 32 wv + l % 32 of
+    // rows 32 i + 8 (r / 4) + 4 hh + r % 4
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MTA; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (m < rows) h[(size_t)(base + m) * I + f] = (uint16_t)f32_to_bf16_bits(silu_f32(acc[i][0][r]) * acc[i][1][r]);
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int m = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+        *reinterpret_cast<uint16_t*>(lds + m * Out::PITCH + 2 * (32 * wv + (lane & 31))) =
+            (uint16_t)f32_to_bf16_bits(silu_f32(acc[i][0][r]) * acc[i][1][r]);
+      }
+  });
+  __syncthreads();
+  // 16 pieces of 16 bytes per row
+  for (int c = threadIdx.x; c < 16 * rows; c += 256) {
+    const int m = c >> 4, pc = c & 15;
+    *reinterpret_cast<moeq_u32x4*>(h + (size_t)(base + m) * I + ft * 128 + 8 * pc) =
+        *reinterpret_cast<const moeq_u32x4*>(lds + m * Out::PITCH + 16 * pc);
+  }
 }
 
 // down: per (expert, BM-token tile, 256 features of H): y = h Wd^T rounded to
@@ -453,8 +607,9 @@ __global__ __launch_bounds__(256, 2) void mfma_down_kernel(const uint8_t* __rest
                                                            const int32_t* __restrict__ sorted,
                                                            const int32_t* __restrict__ sched,
                                                            uint16_t* __restrict__ y) {
-  constexpr int MT = BM / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t As[3][BM * 64];
+  static_assert(BM == 128, "tile");
+  using Out = OutTile<256>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[cmax(lds_bytes<BITS, BM>(), Out::BYTES)];
   int wi, ft;
   block_tile(H / 256, wi, ft);
   if (wi >= sched[0]) return;
@@ -463,7 +618,6 @@ __global__ __launch_bounds__(256, 2) void mfma_down_kernel(const uint8_t* __rest
   const int rows = min(BM, counts[e] - mt * BM);
   const int lane = threadIdx.x & 63, hh = lane >> 5;
   const int wv = uniform(threadIdx.x >> 6);
-  const int f0 = ft * 256 + 64 * wv + (lane & 31);   // features f0 and f0 + 32
   ADma<BM> ad;
   {
     const uint16_t* rowp[ADma<BM>::N];
@@ -471,22 +625,35 @@ __global__ __launch_bounds__(256, 2) void mfma_down_kernel(const uint8_t* __rest
     for (int j = 0; j < ADma<BM>::N; ++j) rowp[j] = h + (size_t)(base + min(ADma<BM>::row_of(j), rows - 1)) * I;
     ad.init(rowp);
   }
-  BCol<BITS> c0, c1;
-  c0.init(dq, dsz, e, H, f0, I, hh);
-  c1.init(dq, dsz, e, H, f0 + 32, I, hh);
-  f32x16_t acc[MT][2];
-  Mainloop<BITS, BM>(ad, c0, c1, I / 64, acc, &As[0][0]).run();
+  BDma<BITS> bd;
+  {
+    const uint8_t* const q[2] = {dq, dq};
+    const uint32_t* const sz[2] = {dsz, dsz};
+    const size_t row0 = (size_t)e * H + ft * 256 + 64 * wv;   // the wavefront's two 32-row blocks
+    const size_t row[2] = {row0, row0 + 32};
+    bd.init(q, sz, row, I);
+  }
+  with_mtiles(rows, [&](auto mta) {
+    constexpr int MTA = decltype(mta)::value;
+    f32x16_t acc[BM / 32][2];
+    Mainloop<BITS, BM, MTA>(ad, bd, I / 64, acc, lds).run();
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MTA; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (m < rows) {
-        const size_t a = (size_t)sorted[base + m];
-        y[a * H + f0] = (uint16_t)f32_to_bf16_bits(acc[i][0][r]);
-        y[a * H + f0 + 32] = (uint16_t)f32_to_bf16_bits(acc[i][1][r]);
+      for (int r = 0; r < 16; ++r) {
+        const int m = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+        uint8_t* o = lds + m * Out::PITCH + 2 * (64 * wv + (lane & 31));
+        *reinterpret_cast<uint16_t*>(o) = (uint16_t)f32_to_bf16_bits(acc[i][0][r]);
+        *reinterpret_cast<uint16_t*>(o + 64) = (uint16_t)f32_to_bf16_bits(acc[i][1][r]);
       }
-    }
+  });
+  __syncthreads();
+  // 32 pieces of 16 bytes per row, each row to its assignment
+  for (int c = threadIdx.x; c < 32 * rows; c += 256) {
+    const int m = c >> 5, pc = c & 31;
+    *reinterpret_cast<moeq_u32x4*>(y + (size_t)sorted[base + m] * H + ft * 256 + 8 * pc) =
+        *reinterpret_cast<const moeq_u32x4*>(lds + m * Out::PITCH + 16 * pc);
+  }
 }
 
 // Router logits at large batch: C[m][n] = sum_k A[m][k] B[n][k] + bias[n],
