@@ -107,6 +107,14 @@ MOEQ_DEV void load_lds_12(const void* g, void* lds) {
 MOEQ_DEV void load_lds_4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
 }
+MOEQ_DEV void load_lds_16(gbytes g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+MOEQ_DEV void load_lds_12(gbytes g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 12, 0, 0);
+}
 
 // The codes of a wavefront's two B columns (32 weight rows each) for one
 // slice, and those rows' scale/zero words, moved global -> LDS by the
@@ -124,30 +132,33 @@ struct BDma {
   static constexpr int STAGE = 2 * COL + 256;              // LDS bytes per wavefront per slice
   static constexpr int LOADS = 2 * NI + 1;                 // vector-memory loads per slice
   static constexpr size_t QSLICE = 64 * 64 * BITS / 8;     // code bytes of one slice of a 64-row tile
-  const uint8_t* src[2][NI];   // this lane's code source at slice 0
-  const uint32_t* szsrc;       // this lane's scale/zero source at slice 0 (column lane / 32)
+  gbytes q0[2];            // uniform: column c's first code byte (row 0 of its 32-row block, chunk 0)
+  uint32_t qo[NI];         // this lane's byte offsets from them (the same for both columns)
+  const uint32_t* szsrc;   // this lane's scale/zero source at slice 0 (column lane / 32)
   // q, szm: the columns' matrices; row[c]: the first of column c's 32 rows
   // (over all experts' rows, a multiple of 32); K: row length
   MOEQ_DEV void init(const uint8_t* const (&q)[2], const uint32_t* const (&szm)[2], const size_t (&row)[2], int K) {
     const int lane = threadIdx.x & 63;
     const size_t cpr = (size_t)(K / F::CODES), gpr = (size_t)(K / 64);
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c) q0[c] = uniform_ptr(q[c] + chunk_offset<BITS>(row[c], 0, cpr));
+    // chunk 2j + lane / 32 of the slice, row lane % 32 of the block: rows of
+    // one tile are F::BYTES apart, chunks 64 F::BYTES
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
-        src[c][j] = q[c] + chunk_offset<BITS>(row[c] + (lane & 31), (size_t)(2 * j + (lane >> 5)), cpr);
+    for (int j = 0; j < NI; ++j) qo[j] = (uint32_t)(((2 * j + (lane >> 5)) * 64 + (lane & 31)) * F::BYTES);
     const int c = lane >> 5;
     szsrc = szm[c] + sz_index(row[c] + (lane & 31), 0, gpr);
   }
   MOEQ_DEV void issue(int s, uint8_t* stage) const {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c) {
+      const gbytes base = q0[c] + (size_t)s * QSLICE;
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const uint8_t* g = src[c][j] + (size_t)s * QSLICE;
-        if constexpr (BITS == 6) load_lds_12(g, stage + c * COL + 1024 * j);
-        else load_lds_16(g, stage + c * COL + 1024 * j);
+        if constexpr (BITS == 6) load_lds_12(base + qo[j], stage + c * COL + 1024 * j);
+        else load_lds_16(base + qo[j], stage + c * COL + 1024 * j);
       }
+    }
     load_lds_4(szsrc + (size_t)s * 64, stage + 2 * COL);
   }
 };
@@ -219,10 +230,10 @@ MOEQ_DEV uint32_t bf16_pair(float lo, float hi) {
 }
 
 // The 8 weights this lane supplies at MFMA step st, dequantised and rounded
-// to bf16: codes (2j, 2j + 1) of the step's 8 become pair P[j].
+// to bf16: codes (2j, 2j + 1) of the step's 8 become pair P[j].  M:
+// magic_1024_pair().
 template <int BITS>
-MOEQ_DEV bf16x8_t dequant_step(const SliceCodes<BITS>& sc, const GroupDq& g, int st) {
-  const uint32_t M = magic_1024_pair();
+MOEQ_DEV bf16x8_t dequant_step(const SliceCodes<BITS>& sc, const GroupDq& g, int st, uint32_t M) {
   const int j = st >> 1, sub = st & 1;
   uint32_t r[4];
   if constexpr (BITS == 4) {
@@ -405,8 +416,9 @@ struct Mainloop {
   MOEQ_DEV static void dequant_first(Ready& r) {
     r.g[0] = group_dq<BITS>(r.cur[0].sz);
     r.g[1] = group_dq<BITS>(r.cur[1].sz);
-    r.w[0] = dequant_step<BITS>(r.cur[0], r.g[0], 0);
-    r.w[1] = dequant_step<BITS>(r.cur[1], r.g[1], 0);
+    const uint32_t M = magic_1024_pair();
+    r.w[0] = dequant_step<BITS>(r.cur[0], r.g[0], 0, M);
+    r.w[1] = dequant_step<BITS>(r.cur[1], r.g[1], 0, M);
   }
 
   MOEQ_DEV void run() {
@@ -457,6 +469,7 @@ struct Mainloop {
     // weights of step st + 1 are fetched and dequantised while the matrix
     // cores run step st, vector and matrix instructions interleaved
     bf16x8_t w0 = r.w[0], w1 = r.w[1];
+    const uint32_t M = magic_1024_pair();
     bf16x8_t a[MTA];
 #pragma unroll
     for (int i = 0; i < MTA; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(A + 4096 * i + aoff[0]);
@@ -467,8 +480,8 @@ struct Mainloop {
       if (st < 3) {
 #pragma unroll
         for (int i = 0; i < MTA; ++i) an[i] = *reinterpret_cast<const bf16x8_t*>(A + 4096 * i + aoff[st + 1]);
-        n0 = dequant_step<BITS>(cur[0], g0, st + 1);
-        n1 = dequant_step<BITS>(cur[1], g1, st + 1);
+        n0 = dequant_step<BITS>(cur[0], g0, st + 1, M);
+        n1 = dequant_step<BITS>(cur[1], g1, st + 1, M);
       } else {
         // this wave's loads of slice s + 1 are complete once WAIT remain
         wait_vmcnt<WAIT>();
