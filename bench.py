@@ -455,11 +455,28 @@ def main():
 
     prefill = T > bq.DECODE_MAX_T
     if prefill:
-        achieved = (flops - 2 * T * w.E * w.H) / (kern_ms * 1e-3) / 1e12   # expert FFN flops only
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(w.name, T),
-                "kernel": "moe_qgemm_prefill (gate/up + down grouped GEMM kernels)",
-                "alg_flops_per_launch": flops - 2 * T * w.E * w.H, "kernel_us": round(kern_ms * 1e3, 3)}
+        # The grouped GEMM is bound by the matrix cores or by HBM, whichever
+        # needs longer at peak: its flops (expert FFN only) against the bf16
+        # MFMA peak, its algorithmic bytes (each touched expert's weights
+        # once, x in, h out and back in, y out) against the HBM peak.
+        A = T * (w.k + w.S)
+        exp_flops = flops - 2 * T * w.E * w.H
+        pf_bytes = float(np.mean(distinct)) * expert_bytes(w, bits) + T * w.H * 2 + 2 * A * w.I * 2 + A * w.H * 2
+        t_mfma = exp_flops / (PEAK_BF16_TFLOPS * 1e12)
+        t_hbm = pf_bytes / (PEAK_HBM_GBS * 1e9)
+        tflops = exp_flops / (kern_ms * 1e-3) / 1e12
+        gbps = pf_bytes / (kern_ms * 1e-3) / 1e9
+        common = {"traffic": measured_traffic(w.name, T),
+                  "kernel": "moe_qgemm_prefill (gate/up + down grouped GEMM kernels)",
+                  "alg_flops_per_launch": exp_flops, "alg_bytes_per_launch": round(pf_bytes),
+                  "kernel_us": round(kern_ms * 1e3, 3),
+                  "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4)}
+        if t_mfma >= t_hbm:
+            roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4), **common}
+        else:
+            roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbps / PEAK_HBM_GBS, 4), **common}
     else:
         achieved = alg_expert_bytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
