@@ -153,20 +153,32 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int nblk, int nexp, 
   if (threadIdx.x == 0) status[0] = (int)(A - total);
 }
 
-// Large A, pass 3: stable scatter.
+// Large A, pass 3: stable scatter.  The rank of an assignment among the
+// block's earlier ones of the same expert is the count in the earlier
+// 256-assignment parts of the block (histograms of the parts, order-free
+// atomic counts) plus a direct count over the earlier ids of its own part.
+constexpr int kPart = 256;
 __global__ __launch_bounds__(1024) void permute_scatter_kernel(const int32_t* __restrict__ idx, long A, int k, int kS,
                                                                 int E, int nexp, const int32_t* __restrict__ hist,
                                                                 const int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ sorted,
                                                                 int32_t* __restrict__ inverse) {
   __shared__ int sid[kB];
+  __shared__ int part_cnt[kB / kPart - 1][kMaxExperts];   // the last part's counts are never needed
   const long a = (long)blockIdx.x * kB + threadIdx.x;
   const int id = a < A ? assignment_expert(idx, a, k, kS, E) : -2;
+  const int part = threadIdx.x / kPart;
+  for (int i = threadIdx.x; i < (kB / kPart - 1) * nexp; i += kB) part_cnt[i / nexp][i % nexp] = 0;
   sid[threadIdx.x] = id;
+  __syncthreads();
+  if (id >= 0 && part < kB / kPart - 1) atomicAdd(&part_cnt[part][id], 1);
   __syncthreads();
   if (a >= A) return;
   if (id < 0) { inverse[a] = -1; return; }
-  const int rank = local_rank(sid, threadIdx.x, id);
+  int rank = 0;
+  for (int q = 0; q < part; ++q) rank += part_cnt[q][id];
+  const int p0 = part * kPart;
+  for (int j = p0; j < (int)threadIdx.x; ++j) rank += (sid[j] == id);
   const int p = offsets[id] + hist[(size_t)blockIdx.x * nexp + id] + rank;
   sorted[p] = (int32_t)a;
   inverse[a] = p;

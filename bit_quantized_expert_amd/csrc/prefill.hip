@@ -27,39 +27,40 @@ constexpr int BM = kPrefillBM;   // 128 tokens per tile
 // Work items are listed by the number of 32-row M-tiles they fill, most
 // first (full tiles, then partial ones from the largest down), so that
 // blocks dealt out last are the short ones and fill the tail of the launch.
-__global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restrict__ counts, int nexp,
-                                                        int32_t* __restrict__ sched) {
+// One block of 256 threads; thread i takes a contiguous range of experts;
+// the four per-bucket counts are scanned together.
+__global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict__ counts, int nexp,
+                                                       int32_t* __restrict__ sched) {
   constexpr int NBK = BM / 32;   // buckets: 1 .. NBK M-tiles
-  __shared__ int part[1024];
-  __shared__ int total[NBK + 1];
+  static_assert(NBK == 4, "four buckets");
+  __shared__ int4 part[256];
   const int tid = threadIdx.x;
-  const int per = (nexp + 1023) / 1024;
+  const int per = (nexp + 255) / 256;
   const int e0 = min(nexp, tid * per), e1 = min(nexp, e0 + per);
   auto mtiles = [](int c, int m) { return (min(BM, c - m * BM) + 31) / 32; };
+  int mine[NBK + 1] = {0, 0, 0, 0, 0};
+  for (int e = e0; e < e1; ++e) {
+    const int c = counts[e];
+    mine[4] += c / BM;   // full tiles
+    if (c % BM) mine[mtiles(c, c / BM)] += 1;
+  }
+  int4 v = make_int4(mine[1], mine[2], mine[3], mine[4]);
+  part[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {   // inclusive Hillis-Steele scan of the four counts
+    const int4 u = tid >= o ? part[tid - o] : make_int4(0, 0, 0, 0);
+    __syncthreads();
+    v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    part[tid] = v;
+    __syncthreads();
+  }
+  const int4 tot = part[255];
+  // bucket order 4, 3, 2, 1: exclusive start of this thread in each
   int pos[NBK + 1];
-  for (int bk = NBK; bk >= 1; --bk) {   // exclusive scan of this thread's tiles in bucket bk
-    int mine = 0;
-    for (int e = e0; e < e1; ++e) {
-      const int c = counts[e], nt = (c + BM - 1) / BM;
-      for (int m = 0; m < nt; ++m) mine += mtiles(c, m) == bk;
-    }
-    part[tid] = mine;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {   // inclusive Hillis-Steele scan
-      const int v = tid >= o ? part[tid - o] : 0;
-      __syncthreads();
-      part[tid] += v;
-      __syncthreads();
-    }
-    pos[bk] = part[tid] - mine;
-    if (tid == 1023) total[bk] = part[1023];
-    __syncthreads();
-  }
-  int start = 0;
-  for (int bk = NBK; bk >= 1; --bk) {
-    pos[bk] += start;
-    start += total[bk];
-  }
+  pos[4] = v.w - mine[4];
+  pos[3] = tot.w + v.z - mine[3];
+  pos[2] = tot.w + tot.z + v.y - mine[2];
+  pos[1] = tot.w + tot.z + tot.y + v.x - mine[1];
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e], nt = (c + BM - 1) / BM;
     for (int m = 0; m < nt; ++m) {
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t* __restric
       sched[3 + 2 * p] = m;
     }
   }
-  if (tid == 0) sched[0] = start;
+  if (tid == 0) sched[0] = tot.x + tot.y + tot.z + tot.w;
 }
 
 // ---------------------------------------------------------------------------
@@ -833,7 +834,7 @@ extern "C" int moe_qgemm_prefill(const moe_layer_desc* L, const uint16_t* x, int
   const int nexp = L->E + L->S, kS = L->k + L->S;
   const long A = (long)T * kS;
   const long max_tiles = prefill_max_tiles(A, nexp);
-  schedule_kernel<<<1, 1024, 0, stream>>>(counts, nexp, sched);
+  schedule_kernel<<<1, 256, 0, stream>>>(counts, nexp, sched);
   if ((rc = check_launch("moe_qgemm_prefill (schedule)")) != MOEQ_OK) return rc;
   const unsigned nw = (unsigned)((max_tiles + 7) / 8 * 8);   // work items, padded for the XCD mapping
   const unsigned g1 = nw * (unsigned)(L->I / 128), g2 = nw * (unsigned)(L->H / 256);

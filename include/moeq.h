@@ -192,10 +192,14 @@ int moe_qgemv_decode(const moe_layer_desc* L, const uint16_t* x, int T,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Prefill path (large T): the same y as moe_qgemv_decode, computed as a
- * grouped GEMM over expert-sorted tokens on the bf16 matrix cores: weights
- * are dequantised (fp32, then rounded to bf16) into LDS tiles, products
- * accumulate in fp32, h is rounded to bf16 between the two GEMMs.  y is
- * device bf16 [T*(k+S)][H], rows in assignment order. */
+ * grouped GEMM over expert-sorted tokens on the bf16 matrix cores (a prompt
+ * touches nearly every expert: Qwen-tin page, "Memory layout and
+ * performance").  Codes and scale/zero words are staged in LDS and
+ * dequantised in registers (w = (q - z) s in fp32, rounded to bf16) into the
+ * MFMA operand; products accumulate in fp32; h is rounded to bf16 between
+ * the two GEMMs.  y is device bf16 [T*(k+S)][H], rows in assignment order.
+ * Needs I % 128 == 0 and H % 256 == 0 (MOEQ_ERR_UNSUPPORTED otherwise);
+ * counts/offsets/sorted as produced by moe_permute. */
 int moe_qgemm_prefill(const moe_layer_desc* L, const uint16_t* x, int T,
                       const int32_t* counts, const int32_t* offsets,
                       const int32_t* sorted, uint16_t* y,
