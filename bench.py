@@ -100,7 +100,11 @@ def copy_calibrate(mib):
 
 
 class Step:
-    """Preallocated buffers and the ctypes calls of one layer step."""
+    """Preallocated buffers and the ctypes calls of one layer step.
+
+    Decode batches that moe_decode_forward takes run as that one call
+    (router; routing + gate/up; down + combine); the others as
+    route/permute, the expert FFN call and the combine."""
 
     def __init__(self, bq, layer, wr, bias, x, T, ws):
         import torch
@@ -119,9 +123,16 @@ class Step:
         self.inverse = torch.empty(A, dtype=torch.int32, device=dev)
         self.active = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
         self.prefill = T > bq.DECODE_MAX_T
+        self.layer_fused = not self.prefill and bq.decode_forward_ok(layer, T)
         self.fused = not self.prefill and bq.fused_route_ok(T, H, E, k, S)
         self.y = torch.empty((A, H), dtype=torch.bfloat16 if self.prefill else torch.float32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.residual = None
+
+    def distinct_experts(self) -> int:
+        """Experts the batch touched (routed ones from the top-k ids, plus the shared)."""
+        import torch
+        return int(torch.unique(self.idx).numel()) + self.L.S
 
     def route_permute(self, s):
         lib, p, L = self.bq.lib(), self.bq._p, self.L
@@ -148,13 +159,35 @@ class Step:
 
     def combine(self, s):
         lib, p, L = self.bq.lib(), self.bq._p, self.L
-        self.bq._check(lib.moe_combine(p(self.y), 1 if self.prefill else 0, p(self.w), None, self.T, L.k, L.S, L.H,
-                                       p(self.out), s))
+        self.bq._check(lib.moe_combine(p(self.y), 1 if self.prefill else 0, p(self.w), p(self.residual), self.T, L.k,
+                                       L.S, L.H, p(self.out), s))
+
+    def decode_forward(self, s):
+        lib, p = self.bq.lib(), self.bq._p
+        self.bq._check(lib.moe_decode_forward(ctypes.byref(self.desc), p(self.x), p(self.wr), p(self.bias), self.T,
+                                              p(self.residual), p(self.logits), p(self.idx), p(self.w),
+                                              p(self.out), p(self.ws), self.ws.numel(), s))
+
+    # the step split around the part whose duration the roofline uses: the
+    # expert FFN call, or the whole fused decode call
+    def pre(self, s):
+        if not self.layer_fused:
+            self.route_permute(s)
+
+    def timed(self, s):
+        if self.layer_fused:
+            self.decode_forward(s)
+        else:
+            self.experts(s)
+
+    def post(self, s):
+        if not self.layer_fused:
+            self.combine(s)
 
     def run(self, s):
-        self.route_permute(s)
-        self.experts(s)
-        self.combine(s)
+        self.pre(s)
+        self.timed(s)
+        self.post(s)
 
 
 class StackStep:
@@ -164,36 +197,18 @@ class StackStep:
     def __init__(self, bq, layers, wrs, x, ws):
         import torch
         self.bq, self.layers, self.wrs, self.x, self.ws = bq, layers, wrs, x, ws
-        L0 = layers[0]
-        dev = x.device
         self.n = torch.empty_like(x)
         self.steps = [Step(bq, L, wr, None, self.n, x.shape[0], ws) for L, wr in zip(layers, wrs)]
         for st in self.steps:      # every block adds into the residual stream x
             st.out = x
+            st.residual = x
 
     def run(self, s):
         lib, p = self.bq.lib(), self.bq._p
         T, H = self.x.shape
         for st in self.steps:
             self.bq._check(lib.moe_rmsnorm(p(self.x), None, T, H, ctypes.c_float(1e-6), p(self.n), s))
-            st.route_permute(s)
-            st.experts(s)
-            L = st.L
-            self.bq._check(lib.moe_combine(p(st.y), 0, p(st.w), p(self.x), T, L.k, L.S, L.H, p(self.x), s))
-
-
-def build_stack(bq, w, device):
-    """All blocks of the stacked workload, each with its own weights and bit
-    width (quantised on the device)."""
-    import torch
-    from tests.gpu_util import bf16_tensor, gpu_layer
-    bits = synth.layer_bits(w)
-    layers, wrs = [], []
-    for l, b in enumerate(bits):
-        layers.append(gpu_layer(w, layer=l, bits=b, device=device))
-        wrs.append(bf16_tensor(synth.router_weight_bf16(w, layer=l), device=device))
-    torch.cuda.synchronize()
-    return layers, wrs, bits
+            st.run(s)
 
 
 def main_stack(a, w, bq, dev):
@@ -236,22 +251,31 @@ def main_stack(a, w, bq, dev):
     total_ms = ev0.elapsed_time(ev1)
     per_tok = total_ms / n_tok
     # algorithmic bytes per token: routed experts (realised, per layer) + routers + x, out
-    distinct = [int((ss.counts > 0).sum().item()) for ss in st.steps]
+    distinct = [ss.distinct_experts() for ss in st.steps]
     alg = sum(d * expert_bytes(w, b) for d, b in zip(distinct, bits)) + len(bits) * (w.E * w.H * 2 + 4 * w.H * 2)
-    # expert kernels alone: time one token's decode calls with events
+    # the timed part of each block (the fused decode call, or the expert FFN
+    # call) for one token, with events
     kev = []
     with torch.cuda.stream(s):
         x.copy_(xs[0])
         for ss in st.steps:
-            ss.route_permute(sp)
+            bq._check(bq.lib().moe_rmsnorm(bq._p(x), None, 1, w.H, ctypes.c_float(1e-6), bq._p(st.n), sp))
+            ss.pre(sp)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(s)
-            ss.experts(sp)
+            ss.timed(sp)
             e1.record(s)
+            ss.post(sp)
             kev.append((e0, e1))
     torch.cuda.synchronize()
     kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in kev)
-    exp_bytes = sum(d * expert_bytes(w, b) for d, b in zip(distinct, bits))
+    fused = all(ss.layer_fused for ss in st.steps)
+    if fused:   # the whole block: routers and x/out traffic included
+        exp_bytes = alg
+        kname = "moe_decode_forward (router; routing + gate/up; down + combine), summed over the blocks of one token"
+    else:
+        exp_bytes = sum(d * expert_bytes(w, b) for d, b in zip(distinct, bits))
+        kname = "moe_qgemv_decode (gate/up + down), summed over the blocks of one token"
     achieved = exp_bytes / (kern_ms * 1e-3) / 1e9
     res = {
         "metric": "MoE-layer tokens/s", "value": round(n_tok / (total_ms * 1e-3), 1), "unit": "tokens/s",
@@ -263,8 +287,8 @@ def main_stack(a, w, bq, dev):
                    "hip_graph": True, "alg_bytes_per_token": round(alg),
                    "GBps_per_token_stream": round(alg / (per_tok * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "moe_qgemv_decode (gate/up + down), summed over the 48 blocks of one token"},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": kname,
+                     "alg_bytes_per_token": round(exp_bytes), "kernel_us_per_token": round(kern_ms * 1e3, 3)},
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_stack(w, bits, a.cpu_budget)
@@ -402,7 +426,7 @@ def main():
     torch.cuda.synchronize()
 
     # realised distinct experts per step -> algorithmic bytes of the expert kernels
-    distinct = [int((st.counts > 0).sum().item()) for st in steps]
+    distinct = [st.distinct_experts() for st in steps]
     alg_expert_bytes = float(np.mean(distinct)) * expert_bytes(w, bits) + T * w.H * 2
     alg_layer_bytes = alg_expert_bytes + w.E * w.H * 2 + T * w.H * 2
     flops = T * (w.k + w.S) * 6 * w.I * w.H + 2 * T * w.E * w.H
@@ -438,20 +462,32 @@ def main():
     total_ms = ev0.elapsed_time(ev1)
     ms_per_step = total_ms / K
 
-    # dominant kernel(s): the expert FFN call, timed alone with events on its stream
-    kev = []
+    # dominant kernel(s): the expert FFN call (or the whole fused decode
+    # call), timed with events on its stream around replays of a graph that
+    # holds only that part of every step (the routing results it reads are
+    # those of the last full pass); eager launches when graphs are off
+    kgraph = None
+    if graph is not None:
+        kgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(kgraph, stream=s):
+            for st in steps:
+                st.timed(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
     with torch.cuda.stream(s):
-        for i in range(2 * G):
-            st = steps[i % G]
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            st.route_permute(sp)
-            e0.record(s)
-            st.experts(sp)
-            e1.record(s)
-            st.combine(sp)
-            kev.append((e0, e1))
+        if kgraph is not None:
+            kgraph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(2, min(50, K // G))
+        e0.record(s)
+        for _ in range(reps):
+            if kgraph is not None:
+                kgraph.replay()
+            else:
+                for st in steps:
+                    st.timed(sp)
+        e1.record(s)
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in kev]))
+    kern_ms = e0.elapsed_time(e1) / (reps * G)
 
     prefill = T > bq.DECODE_MAX_T
     if prefill:
@@ -478,11 +514,15 @@ def main():
             roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(gbps / PEAK_HBM_GBS, 4), **common}
     else:
-        achieved = alg_expert_bytes / (kern_ms * 1e-3) / 1e9
+        fused = steps[0].layer_fused
+        # fused: the whole layer call (router rows, x and out included)
+        dec_bytes = alg_layer_bytes if fused else alg_expert_bytes
+        achieved = dec_bytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name, T),
-                "kernel": "moe_qgemv_decode (gate/up + down grouped GEMV kernels)",
-                "alg_bytes_per_launch": round(alg_expert_bytes), "kernel_us": round(kern_ms * 1e3, 3)}
+                "kernel": ("moe_decode_forward (router; routing + gate/up; down + combine)" if fused
+                           else "moe_qgemv_decode (gate/up + down grouped GEMV kernels)"),
+                "alg_bytes_per_launch": round(dec_bytes), "kernel_us": round(kern_ms * 1e3, 3)}
 
     res = {
         "metric": "MoE-layer tokens/s",

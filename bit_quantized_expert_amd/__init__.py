@@ -8,8 +8,9 @@ package without the built library raises -- there is no fallback.
 
 Functions carry the names of the C entry points (see ``include/moeq.h``):
 ``moe_quantize``, ``moe_unpack``, ``moe_route_topk``, ``moe_permute``,
-``moe_qgemv_decode``, ``moe_qgemm_prefill``, ``moe_combine``,
-``moe_rmsnorm``, ``moe_workspace_bytes``, ``moe_read_status``.
+``moe_route_permute_decode``, ``moe_qgemv_decode``, ``moe_qgemm_prefill``,
+``moe_combine``, ``moe_decode_forward``, ``moe_rmsnorm``,
+``moe_workspace_bytes``, ``moe_read_status``.
 """
 from __future__ import annotations
 
@@ -64,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "moe_permute": (I, [P, I, I, I, I, P, P, P, P, P, P, SZ, P]),
             "moe_route_permute_decode": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_qgemv_decode": (I, [P, P, I, P, P, P, P, P, SZ, P]),
+            "moe_decode_forward": (I, [P, P, P, P, I, P, P, P, P, P, P, SZ, P]),
             "moe_qgemm_prefill": (I, [P, P, I, P, P, P, P, P, SZ, P]),
             "moe_combine": (I, [P, I, P, P, I, I, I, I, P, P]),
             "moe_rmsnorm": (I, [P, P, I, I, ctypes.c_float, P, P]),
@@ -264,6 +266,32 @@ def moe_qgemv_decode(layer: QuantLayer, x: torch.Tensor, offsets, sorted_a, acti
     return y
 
 
+def decode_forward_ok(layer: QuantLayer, T: int) -> bool:
+    """Whether moe_decode_forward takes this layer and batch (its documented limits)."""
+    return (0 < T <= 64 and layer.E <= 1024 and T * layer.k <= 1024 and layer.k + layer.S <= 16
+            and layer.H in (512, 1024, 2048, 4096) and layer.gate.bits == layer.up.bits
+            and (layer.I in (256, 512, 768) or (layer.I == 1024 and layer.down.bits == 4)))
+
+
+def moe_decode_forward(layer: QuantLayer, x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor],
+                       ws: torch.Tensor, residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       stream=None):
+    """The whole decode layer in three launches.  Returns (out, logits, idx, w)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w_router, torch.bfloat16, "w_router")
+    T = x.shape[0]
+    dev = x.device
+    logits = torch.empty((T, layer.E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, layer.k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, layer.k), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, layer.H), dtype=torch.bfloat16, device=dev)
+    d = layer.desc()
+    _check(lib().moe_decode_forward(ctypes.byref(d), _p(x), _p(w_router), _p(bias), T, _p(residual), _p(logits),
+                                    _p(idx), _p(w), _p(out), _p(ws), ws.numel(), _stream(stream)))
+    return out, logits, idx, w
+
+
 def moe_qgemm_prefill(layer: QuantLayer, x: torch.Tensor, counts, offsets, sorted_a, ws: torch.Tensor,
                       y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     _dev(x, torch.bfloat16, "x")
@@ -333,11 +361,21 @@ class MoELayer:
             self.T_max = T_max
 
     def forward(self, x: torch.Tensor, residual: Optional[torch.Tensor] = None, stream=None, prefill=None,
-                fused_route=None):
+                fused_route=None, fused_layer=None):
+        """Decode batches (T <= 64) go through moe_decode_forward when it takes
+        the layer (fused_layer=False: the five calls instead); the result then
+        has no permutation arrays or expert outputs (None)."""
         T = x.shape[0]
         self.reserve(T)
         q = self.q
         use_prefill = T > DECODE_MAX_T if prefill is None else prefill
+        if fused_layer is None:
+            fused_layer = not use_prefill and decode_forward_ok(q, T)
+        if fused_layer:
+            out, logits, idx, w = moe_decode_forward(q, x, self.w_router, self.bias, self.ws, residual=residual,
+                                                     stream=stream)
+            return dict(out=out, logits=logits, idx=idx, w=w, counts=None, offsets=None, sorted=None,
+                        inverse=None, active=None, y=None)
         if fused_route is None:
             fused_route = not use_prefill and T > 0 and fused_route_ok(T, q.H, q.E, q.k, q.S)
         if fused_route:

@@ -41,6 +41,10 @@ int perm_blocks(long A);
 long prefill_max_tiles(long A, int nexp);
 WsLayout ws_layout(int H, int I, int E, int S, int k, int T_max);
 int validate_layer(const moe_layer_desc* L);
+// Router logits of a decode batch, one wavefront per router row (H in
+// {512, 1024, 2048, 4096}, checked by the caller).
+int launch_router_rows(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E,
+                       float* logits, hipStream_t stream);
 
 }  // namespace moeq
 
@@ -170,6 +174,38 @@ MOEQ_DEV int wave_topk_next(const float (&v)[NS], uint64_t& taken, float& best) 
   const int l = __builtin_ctzll(hit);
   if (lane == l) taken |= 1ull << slot;
   return 64 * slot + l;
+}
+
+// The top k of one token's E logits, by one wavefront (wave_topk_next
+// rounds), and their softmax weights renormalised over the k chosen:
+// w_j = e^(l_j - l_0) / sum_i e^(l_i - l_0), l_0 the largest.  On return
+// lane j < k holds choice j in idx and its weight in w (other lanes: -1 and
+// 0).  Needs k <= 64.
+template <int NS>
+MOEQ_DEV void select_token(const float* __restrict__ L, int E, int k, int& idx, float& w) {
+  const int lane = threadIdx.x & 63;
+  float v[NS];
+  uint64_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? L[e] : -INFINITY;
+    if (e >= E) taken |= 1ull << i;
+  }
+  float top0 = 0.0f, wsum = 0.0f, myw = 0.0f;
+  idx = -1;
+  for (int j = 0; j < k; ++j) {
+    float bv;
+    const int bi = wave_topk_next<NS>(v, taken, bv);
+    if (j == 0) top0 = bv;
+    const float ex = __expf(bv - top0);
+    wsum += ex;
+    if (lane == j) {
+      myw = ex;
+      idx = bi;
+    }
+  }
+  w = lane < k ? myw / wsum : 0.0f;
 }
 
 // silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (about

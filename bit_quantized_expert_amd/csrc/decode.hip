@@ -1,7 +1,8 @@
-// Host side of the decode path (moe_qgemv_decode): argument checks, block
-// shape and grid sizing.  The kernels are in decode_impl.h, instantiated per
-// bit width in decode_b{4,6,8}.hip.
-#include "decode_impl.h"
+// Host side of the decode path (moe_qgemv_decode, moe_decode_forward):
+// argument checks, block shape and grid sizing.  The kernels are in
+// decode_impl.h and decode_fused.h, instantiated per bit width in
+// decode_b{4,6,8}.hip.
+#include "decode_fused.h"
 
 using namespace moeq;
 
@@ -74,6 +75,55 @@ extern "C" int moe_qgemv_decode(const moe_layer_desc* L, const uint16_t* x, int 
     case 4: rc = decode_down_b4(L, hh, offsets, sorted, active, T, w2, cw2, y, stream); break;
     case 6: rc = decode_down_b6(L, hh, offsets, sorted, active, T, w2, cw2, y, stream); break;
     default: rc = decode_down_b8(L, hh, offsets, sorted, active, T, w2, cw2, y, stream); break;
+  }
+  return rc;
+}
+
+extern "C" int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, const uint16_t* w_router,
+                                  const float* bias, int T, const uint16_t* residual, float* logits,
+                                  int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  using namespace decode_detail;
+  int rc = validate_layer(L);
+  if (rc != MOEQ_OK) return rc;
+  if (T < 0) return set_error(MOEQ_ERR_INVALID_ARG, "moe_decode_forward: T=%d", T);
+  if (T == 0) return MOEQ_OK;
+  const int H = L->H, I = L->I, E = L->E, S = L->S, k = L->k;
+  if (T > kFusedMaxT || E > kFusedMaxE || k > 64 || (long)T * k > kFusedMaxSel || k + S > kFusedMaxSlots)
+    return set_error(MOEQ_ERR_UNSUPPORTED,
+                     "moe_decode_forward: needs T <= %d, E <= %d, T*k <= %d and k+S <= %d (T=%d E=%d k=%d S=%d)",
+                     kFusedMaxT, kFusedMaxE, kFusedMaxSel, kFusedMaxSlots, T, E, k, S);
+  if (H != 512 && H != 1024 && H != 2048 && H != 4096)
+    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward: H=%d must be 512, 1024, 2048 or 4096", H);
+  if (I != 256 && I != 512 && I != 768 && I != 1024)
+    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward: I=%d must be 256, 512, 768 or 1024", I);
+  if (L->gate.bits != L->up.bits)
+    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward: gate and up must share a bit width");
+  if (!x || !w_router || !logits || !topk_idx || !topk_w || !out)
+    return set_error(MOEQ_ERR_INVALID_ARG, "moe_decode_forward: NULL pointer");
+  if (!aligned16(x) || !aligned16(w_router))
+    return set_error(MOEQ_ERR_MISALIGNED, "moe_decode_forward: x and w_router must be 16-byte aligned");
+  int w1, cw1;
+  if (!pick_shape(H, L->gate.bits, MOEQ_GATEUP_RUN, w1, cw1))
+    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward: no gate/up kernel for H=%d at %d bits", H,
+                     L->gate.bits);
+  const WsLayout wl = ws_layout(H, I, E, S, k, T);
+  if (!ws || ws_bytes < wl.total)
+    return set_error(MOEQ_ERR_WORKSPACE, "moe_decode_forward: workspace of %zu bytes, need %zu", ws_bytes, wl.total);
+  // h: bf16 [T (k+S)][I], rows in assignment order
+  uint16_t* hh = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.h);
+  rc = launch_router_rows(x, w_router, bias, T, H, E, logits, stream);
+  if (rc != MOEQ_OK) return rc;
+  switch (L->gate.bits) {
+    case 4: rc = decode_gateup_routed_b4(L, x, logits, T, w1, cw1, topk_idx, topk_w, hh, stream); break;
+    case 6: rc = decode_gateup_routed_b6(L, x, logits, T, w1, cw1, topk_idx, topk_w, hh, stream); break;
+    default: rc = decode_gateup_routed_b8(L, x, logits, T, w1, cw1, topk_idx, topk_w, hh, stream); break;
+  }
+  if (rc != MOEQ_OK) return rc;
+  switch (L->down.bits) {
+    case 4: rc = decode_down_combine_b4(L, hh, T, topk_idx, topk_w, residual, out, stream); break;
+    case 6: rc = decode_down_combine_b6(L, hh, T, topk_idx, topk_w, residual, out, stream); break;
+    default: rc = decode_down_combine_b8(L, hh, T, topk_idx, topk_w, residual, out, stream); break;
   }
   return rc;
 }

@@ -1,5 +1,6 @@
-// Decode kernels instantiated for 8-bit weights (see decode_impl.h).
-#include "decode_impl.h"
+// Decode kernels instantiated for 8-bit weights (see decode_impl.h and
+// decode_fused.h).
+#include "decode_fused.h"
 
 // one launch per (W, CW) shape that covers whole groups at this width
 #define MOEQ_LAUNCH_GU(W_, CW_)                                                                        \
@@ -16,7 +17,15 @@
         L->down.q, L->down.sz, hh, L->H, L->I, dg, offsets, sorted, active, y);                        \
     launched = true;                                                                                   \
   }
+#define MOEQ_LAUNCH_GUR(W_, CW_)                                                                       \
+  if constexpr (CW_ % Fmt<8>::CHUNKS_PER_GROUP == 0 && CW_ / Fmt<8>::CHUNKS_PER_GROUP <= 8)           \
+  if (W == W_ && CW == CW_) {                                                                          \
+    decode_detail::gateup_routed_kernel<8, W_, CW_><<<grid, 64 * W_, 0, s>>>(                        \
+        L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, fg, logits, topk_idx, topk_w, hh);    \
+    launched = true;                                                                                   \
+  }
 
 namespace moeq {
 MOEQ_DEFINE_DECODE(8)
+MOEQ_DEFINE_DECODE_FUSED(8)
 }  // namespace moeq

@@ -137,25 +137,33 @@ struct Stream {
 MOEQ_DEV void stage_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Sums of x over the wavefront's NG groups [g0, g0 + NG) for up to two token
-// rows, computed cooperatively (lane 8 g + j adds x values 8 j .. 8 j + 7 of
-// group g); the sum of group g ends in lane 8 g + 7.
+// rows, computed cooperatively: for NG <= 8 lane 8 g + j adds x values
+// 8 j .. 8 j + 7 of group g, for NG <= 16 lane 4 g + j adds values
+// 16 j .. 16 j + 15; the sum of group g ends in lane xs_lane<NG>(g).
+template <int NG>
+constexpr int xs_lane(int g) { return NG <= 8 ? 8 * g + 7 : 4 * g + 3; }
+
 template <int NG>
 MOEQ_DEV void group_sums(const uint16_t* const (&xr)[kMaxNT], int nt, int g0, float (&xs)[kMaxNT]) {
-  static_assert(NG >= 1 && NG <= 8, "at most 8 groups per wavefront");
+  static_assert(NG >= 1 && NG <= 16, "at most 16 groups per wavefront");
   const int lane = threadIdx.x & 63;
   const uint32_t ones = 0x3F803F80u;   // bf16 (1, 1): dot2 with it sums a pair
-  const int off = g0 * 64 + 8 * (lane < 8 * NG ? lane : 0);
+  constexpr int PER = NG <= 8 ? 8 : 16;   // values per lane
+  const int off = g0 * 64 + PER * (lane < 64 / PER * NG ? lane : 0);
 #pragma unroll
   for (int t = 0; t < kMaxNT; ++t) {
     float s = 0.0f;
     if (t < nt) {
-      const moeq_u32x4 v = *reinterpret_cast<const moeq_u32x4*>(xr[t] + off);
-      s = dot2_bf16(v.x, ones, s);
-      s = dot2_bf16(v.y, ones, s);
-      s = dot2_bf16(v.z, ones, s);
-      s = dot2_bf16(v.w, ones, s);
+#pragma unroll
+      for (int h = 0; h < PER / 8; ++h) {
+        const moeq_u32x4 v = *reinterpret_cast<const moeq_u32x4*>(xr[t] + off + 8 * h);
+        s = dot2_bf16(v.x, ones, s);
+        s = dot2_bf16(v.y, ones, s);
+        s = dot2_bf16(v.z, ones, s);
+        s = dot2_bf16(v.w, ones, s);
+      }
     }
-    xs[t] = group_sum_last<8>(s);
+    xs[t] = group_sum_last<64 / PER>(s);
   }
 }
 
@@ -233,7 +241,7 @@ MOEQ_DEV void stream_rows(const Stream<BITS, NM>& st, ChunkBuf<BITS, NM> (&buf)[
       const int gl = c / CPG;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const float x_sum = lane_value(xs[t], 8 * gl + 7);
+        const float x_sum = lane_value(xs[t], xs_lane<CW / CPG>(gl));
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           out[m][t] = fmaf(s[m], (acc[m][t][0] + acc[m][t][1]) - zc[m] * x_sum, out[m][t]);

@@ -112,32 +112,17 @@ __global__ __launch_bounds__(kThreads) void select_group_kernel(const float* __r
   for (int ee = threadIdx.x; ee < nexp; ee += kThreads) { cnt[ee] = 0; mlo[ee] = 0u; mhi[ee] = 0u; }
   __syncthreads();
   for (int t = wave; t < T; t += kWaves) {
-    const float* L = logits + (size_t)t * E;
-    float v[NS];
-    uint64_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int ee = lane + 64 * i;
-      v[i] = ee < E ? L[ee] : -INFINITY;
-      if (ee >= E) taken |= 1ull << i;
-    }
-    float top0 = 0.0f, wsum = 0.0f, myw = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      float bv;
-      const int bi = wave_topk_next<NS>(v, taken, bv);
-      if (j == 0) top0 = bv;
-      const float ex = __expf(bv - top0);
-      wsum += ex;
-      if (lane == (j & 63)) {
-        sid[t * kS + j] = bi;
-        topk_idx[(size_t)t * k + j] = bi;
-        if (masks) atomicOr(t < 32 ? &mlo[bi] : &mhi[bi], 1u << (t & 31));
-        else atomicAdd(&cnt[bi], 1);
-      }
-      if (lane == j) myw = ex;
+    int bi;
+    float w;
+    select_token<NS>(logits + (size_t)t * E, E, k, bi, w);
+    if (lane < k) {
+      sid[t * kS + lane] = bi;
+      topk_idx[(size_t)t * k + lane] = bi;
+      topk_w[(size_t)t * k + lane] = w;
+      if (masks) atomicOr(t < 32 ? &mlo[bi] : &mhi[bi], 1u << (t & 31));
+      else atomicAdd(&cnt[bi], 1);
     }
     for (int j = lane; j < S; j += 64) sid[t * kS + k + j] = E + j;
-    if (lane < k) topk_w[(size_t)t * k + lane] = myw / wsum;
   }
   __syncthreads();
   if (masks)
@@ -185,6 +170,21 @@ __global__ __launch_bounds__(kThreads) void select_group_kernel(const float* __r
 
 }  // namespace
 
+namespace moeq {
+
+int launch_router_rows(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E,
+                       float* logits, hipStream_t stream) {
+  switch (H / 512) {
+    case 1: router_rows_kernel<1><<<E, 64, 0, stream>>>(x, wr, bias, T, E, logits); break;
+    case 2: router_rows_kernel<2><<<E, 64, 0, stream>>>(x, wr, bias, T, E, logits); break;
+    case 4: router_rows_kernel<4><<<E, 64, 0, stream>>>(x, wr, bias, T, E, logits); break;
+    default: router_rows_kernel<8><<<E, 64, 0, stream>>>(x, wr, bias, T, E, logits); break;
+  }
+  return check_launch("router logits");
+}
+
+}  // namespace moeq
+
 extern "C" int moe_route_permute_decode(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
                                         int H, int E, int k, int S, float* logits, int32_t* topk_idx,
                                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted,
@@ -205,13 +205,7 @@ extern "C" int moe_route_permute_decode(const uint16_t* x, const uint16_t* w_rou
   if (!ws || ws_bytes < 256) return set_error(MOEQ_ERR_WORKSPACE, "moe_route_permute_decode: workspace too small");
   if (T == 0) return MOEQ_OK;
   int* status = static_cast<int*>(ws);
-  switch (H / 512) {
-    case 1: router_rows_kernel<1><<<E, 64, 0, stream>>>(x, w_router, bias, T, E, logits); break;
-    case 2: router_rows_kernel<2><<<E, 64, 0, stream>>>(x, w_router, bias, T, E, logits); break;
-    case 4: router_rows_kernel<4><<<E, 64, 0, stream>>>(x, w_router, bias, T, E, logits); break;
-    default: router_rows_kernel<8><<<E, 64, 0, stream>>>(x, w_router, bias, T, E, logits); break;
-  }
-  int rc = check_launch("moe_route_permute_decode (router)");
+  int rc = launch_router_rows(x, w_router, bias, T, H, E, logits, stream);
   if (rc != MOEQ_OK) return rc;
   const int ns = (E + 63) / 64;
   if (ns <= 1) select_group_kernel<1><<<1, kThreads, 0, stream>>>(logits, T, E, k, S, topk_idx, topk_w, counts, offsets, sorted, inverse, active, status);

@@ -58,10 +58,11 @@ def layer_for(bq, name, bits=None):
     return _LAYERS[key]
 
 
-def check_layer(bq, name, T, prefill, sample=None, bits=None, batch=0):
+def check_layer(bq, name, T, prefill, sample=None, bits=None, batch=0, fused=False):
+    """fused: the decode layer through moe_decode_forward (no y to check)."""
     w, layer, olayer = layer_for(bq, name, bits)
     x = synth.activations_bf16(w, T, batch=batch)
-    r = layer.forward(bf16_tensor(x), prefill=prefill)
+    r = layer.forward(bf16_tensor(x), prefill=prefill, fused_layer=fused)
     torch.cuda.synchronize()
     logits = r["logits"].cpu().numpy()
     wr = synth.router_weight_bf16(w)
@@ -77,6 +78,11 @@ def check_layer(bq, name, T, prefill, sample=None, bits=None, batch=0):
     out = oracle.bf16_to_f32(to_bits(r["out"]))[rows]
     err = rel_err(out, ref["out"])
     assert err <= SPEC_TOL, err
+    if fused:
+        ref_b = oracle.moe_layer(olayer, x[rows], logits=logits[rows], h_bf16=True)
+        err_b = rel_err(out, ref_b["out"])
+        assert err_b <= DECODE_TOL, err_b
+        return r, err, None
     kS = w.k + w.S
     y = r["y"]
     y = (oracle.bf16_to_f32(to_bits(y)) if y.dtype == torch.bfloat16 else y.cpu().numpy())
@@ -109,6 +115,46 @@ def test_decode_layer_6_8_bit(bq, bits, T):
     # the stacked workload's 6- and 8-bit layers use the 128-expert shapes
     print(f"decode 128-expert {bits}-bit T={T}", flush=True)
     check_layer(bq, "moe_h2048_e128_k8_b4", T, prefill=False, bits=bits, batch=bits)
+
+
+FUSED_CASES = [("moe_h2048_e256_k8_s1_b4", 1), ("moe_h2048_e256_k8_s1_b4", 3), ("moe_h2048_e256_k8_s1_b4", 8),
+               ("moe_h2048_e256_k8_s1_b4", 64), ("moe_h2048_e128_k8_b4", 16), ("moe_h2048_e128_k8_b4", 64),
+               ("moe_h4096_e512_k10_b4_hot", 1), ("moe_h4096_e512_k10_b4_hot", 37)]
+
+
+@pytest.mark.parametrize("name,T", FUSED_CASES)
+def test_decode_forward(bq, name, T):
+    """moe_decode_forward: routing inside the gate/up kernel, combine inside
+    the down kernel.  At T = 64 on 128 experts most experts serve three or
+    more tokens (several work items each)."""
+    print(f"decode forward {name} T={T}", flush=True)
+    check_layer(bq, name, T, prefill=False, fused=True, batch=5)
+
+
+@pytest.mark.parametrize("bits", [6, 8])
+@pytest.mark.parametrize("T", [2, 17])
+def test_decode_forward_6_8_bit(bq, bits, T):
+    print(f"decode forward 128-expert {bits}-bit T={T}", flush=True)
+    check_layer(bq, "moe_h2048_e128_k8_b4", T, prefill=False, bits=bits, batch=bits, fused=True)
+
+
+def test_decode_forward_matches_route_and_residual(bq):
+    """The fused layer's logits, top-k ids and weights are those of
+    moe_route_permute_decode bit for bit; with a residual its output is
+    bf16(residual + bf16(sum)) of its own output without one."""
+    w, layer, _ = layer_for(bq, "moe_h2048_e256_k8_s1_b4")
+    T = 8
+    x = bf16_tensor(synth.activations_bf16(w, T, batch=11))
+    a = layer.forward(x, fused_layer=True)
+    b = layer.forward(x, fused_layer=False, fused_route=True)
+    for key in ("logits", "idx", "w"):
+        assert torch.equal(a[key], b[key]), key
+    res = bf16_tensor(synth.activations_bf16(w, T, batch=12))
+    c = layer.forward(x, residual=res, fused_layer=True)
+    expect = oracle.f32_to_bf16(oracle.bf16_to_f32(to_bits(res)) + oracle.bf16_to_f32(to_bits(a["out"])))
+    assert np.array_equal(to_bits(c["out"]), expect)
+    d = layer.forward(x, fused_layer=True)
+    assert torch.equal(a["out"].view(torch.uint8), d["out"].view(torch.uint8))
 
 
 @pytest.mark.parametrize("T", [1, 100, 512])
@@ -149,8 +195,8 @@ def test_decode_prefill_agree(bq, name, T):
 def test_deterministic(bq, prefill, T):
     w, layer, _ = layer_for(bq, "moe_h2048_e128_k8_b4")
     x = bf16_tensor(synth.activations_bf16(w, T, batch=9))
-    a = layer.forward(x, prefill=prefill)
-    b = layer.forward(x, prefill=prefill)
+    a = layer.forward(x, prefill=prefill, fused_layer=False)
+    b = layer.forward(x, prefill=prefill, fused_layer=False)
     for key in ("out", "idx", "sorted", "y"):
         assert torch.equal(a[key].view(torch.uint8) if a[key].dtype == torch.bfloat16 else a[key],
                            b[key].view(torch.uint8) if b[key].dtype == torch.bfloat16 else b[key]), key
