@@ -268,7 +268,7 @@ def moe_qgemv_decode(layer: QuantLayer, x: torch.Tensor, offsets, sorted_a, acti
 
 def decode_forward_ok(layer: QuantLayer, T: int) -> bool:
     """Whether moe_decode_forward takes this layer and batch (its documented limits)."""
-    return (0 < T <= 64 and layer.E <= 1024 and T * layer.k <= 1024 and layer.k + layer.S <= 16
+    return (0 < T <= 64 and layer.E <= 1024 and layer.k + layer.S <= 16
             and layer.H in (512, 1024, 2048, 4096) and layer.gate.bits == layer.up.bits
             and (layer.I in (256, 512, 768) or (layer.I == 1024 and layer.down.bits == 4)))
 

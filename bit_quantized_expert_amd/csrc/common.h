@@ -8,6 +8,7 @@
 #include <stddef.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <limits.h>
 
 #include "moeq.h"
 
@@ -176,33 +177,79 @@ MOEQ_DEV int wave_topk_next(const float (&v)[NS], uint64_t& taken, float& best) 
   return 64 * slot + l;
 }
 
-// The top k of one token's E logits, by one wavefront (wave_topk_next
-// rounds), and their softmax weights renormalised over the k chosen:
-// w_j = e^(l_j - l_0) / sum_i e^(l_i - l_0), l_0 the largest.  On return
-// lane j < k holds choice j in idx and its weight in w (other lanes: -1 and
-// 0).  Needs k <= 64.
+// Selection keys: a signed integer per logit whose order is the routing
+// order of the values (larger first); -0 counts as +0, NaN below every
+// number, and kKeyGone (padding, already chosen) below NaN.
+constexpr int kKeyGone = INT_MIN;
+constexpr int kKeyNaN = INT_MIN + 1;
+MOEQ_DEV int logit_key(float f) {
+  if (f != f) return kKeyNaN;
+  const int b = __float_as_int(f + 0.0f);   // -0 + 0 = +0
+  return b >= 0 ? b : b ^ 0x7FFFFFFF;
+}
+MOEQ_DEV float key_value(int key) {
+  if (key == kKeyNaN) return __builtin_nanf("");
+  return __int_as_float(key >= 0 ? key : key ^ 0x7FFFFFFF);
+}
+
+template <int CTRL, int ROW_MASK>
+MOEQ_DEV int dpp_max_i32(int v) {
+  return max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, CTRL, ROW_MASK, 0xF, false));
+}
+
+// Wave maximum of an int with DPP, returned (uniform) from lane 63.
+MOEQ_DEV int wave_max_i32(int v) {
+  v = dpp_max_i32<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v = dpp_max_i32<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v = dpp_max_i32<0x141, 0xF>(v);   // row_half_mirror
+  v = dpp_max_i32<0x140, 0xF>(v);   // row_mirror
+  v = dpp_max_i32<0x142, 0xA>(v);   // row_bcast:15
+  v = dpp_max_i32<0x143, 0x8>(v);   // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// The top k of one token's E logits, by one wavefront, and their softmax
+// weights renormalised over the k chosen: w_j = e^(l_j - l_0) /
+// sum_i e^(l_i - l_0), l_0 the largest.  Lane l holds experts NS l ..
+// NS l + NS - 1, so among equal values the lowest index is on the lowest
+// lane holding the maximum, in its lowest slot: each of the k rounds is a
+// lane maximum, a DPP wave maximum and one ballot.  Order: larger value
+// first, ties to the lower index, NaN after every number (in index order).
+// On return lane j < k holds choice j in idx and its weight in w (other
+// lanes: -1 and 0).  Needs k <= min(E, 64).  With rounds < k only the
+// first `rounds` choices are made (lanes j < rounds), and w is not valid.
 template <int NS>
-MOEQ_DEV void select_token(const float* __restrict__ L, int E, int k, int& idx, float& w) {
+MOEQ_DEV void select_token(const float* __restrict__ L, int E, int k, int rounds, int& idx, float& w) {
   const int lane = threadIdx.x & 63;
-  float v[NS];
-  uint64_t taken = 0;
+  int key[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? L[e] : -INFINITY;
-    if (e >= E) taken |= 1ull << i;
+    const int e = NS * lane + i;
+    key[i] = e < E ? logit_key(L[e]) : kKeyGone;
   }
   float top0 = 0.0f, wsum = 0.0f, myw = 0.0f;
   idx = -1;
-  for (int j = 0; j < k; ++j) {
-    float bv;
-    const int bi = wave_topk_next<NS>(v, taken, bv);
+  for (int j = 0; j < rounds; ++j) {
+    int m = key[0];
+#pragma unroll
+    for (int i = 1; i < NS; ++i) m = max(m, key[i]);
+    const int M = wave_max_i32(m);
+    const int wl = __builtin_ctzll(__ballot(m == M));   // lowest lane holding the maximum
+    int slot = NS - 1;
+#pragma unroll
+    for (int i = NS - 2; i >= 0; --i) slot = key[i] == M ? i : slot;
+    const int ws = __builtin_amdgcn_readlane(slot, wl);
+    if (lane == wl) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) key[i] = i == ws ? kKeyGone : key[i];
+    }
+    const float bv = key_value(M);
     if (j == 0) top0 = bv;
     const float ex = __expf(bv - top0);
     wsum += ex;
     if (lane == j) {
       myw = ex;
-      idx = bi;
+      idx = NS * wl + ws;
     }
   }
   w = lane < k ? myw / wsum : 0.0f;

@@ -1,13 +1,13 @@
 // The decode layer in three launches (moe_decode_forward):
 //
 //  1. router logits (one wavefront per router row, route_decode.hip);
-//  2. routing + gate/up: every block that serves a routed expert first
-//     repeats the selection of the whole batch from the logits (one
-//     wavefront per token, a few microseconds), so no launch sits between
-//     the router and the expert GEMV; it then finds its work item -- a pair
-//     of the tokens of one expert, experts ascending -- and streams that
-//     expert's gate and up rows exactly as gateup_rows_kernel does.  h goes
-//     to the workspace in assignment order (row t (k+S) + j);
+//  2. selection + gate/up: one block per (routed assignment t k + j, 64-row
+//     tile of I); its first wavefront makes the first j + 1 choices of token
+//     t from the logits (select_token), then the block streams that
+//     expert's gate and up rows for token t as gateup_rows_kernel does.  No
+//     launch sits between the router and the expert GEMV, and no block
+//     needs the selection of any other token.  h goes to the workspace in
+//     assignment order (row t (k+S) + j);
 //  3. down + combine: one block per (token, 64-row tile of H), one wavefront
 //     per expert slot of the token; each wavefront streams its expert's down
 //     rows over the whole of I, and the block adds the k+S results with the
@@ -16,19 +16,17 @@
 //
 // Removing the dependent small launches between routing, expert GEMVs and
 // combine is the decode lever the pages report (Raon-1-mini on an RTX
-// 5070 Ti, optimisation table).  A routed expert chosen by more than two
-// tokens of the batch gets one work item per pair, each reading its weights
-// (the later ones mostly from cache); the expert outputs of step 3 are read
-// once per token (at decode sizes nearly every expert of a token is its own).
+// 5070 Ti, optimisation table).  The price: an expert that several tokens
+// of the batch chose is streamed once per token, by blocks of one row tile
+// that share an XCD (so mostly from its L2 after the first).
 #pragma once
 #include "decode_impl.h"
 
 namespace moeq {
 namespace decode_detail {
 
-constexpr int kFusedMaxT = 64;       // tokens per batch: one 64-bit token mask per expert
-constexpr int kFusedMaxE = 1024;     // routed experts
-constexpr int kFusedMaxSel = 1024;   // T * k choices
+constexpr int kFusedMaxT = 64;       // tokens per batch
+constexpr int kFusedMaxE = 1024;     // routed experts (select_token holds 16 per lane)
 constexpr int kFusedMaxSlots = 16;   // k + S: one wavefront per slot in the down + combine block
 
 struct FusedGrid {
@@ -39,65 +37,18 @@ struct FusedGrid {
   int groups;          // token pairs: ceil(T / 2)
 };
 
-// Exclusive prefix sum of v over the block's threads in thread order; total
-// receives the sum over the block.  tmp: LDS of one int per wavefront.
-MOEQ_DEV int block_scan_excl(int v, int* tmp, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o);
-    if (lane >= o) incl += u;
-  }
-  if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < nw; ++w) {
-    const int s = tmp[w];
-    if (w < wave) before += s;
-    all += s;
-  }
-  __syncthreads();
-  total = all;
-  return before + incl - v;
-}
-
-// The routing of the batch: sel[t k + j] = choice j of token t; bit t of
-// mask[e] set when token t chose e (mask zeroed by the caller).  With
-// idx_out set, the top-k ids and weights are stored there too.
-template <int NS>
-MOEQ_DEV void route_batch(const float* __restrict__ logits, int T, int E, int k, int* sel,
-                          unsigned long long* mask, int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int t = wave; t < T; t += nw) {
-    int bi;
-    float w;
-    select_token<NS>(logits + (size_t)t * E, E, k, bi, w);
-    if (lane < k) {
-      sel[t * k + lane] = bi;
-      atomicOr(&mask[bi], 1ull << t);
-      if (idx_out) {
-        idx_out[(size_t)t * k + lane] = bi;
-        w_out[(size_t)t * k + lane] = w;
-      }
-    }
-  }
-}
-
-MOEQ_DEV void route_batch_any(const float* logits, int T, int E, int k, int* sel, unsigned long long* mask,
-                              int32_t* idx_out, float* w_out) {
+MOEQ_DEV void select_token_any(const float* L, int E, int k, int rounds, int& idx, float& w) {
   const int ns = (E + 63) / 64;
-  if (ns <= 1) route_batch<1>(logits, T, E, k, sel, mask, idx_out, w_out);
-  else if (ns <= 2) route_batch<2>(logits, T, E, k, sel, mask, idx_out, w_out);
-  else if (ns <= 4) route_batch<4>(logits, T, E, k, sel, mask, idx_out, w_out);
-  else if (ns <= 8) route_batch<8>(logits, T, E, k, sel, mask, idx_out, w_out);
-  else route_batch<16>(logits, T, E, k, sel, mask, idx_out, w_out);
+  if (ns <= 1) select_token<1>(L, E, k, rounds, idx, w);
+  else if (ns <= 2) select_token<2>(L, E, k, rounds, idx, w);
+  else if (ns <= 4) select_token<4>(L, E, k, rounds, idx, w);
+  else if (ns <= 8) select_token<8>(L, E, k, rounds, idx, w);
+  else select_token<16>(L, E, k, rounds, idx, w);
 }
 
 // -------------------------------------------------------------------------
-// routing + gate/up.  Grid: the shared-expert part of DecodeGrid, then one
-// block per (work item, row tile) for T * k work items (an upper bound; the
-// blocks past the last item exit after the routing).  h[a][i] =
+// selection + gate/up.  Grid: the shared-expert part of DecodeGrid, then one
+// block per (routed assignment, row tile), T k tiles of them.  h[a][i] =
 // bf16(silu(Wg x_t)[i] * (Wu x_t)[i]) for assignment a = t (k+S) + j.
 // -------------------------------------------------------------------------
 template <int BITS, int W, int CW>
@@ -113,10 +64,7 @@ __global__ __launch_bounds__(64 * W, 4) void gateup_routed_kernel(const uint8_t*
   using F = Fmt<BITS>;
   constexpr int D = CW < kDepth ? CW : kDepth;
   __shared__ Partials<W, 2> part;
-  __shared__ int sel[kFusedMaxSel];
-  __shared__ unsigned long long mask[kFusedMaxE];
-  __shared__ int tmp[W];
-  __shared__ int work[2];
+  __shared__ int chosen;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = (int)blockIdx.x;
   Stream<BITS, 2> st;
@@ -146,44 +94,27 @@ __global__ __launch_bounds__(64 * W, 4) void gateup_routed_kernel(const uint8_t*
     a0 = t0 * fg.kS + fg.k + s;
     a1 = t1 * fg.kS + fg.k + s;
   } else {
+    // wavefront 0 makes the first j + 1 choices of token t (all k, and the
+    // weights, in the block that stores them for the down + combine kernel)
     const int r = b - fg.shared_blocks;
-    const int q = r / fg.tiles;
+    const int a = r / fg.tiles, t = a / fg.k, j = a % fg.k;
     tile = r % fg.tiles;
-    for (int i = threadIdx.x; i < fg.E; i += 64 * W) mask[i] = 0ull;
-    __syncthreads();
-    route_batch_any(logits, fg.T, fg.E, fg.k, sel, mask, r == 0 ? topk_idx : nullptr, topk_w);
-    __syncthreads();
-    // work items: ceil(tokens / 2) per expert, experts ascending
-    const int nthr = 64 * W, per = (fg.E + nthr - 1) / nthr;
-    const int e0 = min(fg.E, (int)threadIdx.x * per), e1 = min(fg.E, e0 + per);
-    int items = 0;
-    for (int e = e0; e < e1; ++e) items += (__popcll(mask[e]) + 1) >> 1;
-    int total;
-    int base = block_scan_excl(items, tmp, total);
-    if (q >= total) return;   // the same for every thread of the block
-    for (int e = e0; e < e1; ++e) {
-      const int n = (__popcll(mask[e]) + 1) >> 1;
-      if (q >= base && q < base + n) {
-        work[0] = e;
-        work[1] = q - base;
+    const bool writer = j == 0 && tile == 0;
+    if (wave == 0) {
+      int bi;
+      float w;
+      select_token_any(logits + (size_t)t * fg.E, fg.E, fg.k, writer ? fg.k : j + 1, bi, w);
+      if (writer && lane < fg.k) {
+        topk_idx[(size_t)t * fg.k + lane] = bi;
+        topk_w[(size_t)t * fg.k + lane] = w;
       }
-      base += n;
+      if (lane == 0) chosen = __builtin_amdgcn_readlane(bi, j);
     }
     __syncthreads();
-    const int e = uniform(work[0]), pair = uniform(work[1]);
-    start(e, tile);
-    // tokens 2 pair and 2 pair + 1 of the expert (ascending), and the slot
-    // each chose it in
-    unsigned long long m = mask[e];
-    for (int i = 0; i < 2 * pair; ++i) m &= m - 1;
-    t0 = __builtin_ctzll(m);
-    m &= m - 1;
-    nt = m ? 2 : 1;
-    t1 = m ? __builtin_ctzll(m) : t0;
-    const unsigned long long b0 = __ballot(lane < fg.k && sel[t0 * fg.k + lane] == e);
-    const unsigned long long b1 = __ballot(lane < fg.k && sel[t1 * fg.k + lane] == e);
-    a0 = t0 * fg.kS + __builtin_ctzll(b0);
-    a1 = t1 * fg.kS + __builtin_ctzll(b1);
+    start(uniform(chosen), tile);
+    t0 = t1 = t;
+    nt = 1;
+    a0 = a1 = t * fg.kS + j;
   }
   tile = uniform(tile);
   t0 = uniform(t0);
@@ -231,6 +162,11 @@ __global__ __launch_bounds__(64 * kFusedMaxSlots) void down_combine_kernel(const
     tile = b / fg.T;
     t = b % fg.T;
   }
+  // the h row's loads first: its group sums need nothing else, and the
+  // expert id comes meanwhile (a scalar load)
+  const uint16_t* hrow = hh + (size_t)(t * fg.kS + j) * I;
+  GroupX<NG> gx;
+  gx.load(hrow, 0);
   const int e = uniform(j < fg.k ? topk_idx[(size_t)t * fg.k + j] : fg.E + (j - fg.k));
   Stream<BITS, 1> st;
   {
@@ -243,10 +179,8 @@ __global__ __launch_bounds__(64 * kFusedMaxSlots) void down_combine_kernel(const
   for (int c = 0; c < D; ++c) st.load(c, buf[c]);
   stage_fence();
   const float wj = j < fg.k ? topk_w[(size_t)t * fg.k + j] : 1.0f;
-  const uint16_t* hrow = hh + (size_t)(t * fg.kS + j) * I;
   const uint16_t* const xr[kMaxNT] = {hrow, hrow};
-  float xs[kMaxNT];
-  group_sums<NG>(xr, 1, 0, xs);
+  float xs[kMaxNT] = {gx.sum(), 0.0f};
   stage_fence();
   float y[1][kMaxNT];
   stream_rows<BITS, 1, 1, CPR, D>(st, buf, xr, xs, y);

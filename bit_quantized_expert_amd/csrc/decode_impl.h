@@ -143,27 +143,40 @@ MOEQ_DEV void stage_fence() { __builtin_amdgcn_sched_barrier(0); }
 template <int NG>
 constexpr int xs_lane(int g) { return NG <= 8 ? 8 * g + 7 : 4 * g + 3; }
 
+// The two halves of one row's group sums, so that the loads can be issued
+// early: GroupX<NG>::load, then GroupX<NG>::sum.
+template <int NG>
+struct GroupX {
+  static_assert(NG >= 1 && NG <= 16, "at most 16 groups per wavefront");
+  static constexpr int PER = NG <= 8 ? 8 : 16;   // values per lane
+  moeq_u32x4 v[PER / 8];
+  MOEQ_DEV void load(const uint16_t* xr, int g0) {
+    const int lane = threadIdx.x & 63;
+    const int off = g0 * 64 + PER * (lane < 64 / PER * NG ? lane : 0);
+#pragma unroll
+    for (int h = 0; h < PER / 8; ++h) v[h] = *reinterpret_cast<const moeq_u32x4*>(xr + off + 8 * h);
+  }
+  MOEQ_DEV float sum() const {
+    const uint32_t ones = 0x3F803F80u;   // bf16 (1, 1): dot2 with it sums a pair
+    float s = 0.0f;
+#pragma unroll
+    for (int h = 0; h < PER / 8; ++h) {
+      s = dot2_bf16(v[h].x, ones, s);
+      s = dot2_bf16(v[h].y, ones, s);
+      s = dot2_bf16(v[h].z, ones, s);
+      s = dot2_bf16(v[h].w, ones, s);
+    }
+    return group_sum_last<64 / PER>(s);
+  }
+};
+
 template <int NG>
 MOEQ_DEV void group_sums(const uint16_t* const (&xr)[kMaxNT], int nt, int g0, float (&xs)[kMaxNT]) {
-  static_assert(NG >= 1 && NG <= 16, "at most 16 groups per wavefront");
-  const int lane = threadIdx.x & 63;
-  const uint32_t ones = 0x3F803F80u;   // bf16 (1, 1): dot2 with it sums a pair
-  constexpr int PER = NG <= 8 ? 8 : 16;   // values per lane
-  const int off = g0 * 64 + PER * (lane < 64 / PER * NG ? lane : 0);
 #pragma unroll
   for (int t = 0; t < kMaxNT; ++t) {
-    float s = 0.0f;
-    if (t < nt) {
-#pragma unroll
-      for (int h = 0; h < PER / 8; ++h) {
-        const moeq_u32x4 v = *reinterpret_cast<const moeq_u32x4*>(xr[t] + off + 8 * h);
-        s = dot2_bf16(v.x, ones, s);
-        s = dot2_bf16(v.y, ones, s);
-        s = dot2_bf16(v.z, ones, s);
-        s = dot2_bf16(v.w, ones, s);
-      }
-    }
-    xs[t] = group_sum_last<64 / PER>(s);
+    GroupX<NG> gx;
+    if (t < nt) gx.load(xr[t], g0);
+    xs[t] = t < nt ? gx.sum() : 0.0f;
   }
 }
 

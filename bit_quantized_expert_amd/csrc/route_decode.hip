@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void select_group_kernel(const float* __r
   for (int t = wave; t < T; t += kWaves) {
     int bi;
     float w;
-    select_token<NS>(logits + (size_t)t * E, E, k, bi, w);
+    select_token<NS>(logits + (size_t)t * E, E, k, k, bi, w);
     if (lane < k) {
       sid[t * kS + lane] = bi;
       topk_idx[(size_t)t * k + lane] = bi;

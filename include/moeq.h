@@ -192,22 +192,22 @@ int moe_qgemv_decode(const moe_layer_desc* L, const uint16_t* x, int T,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* The whole decode layer (router, top-k, expert FFNs, combine) in three
- * launches instead of five: router logits; then the gate/up GEMV, whose
- * blocks each repeat the batch's top-k selection from the logits before
- * streaming their expert (the selection is a few microseconds of one
- * wavefront per token, cheaper than a launch between them); then per token
- * the down GEMVs of its k+S experts and their routing-weighted sum, so the
- * expert outputs stay on chip.  Dependent small launches are the decode cost
- * the pages single out (Raon-1-mini on an RTX 5070 Ti, optimisation table).
+ * launches instead of five: router logits; then the gate/up GEMV with one
+ * block per (routed assignment, row tile), whose first wavefront makes that
+ * token's selection from the logits before the block streams its expert
+ * (cheaper than a launch between them); then per token the down GEMVs of
+ * its k+S experts and their routing-weighted sum, so the expert outputs
+ * stay on chip.  Dependent small launches are the decode cost the pages
+ * single out (Raon-1-mini on an RTX 5070 Ti, optimisation table).
  * Results: logits [T][E] fp32 and topk_idx/topk_w [T][k] exactly as
  * moe_route_permute_decode gives them; out [T][H] bf16 as moe_combine gives it
  * from moe_qgemv_decode's y, up to fp32 summation order inside each expert
  * dot product (residual: as in moe_combine; may alias out).
  * x, w_router: device bf16, 16-byte aligned; bias: device fp32 [E] or NULL.
  * ws: moe_workspace_bytes(L, T) bytes (holds h, bf16 [T (k+S)][I]).
- * Limits (MOEQ_ERR_UNSUPPORTED otherwise): T <= 64, E <= 1024, T*k <= 1024,
- * k+S <= 16, H in {512, 1024, 2048, 4096}, I in {256, 512, 768, 1024}, gate and
- * up at one bit width. */
+ * Limits (MOEQ_ERR_UNSUPPORTED otherwise): T <= 64, E <= 1024, k+S <= 16,
+ * H in {512, 1024, 2048, 4096}, I in {256, 512, 768} (and 1024 with 4-bit
+ * down weights), gate and up at one bit width. */
 int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, const uint16_t* w_router,
                        const float* bias, int T, const uint16_t* residual, float* logits,
                        int32_t* topk_idx, float* topk_w, uint16_t* out,

@@ -157,6 +157,37 @@ def test_decode_forward_matches_route_and_residual(bq):
     assert torch.equal(a["out"].view(torch.uint8), d["out"].view(torch.uint8))
 
 
+@pytest.mark.parametrize("case", ["lanes", "slots", "nan_inf"])
+def test_decode_select_ties_bitexact(bq, case):
+    """The decode selection (both moe_route_permute_decode and the copy inside
+    moe_decode_forward's gate/up kernel) on logits full of exact ties, -inf
+    and NaN: ids equal the oracle's stable descending sort bit for bit.
+    Ties come from repeated router rows (identical rows give identical
+    logits), NaN and -inf from the bias."""
+    w, layer, _ = layer_for(bq, "moe_h2048_e256_k8_s1_b4")
+    base = synth.router_weight_bf16(w)[:16]
+    e = np.arange(w.E)
+    bias = np.zeros(w.E, np.float32)
+    T = 8
+    x = synth.activations_bf16(w, T, batch=13)
+    if case == "lanes":        # equal values 16 experts apart (different lanes)
+        wr = base[e % 16]
+    elif case == "slots":      # equal values in 4 neighbouring experts, repeated every 64
+        wr = base[(e // 4) % 16]
+    else:                      # zero tokens: the bias alone; six numbers (ties, -inf), then NaN in index order
+        wr = base[e % 16]
+        x = np.zeros_like(x)
+        bias[:] = np.nan
+        bias[[10, 40, 77, 130, 200, 255]] = [1.0, -np.inf, 1.0, 0.0, -np.inf, 2.0]
+    ml = bq.MoELayer(layer.q, bf16_tensor(np.ascontiguousarray(wr)), torch.from_numpy(bias).cuda(), T_max=T)
+    xt = bf16_tensor(x)
+    for fused_layer in (True, False):
+        r = ml.forward(xt, fused_layer=fused_layer, fused_route=True)
+        torch.cuda.synchronize()
+        L = r["logits"].cpu().numpy()
+        assert np.array_equal(r["idx"].cpu().numpy(), oracle.select_topk(L, w.k)), (case, fused_layer)
+
+
 @pytest.mark.parametrize("T", [1, 100, 512])
 def test_prefill_layer_small(bq, T):
     print(f"prefill 128-expert 6-bit zipf T={T}", flush=True)
