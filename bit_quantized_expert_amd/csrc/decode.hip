@@ -39,11 +39,7 @@ bool pick_shape(int K, int bits, int want, int& W, int& CW) {
 #ifndef MOEQ_DOWN_RUN
 #define MOEQ_DOWN_RUN 8
 #endif
-// moe_decode_forward's gate/up blocks serve one token each: fewer, longer
-// wavefronts per block let more blocks share a CU (measured best at 16)
-#ifndef MOEQ_FUSED_GATEUP_RUN
-#define MOEQ_FUSED_GATEUP_RUN 16
-#endif
+
 
 }  // namespace
 
@@ -107,10 +103,6 @@ extern "C" int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, co
     return set_error(MOEQ_ERR_INVALID_ARG, "moe_decode_forward: NULL pointer");
   if (!aligned16(x) || !aligned16(w_router))
     return set_error(MOEQ_ERR_MISALIGNED, "moe_decode_forward: x and w_router must be 16-byte aligned");
-  int w1, cw1;
-  if (!pick_shape(H, L->gate.bits, MOEQ_FUSED_GATEUP_RUN, w1, cw1))
-    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward: no gate/up kernel for H=%d at %d bits", H,
-                     L->gate.bits);
   const WsLayout wl = ws_layout(H, I, E, S, k, T);
   if (!ws || ws_bytes < wl.total)
     return set_error(MOEQ_ERR_WORKSPACE, "moe_decode_forward: workspace of %zu bytes, need %zu", ws_bytes, wl.total);
@@ -119,9 +111,9 @@ extern "C" int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, co
   rc = launch_router_rows(x, w_router, bias, T, H, E, logits, stream);
   if (rc != MOEQ_OK) return rc;
   switch (L->gate.bits) {
-    case 4: rc = decode_gateup_routed_b4(L, x, logits, T, w1, cw1, topk_idx, topk_w, hh, stream); break;
-    case 6: rc = decode_gateup_routed_b6(L, x, logits, T, w1, cw1, topk_idx, topk_w, hh, stream); break;
-    default: rc = decode_gateup_routed_b8(L, x, logits, T, w1, cw1, topk_idx, topk_w, hh, stream); break;
+    case 4: rc = decode_gateup_routed_b4(L, x, logits, T, topk_idx, topk_w, hh, stream); break;
+    case 6: rc = decode_gateup_routed_b6(L, x, logits, T, topk_idx, topk_w, hh, stream); break;
+    default: rc = decode_gateup_routed_b8(L, x, logits, T, topk_idx, topk_w, hh, stream); break;
   }
   if (rc != MOEQ_OK) return rc;
   switch (L->down.bits) {

@@ -1,18 +1,19 @@
 // The decode layer in three launches (moe_decode_forward):
 //
-//  1. router logits (one wavefront per router row, route_decode.hip);
-//  2. selection + gate/up: one block per (routed assignment t k + j, 64-row
+//  1. router logits (router_rows_kernel, route_decode.hip);
+//  2. gate/up: the shared experts' tiles (every token uses them, so they
+//     need no routing), then one block per (routed assignment t k + j, 64-row
 //     tile of I); its first wavefront makes the first j + 1 choices of token
-//     t from the logits (select_token), then the block streams that
-//     expert's gate and up rows for token t as gateup_rows_kernel does.  No
-//     launch sits between the router and the expert GEMV, and no block
-//     needs the selection of any other token.  h goes to the workspace in
-//     assignment order (row t (k+S) + j);
+//     t from the logits (select_token), then the block streams that expert's
+//     gate and up rows for token t as gateup_rows_kernel does.  No launch
+//     sits between the router and the expert GEMV, and no block needs the
+//     selection of any other token;
 //  3. down + combine: one block per (token, 64-row tile of H), one wavefront
 //     per expert slot of the token; each wavefront streams its expert's down
 //     rows over the whole of I, and the block adds the k+S results with the
 //     routing weights in ascending slot order, as moe_combine does.  The
 //     expert outputs never leave the chip.
+// h goes through the workspace in assignment order (row t (k+S) + j).
 //
 // Removing the dependent small launches between routing, expert GEMVs and
 // combine is the decode lever the pages report (Raon-1-mini on an RTX
@@ -29,11 +30,22 @@ constexpr int kFusedMaxT = 64;       // tokens per batch
 constexpr int kFusedMaxE = 1024;     // routed experts (select_token holds 16 per lane)
 constexpr int kFusedMaxSlots = 16;   // k + S: one wavefront per slot in the down + combine block
 
+// Gate/up block shape of the fused path for rows of H codes: W wavefronts
+// of CW chunks each; 16-chunk runs (8 at H = 512, 4-bit), so that blocks are
+// short in wavefronts and several share a CU.
+template <int BITS, int NCH>
+struct FusedShape {
+  static constexpr int CPR = NCH * 512 / Fmt<BITS>::CODES;
+  static constexpr int CW = CPR >= 32 ? 16 : CPR / 2;
+  static constexpr int W = CPR / CW;
+  static_assert(W * CW == CPR && W <= 16 && CW % Fmt<BITS>::CHUNKS_PER_GROUP == 0, "shape");
+};
+
 struct FusedGrid {
   int E, S, k, T;
   int kS;              // k + S
   int tiles;           // 64-row tiles of I
-  int shared_blocks;   // as DecodeGrid: S * tiles rounded up to 8, times ceil(T / 2)
+  int shared_blocks;   // shared-expert blocks: S * tiles rounded up to 8, times ceil(T / 2)
   int groups;          // token pairs: ceil(T / 2)
 };
 
@@ -46,31 +58,20 @@ MOEQ_DEV void select_token_any(const float* L, int E, int k, int rounds, int& id
   else select_token<16>(L, E, k, rounds, idx, w);
 }
 
-// -------------------------------------------------------------------------
-// selection + gate/up.  Grid: the shared-expert part of DecodeGrid, then one
-// block per (routed assignment, row tile), T k tiles of them.  h[a][i] =
-// bf16(silu(Wg x_t)[i] * (Wu x_t)[i]) for assignment a = t (k+S) + j.
-// -------------------------------------------------------------------------
+// One block's gate/up tile: rows tile*64 .. +63 of expert e's gate and up
+// matrices for up to two tokens, h = bf16(silu(g) u) stored to h rows a0
+// (and a1).  start() issues the first loads; finish() streams the rest.
 template <int BITS, int W, int CW>
-__global__ __launch_bounds__(64 * W, 4) void gateup_routed_kernel(const uint8_t* __restrict__ gq,
-                                                                  const uint32_t* __restrict__ gsz,
-                                                                  const uint8_t* __restrict__ uq,
-                                                                  const uint32_t* __restrict__ usz,
-                                                                  const uint16_t* __restrict__ x, int H, int I,
-                                                                  FusedGrid fg, const float* __restrict__ logits,
-                                                                  int32_t* __restrict__ topk_idx,
-                                                                  float* __restrict__ topk_w,
-                                                                  uint16_t* __restrict__ hh) {
+struct GateupTile {
   using F = Fmt<BITS>;
-  constexpr int D = CW < kDepth ? CW : kDepth;
-  __shared__ Partials<W, 2> part;
-  __shared__ int chosen;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = (int)blockIdx.x;
+  static constexpr int D = CW < kDepth ? CW : kDepth;
   Stream<BITS, 2> st;
   ChunkBuf<BITS, 2> buf[D];
-  // weights of expert e, row tile `tile`: the first D chunk loads go out at once
-  auto start = [&](int e, int tile) {
+  int tile;
+  MOEQ_DEV void start(const uint8_t* gq, const uint32_t* gsz, const uint8_t* uq, const uint32_t* usz, int H, int I,
+                      int e, int tile_) {
+    tile = tile_;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const size_t ebytes = (size_t)I * row_bytes(H, BITS), ewords = (size_t)I * (H / 64);
     const uint8_t* const qe[2] = {gq + e * ebytes, uq + e * ebytes};
     const uint32_t* const sze[2] = {gsz + e * ewords, usz + e * ewords};
@@ -78,53 +79,70 @@ __global__ __launch_bounds__(64 * W, 4) void gateup_routed_kernel(const uint8_t*
 #pragma unroll
     for (int c = 0; c < D; ++c) st.load(c, buf[c]);
     stage_fence();
-  };
-  int tile, t0, t1, nt, a0, a1;
+  }
+  MOEQ_DEV void finish(const uint16_t* x, int H, int I, int t0, int t1, int nt, int a0, int a1,
+                       Partials<W, 2>& part, uint16_t* hh) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    t0 = uniform(t0);
+    t1 = uniform(t1);
+    nt = uniform(nt);
+    const uint16_t* const xr[kMaxNT] = {x + (size_t)t0 * H, x + (size_t)t1 * H};
+    float tot[2];
+    block_pass<BITS, 2, W, CW>(st, buf, xr, nt, part, tot);
+    if (wave < nt)
+      hh[(size_t)(wave == 0 ? a0 : a1) * I + tile * 64 + lane] = (uint16_t)f32_to_bf16_bits(silu_f32(tot[0]) * tot[1]);
+  }
+};
+
+// -------------------------------------------------------------------------
+// gate/up: the shared part of DecodeGrid (each block a row tile of a shared
+// expert for a pair of tokens, the pairs of one tile on one XCD a few
+// dispatches apart), then one block per (routed assignment, row tile), T k
+// tiles of them.  h[a][i] = bf16(silu(Wg x_t)[i] * (Wu x_t)[i]) for
+// assignment a = t (k+S) + j.
+// -------------------------------------------------------------------------
+template <int BITS, int NCH>
+__global__ __launch_bounds__((64 * FusedShape<BITS, NCH>::W), 4) void gateup_routed_kernel(
+    const uint8_t* __restrict__ gq, const uint32_t* __restrict__ gsz, const uint8_t* __restrict__ uq,
+    const uint32_t* __restrict__ usz, const uint16_t* __restrict__ x, int I, FusedGrid fg,
+    const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    uint16_t* __restrict__ hh) {
+  using Sh = FusedShape<BITS, NCH>;
+  constexpr int H = NCH * 512;
+  __shared__ Partials<Sh::W, 2> part;
+  __shared__ int chosen;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = (int)blockIdx.x;
+  GateupTile<BITS, Sh::W, Sh::CW> gt;
   if (b < fg.shared_blocks) {
     const int span = 8 * fg.groups;
     const int l = (b / span) * 8 + (b % 8);   // (shared expert, row tile)
     if (l >= fg.S * fg.tiles) return;
     const int pair = (b % span) / 8;
     const int s = l / fg.tiles;
-    tile = l % fg.tiles;
-    start(fg.E + s, tile);
-    t0 = 2 * pair;
-    nt = min(2, fg.T - t0);
-    t1 = nt > 1 ? t0 + 1 : t0;
-    a0 = t0 * fg.kS + fg.k + s;
-    a1 = t1 * fg.kS + fg.k + s;
-  } else {
-    // wavefront 0 makes the first j + 1 choices of token t (all k, and the
-    // weights, in the block that stores them for the down + combine kernel)
-    const int r = b - fg.shared_blocks;
-    const int a = r / fg.tiles, t = a / fg.k, j = a % fg.k;
-    tile = r % fg.tiles;
-    const bool writer = j == 0 && tile == 0;
-    if (wave == 0) {
-      int bi;
-      float w;
-      select_token_any(logits + (size_t)t * fg.E, fg.E, fg.k, writer ? fg.k : j + 1, bi, w);
-      if (writer && lane < fg.k) {
-        topk_idx[(size_t)t * fg.k + lane] = bi;
-        topk_w[(size_t)t * fg.k + lane] = w;
-      }
-      if (lane == 0) chosen = __builtin_amdgcn_readlane(bi, j);
-    }
-    __syncthreads();
-    start(uniform(chosen), tile);
-    t0 = t1 = t;
-    nt = 1;
-    a0 = a1 = t * fg.kS + j;
+    gt.start(gq, gsz, uq, usz, H, I, fg.E + s, l % fg.tiles);
+    const int t0 = 2 * pair, nt = min(2, fg.T - t0), t1 = nt > 1 ? t0 + 1 : t0;
+    gt.finish(x, H, I, t0, t1, nt, t0 * fg.kS + fg.k + s, t1 * fg.kS + fg.k + s, part, hh);
+    return;
   }
-  tile = uniform(tile);
-  t0 = uniform(t0);
-  t1 = uniform(t1);
-  nt = uniform(nt);
-  const uint16_t* const xr[kMaxNT] = {x + (size_t)t0 * H, x + (size_t)t1 * H};
-  float tot[2];
-  block_pass<BITS, 2, W, CW>(st, buf, xr, nt, part, tot);
-  if (wave < nt)
-    hh[(size_t)(wave == 0 ? a0 : a1) * I + tile * 64 + lane] = (uint16_t)f32_to_bf16_bits(silu_f32(tot[0]) * tot[1]);
+  const int r = b - fg.shared_blocks;
+  const int a = r / fg.tiles, t = a / fg.k, j = a % fg.k, tile = r % fg.tiles;
+  // wavefront 0 makes the first j + 1 choices of token t (all k, and the
+  // weights, in the block that stores them for the down + combine kernel)
+  const bool writer = j == 0 && tile == 0;
+  if (wave == 0) {
+    int bi;
+    float w;
+    select_token_any(logits + (size_t)t * fg.E, fg.E, fg.k, writer ? fg.k : j + 1, bi, w);
+    if (writer && lane < fg.k) {
+      topk_idx[(size_t)t * fg.k + lane] = bi;
+      topk_w[(size_t)t * fg.k + lane] = w;
+    }
+    if (lane == 0) chosen = __builtin_amdgcn_readlane(bi, j);
+  }
+  __syncthreads();
+  gt.start(gq, gsz, uq, usz, H, I, uniform(chosen), tile);
+  gt.finish(x, H, I, t, t, 1, t * fg.kS + j, t * fg.kS + j, part, hh);
 }
 
 // -------------------------------------------------------------------------
@@ -202,8 +220,7 @@ __global__ __launch_bounds__(64 * kFusedMaxSlots) void down_combine_kernel(const
 // Launchers per bit width (decode_b{4,6,8}.hip).
 #define MOEQ_DECODE_FUSED_LAUNCHERS(B)                                                                     \
   int decode_gateup_routed_b##B(const moe_layer_desc* L, const uint16_t* x, const float* logits, int T,     \
-                                int W, int CW, int32_t* topk_idx, float* topk_w, uint16_t* hh,             \
-                                hipStream_t s);                                                            \
+                                int32_t* topk_idx, float* topk_w, uint16_t* hh, hipStream_t s);            \
   int decode_down_combine_b##B(const moe_layer_desc* L, const uint16_t* hh, int T, const int32_t* topk_idx, \
                                const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t s)
 
@@ -222,6 +239,31 @@ inline decode_detail::FusedGrid fused_grid(const moe_layer_desc* L, int T) {
   fg.groups = (T + 1) / 2;
   fg.shared_blocks = L->S > 0 ? (L->S * fg.tiles + 7) / 8 * 8 * fg.groups : 0;
   return fg;
+}
+
+// Runs fn(std::integral_constant<int, NCH>) for H = 512 NCH, NCH in {1, 2, 4, 8}.
+template <class Fn>
+int with_nch(int H, Fn&& fn) {
+  switch (H) {
+    case 512: return fn(std::integral_constant<int, 1>());
+    case 1024: return fn(std::integral_constant<int, 2>());
+    case 2048: return fn(std::integral_constant<int, 4>());
+    case 4096: return fn(std::integral_constant<int, 8>());
+    default: return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward: H=%d not in {512, 1024, 2048, 4096}", H);
+  }
+}
+
+template <int B>
+int launch_gateup_routed(const moe_layer_desc* L, const uint16_t* x, const float* logits, int T, int32_t* topk_idx,
+                         float* topk_w, uint16_t* hh, hipStream_t s) {
+  return with_nch(L->H, [&](auto nch) {
+    constexpr int NCH = decltype(nch)::value;
+    const decode_detail::FusedGrid fg = fused_grid(L, T);
+    decode_detail::gateup_routed_kernel<B, NCH><<<fg.shared_blocks + T * L->k * fg.tiles, 64 * decode_detail::FusedShape<B, NCH>::W,
+                                                 0, s>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->I, fg,
+                                                         logits, topk_idx, topk_w, hh);
+    return check_launch("moe_decode_forward (selection + gate/up)");
+  });
 }
 
 // One down + combine launch: I / 64 groups in {4, 8, 12}, and 16 at 4 bits
@@ -254,14 +296,8 @@ int launch_down_combine(const moe_layer_desc* L, const uint16_t* hh, int T, cons
 
 #define MOEQ_DEFINE_DECODE_FUSED(B)                                                                        \
   int decode_gateup_routed_b##B(const moe_layer_desc* L, const uint16_t* x, const float* logits, int T,     \
-                                int W, int CW, int32_t* topk_idx, float* topk_w, uint16_t* hh,             \
-                                hipStream_t s) {                                                           \
-    const decode_detail::FusedGrid fg = fused_grid(L, T);                                                  \
-    const int grid = fg.shared_blocks + T * L->k * fg.tiles;                                               \
-    bool launched = false;                                                                                 \
-    MOEQ_DECODE_SHAPES(MOEQ_LAUNCH_GUR)                                                                    \
-    if (!launched) return set_error(MOEQ_ERR_UNSUPPORTED, "decode: no gate/up kernel for W=%d CW=%d", W, CW); \
-    return check_launch("moe_decode_forward (routing + gate/up)");                                         \
+                                int32_t* topk_idx, float* topk_w, uint16_t* hh, hipStream_t s) {           \
+    return launch_gateup_routed<B>(L, x, logits, T, topk_idx, topk_w, hh, s);                              \
   }                                                                                                        \
   int decode_down_combine_b##B(const moe_layer_desc* L, const uint16_t* hh, int T, const int32_t* topk_idx, \
                                const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t s) { \

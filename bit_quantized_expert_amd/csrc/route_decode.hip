@@ -3,15 +3,16 @@
 // latency (decode is where small launches dominate: Raon-1-mini on an RTX
 // 5070 Ti, optimisation table).
 //
-//  1. router_rows_kernel: one wavefront (one 64-thread block) per router row;
-//     the row is loaded once into registers, the tokens come straight from
-//     global memory (they stay in L2), dot products in fp32 via dot2, DPP
-//     reduction.  Many tiny blocks spread the row loads over every CU.
+//  1. router_rows_kernel: one wavefront (one 64-thread block) per router row
+//     (router_row, router.h): the row is loaded once into registers, the
+//     tokens come straight from global memory (they stay in L2), dot
+//     products in fp32 via dot2, DPP reduction.  Many tiny blocks spread the
+//     row loads over every CU.
 //  2. select_group_kernel: one block of 16 wavefronts; each wavefront selects
 //     the top k of one token (candidates in registers, DPP arg-max), then
 //     the block groups the assignments by expert exactly as moe_permute does.
 // The kernel boundary orders the two; no cross-block synchronisation.
-#include "format.h"
+#include "router.h"
 
 using namespace moeq;
 
@@ -23,46 +24,12 @@ constexpr int kMaxRowChunks = 8;                 // H <= 4096 (8 x 16 B per lane
 constexpr int kMaxA = 1024;
 constexpr int kMaxExp = 1024;
 
-// tokens whose activations are loaded together (at most 128 registers of them)
-constexpr int tok_group(int nch) { return nch <= 4 ? 8 : 4; }
-
 template <int NCH>
 __global__ __launch_bounds__(64) void router_rows_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ wr,
                                                          const float* __restrict__ bias, int T, int E,
                                                          float* __restrict__ logits) {
-  const int lane = threadIdx.x;
-  const int e = blockIdx.x;
-  constexpr int H = NCH * 512;
-  moeq_u32x4 w4[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) w4[i] = *reinterpret_cast<const moeq_u32x4*>(wr + (size_t)e * H + 8 * (lane + 64 * i));
-  const float be = bias ? bias[e] : 0.0f;
-  constexpr int kTokGroup = tok_group(NCH);
-  for (int t0 = 0; t0 < T; t0 += kTokGroup) {
-    // every activation load of the group is issued before the first use
-    moeq_u32x4 xv[kTokGroup][NCH];
-#pragma unroll
-    for (int u = 0; u < kTokGroup; ++u) {
-      const int t = min(t0 + u, T - 1);   // past the end: repeat the last token, never stored
-#pragma unroll
-      for (int i = 0; i < NCH; ++i)
-        xv[u][i] = *reinterpret_cast<const moeq_u32x4*>(x + (size_t)t * H + 8 * (lane + 64 * i));
-    }
-#pragma unroll
-    for (int u = 0; u < kTokGroup; ++u) {
-      float a = 0.0f;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        a = dot2_bf16(w4[i].x, xv[u][i].x, a);
-        a = dot2_bf16(w4[i].y, xv[u][i].y, a);
-        a = dot2_bf16(w4[i].z, xv[u][i].z, a);
-        a = dot2_bf16(w4[i].w, xv[u][i].w, a);
-      }
-      a = group_sum_last<64>(a);
-      if (lane == 63 && t0 + u < T) logits[(size_t)(t0 + u) * E + e] = a + be;
-    }
-  }
+  router_row<NCH>(x, wr, bias, T, E, (int)blockIdx.x, logits);
 }
 
 MOEQ_DEV int block_excl_scan(int v, int* tmp, int& total) {
