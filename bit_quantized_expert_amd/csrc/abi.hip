@@ -44,6 +44,9 @@ WsLayout ws_layout(int H, int I, int E, int S, int k, int T_max) {
   off = align_up(off + (size_t)(prefill_max_tiles(A, nexp) + 4) * 2 * sizeof(int32_t), 256);
   w.h = off;
   off = align_up(off + (size_t)A * I * sizeof(float), 256);   // fp32 covers bf16 too
+  w.shared_part = off;   // [S][T][slice][gate, up][I]
+  const long Tf = T_max < kFusedMaxTokens ? T_max : kFusedMaxTokens;
+  off = align_up(off + (size_t)S * Tf * kSharedMaxSplit * 2 * I * sizeof(float), 256);
   w.total = off;
   return w;
 }

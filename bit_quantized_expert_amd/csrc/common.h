@@ -34,10 +34,13 @@ struct WsLayout {
   size_t perm_hist;  // int32 [perm_blocks][E+S] block histograms
   size_t h;          // decode: fp32 [A][I]; prefill: bf16 [A][I]
   size_t sched;      // prefill: int32 tile schedule
+  size_t shared_part;   // moe_decode_forward: fp32 partial gate/up sums of the shared experts
   size_t total;
 };
 constexpr int kPermBlock = 1024;          // assignments per permute block
 constexpr int kPrefillBM = 128;           // prefill token tile
+constexpr int kFusedMaxTokens = 64;       // moe_decode_forward batches
+constexpr int kSharedMaxSplit = 16;       // moe_decode_forward: K slices of a shared-expert row
 int perm_blocks(long A);
 long prefill_max_tiles(long A, int nexp);
 WsLayout ws_layout(int H, int I, int E, int S, int k, int T_max);

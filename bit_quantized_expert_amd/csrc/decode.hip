@@ -108,12 +108,17 @@ extern "C" int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, co
     return set_error(MOEQ_ERR_WORKSPACE, "moe_decode_forward: workspace of %zu bytes, need %zu", ws_bytes, wl.total);
   // h: bf16 [T (k+S)][I], rows in assignment order
   uint16_t* hh = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.h);
-  rc = launch_router_rows(x, w_router, bias, T, H, E, logits, stream);
+  float* spart = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.shared_part);
+  switch (L->gate.bits) {
+    case 4: rc = decode_router_shared_b4(L, x, w_router, bias, T, logits, spart, stream); break;
+    case 6: rc = decode_router_shared_b6(L, x, w_router, bias, T, logits, spart, stream); break;
+    default: rc = decode_router_shared_b8(L, x, w_router, bias, T, logits, spart, stream); break;
+  }
   if (rc != MOEQ_OK) return rc;
   switch (L->gate.bits) {
-    case 4: rc = decode_gateup_routed_b4(L, x, logits, T, topk_idx, topk_w, hh, stream); break;
-    case 6: rc = decode_gateup_routed_b6(L, x, logits, T, topk_idx, topk_w, hh, stream); break;
-    default: rc = decode_gateup_routed_b8(L, x, logits, T, topk_idx, topk_w, hh, stream); break;
+    case 4: rc = decode_gateup_routed_b4(L, x, logits, spart, T, topk_idx, topk_w, hh, stream); break;
+    case 6: rc = decode_gateup_routed_b6(L, x, logits, spart, T, topk_idx, topk_w, hh, stream); break;
+    default: rc = decode_gateup_routed_b8(L, x, logits, spart, T, topk_idx, topk_w, hh, stream); break;
   }
   if (rc != MOEQ_OK) return rc;
   switch (L->down.bits) {

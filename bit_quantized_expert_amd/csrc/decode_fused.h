@@ -1,13 +1,19 @@
 // The decode layer in three launches (moe_decode_forward):
 //
-//  1. router logits (router_rows_kernel, route_decode.hip);
-//  2. gate/up: the shared experts' tiles (every token uses them, so they
-//     need no routing), then one block per (routed assignment t k + j, 64-row
-//     tile of I); its first wavefront makes the first j + 1 choices of token
-//     t from the logits (select_token), then the block streams that expert's
-//     gate and up rows for token t as gateup_rows_kernel does.  No launch
-//     sits between the router and the expert GEMV, and no block needs the
-//     selection of any other token;
+//  1. router + shared experts: blocks of four wavefronts, one router row per
+//     wavefront (router_row), and the shared experts' gate/up rows, which
+//     every token uses and so need no routing: one block per (shared
+//     expert, 64-row tile, K slice, pair of tokens) writes partial sums;
+//  2. selection + routed gate/up: one block per (routed assignment
+//     t k + j, 64-row tile of I); its first wavefront makes the first j + 1
+//     choices of token t from the logits (select_token), then the block
+//     streams that expert's gate and up rows for token t as
+//     gateup_rows_kernel does.  Meanwhile the blocks of slot 0 add up the
+//     shared experts' slices for their token and tile into h.  No launch
+//     sits between the router and the expert GEMV, no block needs the
+//     selection of any other token, and every block carries the same work,
+//     T k tiles of them (shared-expert tiles here would leave some CUs one
+//     block more than the rest, and the launch waiting on those);
 //  3. down + combine: one block per (token, 64-row tile of H), one wavefront
 //     per expert slot of the token; each wavefront streams its expert's down
 //     rows over the whole of I, and the block adds the k+S results with the
@@ -22,11 +28,12 @@
 // that share an XCD (so mostly from its L2 after the first).
 #pragma once
 #include "decode_impl.h"
+#include "router.h"
 
 namespace moeq {
 namespace decode_detail {
 
-constexpr int kFusedMaxT = 64;       // tokens per batch
+constexpr int kFusedMaxT = kFusedMaxTokens;   // tokens per batch
 constexpr int kFusedMaxE = 1024;     // routed experts (select_token holds 16 per lane)
 constexpr int kFusedMaxSlots = 16;   // k + S: one wavefront per slot in the down + combine block
 
@@ -41,11 +48,22 @@ struct FusedShape {
   static_assert(W * CW == CPR && W <= 16 && CW % Fmt<BITS>::CHUNKS_PER_GROUP == 0, "shape");
 };
 
+// Shared-expert gate/up in launch 1: blocks of four wavefronts of CW = 4
+// chunks each, so a block covers one K slice of 16 chunks; Q slices per row.
+template <int BITS, int NCH>
+struct SharedShape {
+  static constexpr int W = 4, CW = 4;
+  static constexpr int Q = NCH * 512 / Fmt<BITS>::CODES / (W * CW);
+  static_assert(Q >= 1 && Q <= kSharedMaxSplit && CW % Fmt<BITS>::CHUNKS_PER_GROUP == 0, "shape");
+};
+
 struct FusedGrid {
   int E, S, k, T;
   int kS;              // k + S
   int tiles;           // 64-row tiles of I
-  int shared_blocks;   // shared-expert blocks: S * tiles rounded up to 8, times ceil(T / 2)
+  int router_blocks;   // launch 1: blocks of four router rows (a multiple of 8)
+  int shared_blocks;   // launch 1: S tiles Q slices rounded up to 8, times ceil(T / 2)
+  int Q;               // K slices of a shared-expert row
   int groups;          // token pairs: ceil(T / 2)
 };
 
@@ -95,38 +113,81 @@ struct GateupTile {
 };
 
 // -------------------------------------------------------------------------
-// gate/up: the shared part of DecodeGrid (each block a row tile of a shared
-// expert for a pair of tokens, the pairs of one tile on one XCD a few
-// dispatches apart), then one block per (routed assignment, row tile), T k
-// tiles of them.  h[a][i] = bf16(silu(Wg x_t)[i] * (Wu x_t)[i]) for
-// assignment a = t (k+S) + j.
+// launch 1: router rows, then the shared experts' gate/up slices: block
+// (shared expert s, row tile, K slice q, token pair) writes, for each of
+// its tokens t, the slice's sums part[s][t][q][gate, up][row] (fp32).  The
+// pairs of one (s, tile, q) land on one XCD a few dispatches apart, so the
+// weights they all read come from its L2 after the first.
+// -------------------------------------------------------------------------
+template <int BITS, int NCH>
+__global__ __launch_bounds__(256) void router_shared_kernel(const uint16_t* __restrict__ wr,
+                                                            const float* __restrict__ bias,
+                                                            const uint8_t* __restrict__ gq,
+                                                            const uint32_t* __restrict__ gsz,
+                                                            const uint8_t* __restrict__ uq,
+                                                            const uint32_t* __restrict__ usz,
+                                                            const uint16_t* __restrict__ x, int I, FusedGrid fg,
+                                                            float* __restrict__ logits, float* __restrict__ spart) {
+  using Sh = SharedShape<BITS, NCH>;
+  constexpr int H = NCH * 512;
+  __shared__ Partials<Sh::W, 2> part;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = (int)blockIdx.x;
+  if (b < fg.router_blocks) {
+    const int e = b * 4 + wave;
+    if (e < fg.E) router_row<NCH>(x, wr, bias, fg.T, fg.E, e, logits);
+    return;
+  }
+  const int bs = b - fg.router_blocks;
+  const int span = 8 * fg.groups;
+  const int l = (bs / span) * 8 + (bs % 8);   // (shared expert, row tile, slice)
+  if (l >= fg.S * fg.tiles * Sh::Q) return;
+  const int pair = (bs % span) / 8;
+  const int s = l / (fg.tiles * Sh::Q), tile = (l / Sh::Q) % fg.tiles, q = l % Sh::Q;
+  Stream<BITS, 2> st;
+  ChunkBuf<BITS, 2> buf[Sh::CW];
+  {
+    const size_t ebytes = (size_t)I * row_bytes(H, BITS), ewords = (size_t)I * (H / 64);
+    const int e = fg.E + s;
+    const uint8_t* const qe[2] = {gq + e * ebytes, uq + e * ebytes};
+    const uint32_t* const sze[2] = {gsz + e * ewords, usz + e * ewords};
+    st.init(qe, sze, H / Fmt<BITS>::CODES, H / 64, tile, (q * Sh::W + wave) * Sh::CW);
+#pragma unroll
+    for (int c = 0; c < Sh::CW; ++c) st.load(c, buf[c]);
+    stage_fence();
+  }
+  const int t0 = 2 * pair, nt = uniform(min(2, fg.T - t0)), t1 = nt > 1 ? t0 + 1 : t0;
+  const uint16_t* const xr[kMaxNT] = {x + (size_t)t0 * H, x + (size_t)t1 * H};
+  float tot[2];
+  block_pass<BITS, 2, Sh::W, Sh::CW>(st, buf, xr, nt, part, tot);
+  if (wave < nt) {
+    float* p = spart + ((((size_t)s * fg.T + t0 + wave) * Sh::Q + q) * 2) * I + tile * 64 + lane;
+    p[0] = tot[0];
+    p[I] = tot[1];
+  }
+}
+
+// -------------------------------------------------------------------------
+// launch 2: selection + routed gate/up, one block per (routed assignment,
+// row tile), T k tiles of them.  h[a][i] = bf16(silu(Wg x_t)[i] *
+// (Wu x_t)[i]) for assignment a = t (k+S) + j.  The blocks of slot 0 also
+// finish the shared experts' h rows of their token and tile from launch 1's
+// slices (summed in slice order).
 // -------------------------------------------------------------------------
 template <int BITS, int NCH>
 __global__ __launch_bounds__((64 * FusedShape<BITS, NCH>::W), 4) void gateup_routed_kernel(
     const uint8_t* __restrict__ gq, const uint32_t* __restrict__ gsz, const uint8_t* __restrict__ uq,
     const uint32_t* __restrict__ usz, const uint16_t* __restrict__ x, int I, FusedGrid fg,
-    const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    uint16_t* __restrict__ hh) {
+    const float* __restrict__ logits, const float* __restrict__ spart, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, uint16_t* __restrict__ hh) {
   using Sh = FusedShape<BITS, NCH>;
+  static_assert(Sh::W >= 2, "a second wavefront finishes the shared rows");
   constexpr int H = NCH * 512;
   __shared__ Partials<Sh::W, 2> part;
   __shared__ int chosen;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = (int)blockIdx.x;
-  GateupTile<BITS, Sh::W, Sh::CW> gt;
-  if (b < fg.shared_blocks) {
-    const int span = 8 * fg.groups;
-    const int l = (b / span) * 8 + (b % 8);   // (shared expert, row tile)
-    if (l >= fg.S * fg.tiles) return;
-    const int pair = (b % span) / 8;
-    const int s = l / fg.tiles;
-    gt.start(gq, gsz, uq, usz, H, I, fg.E + s, l % fg.tiles);
-    const int t0 = 2 * pair, nt = min(2, fg.T - t0), t1 = nt > 1 ? t0 + 1 : t0;
-    gt.finish(x, H, I, t0, t1, nt, t0 * fg.kS + fg.k + s, t1 * fg.kS + fg.k + s, part, hh);
-    return;
-  }
-  const int r = b - fg.shared_blocks;
-  const int a = r / fg.tiles, t = a / fg.k, j = a % fg.k, tile = r % fg.tiles;
+  const int a = b / fg.tiles, t = a / fg.k, j = a % fg.k, tile = b % fg.tiles;
   // wavefront 0 makes the first j + 1 choices of token t (all k, and the
   // weights, in the block that stores them for the down + combine kernel)
   const bool writer = j == 0 && tile == 0;
@@ -139,8 +200,19 @@ __global__ __launch_bounds__((64 * FusedShape<BITS, NCH>::W), 4) void gateup_rou
       topk_w[(size_t)t * fg.k + lane] = w;
     }
     if (lane == 0) chosen = __builtin_amdgcn_readlane(bi, j);
+  } else if (wave == 1 && j == 0) {
+    for (int s = 0; s < fg.S; ++s) {
+      const float* p = spart + (((size_t)s * fg.T + t) * fg.Q * 2) * I + tile * 64 + lane;
+      float g = 0.0f, u = 0.0f;
+      for (int q = 0; q < fg.Q; ++q) {
+        g += p[(size_t)q * 2 * I];
+        u += p[(size_t)q * 2 * I + I];
+      }
+      hh[(size_t)(t * fg.kS + fg.k + s) * I + tile * 64 + lane] = (uint16_t)f32_to_bf16_bits(silu_f32(g) * u);
+    }
   }
   __syncthreads();
+  GateupTile<BITS, Sh::W, Sh::CW> gt;
   gt.start(gq, gsz, uq, usz, H, I, uniform(chosen), tile);
   gt.finish(x, H, I, t, t, 1, t * fg.kS + j, t * fg.kS + j, part, hh);
 }
@@ -219,8 +291,11 @@ __global__ __launch_bounds__(64 * kFusedMaxSlots) void down_combine_kernel(const
 
 // Launchers per bit width (decode_b{4,6,8}.hip).
 #define MOEQ_DECODE_FUSED_LAUNCHERS(B)                                                                     \
-  int decode_gateup_routed_b##B(const moe_layer_desc* L, const uint16_t* x, const float* logits, int T,     \
-                                int32_t* topk_idx, float* topk_w, uint16_t* hh, hipStream_t s);            \
+  int decode_router_shared_b##B(const moe_layer_desc* L, const uint16_t* x, const uint16_t* wr,           \
+                                const float* bias, int T, float* logits, float* spart, hipStream_t s);     \
+  int decode_gateup_routed_b##B(const moe_layer_desc* L, const uint16_t* x, const float* logits,          \
+                                const float* spart, int T, int32_t* topk_idx, float* topk_w, uint16_t* hh, \
+                                hipStream_t s);                                                            \
   int decode_down_combine_b##B(const moe_layer_desc* L, const uint16_t* hh, int T, const int32_t* topk_idx, \
                                const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t s)
 
@@ -228,7 +303,8 @@ MOEQ_DECODE_FUSED_LAUNCHERS(4);
 MOEQ_DECODE_FUSED_LAUNCHERS(6);
 MOEQ_DECODE_FUSED_LAUNCHERS(8);
 
-inline decode_detail::FusedGrid fused_grid(const moe_layer_desc* L, int T) {
+template <int B, int NCH>
+decode_detail::FusedGrid fused_grid(const moe_layer_desc* L, int T) {
   decode_detail::FusedGrid fg;
   fg.E = L->E;
   fg.S = L->S;
@@ -237,7 +313,9 @@ inline decode_detail::FusedGrid fused_grid(const moe_layer_desc* L, int T) {
   fg.kS = L->k + L->S;
   fg.tiles = L->I / 64;
   fg.groups = (T + 1) / 2;
-  fg.shared_blocks = L->S > 0 ? (L->S * fg.tiles + 7) / 8 * 8 * fg.groups : 0;
+  fg.Q = decode_detail::SharedShape<B, NCH>::Q;
+  fg.router_blocks = ((L->E + 3) / 4 + 7) / 8 * 8;
+  fg.shared_blocks = L->S > 0 ? (L->S * fg.tiles * fg.Q + 7) / 8 * 8 * fg.groups : 0;
   return fg;
 }
 
@@ -254,15 +332,27 @@ int with_nch(int H, Fn&& fn) {
 }
 
 template <int B>
-int launch_gateup_routed(const moe_layer_desc* L, const uint16_t* x, const float* logits, int T, int32_t* topk_idx,
-                         float* topk_w, uint16_t* hh, hipStream_t s) {
+int launch_router_shared(const moe_layer_desc* L, const uint16_t* x, const uint16_t* wr, const float* bias, int T,
+                         float* logits, float* spart, hipStream_t s) {
   return with_nch(L->H, [&](auto nch) {
     constexpr int NCH = decltype(nch)::value;
-    const decode_detail::FusedGrid fg = fused_grid(L, T);
-    decode_detail::gateup_routed_kernel<B, NCH><<<fg.shared_blocks + T * L->k * fg.tiles, 64 * decode_detail::FusedShape<B, NCH>::W,
+    const decode_detail::FusedGrid fg = fused_grid<B, NCH>(L, T);
+    decode_detail::router_shared_kernel<B, NCH><<<fg.router_blocks + fg.shared_blocks, 256, 0, s>>>(
+        wr, bias, L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->I, fg, logits, spart);
+    return check_launch("moe_decode_forward (router + shared gate/up)");
+  });
+}
+
+template <int B>
+int launch_gateup_routed(const moe_layer_desc* L, const uint16_t* x, const float* logits, const float* spart, int T,
+                         int32_t* topk_idx, float* topk_w, uint16_t* hh, hipStream_t s) {
+  return with_nch(L->H, [&](auto nch) {
+    constexpr int NCH = decltype(nch)::value;
+    const decode_detail::FusedGrid fg = fused_grid<B, NCH>(L, T);
+    decode_detail::gateup_routed_kernel<B, NCH><<<T * L->k * fg.tiles, 64 * decode_detail::FusedShape<B, NCH>::W,
                                                  0, s>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->I, fg,
-                                                         logits, topk_idx, topk_w, hh);
-    return check_launch("moe_decode_forward (selection + gate/up)");
+                                                         logits, spart, topk_idx, topk_w, hh);
+    return check_launch("moe_decode_forward (selection + routed gate/up)");
   });
 }
 
@@ -272,7 +362,7 @@ int launch_gateup_routed(const moe_layer_desc* L, const uint16_t* x, const float
 template <int B>
 int launch_down_combine(const moe_layer_desc* L, const uint16_t* hh, int T, const int32_t* topk_idx,
                         const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t s) {
-  const decode_detail::FusedGrid fg = fused_grid(L, T);
+  const decode_detail::FusedGrid fg = fused_grid<B, 1>(L, T);
   const int grid = T * (L->H / 64), threads = 64 * fg.kS;
   auto go = [&](auto ng) {
     decode_detail::down_combine_kernel<B, decltype(ng)::value><<<grid, threads, 0, s>>>(
@@ -295,9 +385,14 @@ int launch_down_combine(const moe_layer_desc* L, const uint16_t* hh, int T, cons
 }
 
 #define MOEQ_DEFINE_DECODE_FUSED(B)                                                                        \
-  int decode_gateup_routed_b##B(const moe_layer_desc* L, const uint16_t* x, const float* logits, int T,     \
-                                int32_t* topk_idx, float* topk_w, uint16_t* hh, hipStream_t s) {           \
-    return launch_gateup_routed<B>(L, x, logits, T, topk_idx, topk_w, hh, s);                              \
+  int decode_router_shared_b##B(const moe_layer_desc* L, const uint16_t* x, const uint16_t* wr,           \
+                                const float* bias, int T, float* logits, float* spart, hipStream_t s) {    \
+    return launch_router_shared<B>(L, x, wr, bias, T, logits, spart, s);                                   \
+  }                                                                                                        \
+  int decode_gateup_routed_b##B(const moe_layer_desc* L, const uint16_t* x, const float* logits,          \
+                                const float* spart, int T, int32_t* topk_idx, float* topk_w, uint16_t* hh, \
+                                hipStream_t s) {                                                           \
+    return launch_gateup_routed<B>(L, x, logits, spart, T, topk_idx, topk_w, hh, s);                       \
   }                                                                                                        \
   int decode_down_combine_b##B(const moe_layer_desc* L, const uint16_t* hh, int T, const int32_t* topk_idx, \
                                const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t s) { \
