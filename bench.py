@@ -211,6 +211,20 @@ class StackStep:
             st.run(s)
 
 
+def build_stack(bq, w, device):
+    """All blocks of the stacked workload, each with its own weights and bit
+    width (quantised on the device)."""
+    import torch
+    from tests.gpu_util import bf16_tensor, gpu_layer
+    bits = synth.layer_bits(w)
+    layers, wrs = [], []
+    for l, b in enumerate(bits):
+        layers.append(gpu_layer(w, layer=l, bits=b, device=device))
+        wrs.append(bf16_tensor(synth.router_weight_bf16(w, layer=l), device=device))
+    torch.cuda.synchronize()
+    return layers, wrs, bits
+
+
 def main_stack(a, w, bq, dev):
     """Stacked decode: 256 consecutive batch-1 tokens through all blocks,
     one HIP graph per token step, timed end to end."""
