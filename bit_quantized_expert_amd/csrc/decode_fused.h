@@ -37,13 +37,18 @@ constexpr int kFusedMaxT = kFusedMaxTokens;   // tokens per batch
 constexpr int kFusedMaxE = 1024;     // routed experts (select_token holds 16 per lane)
 constexpr int kFusedMaxSlots = 16;   // k + S: one wavefront per slot in the down + combine block
 
+constexpr int cmax_i(int a, int b) { return a > b ? a : b; }
+
 // Gate/up block shape of the fused path for rows of H codes: W wavefronts
 // of CW chunks each; 16-chunk runs (8 at H = 512, 4-bit), so that blocks are
 // short in wavefronts and several share a CU.
 template <int BITS, int NCH>
 struct FusedShape {
   static constexpr int CPR = NCH * 512 / Fmt<BITS>::CODES;
-  static constexpr int CW = CPR >= 32 ? 16 : CPR / 2;
+#ifndef MOEQ_FUSED_RUN
+#define MOEQ_FUSED_RUN 16
+#endif
+  static constexpr int CW = CPR >= 2 * MOEQ_FUSED_RUN ? cmax_i(MOEQ_FUSED_RUN, CPR / 16) : CPR / 2;
   static constexpr int W = CPR / CW;
   static_assert(W * CW == CPR && W <= 16 && CW % Fmt<BITS>::CHUNKS_PER_GROUP == 0, "shape");
 };
