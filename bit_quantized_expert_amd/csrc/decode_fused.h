@@ -68,6 +68,8 @@ struct FusedGrid {
   int tiles;           // 64-row tiles of I
   int router_blocks;   // launch 1: blocks of four router rows (a multiple of 8)
   int shared_blocks;   // launch 1: S tiles Q slices rounded up to 8, times ceil(T / 2)
+  int shared_late;     // shared experts in launch 2 instead (whole rows, as extra blocks)
+  int late_blocks;     // launch 2: S tiles rounded up to 8, times ceil(T / 2), if shared_late
   int Q;               // K slices of a shared-expert row
   int groups;          // token pairs: ceil(T / 2)
 };
@@ -192,6 +194,21 @@ __global__ __launch_bounds__((64 * FusedShape<BITS, NCH>::W), 4) void gateup_rou
   __shared__ int chosen;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = (int)blockIdx.x;
+  GateupTile<BITS, Sh::W, Sh::CW> gt;
+  const int routed = fg.T * fg.k * fg.tiles;
+  if (b >= routed) {
+    // a shared expert's tile for a pair of tokens, whole rows (small
+    // batches: the launch has CUs to spare); the pairs of one tile on one
+    // XCD a few dispatches apart
+    const int bs = b - routed, span = 8 * fg.groups;
+    const int l = (bs / span) * 8 + (bs % 8);
+    if (l >= fg.S * fg.tiles) return;
+    const int pair = (bs % span) / 8, s = l / fg.tiles;
+    gt.start(gq, gsz, uq, usz, H, I, fg.E + s, l % fg.tiles);
+    const int t0 = 2 * pair, nt = min(2, fg.T - t0), t1 = nt > 1 ? t0 + 1 : t0;
+    gt.finish(x, H, I, t0, t1, nt, t0 * fg.kS + fg.k + s, t1 * fg.kS + fg.k + s, part, hh);
+    return;
+  }
   const int a = b / fg.tiles, t = a / fg.k, j = a % fg.k, tile = b % fg.tiles;
   // wavefront 0 makes the first j + 1 choices of token t (all k, and the
   // weights, in the block that stores them for the down + combine kernel)
@@ -205,7 +222,7 @@ __global__ __launch_bounds__((64 * FusedShape<BITS, NCH>::W), 4) void gateup_rou
       topk_w[(size_t)t * fg.k + lane] = w;
     }
     if (lane == 0) chosen = __builtin_amdgcn_readlane(bi, j);
-  } else if (wave == 1 && j == 0) {
+  } else if (wave == 1 && j == 0 && !fg.shared_late) {
     for (int s = 0; s < fg.S; ++s) {
       const float* p = spart + (((size_t)s * fg.T + t) * fg.Q * 2) * I + tile * 64 + lane;
       float g = 0.0f, u = 0.0f;
@@ -217,7 +234,6 @@ __global__ __launch_bounds__((64 * FusedShape<BITS, NCH>::W), 4) void gateup_rou
     }
   }
   __syncthreads();
-  GateupTile<BITS, Sh::W, Sh::CW> gt;
   gt.start(gq, gsz, uq, usz, H, I, uniform(chosen), tile);
   gt.finish(x, H, I, t, t, 1, t * fg.kS + j, t * fg.kS + j, part, hh);
 }
@@ -308,6 +324,10 @@ MOEQ_DECODE_FUSED_LAUNCHERS(4);
 MOEQ_DECODE_FUSED_LAUNCHERS(6);
 MOEQ_DECODE_FUSED_LAUNCHERS(8);
 
+#ifndef MOEQ_SHARED_LATE_BLOCKS
+#define MOEQ_SHARED_LATE_BLOCKS 256
+#endif
+
 template <int B, int NCH>
 decode_detail::FusedGrid fused_grid(const moe_layer_desc* L, int T) {
   decode_detail::FusedGrid fg;
@@ -320,7 +340,11 @@ decode_detail::FusedGrid fused_grid(const moe_layer_desc* L, int T) {
   fg.groups = (T + 1) / 2;
   fg.Q = decode_detail::SharedShape<B, NCH>::Q;
   fg.router_blocks = ((L->E + 3) / 4 + 7) / 8 * 8;
-  fg.shared_blocks = L->S > 0 ? (L->S * fg.tiles * fg.Q + 7) / 8 * 8 * fg.groups : 0;
+  // shared experts: beside the router as K slices, unless the routed launch
+  // leaves CUs idle anyway (small batches), where whole rows there are cheaper
+  fg.shared_late = L->S > 0 && T * L->k * fg.tiles < MOEQ_SHARED_LATE_BLOCKS;
+  fg.shared_blocks = L->S > 0 && !fg.shared_late ? (L->S * fg.tiles * fg.Q + 7) / 8 * 8 * fg.groups : 0;
+  fg.late_blocks = fg.shared_late ? (L->S * fg.tiles + 7) / 8 * 8 * fg.groups : 0;
   return fg;
 }
 
@@ -354,7 +378,7 @@ int launch_gateup_routed(const moe_layer_desc* L, const uint16_t* x, const float
   return with_nch(L->H, [&](auto nch) {
     constexpr int NCH = decltype(nch)::value;
     const decode_detail::FusedGrid fg = fused_grid<B, NCH>(L, T);
-    decode_detail::gateup_routed_kernel<B, NCH><<<T * L->k * fg.tiles, 64 * decode_detail::FusedShape<B, NCH>::W,
+    decode_detail::gateup_routed_kernel<B, NCH><<<T * L->k * fg.tiles + fg.late_blocks, 64 * decode_detail::FusedShape<B, NCH>::W,
                                                  0, s>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->I, fg,
                                                          logits, spart, topk_idx, topk_w, hh);
     return check_launch("moe_decode_forward (selection + routed gate/up)");
