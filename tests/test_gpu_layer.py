@@ -157,6 +157,42 @@ def test_decode_forward_matches_route_and_residual(bq):
     assert torch.equal(a["out"].view(torch.uint8), d["out"].view(torch.uint8))
 
 
+ODD = {
+    # 100 experts (two candidates per lane, 28 padding slots), H 512, I 256
+    "e100": synth.Workload("odd_e100", 91, 512, 256, 100, 6, 1, 4, (1, 5)),
+    # 1000 experts (16 per lane), k + S = 16 slots (the largest down block), 8-bit
+    "e1000": synth.Workload("odd_e1000", 92, 1024, 256, 1000, 15, 1, 8, (3,)),
+}
+
+
+@pytest.mark.parametrize("name", ["e100", "e1000"])
+def test_decode_forward_odd_shapes(bq, name):
+    """moe_decode_forward on shapes the named workloads do not reach: expert
+    counts that are not multiples of 64, the widest selection, 16 slots,
+    H = 512 and 1024, I = 256."""
+    w = ODD[name]
+    q = gpu_layer(w)
+    wr = synth.router_weight_bf16(w)
+    ml = bq.MoELayer(q, bf16_tensor(wr), None, T_max=max(w.tokens))
+    ol = oracle_layer(w)
+    for T in w.tokens:
+        print(f"decode forward {w.name} T={T}", flush=True)
+        x = synth.activations_bf16(w, T, batch=2)
+        r = ml.forward(bf16_tensor(x), fused_layer=True)
+        torch.cuda.synchronize()
+        logits = r["logits"].cpu().numpy()
+        assert np.max(np.abs(logits - oracle.router_logits(x, wr, None))) <= 1e-5 * np.max(np.abs(logits))
+        ref = oracle.moe_layer(ol, x, logits=logits)
+        assert np.array_equal(r["idx"].cpu().numpy(), ref["idx"])
+        assert np.max(np.abs(r["w"].cpu().numpy() - ref["w"]) / ref["w"]) <= 1e-5
+        out = oracle.bf16_to_f32(to_bits(r["out"]))
+        assert rel_err(out, ref["out"]) <= SPEC_TOL
+        ref_b = oracle.moe_layer(ol, x, logits=logits, h_bf16=True)
+        assert rel_err(out, ref_b["out"]) <= DECODE_TOL
+    del ml, q
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("case", ["lanes", "slots", "nan_inf"])
 def test_decode_select_ties_bitexact(bq, case):
     """The decode selection (both moe_route_permute_decode and the copy inside
