@@ -305,9 +305,10 @@ struct ATile {
 // A (token rows) via direct global -> LDS loads (global_load_lds_dwordx4),
 // no registers involved: a slice of the tile is BM rows x 128 bytes, written
 // as 1 KB pieces of 8 rows whose 64 lanes fill consecutive 16-byte slots.
-// Slot t of row r holds the row's 16-byte part t ^ (r % 8): the MFMA operand
-// reads of 8 consecutive rows at one k then hit 8 different slots, i.e.
-// every LDS bank once.
+// Slot t of row r holds the row's 16-byte part t ^ swz(r), swz(r) =
+// (r / 2) % 8: rows are 128 bytes, so even and odd rows start on opposite
+// halves of the 64 banks, and the MFMA operand reads of 16 consecutive rows
+// at one k hit 16 different (half, slot) pairs, i.e. every bank once.
 template <int BM>
 struct ADma {
   static constexpr int N = BM / 32;   // pieces per wavefront per slice
@@ -315,10 +316,11 @@ struct ADma {
   // Token row of piece j for this lane: row_of(j); rowp[j]: pointer to it
   // (any valid row past the tile's end: those results are never stored)
   MOEQ_DEV static int row_of(int j) { return 8 * (N * (int)(threadIdx.x >> 6) + j) + (int)((threadIdx.x & 63) >> 3); }
+  MOEQ_DEV static int swz(int r) { return (r >> 1) & 7; }
   MOEQ_DEV void init(const uint16_t* const (&rowp)[N]) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int j = 0; j < N; ++j) src[j] = rowp[j] + 8 * ((lane & 7) ^ (lane >> 3));
+    for (int j = 0; j < N; ++j) src[j] = rowp[j] + 8 * ((lane & 7) ^ swz(row_of(j)));
   }
   MOEQ_DEV void issue(int s, uint16_t* tile) const {
     const int wv = uniform(threadIdx.x >> 6);
@@ -391,7 +393,8 @@ struct Mainloop {
     hh = lane >> 5;
     wv = uniform(threadIdx.x >> 6);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) aoff[st] = 2 * ((lane & 31) * 64 + 8 * ((step_k(st, hh) >> 3) ^ (lane & 7)));
+    for (int st = 0; st < 4; ++st)
+      aoff[st] = 2 * ((lane & 31) * 64 + 8 * ((step_k(st, hh) >> 3) ^ ADma<BM>::swz(lane & 31)));
   }
   MOEQ_DEV uint16_t* a_tile(int t) const { return reinterpret_cast<uint16_t*>(lds + ATILE * t); }
   MOEQ_DEV uint8_t* b_stage(int t) const { return lds + NA * ATILE + (4 * t + wv) * BDma<BITS>::STAGE; }
