@@ -193,6 +193,50 @@ def test_decode_forward_odd_shapes(bq, name):
     torch.cuda.empty_cache()
 
 
+def test_stacked_blocks(bq):
+    """The stacked workload's first five blocks (6-, 4-, 4-, 4- and 8-bit):
+    n = RMSNorm(x); x = bf16(x + bf16(moe(n))) per block, the GPU side with
+    moe_decode_forward adding into x in place (residual and out alias), for
+    three consecutive batch-1 tokens.  Each block is checked against the
+    oracle on the GPU's own block input, and the final residual stream
+    against the oracle's chain run from the token alone (routed on the GPU's
+    logits of each block)."""
+    _LAYERS.clear()
+    torch.cuda.empty_cache()
+    w = synth.get_workload("stack48_h2048_e128_k8_mixed")
+    bits = synth.layer_bits(w)[:5]
+    assert set(bits) == {4, 6, 8}
+    layers = [gpu_layer(w, layer=l, bits=b) for l, b in enumerate(bits)]
+    wrs = [bf16_tensor(synth.router_weight_bf16(w, layer=l)) for l in range(len(bits))]
+    ols = [oracle_layer(w, layer=l, bits=b) for l, b in enumerate(bits)]
+    ws = layers[0].workspace(1)
+    for step in range(3):
+        x0 = synth.activations_bf16(w, 1, batch=step)
+        x = bf16_tensor(x0)
+        xo = x0.copy()
+        for l in range(len(bits)):
+            before = to_bits(x)
+            n = bq.moe_rmsnorm(x)
+            nb = to_bits(n)
+            _, logits, idx, _ = bq.moe_decode_forward(layers[l], n, wrs[l], None, ws, residual=x, out=x)
+            torch.cuda.synchronize()
+            lg = logits.cpu().numpy()
+            blk = oracle.moe_layer(ols[l], nb, logits=lg)
+            assert np.array_equal(idx.cpu().numpy(), blk["idx"])
+            want = oracle.bf16_to_f32(oracle.residual_bf16(before, blk["out"])).astype(np.float64)
+            got = oracle.bf16_to_f32(to_bits(x)).astype(np.float64)
+            # the block output to the layer tolerance, plus one bf16 ulp of x
+            # for the two roundings of the sum
+            bound = 2.0 ** -7 * np.abs(want) + SPEC_TOL * np.max(np.abs(blk["out"]))
+            assert np.all(np.abs(got - want) <= bound), (step, l)
+            xo = oracle.residual_bf16(xo, oracle.moe_layer(ols[l], oracle.rmsnorm_bf16(xo), logits=lg)["out"])
+        err = rel_err(oracle.bf16_to_f32(to_bits(x)), oracle.bf16_to_f32(xo))
+        print(f"  stacked token {step}: rel err {err:.2e}", flush=True)
+        assert err <= SPEC_TOL, (step, err)
+    del layers
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("case", ["lanes", "slots", "nan_inf"])
 def test_decode_select_ties_bitexact(bq, case):
     """The decode selection (both moe_route_permute_decode and the copy inside
