@@ -384,6 +384,65 @@ def cpu_baseline(w, T, budget_s=20.0):
                       f"host has {len(os.sched_getaffinity(0))} usable cores"}
 
 
+def main_curve(a, w, bq, dev):
+    """Decode cost against batch size: the whole layer (moe_decode_forward)
+    at T = 1 .. 16 tokens per call, each timed like the default bench (HIP
+    graph of steps over weight replicas and token batches), relative to
+    T = 1 -- the price of verifying T - 1 speculated tokens with the target
+    token in one call."""
+    import torch
+    from tests.gpu_util import bf16_tensor
+    layer_bytes = expert_bytes(w, w.bits) * w.n_mats
+    R = a.replicas or max(2, min(16, math.ceil(2e9 / layer_bytes)))
+    reps = build_replicas(bq, w, R, dev)
+    wr = bf16_tensor(synth.router_weight_bf16(w))
+    bias = synth.router_bias(w)
+    bias_t = None if bias is None else torch.from_numpy(bias).to(dev)
+    s = torch.cuda.Stream()
+    curve = []
+    for T in range(1, a.curve_max + 1):
+        NB = a.batches
+        xs = [bf16_tensor(synth.activations_bf16(w, T, batch=b)) for b in range(NB)]
+        ws = [reps[0].workspace(T, device=dev) for _ in range(R)]
+        G = max(R, NB)
+        steps = [Step(bq, reps[i % R], wr, bias_t, xs[i % NB], T, ws[i % R]) for i in range(G)]
+        with torch.cuda.stream(s):
+            for st in steps:
+                st.run(ctypes.c_void_p(s.cuda_stream))
+        torch.cuda.synchronize()
+        distinct = float(np.mean([st.distinct_experts() for st in steps]))
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            for st in steps:
+                st.run(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        n = max(1, a.steps // G)
+        with torch.cuda.stream(s):
+            for _ in range(max(1, a.warmup // G)):
+                graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        with torch.cuda.stream(s):
+            for _ in range(n):
+                graph.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (n * G)
+        alg = distinct * expert_bytes(w, w.bits) + w.E * w.H * 2 + 2 * T * w.H * 2
+        curve.append({"T": T, "us_per_step": round(us, 3), "distinct_experts": round(distinct, 2),
+                      "alg_bytes": round(alg), "GBps": round(alg / (us * 1e-6) / 1e9, 1),
+                      "fused_layer": bool(steps[0].layer_fused)})
+        print(f"# T={T}: {us:.2f} us/step, {distinct:.1f} experts", file=sys.stderr, flush=True)
+        del graph, steps, ws, xs
+        torch.cuda.empty_cache()
+    t1 = curve[0]["us_per_step"]
+    for c in curve:
+        c["rel_to_T1"] = round(c["us_per_step"] / t1, 3)
+    print(json.dumps({"metric": "decode step time relative to one token", "workload": w.name,
+                      "data": "synthetic", "curve": curve}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,6 +454,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--curve-max", type=int, default=0, metavar="T",
+                    help="only measure the decode layer at 1 .. T tokens per call (cost curve)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (counter calibration)")
     a = ap.parse_args()
@@ -416,6 +477,8 @@ def main():
     w, T = parse_workload(a.workload)
     if w.layers > 1:
         return main_stack(a, w, bq, dev)
+    if a.curve_max:
+        return main_curve(a, w, bq, dev)
     bits = w.bits
     layer_bytes = expert_bytes(w, bits) * w.n_mats
     R = a.replicas or max(2, min(16, math.ceil(2e9 / layer_bytes)))

@@ -131,6 +131,14 @@ def test_decode_forward(bq, name, T):
     check_layer(bq, name, T, prefill=False, fused=True, batch=5)
 
 
+def test_decode_forward_verify_batches(bq):
+    """Every batch the speculative-verify cost curve measures (1 .. 16 tokens
+    per call on the 256-expert + shared layer), each against the oracle."""
+    for T in range(1, 17):
+        print(f"decode forward verify batch T={T}", flush=True)
+        check_layer(bq, "moe_h2048_e256_k8_s1_b4", T, prefill=False, fused=True, batch=40 + T)
+
+
 @pytest.mark.parametrize("bits", [6, 8])
 @pytest.mark.parametrize("T", [2, 17])
 def test_decode_forward_6_8_bit(bq, bits, T):
