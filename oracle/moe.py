@@ -13,7 +13,7 @@ __all__ = [
     "bf16_to_f32", "f32_to_bf16", "quantize", "pack", "unpack", "dequant",
     "router_logits", "select_topk", "topk_weights", "assignment_experts",
     "permute", "expert_ffn", "combine", "QuantLayer", "moe_layer",
-    "rmsnorm_bf16", "residual_bf16", "silu",
+    "rmsnorm_bf16", "residual_bf16", "silu", "shrink_lp", "tree_mean64", "hqq_refine",
 ]
 
 GROUP = 64
@@ -83,6 +83,89 @@ def quantize(w: np.ndarray, bits: int, group: int = GROUP):
     q = np.clip(np.rint(v), np.float32(0), qmax)
     q[degenerate] = 0
     return q.astype(np.uint8).reshape(N, K), s16, z16
+
+
+# --------------------------------------------------------------------------
+# HQQ zero-point refinement (the step that produces the format's z)
+# --------------------------------------------------------------------------
+# The pages only name HQQ (Krasis update, "Latest results (v1.0)" and "Latest
+# updates"); the solver is the published half-quadratic one (Badri & Shaji,
+# "Half-Quadratic Quantization of Large Machine Learning Models", 2023),
+# restated here from its description: with the scale s held, the zero z of a
+# group minimises the lp error (p < 1) of the reconstruction, split with an
+# auxiliary residual e and solved by alternating the two closed-form
+# sub-problems while the coupling weight beta grows by kappa each round.
+# Everything below is fp32 with IEEE division and ties-to-even rounding, as
+# the GPU quantiser computes it, so that both sides take every rounding
+# decision (a code, a zero rounded to fp16, stopping) from the same values.
+
+def shrink_lp(x: np.ndarray, beta, p) -> np.ndarray:
+    """Proximal step of the lp penalty (p <= 1), generalised soft threshold:
+    sign(x) * max(|x| - |x|^(p-1) / beta, 0) in fp32.  At x = 0 and p < 1
+    the threshold is infinite and the result 0."""
+    x = np.asarray(x, np.float32)
+    a = np.abs(x)
+    with np.errstate(divide="ignore"):
+        t = np.power(a, np.float32(p) - np.float32(1)) / np.float32(beta)
+    return np.copysign(np.maximum(a - t, np.float32(0)), x).astype(np.float32)
+
+
+def tree_mean64(x: np.ndarray) -> np.ndarray:
+    """Mean over the last axis (64 values) as the GPU forms it: fp32 sums of
+    adjacent pairs, then of adjacent pair sums, and so on (a balanced binary
+    tree over consecutive halves), times 1/64 (exact)."""
+    x = np.asarray(x, np.float32)
+    assert x.shape[-1] == 64
+    while x.shape[-1] > 1:
+        x = (x[..., 0::2] + x[..., 1::2]).astype(np.float32)
+    return (x[..., 0] * np.float32(1.0 / 64.0)).astype(np.float32)
+
+
+def hqq_refine(w: np.ndarray, bits: int, lp: float = 0.7, beta: float = 10.0, kappa: float = 1.01,
+               iters: int = 20, group: int = GROUP):
+    """Min-max quantisation (``quantize``) followed by HQQ's zero-point
+    refinement, group by group with s fixed.  One round, from the group's
+    current fp16 zero z:
+        q  = clip(rint(w / s + z), 0, 2^b - 1)          (codes for z)
+        r  = w - (q - z) s;  E = mean |r|               (its error)
+        stop if E is not below the group's best so far; else keep z as best
+        e  = shrink_lp(r, beta, lp)                     (residual sub-problem)
+        z  = fp16(mean(q - (w - e) / s))                (zero sub-problem)
+        beta = beta * kappa
+    The group keeps the zero of its lowest error and the codes for it, so its
+    mean absolute error never exceeds the min-max one.  Groups whose fp16
+    scale is zero keep the min-max result.  Returns q, s16, z16 as
+    ``quantize``."""
+    if group != 64:
+        raise ValueError("the refinement reduces over groups of 64")
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    q0, s16, z16 = quantize(w, bits, group)
+    qmax = np.float32(2 ** bits - 1)
+    wg = w.reshape(N, K // group, group)
+    degenerate = ((wg.max(axis=2) - wg.min(axis=2)) / qmax).astype(np.float16) == np.float16(0)
+    sf = s16.astype(np.float32)[..., None]
+    z = z16.astype(np.float32)
+    zb = z.copy()
+    best = np.full(z.shape, np.inf, np.float32)
+    active = ~degenerate
+    b = np.float32(beta)
+    for _ in range(iters):
+        if not active.any():
+            break
+        qv = np.clip(np.rint(wg / sf + z[..., None]), np.float32(0), qmax).astype(np.float32)
+        r = (wg - (qv - z[..., None]) * sf).astype(np.float32)
+        E = tree_mean64(np.abs(r))
+        active = active & (E < best)
+        best = np.where(active, E, best)
+        zb = np.where(active, z, zb)
+        e = shrink_lp(r, b, lp)
+        znew = tree_mean64(qv - (wg - e) / sf)
+        z = np.where(active, znew.astype(np.float16).astype(np.float32), z)
+        b = np.float32(b * np.float32(kappa))
+    q = np.clip(np.rint(wg / sf + zb[..., None]), np.float32(0), qmax)
+    q[degenerate] = 0
+    return q.astype(np.uint8).reshape(N, K), s16, zb.astype(np.float16)
 
 
 def pack(q: np.ndarray, bits: int) -> np.ndarray:

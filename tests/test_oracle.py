@@ -58,3 +58,20 @@ def test_bf16_and_norm():
 
 def test_ffn_bf16_h():
     pins.pin_ffn_bf16_h(oracle)
+
+
+def test_shrink_closed_form():
+    pins.pin_shrink_closed_form(oracle)
+
+
+def test_tree_mean():
+    pins.pin_tree_mean(oracle)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_hqq_refine(bits):
+    pins.pin_hqq_refine(oracle, bits)
+
+
+def test_hqq_least_squares_round():
+    pins.pin_hqq_least_squares_round(oracle)

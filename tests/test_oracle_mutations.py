@@ -125,6 +125,55 @@ def _residual_no_block_rounding(x_bf16, moe_out):
     return om.f32_to_bf16(om.bf16_to_f32(x_bf16).astype(np.float64) + np.asarray(moe_out, np.float64))
 
 
+def _shrink_identity(x, beta, p):
+    # mistake: the residual is not shrunk at all
+    return np.asarray(x, np.float32)
+
+
+def _mean_left_to_right(x):
+    # mistake: a left-to-right fp32 sum instead of the pairwise tree
+    x = np.asarray(x, np.float32)
+    acc = np.zeros(x.shape[:-1], np.float32)
+    for i in range(x.shape[-1]):
+        acc = (acc + x[..., i]).astype(np.float32)
+    return (acc * np.float32(1 / 64)).astype(np.float32)
+
+
+def _hqq_variant(sign=1.0, keep_best=True):
+    def refine(w, bits, lp=0.7, beta=10.0, kappa=1.01, iters=20, group=64):
+        w = np.asarray(w, np.float32)
+        N, K = w.shape
+        q0, s16, z16 = _quantize(w, bits, group)
+        qmax = np.float32(2 ** bits - 1)
+        wg = w.reshape(N, K // group, group)
+        sf = s16.astype(np.float32)[..., None]
+        z = z16.astype(np.float32)
+        zb, best, active, b = z.copy(), np.full(z.shape, np.inf, np.float32), np.ones(z.shape, bool), np.float32(beta)
+        for _ in range(iters):
+            qv = np.clip(np.rint(wg / sf + z[..., None]), 0, qmax).astype(np.float32)
+            r = (wg - (qv - z[..., None]) * sf).astype(np.float32)
+            E = om.tree_mean64(np.abs(r))
+            if keep_best:
+                active = active & (E < best)
+                best = np.where(active, E, best)
+                zb = np.where(active, z, zb)
+            e = om.shrink_lp(r, b, lp)
+            znew = om.tree_mean64(qv + np.float32(sign) * (-(wg - e) / sf))
+            z = np.where(active, znew.astype(np.float16).astype(np.float32), z)
+            if not keep_best:
+                zb = z
+            b = np.float32(b * np.float32(kappa))
+        q = np.clip(np.rint(wg / sf + zb[..., None]), 0, qmax)
+        return q.astype(np.uint8).reshape(N, K), s16, zb.astype(np.float16)
+    return refine
+
+
+_hqq_zero_sign_flipped = _hqq_variant(sign=-1.0)     # mistake: z = mean(q + (w - e) / s)
+_hqq_keeps_last = _hqq_variant(keep_best=False)      # mistake: the last zero, not the best one
+_hqq_zero_sign_flipped.__name__ = "_hqq_zero_sign_flipped"
+_hqq_keeps_last.__name__ = "_hqq_keeps_last"
+
+
 MUTANTS = [
     ("quantize", _quantize_zero_from_max, [pins.pin_quant_golden, lambda o: pins.pin_quant_error_bound(o, 4)]),
     ("quantize", _quantize_trunc, [pins.pin_quant_golden, lambda o: pins.pin_quant_error_bound(o, 6)]),
@@ -139,6 +188,10 @@ MUTANTS = [
     ("combine", _combine_drop_shared, [pins.pin_layer_bruteforce, pins.pin_layer_special_cases]),
     ("rmsnorm_bf16", _rmsnorm_no_eps, [pins.pin_bf16_and_norm]),
     ("residual_bf16", _residual_no_block_rounding, [pins.pin_bf16_and_norm]),
+    ("shrink_lp", _shrink_identity, [pins.pin_shrink_closed_form, lambda o: pins.pin_hqq_refine(o, 4)]),
+    ("tree_mean64", _mean_left_to_right, [pins.pin_tree_mean]),
+    ("hqq_refine", _hqq_zero_sign_flipped, [pins.pin_hqq_least_squares_round]),
+    ("hqq_refine", _hqq_keeps_last, [lambda o: pins.pin_hqq_refine(o, 6)]),
 ]
 
 
