@@ -443,6 +443,55 @@ def main_curve(a, w, bq, dev):
                       "data": "synthetic", "curve": curve}), flush=True)
 
 
+def main_hqq(a, w, bq, dev):
+    """The quantisation step before the path: moe_quantize_hqq (min-max,
+    then HQQ's zero refinement) against plain moe_quantize on one projection
+    of every expert of the workload (gate: [E+S, I, H] fp32 N(0, 0.02) drawn
+    on the device), and the mean absolute reconstruction error of each."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    wt = torch.randn((w.n_mats, w.I, w.H), generator=g, device=dev, dtype=torch.float32) * 0.02
+    bits = w.bits
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def mae(qw):
+        codes = bq.moe_unpack(qw.q, w.H, bits).float().reshape(w.n_mats * w.I, w.H // 64, 64)
+        # device sz order -> [rows][K/64]: tiles of 64 rows are group-major
+        sz = qw.sz.reshape(-1).view(torch.int32)
+        rows = w.n_mats * w.I
+        sz = sz.reshape(rows // 64, w.H // 64, 64).transpose(1, 2).reshape(rows, w.H // 64)
+        s = (sz & 0xFFFF).to(torch.int16).view(torch.float16).float()
+        z = ((sz >> 16) & 0xFFFF).to(torch.int16).view(torch.float16).float()
+        d = (codes - z[..., None]) * s[..., None]
+        return float((wt.reshape(rows, w.H // 64, 64) - d).abs().mean())
+
+    out = bq.moe_quantize(wt, bits)
+    ms_mm = timed(lambda: bq.moe_quantize(wt, bits, out=out), 5)
+    err_mm = mae(out)
+    outh = bq.moe_quantize_hqq(wt, bits)
+    ms_h = timed(lambda: bq.moe_quantize_hqq(wt, bits, out=outh), 3)
+    err_h = mae(outh)
+    n = wt.numel()
+    print(json.dumps({"metric": "HQQ-refined quantisation throughput", "value": round(n / (ms_h * 1e-3) / 1e9, 3),
+                      "unit": "Gweights/s", "workload": w.name, "bits": bits, "weights": n,
+                      "matrix": [w.n_mats, w.I, w.H], "ms_hqq": round(ms_h, 3), "ms_minmax": round(ms_mm, 3),
+                      "minmax_GBps_fp32_in": round(n * 4 / (ms_mm * 1e-3) / 1e9, 1),
+                      "mae_minmax": err_mm, "mae_hqq": err_h, "mae_drop": round(1 - err_h / err_mm, 4),
+                      "solver": {"lp": 0.7, "beta": 10.0, "kappa": 1.01, "iters": 20}, "data": "synthetic"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -454,6 +503,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--hqq", action="store_true",
+                    help="only time the HQQ-refined quantisation of one projection of the workload")
     ap.add_argument("--curve-max", type=int, default=0, metavar="T",
                     help="only measure the decode layer at 1 .. T tokens per call (cost curve)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
@@ -479,6 +530,8 @@ def main():
         return main_stack(a, w, bq, dev)
     if a.curve_max:
         return main_curve(a, w, bq, dev)
+    if a.hqq:
+        return main_hqq(a, w, bq, dev)
     bits = w.bits
     layer_bytes = expert_bytes(w, bits) * w.n_mats
     R = a.replicas or max(2, min(16, math.ceil(2e9 / layer_bytes)))

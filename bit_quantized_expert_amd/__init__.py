@@ -7,7 +7,7 @@ PyTorch supplies device memory and the current stream.  Importing this
 package without the built library raises -- there is no fallback.
 
 Functions carry the names of the C entry points (see ``include/moeq.h``):
-``moe_quantize``, ``moe_unpack``, ``moe_route_topk``, ``moe_permute``,
+``moe_quantize``, ``moe_quantize_hqq``, ``moe_unpack``, ``moe_route_topk``, ``moe_permute``,
 ``moe_route_permute_decode``, ``moe_qgemv_decode``, ``moe_qgemm_prefill``,
 ``moe_combine``, ``moe_decode_forward``, ``moe_rmsnorm``,
 ``moe_workspace_bytes``, ``moe_read_status``.
@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
             "moe_workspace_bytes": (SZ, [P, I]),
             "moe_last_error": (ctypes.c_char_p, []),
             "moe_quantize": (I, [P, L64, I, I, P, P, P]),
+            "moe_quantize_hqq": (I, [P, L64, I, I, ctypes.c_float, ctypes.c_float, ctypes.c_float, I, P, P, P]),
             "moe_unpack": (I, [P, L64, I, I, P, P]),
             "moe_route_topk": (I, [P, P, P, I, I, I, I, P, P, P, P, SZ, P]),
             "moe_permute": (I, [P, I, I, I, I, P, P, P, P, P, P, SZ, P]),
@@ -130,6 +131,21 @@ def moe_quantize(w: torch.Tensor, bits: int, out: Optional[QWeight] = None, stre
         sz = torch.empty(w.shape[:-1] + (K // GROUP,), dtype=torch.int32, device=w.device)
         out = QWeight(q, sz, bits)
     _check(lib().moe_quantize(_p(w), rows, K, bits, _p(out.q), _p(out.sz), _stream(stream)))
+    return out
+
+
+def moe_quantize_hqq(w: torch.Tensor, bits: int, lp: float = 0.7, beta: float = 10.0, kappa: float = 1.01,
+                     iters: int = 20, out: Optional[QWeight] = None, stream=None) -> QWeight:
+    """moe_quantize with HQQ's zero-point refinement of every group."""
+    _dev(w, torch.float32, "w")
+    K = w.shape[-1]
+    rows = w.numel() // K
+    if out is None:
+        q = torch.empty(w.shape[:-1] + (K * bits // 8,), dtype=torch.uint8, device=w.device)
+        sz = torch.empty(w.shape[:-1] + (K // GROUP,), dtype=torch.int32, device=w.device)
+        out = QWeight(q, sz, bits)
+    _check(lib().moe_quantize_hqq(_p(w), rows, K, bits, lp, beta, kappa, iters, _p(out.q), _p(out.sz),
+                                  _stream(stream)))
     return out
 
 

@@ -4,14 +4,51 @@
 
 using namespace moeq;
 
+// HQQ's zero-point refinement (Badri & Shaji, "Half-Quadratic Quantization
+// of Large Machine Learning Models", the half-quadratic solver with the
+// scale held): parameters of the lp penalty, the coupling weight and its
+// growth, and the number of rounds (0: plain min-max quantisation).
+struct HqqParams {
+  float lp, beta, kappa;
+  int iters;
+};
+
+// One round per iteration, for the group in this wavefront (lane l holds
+// value v of the group, sf its scale, z its current zero, an fp16 value):
+// the codes for z and their mean absolute error E; the group stops when E
+// is not below its best; else z is kept as the best and replaced by the
+// zero sub-problem's solution (rounded to fp16) for the shrunk residual.
+// No fused multiply-adds: every step is rounded as written.
+MOEQ_DEV float hqq_zero(float v, float sf, float z, float qmax, const HqqParams& hp) {
+#pragma clang fp contract(off)
+  float best = INFINITY, zb = z, beta = hp.beta;
+  const float pm1 = hp.lp - 1.0f;
+  for (int it = 0; it < hp.iters; ++it) {
+    const float qv = fminf(fmaxf(rintf(v / sf + z), 0.0f), qmax);
+    const float r = v - (qv - z) * sf;
+    const float E = wave_sum(fabsf(r)) * (1.0f / 64.0f);
+    if (!(E < best)) break;                          // the same value in every lane
+    best = E;
+    zb = z;
+    const float a = fabsf(r);
+    const float e = copysignf(fmaxf(a - powf(a, pm1) / beta, 0.0f), r);
+    const float zn = wave_sum(qv - (v - e) / sf) * (1.0f / 64.0f);
+    z = f16_bits_to_f32(f32_to_f16_bits(zn));
+    beta = beta * hp.kappa;
+  }
+  return zb;
+}
+
 // One wavefront per 64-value group: lane l holds value l of the group.
-// Min and max come from wave reductions; the code of every lane is then
-// packed into the tiled field order (format.h) by shuffles.  fp32
-// arithmetic with IEEE division and rint (ties to even) so the codes equal
-// any other IEEE fp32 evaluation of the same formula bit for bit.
+// Min and max come from wave reductions (then the zero is refined if
+// hp.iters > 0); the code of every lane is packed into the tiled field order
+// (format.h) by shuffles.  fp32 arithmetic with IEEE division and rint (ties
+// to even) so the codes equal any other IEEE fp32 evaluation of the same
+// formula bit for bit.
 template <int BITS>
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, long ngroups, int gpr,
-                                                       uint8_t* __restrict__ q, uint32_t* __restrict__ sz) {
+                                                       HqqParams hp, uint8_t* __restrict__ q,
+                                                       uint32_t* __restrict__ sz) {
   using F = Fmt<BITS>;
   const int lane = threadIdx.x & 63;
   const long stride = (long)gridDim.x * 4;
@@ -26,8 +63,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     const bool degenerate = (s16 & 0x7FFFu) == 0;
     if (degenerate) s16 = 0x3C00u;                       // fp16 1.0
     const float sf = f16_bits_to_f32(s16);
-    const uint32_t z16 = f32_to_f16_bits(-mn / sf);
-    const float zf = f16_bits_to_f32(z16);
+    uint32_t z16 = f32_to_f16_bits(-mn / sf);
+    float zf = f16_bits_to_f32(z16);
+    if (!degenerate && hp.iters > 0) {
+      zf = hqq_zero(v, sf, zf, qmax, hp);
+      z16 = f32_to_f16_bits(zf);                     // exact: zf is an fp16 value
+    }
     float r = rintf(v / sf + zf);
     r = fminf(fmaxf(r, 0.0f), qmax);
     const uint32_t code = degenerate ? 0u : (uint32_t)r;
@@ -88,8 +129,8 @@ static int grid_for(long work, int per_block) {
   return (int)b;
 }
 
-extern "C" int moe_quantize(const float* w, long rows, int K, int bits, uint8_t* q, uint32_t* sz,
-                            hipStream_t stream) {
+static int quantize_impl(const float* w, long rows, int K, int bits, HqqParams hp, uint8_t* q, uint32_t* sz,
+                         hipStream_t stream) {
   if (!w || !q || !sz) return set_error(MOEQ_ERR_INVALID_ARG, "moe_quantize: NULL pointer");
   if (rows < 0 || K <= 0) return set_error(MOEQ_ERR_INVALID_ARG, "moe_quantize: rows=%ld K=%d", rows, K);
   if (!bits_ok(bits)) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_quantize: bits=%d not in {4,6,8}", bits);
@@ -101,11 +142,25 @@ extern "C" int moe_quantize(const float* w, long rows, int K, int bits, uint8_t*
   if (ngroups == 0) return MOEQ_OK;
   const int grid = grid_for(ngroups, 4);
   switch (bits) {
-    case 4: quantize_kernel<4><<<grid, 256, 0, stream>>>(w, ngroups, K / 64, q, sz); break;
-    case 6: quantize_kernel<6><<<grid, 256, 0, stream>>>(w, ngroups, K / 64, q, sz); break;
-    default: quantize_kernel<8><<<grid, 256, 0, stream>>>(w, ngroups, K / 64, q, sz); break;
+    case 4: quantize_kernel<4><<<grid, 256, 0, stream>>>(w, ngroups, K / 64, hp, q, sz); break;
+    case 6: quantize_kernel<6><<<grid, 256, 0, stream>>>(w, ngroups, K / 64, hp, q, sz); break;
+    default: quantize_kernel<8><<<grid, 256, 0, stream>>>(w, ngroups, K / 64, hp, q, sz); break;
   }
   return check_launch("moe_quantize");
+}
+
+extern "C" int moe_quantize(const float* w, long rows, int K, int bits, uint8_t* q, uint32_t* sz,
+                            hipStream_t stream) {
+  return quantize_impl(w, rows, K, bits, HqqParams{1.0f, 1.0f, 1.0f, 0}, q, sz, stream);
+}
+
+extern "C" int moe_quantize_hqq(const float* w, long rows, int K, int bits, float lp, float beta, float kappa,
+                                int iters, uint8_t* q, uint32_t* sz, hipStream_t stream) {
+  if (!(lp > 0.0f && lp <= 1.0f) || !(beta > 0.0f && beta < INFINITY) || !(kappa >= 1.0f && kappa < INFINITY) ||
+      iters < 0 || iters > 1000)
+    return set_error(MOEQ_ERR_INVALID_ARG, "moe_quantize_hqq: lp=%g beta=%g kappa=%g iters=%d", (double)lp,
+                     (double)beta, (double)kappa, iters);
+  return quantize_impl(w, rows, K, bits, HqqParams{lp, beta, kappa, iters}, q, sz, stream);
 }
 
 extern "C" int moe_unpack(const uint8_t* q, long rows, int K, int bits, uint8_t* codes, hipStream_t stream) {

@@ -53,6 +53,15 @@ def test_host_validation(bq):
     assert L.moe_quantize(ok, 4, 96, 4, ok, ok, None) == -2
     assert L.moe_quantize(ok, 4, 64, 4, ok, ok, None) == -2 and "multiple of 64" in _err(L)   # rows % 64
     assert L.moe_quantize(mis, 64, 64, 4, ok, ok, None) == -3
+    # moe_quantize_hqq: its own parameters, then moe_quantize's checks
+    assert L.moe_quantize_hqq(ok, 64, 64, 4, 0.0, 10.0, 1.01, 20, ok, ok, None) == -1 and "lp" in _err(L)
+    assert L.moe_quantize_hqq(ok, 64, 64, 4, 1.5, 10.0, 1.01, 20, ok, ok, None) == -1
+    assert L.moe_quantize_hqq(ok, 64, 64, 4, 0.7, 0.0, 1.01, 20, ok, ok, None) == -1
+    assert L.moe_quantize_hqq(ok, 64, 64, 4, 0.7, 10.0, 0.5, 20, ok, ok, None) == -1
+    assert L.moe_quantize_hqq(ok, 64, 64, 4, 0.7, 10.0, 1.01, -1, ok, ok, None) == -1
+    assert L.moe_quantize_hqq(ok, 64, 64, 4, 0.7, 10.0, 1.01, 1001, ok, ok, None) == -1
+    assert L.moe_quantize_hqq(ok, 64, 64, 5, 0.7, 10.0, 1.01, 20, ok, ok, None) == -2
+    assert L.moe_quantize_hqq(mis, 64, 64, 4, 0.7, 10.0, 1.01, 20, ok, ok, None) == -3
     assert L.moe_unpack(ok, 4, 64, 7, ok, None) == -2
     # routing
     assert L.moe_route_topk(ok, ok, None, 4, 64, 8, 9, ok, ok, ok, None, 0, None) == -1    # k > E
