@@ -14,6 +14,7 @@ __all__ = [
     "router_logits", "select_topk", "topk_weights", "assignment_experts",
     "permute", "expert_ffn", "combine", "QuantLayer", "moe_layer",
     "rmsnorm_bf16", "residual_bf16", "silu", "shrink_lp", "tree_mean64", "hqq_refine",
+    "kv_encode", "kv_decode",
 ]
 
 GROUP = 64
@@ -166,6 +167,30 @@ def hqq_refine(w: np.ndarray, bits: int, lp: float = 0.7, beta: float = 10.0, ka
     q = np.clip(np.rint(wg / sf + zb[..., None]), np.float32(0), qmax)
     q[degenerate] = 0
     return q.astype(np.uint8).reshape(N, K), s16, zb.astype(np.float16)
+
+
+# --------------------------------------------------------------------------
+# group-quantised KV-cache codec (the same format on bf16 cache rows)
+# --------------------------------------------------------------------------
+# Krasis update, "Latest updates": the KV cache is also stored in 4- and 6-bit
+# group-quantised form (checked for accuracy against bf16).  The reading here:
+# the weight format of ``quantize``/``pack`` applied to rows of the cache
+# (one row = one token's vector of one head; groups of 64 along it), rows
+# stored one after the other in the packed byte order of ``pack``.
+
+def kv_encode(x_bf16: np.ndarray, bits: int):
+    """bf16 rows [R, D] -> (packed codes [R, D*bits/8] uint8, s16 [R, D/64],
+    z16 [R, D/64]): min-max quantisation (``quantize``) of the exact fp32
+    values of the bf16 inputs, packed by ``pack``."""
+    x = bf16_to_f32(x_bf16)
+    q, s16, z16 = quantize(x, bits)
+    return pack(q, bits), s16, z16
+
+
+def kv_decode(packed: np.ndarray, s16: np.ndarray, z16: np.ndarray, bits: int, D: int) -> np.ndarray:
+    """Inverse map: codes unpacked, dequantised as (q - z) * s in fp32
+    (``dequant``), rounded to bf16 (ties to even) -> bf16 bits [R, D]."""
+    return f32_to_bf16(dequant(unpack(packed, bits, D), s16, z16))
 
 
 def pack(q: np.ndarray, bits: int) -> np.ndarray:

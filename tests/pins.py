@@ -527,3 +527,34 @@ def pin_hqq_least_squares_round(o, bits=4, seed=22, N=64, K=512):
     e0 = _group_mae(o, w, q0, s0, z0)
     e1 = _group_mae(o, w, q1, s1, z1)
     assert np.all(e1[moved] < e0[moved])
+
+
+# --------------------------------------------------------------------------
+# KV-cache codec
+# --------------------------------------------------------------------------
+def pin_kv_codec(o, seed=23):
+    """The codec on bf16 rows: values on a power-of-two grid whose ends are
+    the group's min and max come back exactly; any row comes back within half
+    a quantisation step plus one bf16 rounding; the packed bytes of 4-bit rows
+    hold code 2i in the low nibble of byte i (hand-built row)."""
+    rng = np.random.default_rng(seed)
+    for bits in (4, 6, 8):
+        qmax = 2 ** bits - 1
+        q = rng.integers(0, qmax + 1, size=(16, 128))
+        q[:, 0], q[:, 1], q[:, 64], q[:, 65] = 0, qmax, 0, qmax
+        x = o.f32_to_bf16(((q - 5) * 2.0 ** -6).astype(np.float32))
+        p, s16, z16 = o.kv_encode(x, bits)
+        assert p.shape == (16, 128 * bits // 8) and np.all(s16 == np.float16(2.0 ** -6)) and np.all(z16 == 5)
+        assert np.array_equal(o.kv_decode(p, s16, z16, bits, 128), x)
+        y = o.f32_to_bf16((rng.standard_normal((32, 192)) * 3).astype(np.float32))
+        p, s16, z16 = o.kv_encode(y, bits)
+        back = o.bf16_to_f32(o.kv_decode(p, s16, z16, bits, 192)).astype(np.float64)
+        yf = o.bf16_to_f32(y).astype(np.float64)
+        step = np.repeat(s16.astype(np.float64), 64, axis=1)
+        assert np.all(np.abs(back - yf) <= 0.5 * step * (1 + 1e-3) + 2.0 ** -8 * np.abs(back) + 1e-30)
+    # 4-bit byte order by hand: codes 0..15 then 15..0 repeated
+    codes = np.tile(np.r_[np.arange(16), np.arange(15, -1, -1)], 2)
+    x = o.f32_to_bf16((codes * 0.5).astype(np.float32))[None, :]
+    p, s16, z16 = o.kv_encode(x, 4)
+    assert s16[0, 0] == np.float16(0.5) and z16[0, 0] == 0
+    assert list(p[0, :8]) == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]

@@ -75,3 +75,7 @@ def test_hqq_refine(bits):
 
 def test_hqq_least_squares_round():
     pins.pin_hqq_least_squares_round(oracle)
+
+
+def test_kv_codec():
+    pins.pin_kv_codec(oracle)

@@ -174,6 +174,12 @@ _hqq_zero_sign_flipped.__name__ = "_hqq_zero_sign_flipped"
 _hqq_keeps_last.__name__ = "_hqq_keeps_last"
 
 
+def _kv_decode_truncating(packed, s16, z16, bits, D):
+    # mistake: the decoded value truncated to bf16 instead of rounded
+    d = om.dequant(om.unpack(packed, bits, D), s16, z16).astype(np.float32)
+    return (d.view(np.uint32) >> 16).astype(np.uint16)
+
+
 MUTANTS = [
     ("quantize", _quantize_zero_from_max, [pins.pin_quant_golden, lambda o: pins.pin_quant_error_bound(o, 4)]),
     ("quantize", _quantize_trunc, [pins.pin_quant_golden, lambda o: pins.pin_quant_error_bound(o, 6)]),
@@ -192,6 +198,7 @@ MUTANTS = [
     ("tree_mean64", _mean_left_to_right, [pins.pin_tree_mean]),
     ("hqq_refine", _hqq_zero_sign_flipped, [pins.pin_hqq_least_squares_round]),
     ("hqq_refine", _hqq_keeps_last, [lambda o: pins.pin_hqq_refine(o, 6)]),
+    ("kv_decode", _kv_decode_truncating, [pins.pin_kv_codec]),
 ]
 
 
