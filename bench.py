@@ -492,6 +492,45 @@ def main_hqq(a, w, bq, dev):
           flush=True)
 
 
+def main_kv(a, bq, dev):
+    """The KV-cache codec at a cache's size: 32768 tokens x 8 heads x 128
+    values (bf16 N(0, 4) drawn on the device), encode and decode timed with
+    HIP events; both are HBM-bound (bf16 rows one way, codes + scale/zero
+    words the other)."""
+    import torch
+    R, D = 32768 * 8, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    x = (torch.randn((R, D), generator=g, device=dev) * 2).to(torch.bfloat16)
+    res = {"metric": "KV-cache codec throughput", "rows": R, "D": D, "data": "synthetic", "codec": []}
+
+    def timed(fn, n=20):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for bits in (4, 6, 8):
+        q, sz = bq.moe_kv_encode(x, bits)
+        out = bq.moe_kv_decode(q, sz, D, bits)
+        ms_e = timed(lambda: bq.moe_kv_encode(x, bits, q=q, sz=sz))
+        ms_d = timed(lambda: bq.moe_kv_decode(q, sz, D, bits, out=out))
+        nbytes = x.numel() * 2 + q.numel() + sz.numel() * 4
+        err = float((out.float() - x.float()).abs().mean())
+        res["codec"].append({"bits": bits, "encode_us": round(ms_e * 1e3, 2), "decode_us": round(ms_d * 1e3, 2),
+                             "bytes": nbytes, "encode_GBps": round(nbytes / (ms_e * 1e-3) / 1e9, 1),
+                             "decode_GBps": round(nbytes / (ms_d * 1e-3) / 1e9, 1),
+                             "encode_frac": round(nbytes / (ms_e * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                             "decode_frac": round(nbytes / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                             "mean_abs_err": err})
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,6 +542,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--kv", action="store_true", help="only time the KV-cache codec at a cache's size")
     ap.add_argument("--hqq", action="store_true",
                     help="only time the HQQ-refined quantisation of one projection of the workload")
     ap.add_argument("--curve-max", type=int, default=0, metavar="T",
@@ -525,6 +565,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.kv:
+        return main_kv(a, bq, dev)
     w, T = parse_workload(a.workload)
     if w.layers > 1:
         return main_stack(a, w, bq, dev)

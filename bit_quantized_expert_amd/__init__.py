@@ -7,7 +7,7 @@ PyTorch supplies device memory and the current stream.  Importing this
 package without the built library raises -- there is no fallback.
 
 Functions carry the names of the C entry points (see ``include/moeq.h``):
-``moe_quantize``, ``moe_quantize_hqq``, ``moe_unpack``, ``moe_route_topk``, ``moe_permute``,
+``moe_quantize``, ``moe_quantize_hqq``, ``moe_kv_encode``, ``moe_kv_decode``, ``moe_unpack``, ``moe_route_topk``, ``moe_permute``,
 ``moe_route_permute_decode``, ``moe_qgemv_decode``, ``moe_qgemm_prefill``,
 ``moe_combine``, ``moe_decode_forward``, ``moe_rmsnorm``,
 ``moe_workspace_bytes``, ``moe_read_status``.
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
             "moe_quantize": (I, [P, L64, I, I, P, P, P]),
             "moe_quantize_hqq": (I, [P, L64, I, I, ctypes.c_float, ctypes.c_float, ctypes.c_float, I, P, P, P]),
             "moe_unpack": (I, [P, L64, I, I, P, P]),
+            "moe_kv_encode": (I, [P, L64, I, I, P, P, P]),
+            "moe_kv_decode": (I, [P, P, L64, I, I, P, P]),
             "moe_route_topk": (I, [P, P, P, I, I, I, I, P, P, P, P, SZ, P]),
             "moe_permute": (I, [P, I, I, I, I, P, P, P, P, P, P, SZ, P]),
             "moe_route_permute_decode": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, SZ, P]),
@@ -146,6 +148,31 @@ def moe_quantize_hqq(w: torch.Tensor, bits: int, lp: float = 0.7, beta: float = 
         out = QWeight(q, sz, bits)
     _check(lib().moe_quantize_hqq(_p(w), rows, K, bits, lp, beta, kappa, iters, _p(out.q), _p(out.sz),
                                   _stream(stream)))
+    return out
+
+
+def moe_kv_encode(x: torch.Tensor, bits: int, q: Optional[torch.Tensor] = None, sz: Optional[torch.Tensor] = None,
+                  stream=None):
+    """bf16 cache rows [..., D] -> (packed codes [..., D*bits/8] uint8,
+    scale/zero words [..., D/64] int32)."""
+    _dev(x, torch.bfloat16, "x")
+    D = x.shape[-1]
+    rows = x.numel() // D
+    if q is None:
+        q = torch.empty(x.shape[:-1] + (D * bits // 8,), dtype=torch.uint8, device=x.device)
+    if sz is None:
+        sz = torch.empty(x.shape[:-1] + (D // GROUP,), dtype=torch.int32, device=x.device)
+    _check(lib().moe_kv_encode(_p(x), rows, D, bits, _p(q), _p(sz), _stream(stream)))
+    return q, sz
+
+
+def moe_kv_decode(q: torch.Tensor, sz: torch.Tensor, D: int, bits: int, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    _dev(q, torch.uint8, "q")
+    rows = q.numel() // (D * bits // 8)
+    if out is None:
+        out = torch.empty(q.shape[:-1] + (D,), dtype=torch.bfloat16, device=q.device)
+    _check(lib().moe_kv_decode(_p(q), _p(sz), rows, D, bits, _p(out), _stream(stream)))
     return out
 
 

@@ -1,6 +1,7 @@
 // Group quantisation of fp32 weights into the packed format, and the unpack
 // test entry that runs the decode kernels' in-register unpacking.
 #include "format.h"
+#include "quant_group.h"
 
 using namespace moeq;
 
@@ -55,23 +56,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   const int cpr = gpr * F::CHUNKS_PER_GROUP;
   for (long g = (long)blockIdx.x * 4 + (threadIdx.x >> 6); g < ngroups; g += stride) {
     const float v = w[g * 64 + lane];
-    const float mn = wave_min(v);
-    const float mx = wave_max(v);
-    const float qmax = (float)((1 << BITS) - 1);
-    const float s = (mx - mn) / qmax;
-    uint32_t s16 = f32_to_f16_bits(s);
-    const bool degenerate = (s16 & 0x7FFFu) == 0;
-    if (degenerate) s16 = 0x3C00u;                       // fp16 1.0
-    const float sf = f16_bits_to_f32(s16);
-    uint32_t z16 = f32_to_f16_bits(-mn / sf);
-    float zf = f16_bits_to_f32(z16);
-    if (!degenerate && hp.iters > 0) {
-      zf = hqq_zero(v, sf, zf, qmax, hp);
+    const GroupQuant gq = minmax_group<BITS>(v);
+    const uint32_t s16 = gq.s16;
+    uint32_t z16 = gq.z16;
+    float zf = gq.zf;
+    if (!gq.degenerate && hp.iters > 0) {
+      zf = hqq_zero(v, gq.sf, zf, gq.qmax, hp);
       z16 = f32_to_f16_bits(zf);                     // exact: zf is an fp16 value
     }
-    float r = rintf(v / sf + zf);
-    r = fminf(fmaxf(r, 0.0f), qmax);
-    const uint32_t code = degenerate ? 0u : (uint32_t)r;
+    const uint32_t code = group_code(gq, v, zf);
     const long row = g / gpr;
     const int gi = (int)(g % gpr);
     if constexpr (BITS == 4) {

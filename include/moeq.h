@@ -137,6 +137,30 @@ int moe_quantize_hqq(const float* w, long rows, int K, int bits,
                      float lp, float beta, float kappa, int iters,
                      uint8_t* q, uint32_t* sz, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Group-quantised KV cache (the same codec on cache rows; Krasis update,
+ * "Latest updates", keeps the KV cache in 4- and 6-bit form)
+ * ------------------------------------------------------------------------ */
+
+/* Encode bf16 cache rows x [rows][D] (device; one row = one token's vector of
+ * one head, D a multiple of 64) group by group with moe_quantize's min-max
+ * formulas (on the exact fp32 values of the bf16 inputs).  Writes, row after
+ * row, the packed codes in natural order into q [rows][D*bits/8] (4-bit: code
+ * 2i in the low nibble of byte i; 6-bit: code c at bits 6c..6c+5 of the row's
+ * little-endian bit string; 8-bit: one byte per code) and the scale/zero
+ * words (fp16 s | fp16 z << 16) into sz [rows][D/64].  x and q must be
+ * 16-byte aligned, sz 4-byte aligned; rows >= 0; bits in {4,6,8}.  x must
+ * hold finite values. */
+int moe_kv_encode(const uint16_t* x, long rows, int D, int bits,
+                  uint8_t* q, uint32_t* sz, hipStream_t stream);
+
+/* Decode what moe_kv_encode wrote: out[r][i] = bf16((q - z) * s) with the
+ * difference and the product each rounded in fp32 (no fused multiply-add) and
+ * the result rounded to bf16, ties to even.  q and out 16-byte aligned, sz
+ * 4-byte aligned; sizes as moe_kv_encode. */
+int moe_kv_decode(const uint8_t* q, const uint32_t* sz, long rows, int D, int bits,
+                  uint16_t* out, hipStream_t stream);
+
 /* Unpack codes q (rows*K*bits/8 bytes in the layout of moe_qweight, rows a
  * multiple of 64, device) into one byte per code, codes [rows][K] (device,
  * natural order).  It runs the same in-register unpacking the

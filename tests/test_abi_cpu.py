@@ -53,6 +53,16 @@ def test_host_validation(bq):
     assert L.moe_quantize(ok, 4, 96, 4, ok, ok, None) == -2
     assert L.moe_quantize(ok, 4, 64, 4, ok, ok, None) == -2 and "multiple of 64" in _err(L)   # rows % 64
     assert L.moe_quantize(mis, 64, 64, 4, ok, ok, None) == -3
+    # KV codec
+    assert L.moe_kv_encode(None, 4, 64, 4, ok, ok, None) == -1
+    assert L.moe_kv_encode(ok, 4, 64, 5, ok, ok, None) == -2 and "bits" in _err(L)
+    assert L.moe_kv_encode(ok, 4, 96, 4, ok, ok, None) == -2 and "multiple of 64" in _err(L)
+    assert L.moe_kv_encode(mis, 4, 64, 4, ok, ok, None) == -3
+    assert L.moe_kv_encode(ok, 0, 64, 4, ok, ok, None) == 0      # nothing to do, no launch
+    assert L.moe_kv_decode(ok, None, 4, 64, 4, ok, None) == -1
+    assert L.moe_kv_decode(ok, ok, -1, 64, 4, ok, None) == -1
+    assert L.moe_kv_decode(ok, ok, 4, 64, 7, ok, None) == -2
+    assert L.moe_kv_decode(ok, ok, 4, 64, 4, mis, None) == -3
     # moe_quantize_hqq: its own parameters, then moe_quantize's checks
     assert L.moe_quantize_hqq(ok, 64, 64, 4, 0.0, 10.0, 1.01, 20, ok, ok, None) == -1 and "lp" in _err(L)
     assert L.moe_quantize_hqq(ok, 64, 64, 4, 1.5, 10.0, 1.01, 20, ok, ok, None) == -1

@@ -122,6 +122,58 @@ def test_quantize_hqq_default(bq, bits):
     assert np.all(err(gq, gs, gz) <= err(q0, s0, z0) * (1 + 1e-6))
 
 
+def _kv_rows(seed, R, D):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((R, D)) * 2).astype(np.float32)
+    g = x.reshape(-1, 64)
+    g[0] = 0.37                                          # constant group
+    g[1] = np.linspace(-3, 3, 64)                        # exact end points
+    g[2] *= 1e4                                          # wide range
+    g[3] *= 1e-4                                         # narrow range: subnormal fp16 scale
+    g[4] = (rng.integers(0, 16, 64) - 7) * 2.0 ** -5     # on a power-of-two grid
+    return oracle.f32_to_bf16(x)
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+@pytest.mark.parametrize("R,D", [(5, 64), (37, 128), (64, 192)])
+def test_kv_codec_bitexact(bq, bits, R, D):
+    """KV-cache codec: packed codes and scale/zero words of the encoder, and
+    the decoder's bf16 rows, equal the oracle's bit for bit."""
+    x = _kv_rows(bits * 31 + R, R, D)
+    q, sz = bq.moe_kv_encode(bf16_tensor(x), bits)
+    out = bq.moe_kv_decode(q, sz, D, bits)
+    torch.cuda.synchronize()
+    p, s16, z16 = oracle.kv_encode(x, bits)
+    assert np.array_equal(q.cpu().numpy(), p)
+    assert np.array_equal(sz.cpu().numpy().view(np.uint32), _sz_from_oracle(s16, z16))
+    assert np.array_equal(to_bits(out), oracle.kv_decode(p, s16, z16, bits, D))
+
+
+@pytest.mark.parametrize("bits", [4, 6])
+def test_kv_codec_cache_size(bq, bits):
+    """At a cache's size (32768 tokens x 8 heads x 128, as bench.py --kv
+    times it): sampled rows against the oracle, every row's round trip
+    within half a step plus a bf16 rounding."""
+    R, D = 32768 * 8, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    xt = (torch.randn((R, D), generator=g, device="cuda") * 2).to(torch.bfloat16)
+    q, sz = bq.moe_kv_encode(xt, bits)
+    out = bq.moe_kv_decode(q, sz, D, bits)
+    torch.cuda.synchronize()
+    rows = np.unique(np.linspace(0, R - 1, 257).astype(int))
+    x = to_bits(xt[torch.from_numpy(rows).cuda()])
+    p, s16, z16 = oracle.kv_encode(x, bits)
+    assert np.array_equal(q[torch.from_numpy(rows).cuda()].cpu().numpy(), p)
+    assert np.array_equal(to_bits(out[torch.from_numpy(rows).cuda()]), oracle.kv_decode(p, s16, z16, bits, D))
+    s = (sz & 0xFFFF).to(torch.int16).view(torch.float16).float().repeat_interleave(64, dim=1)
+    err = (out.float() - xt.float()).abs()
+    # half a step, widened by the fp16 rounding of s and z (each at most 2^-11 relative, times
+    # 2^bits - 1 and |z| <= 2^bits - 1 steps), plus the bf16 rounding
+    bound = (0.5 + (2 ** bits - 1) * 2.0 ** -10) * s + 2.0 ** -8 * out.float().abs()
+    assert bool((err <= bound).all())
+
+
 @pytest.mark.parametrize("bits", [4, 6, 8])
 def test_unpack_bitexact(bq, bits):
     rng = np.random.default_rng(bits)
