@@ -559,3 +559,9 @@ def pin_kv_codec(o, seed=23):
     p, s16, z16 = o.kv_encode(x, 4)
     assert s16[0, 0] == np.float16(0.5) and z16[0, 0] == 0
     assert list(p[0, :8]) == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    # decoding rounds to the nearest bf16: 8-bit code 103 with s = 5/512 and
+    # z = 0 is 515/512 = 1.005859375, nearer 1 + 2^-7 (bf16 0x3F81) than 1
+    pk = np.zeros((1, 64), np.uint8)
+    pk[0, 0] = 103
+    out = o.kv_decode(pk, np.array([[5 / 512]], np.float16), np.zeros((1, 1), np.float16), 8, 64)
+    assert out[0, 0] == 0x3F81 and np.all(out[0, 1:] == 0)
