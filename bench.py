@@ -304,6 +304,53 @@ def main_stack(a, w, bq, dev):
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": kname,
                      "alg_bytes_per_token": round(exp_bytes), "kernel_us_per_token": round(kern_ms * 1e3, 3)},
     }
+    # the same tokens through moe_stack_decode: one cooperative launch per
+    # token for all blocks (eager launches: the copy of the token's state
+    # and the launch, per token)
+    sd = bq.StackDecoder(layers, wrs, device=dev)
+
+    def mk_tokens(n):
+        with torch.cuda.stream(s):
+            for i in range(n):
+                x.copy_(xs[i % n_tok])
+                sd.run(x, stream=s)
+
+    mk_tokens(min(a.warmup, n_tok))
+    torch.cuda.synchronize()
+    ev0.record(s)
+    mk_tokens(n_tok)
+    ev1.record(s)
+    torch.cuda.synchronize()
+    mk_total = ev0.elapsed_time(ev1)
+    mev = []
+    with torch.cuda.stream(s):
+        for i in range(min(32, n_tok)):
+            x.copy_(xs[i])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            sd.run(x, stream=s)
+            e1.record(s)
+            mev.append((e0, e1))
+    torch.cuda.synchronize()
+    mk_kern = float(np.mean([e0.elapsed_time(e1) for e0, e1 in mev]))
+    layer_path = {"value": res["value"], "ms_per_step": res["ms_per_step"], "roofline": res["roofline"]}
+    mk = {"value": round(n_tok / (mk_total * 1e-3), 1), "ms_per_step": round(mk_total / n_tok, 6),
+          "kernel_us_per_token": round(mk_kern * 1e3, 3),
+          "achieved": round(alg / (mk_kern * 1e-3) / 1e9, 1)}
+    if mk["value"] > layer_path["value"]:
+        res["value"], res["ms_per_step"] = mk["value"], mk["ms_per_step"]
+        res["config"]["path"] = "moe_stack_decode (one cooperative launch per token for all blocks)"
+        res["config"]["hip_graph"] = False
+        res["config"]["GBps_per_token_stream"] = round(alg / (mk["ms_per_step"] * 1e-3) / 1e9, 1)
+        res["roofline"] = {"bound": "hbm", "achieved": mk["achieved"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(mk["achieved"] / PEAK_HBM_GBS, 4), "traffic": None,
+                           "kernel": "moe_stack_decode (all blocks of one token, one launch)",
+                           "alg_bytes_per_token": round(alg), "kernel_us_per_token": mk["kernel_us_per_token"]}
+        res["layer_path"] = layer_path
+    else:
+        res["config"]["path"] = "moe_rmsnorm + moe_decode_forward per block (HIP graph)"
+        res["megakernel"] = mk
+    del sd
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_stack(w, bits, a.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
             "moe_quantize_hqq": (I, [P, L64, I, I, ctypes.c_float, ctypes.c_float, ctypes.c_float, I, P, P, P]),
             "moe_unpack": (I, [P, L64, I, I, P, P]),
             "moe_kv_encode": (I, [P, L64, I, I, P, P, P]),
+            "moe_stack_table_bytes": (SZ, [I]),
+            "moe_stack_workspace_bytes": (SZ, [P]),
+            "moe_stack_table_write": (I, [P, P, I, P]),
+            "moe_stack_decode": (I, [P, P, I, ctypes.c_float, P, P, SZ, P]),
             "moe_kv_decode": (I, [P, P, L64, I, I, P, P]),
             "moe_route_topk": (I, [P, P, P, I, I, I, I, P, P, P, P, SZ, P]),
             "moe_permute": (I, [P, I, I, I, I, P, P, P, P, P, P, SZ, P]),
@@ -174,6 +178,35 @@ def moe_kv_decode(q: torch.Tensor, sz: torch.Tensor, D: int, bits: int, out: Opt
         out = torch.empty(q.shape[:-1] + (D,), dtype=torch.bfloat16, device=q.device)
     _check(lib().moe_kv_decode(_p(q), _p(sz), rows, D, bits, _p(out), _stream(stream)))
     return out
+
+
+class StackDecoder:
+    """Stacked decode of a batch-1 token through blocks of MoE layers in one
+    launch (moe_stack_decode): the layers' device table is written once
+    here; ``run(x)`` updates the residual stream x (bf16 [H]) in place."""
+
+    def __init__(self, layers, w_routers, device="cuda"):
+        n = len(layers)
+        self.layers, self.w_routers = list(layers), list(w_routers)   # keep the weights alive
+        descs = (_LayerDesc * n)(*[l.desc() for l in layers])
+        wrs = (ctypes.c_void_p * n)(*[w.data_ptr() for w in w_routers])
+        self.table = torch.empty(lib().moe_stack_table_bytes(n), dtype=torch.uint8, device=device)
+        _check(lib().moe_stack_table_write(descs, wrs, n, _p(self.table)))
+        self.n = n
+        self.dims = layers[0].desc()
+        nbytes = lib().moe_stack_workspace_bytes(ctypes.byref(self.dims))
+        if nbytes == 0:
+            raise MoeqError(-2, lib().moe_last_error().decode())
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+    def run(self, x: torch.Tensor, eps: float = 1e-6, nlayers: Optional[int] = None, stream=None) -> torch.Tensor:
+        _dev(x, torch.bfloat16, "x")
+        n = self.n if nlayers is None else nlayers
+        if not 0 <= n <= self.n:
+            raise ValueError(f"nlayers={n}: the table holds {self.n} layers")
+        _check(lib().moe_stack_decode(ctypes.byref(self.dims), _p(self.table), n, eps, _p(x), _p(self.ws),
+                                      self.ws.numel(), _stream(stream)))
+        return x
 
 
 def moe_unpack(q: torch.Tensor, K: int, bits: int, stream=None) -> torch.Tensor:

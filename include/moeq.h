@@ -138,6 +138,43 @@ int moe_quantize_hqq(const float* w, long rows, int K, int bits,
                      uint8_t* q, uint32_t* sz, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Stacked decode in one launch (Raon-1-mini, optimisation table: a persistent
+ * per-layer MoE megakernel instead of many small launches)
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the device table moe_stack_table_write fills for nlayers layers
+ * (64 per layer); 0 if nlayers <= 0. */
+size_t moe_stack_table_bytes(int nlayers);
+
+/* Write the device table of nlayers MoE layers (host array layers[], each
+ * with its own weights and bit widths but the same H, I, E, k and S = 0;
+ * gate and up of a layer share a bit width) and their bf16 router weights
+ * (host array of device pointers w_router[l], [E][H], 16-byte aligned) into
+ * table (device, moe_stack_table_bytes(nlayers) bytes, 16-byte aligned).
+ * A setup call: it copies synchronously (hipMemcpy).  The weights must stay
+ * allocated while the table is used. */
+int moe_stack_table_write(const moe_layer_desc* layers, const uint16_t* const* w_router, int nlayers,
+                          void* table);
+
+/* Workspace bytes moe_stack_decode needs for layers of the dimensions of L
+ * on the current device (it depends on the device's CU count); 0 if L is
+ * not supported (H a multiple of 512 up to 8192, I a multiple of 64 with
+ * k*I <= 16384, k <= 16, k <= E <= 1024, S = 0).  Zero-fill it once. */
+size_t moe_stack_workspace_bytes(const moe_layer_desc* L);
+
+/* One batch-1 token through the first nlayers layers of table: for each
+ * layer, n = RMSNorm(x) (as moe_rmsnorm, gamma = 1, eps), routed MoE of n
+ * (top-k, renormalised weights, SwiGLU experts with h rounded to bf16, fp32
+ * accumulation), x = bf16(x + bf16(moe)).  x: device bf16 [H], updated in
+ * place.  dims: any layer's descriptor (only H, I, E, k, S are read).  One
+ * cooperative launch whose blocks meet at grid-wide barriers three times per
+ * layer; it fails (MOEQ_ERR_HIP) if the device cannot hold the grid at once.
+ * The K sums are split across wavefronts, so results equal
+ * moe_rmsnorm + moe_decode_forward to rounding, not bit for bit. */
+int moe_stack_decode(const moe_layer_desc* dims, const void* table, int nlayers, float eps, uint16_t* x,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Group-quantised KV cache (the same codec on cache rows; Krasis update,
  * "Latest updates", keeps the KV cache in 4- and 6-bit form)
  * ------------------------------------------------------------------------ */

@@ -53,6 +53,10 @@ def test_host_validation(bq):
     assert L.moe_quantize(ok, 4, 96, 4, ok, ok, None) == -2
     assert L.moe_quantize(ok, 4, 64, 4, ok, ok, None) == -2 and "multiple of 64" in _err(L)   # rows % 64
     assert L.moe_quantize(mis, 64, 64, 4, ok, ok, None) == -3
+    # stacked decode: argument checks before any device query or launch
+    assert L.moe_stack_table_bytes(0) == 0 and L.moe_stack_table_bytes(3) == 192
+    assert L.moe_stack_table_write(None, None, 2, ok) == -1
+    assert L.moe_stack_decode(None, ok, 1, ctypes.c_float(1e-6), ok, ok, 0, None) == -1
     # KV codec
     assert L.moe_kv_encode(None, 4, 64, 4, ok, ok, None) == -1
     assert L.moe_kv_encode(ok, 4, 64, 5, ok, ok, None) == -2 and "bits" in _err(L)

@@ -245,6 +245,54 @@ def test_stacked_blocks(bq):
     torch.cuda.empty_cache()
 
 
+def test_stack_megakernel(bq):
+    """The one-launch stacked decode (moe_stack_decode) over the stacked
+    workload's first five blocks (6-, 4-, 4-, 4- and 8-bit), three tokens.
+    Block by block: the megakernel's x after l blocks against block l run by
+    the step-by-step path (moe_rmsnorm + moe_decode_forward) on the
+    megakernel's x after l - 1 blocks and against the oracle on the same
+    input; end to end against the oracle's chain."""
+    _LAYERS.clear()
+    torch.cuda.empty_cache()
+    w = synth.get_workload("stack48_h2048_e128_k8_mixed")
+    bits = synth.layer_bits(w)[:5]
+    layers = [gpu_layer(w, layer=l, bits=b) for l, b in enumerate(bits)]
+    wrs = [bf16_tensor(synth.router_weight_bf16(w, layer=l)) for l in range(len(bits))]
+    ols = [oracle_layer(w, layer=l, bits=b) for l, b in enumerate(bits)]
+    sd = bq.StackDecoder(layers, wrs)
+    ws = layers[0].workspace(1)
+    for step in range(3):
+        x0 = synth.activations_bf16(w, 1, batch=10 + step)
+        prev = x0.copy()
+        xo = x0.copy()
+        for l in range(1, len(bits) + 1):
+            print(f"  stack megakernel token {step} blocks {l}", flush=True)
+            xm = bf16_tensor(x0).reshape(-1)
+            sd.run(xm, nlayers=l)
+            xr = bf16_tensor(prev)
+            n = bq.moe_rmsnorm(xr)
+            _, logits, idx, _ = bq.moe_decode_forward(layers[l - 1], n, wrs[l - 1], None, ws, residual=xr, out=xr)
+            torch.cuda.synchronize()
+            got = oracle.bf16_to_f32(to_bits(xm)).astype(np.float64)
+            step_path = oracle.bf16_to_f32(to_bits(xr)).reshape(-1).astype(np.float64)
+            blk = oracle.moe_layer(ols[l - 1], to_bits(n), logits=logits.cpu().numpy())
+            want = oracle.bf16_to_f32(oracle.residual_bf16(prev, blk["out"])).reshape(-1).astype(np.float64)
+            scale = np.max(np.abs(blk["out"]))
+            assert np.all(np.abs(got - want) <= 2.0 ** -7 * np.abs(want) + SPEC_TOL * scale), (step, l)
+            assert np.all(np.abs(got - step_path) <= 2.0 ** -7 * np.abs(step_path) + DECODE_TOL * scale), (step, l)
+            prev = to_bits(xm).reshape(1, -1)
+            xo = oracle.residual_bf16(xo, oracle.moe_layer(ols[l - 1], oracle.rmsnorm_bf16(xo), wrs_np(w, l - 1))["out"])
+        err = rel_err(oracle.bf16_to_f32(prev), oracle.bf16_to_f32(xo))
+        print(f"  stack megakernel token {step}: end-to-end rel err {err:.2e}", flush=True)
+        assert err <= SPEC_TOL, (step, err)
+    del sd, layers
+    torch.cuda.empty_cache()
+
+
+def wrs_np(w, l):
+    return synth.router_weight_bf16(w, layer=l)
+
+
 @pytest.mark.parametrize("case", ["lanes", "slots", "nan_inf"])
 def test_decode_select_ties_bitexact(bq, case):
     """The decode selection (both moe_route_permute_decode and the copy inside
