@@ -192,7 +192,9 @@ class Step:
 
 class StackStep:
     """One token through every block of the stacked workload:
-    n = RMSNorm(x); route n; experts(n); x = bf16(x + bf16(combine))."""
+    n = RMSNorm(x); route n; experts(n); x = bf16(x + bf16(combine)) --
+    moe_decode_block per block (three launches), or moe_rmsnorm and the
+    block's Step where the fused decode does not apply."""
 
     def __init__(self, bq, layers, wrs, x, ws):
         import torch
@@ -203,12 +205,20 @@ class StackStep:
             st.out = x
             st.residual = x
 
-    def run(self, s):
+    def block(self, st, s):
         lib, p = self.bq.lib(), self.bq._p
         T, H = self.x.shape
-        for st in self.steps:
+        if st.layer_fused:
+            self.bq._check(lib.moe_decode_block(ctypes.byref(st.desc), p(self.x), p(st.wr), None, T,
+                                                ctypes.c_float(1e-6), p(st.logits), p(st.idx), p(st.w), p(st.ws),
+                                                st.ws.numel(), s))
+        else:
             self.bq._check(lib.moe_rmsnorm(p(self.x), None, T, H, ctypes.c_float(1e-6), p(self.n), s))
             st.run(s)
+
+    def run(self, s):
+        for st in self.steps:
+            self.block(st, s)
 
 
 def build_stack(bq, w, device):
@@ -270,23 +280,29 @@ def main_stack(a, w, bq, dev):
     # the timed part of each block (the fused decode call, or the expert FFN
     # call) for one token, with events
     kev = []
+    fused = all(ss.layer_fused for ss in st.steps)
     with torch.cuda.stream(s):
         x.copy_(xs[0])
         for ss in st.steps:
-            bq._check(bq.lib().moe_rmsnorm(bq._p(x), None, 1, w.H, ctypes.c_float(1e-6), bq._p(st.n), sp))
-            ss.pre(sp)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(s)
-            ss.timed(sp)
-            e1.record(s)
-            ss.post(sp)
+            if fused:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                st.block(ss, sp)
+                e1.record(s)
+            else:
+                bq._check(bq.lib().moe_rmsnorm(bq._p(x), None, 1, w.H, ctypes.c_float(1e-6), bq._p(st.n), sp))
+                ss.pre(sp)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                ss.timed(sp)
+                e1.record(s)
+                ss.post(sp)
             kev.append((e0, e1))
     torch.cuda.synchronize()
     kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in kev)
-    fused = all(ss.layer_fused for ss in st.steps)
-    if fused:   # the whole block: routers and x/out traffic included
+    if fused:   # the whole block: norm, routers and x traffic included
         exp_bytes = alg
-        kname = "moe_decode_forward (router; routing + gate/up; down + combine), summed over the blocks of one token"
+        kname = "moe_decode_block (RMSNorm + router; routing + gate/up; down + combine + residual), summed over the blocks of one token"
     else:
         exp_bytes = sum(d * expert_bytes(w, b) for d, b in zip(distinct, bits))
         kname = "moe_qgemv_decode (gate/up + down), summed over the blocks of one token"
@@ -348,7 +364,8 @@ def main_stack(a, w, bq, dev):
                            "alg_bytes_per_token": round(alg), "kernel_us_per_token": mk["kernel_us_per_token"]}
         res["layer_path"] = layer_path
     else:
-        res["config"]["path"] = "moe_rmsnorm + moe_decode_forward per block (HIP graph)"
+        res["config"]["path"] = ("moe_decode_block per block (HIP graph)" if fused
+                                 else "moe_rmsnorm + expert calls per block (HIP graph)")
         res["megakernel"] = mk
     del sd
     if not a.no_cpu_baseline:

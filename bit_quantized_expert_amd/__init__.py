@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "moe_route_permute_decode": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_qgemv_decode": (I, [P, P, I, P, P, P, P, P, SZ, P]),
             "moe_decode_forward": (I, [P, P, P, P, I, P, P, P, P, P, P, SZ, P]),
+            "moe_decode_block": (I, [P, P, P, P, I, ctypes.c_float, P, P, P, P, SZ, P]),
             "moe_qgemm_prefill": (I, [P, P, I, P, P, P, P, P, SZ, P]),
             "moe_combine": (I, [P, I, P, P, I, I, I, I, P, P]),
             "moe_rmsnorm": (I, [P, P, I, I, ctypes.c_float, P, P]),
@@ -366,6 +367,22 @@ def moe_decode_forward(layer: QuantLayer, x: torch.Tensor, w_router: torch.Tenso
     _check(lib().moe_decode_forward(ctypes.byref(d), _p(x), _p(w_router), _p(bias), T, _p(residual), _p(logits),
                                     _p(idx), _p(w), _p(out), _p(ws), ws.numel(), _stream(stream)))
     return out, logits, idx, w
+
+
+def moe_decode_block(layer: QuantLayer, x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor],
+                     ws: torch.Tensor, eps: float = 1e-6, stream=None):
+    """x <- x + moe(RMSNorm(x)) in place (three launches).  Returns (x, logits, idx, w)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w_router, torch.bfloat16, "w_router")
+    T = x.shape[0]
+    dev = x.device
+    logits = torch.empty((T, layer.E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, layer.k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, layer.k), dtype=torch.float32, device=dev)
+    d = layer.desc()
+    _check(lib().moe_decode_block(ctypes.byref(d), _p(x), _p(w_router), _p(bias), T, eps, _p(logits), _p(idx), _p(w),
+                                  _p(ws), ws.numel(), _stream(stream)))
+    return x, logits, idx, w
 
 
 def moe_qgemm_prefill(layer: QuantLayer, x: torch.Tensor, counts, offsets, sorted_a, ws: torch.Tensor,

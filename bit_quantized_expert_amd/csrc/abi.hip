@@ -31,7 +31,6 @@ long prefill_max_tiles(long A, int nexp) {
 }
 
 WsLayout ws_layout(int H, int I, int E, int S, int k, int T_max) {
-  (void)H;
   WsLayout w{};
   long A = (long)T_max * (k + S);
   int nexp = E + S;
@@ -47,6 +46,8 @@ WsLayout ws_layout(int H, int I, int E, int S, int k, int T_max) {
   w.shared_part = off;   // [S][T][slice][gate, up][I]
   const long Tf = T_max < kFusedMaxTokens ? T_max : kFusedMaxTokens;
   off = align_up(off + (size_t)S * Tf * kSharedMaxSplit * 2 * I * sizeof(float), 256);
+  w.norm = off;          // [T][H] bf16, decode batches
+  off = align_up(off + (size_t)Tf * H * sizeof(uint16_t), 256);
   w.total = off;
   return w;
 }

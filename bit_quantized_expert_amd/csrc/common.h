@@ -35,6 +35,7 @@ struct WsLayout {
   size_t h;          // decode: fp32 [A][I]; prefill: bf16 [A][I]
   size_t sched;      // prefill: int32 tile schedule
   size_t shared_part;   // moe_decode_forward: fp32 partial gate/up sums of the shared experts
+  size_t norm;          // moe_decode_block: the normalised token rows, bf16
   size_t total;
 };
 constexpr int kPermBlock = 1024;          // assignments per permute block

@@ -80,45 +80,54 @@ extern "C" int moe_qgemv_decode(const moe_layer_desc* L, const uint16_t* x, int 
   return rc;
 }
 
-extern "C" int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, const uint16_t* w_router,
-                                  const float* bias, int T, const uint16_t* residual, float* logits,
-                                  int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
+namespace {
+
+// moe_decode_forward's body; norm.xraw != nullptr for moe_decode_block
+// (then x is where launch 1 stores the normalised rows).
+int decode_forward_impl(const char* fn, const moe_layer_desc* L, const uint16_t* x, const uint16_t* w_router,
+                        const float* bias, int T, const uint16_t* residual, float* logits, int32_t* topk_idx,
+                        float* topk_w, uint16_t* out, void* ws, size_t ws_bytes, decode_detail::NormArgs norm,
+                        hipStream_t stream) {
   using namespace decode_detail;
   int rc = validate_layer(L);
   if (rc != MOEQ_OK) return rc;
-  if (T < 0) return set_error(MOEQ_ERR_INVALID_ARG, "moe_decode_forward: T=%d", T);
+  if (T < 0) return set_error(MOEQ_ERR_INVALID_ARG, "%s: T=%d", fn, T);
   if (T == 0) return MOEQ_OK;
   const int H = L->H, I = L->I, E = L->E, S = L->S, k = L->k;
   if (T > kFusedMaxT || E > kFusedMaxE || k + S > kFusedMaxSlots)
-    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward: needs T <= %d, E <= %d and k+S <= %d (T=%d E=%d k=%d S=%d)",
+    return set_error(MOEQ_ERR_UNSUPPORTED, "%s: needs T <= %d, E <= %d and k+S <= %d (T=%d E=%d k=%d S=%d)", fn,
                      kFusedMaxT, kFusedMaxE, kFusedMaxSlots, T, E, k, S);
   if (H != 512 && H != 1024 && H != 2048 && H != 4096)
-    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward: H=%d must be 512, 1024, 2048 or 4096", H);
+    return set_error(MOEQ_ERR_UNSUPPORTED, "%s: H=%d must be 512, 1024, 2048 or 4096", fn, H);
   if (I != 256 && I != 512 && I != 768 && I != 1024)
-    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward: I=%d must be 256, 512, 768 or 1024", I);
+    return set_error(MOEQ_ERR_UNSUPPORTED, "%s: I=%d must be 256, 512, 768 or 1024", fn, I);
   if (L->gate.bits != L->up.bits)
-    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward: gate and up must share a bit width");
-  if (!x || !w_router || !logits || !topk_idx || !topk_w || !out)
-    return set_error(MOEQ_ERR_INVALID_ARG, "moe_decode_forward: NULL pointer");
-  if (!aligned16(x) || !aligned16(w_router))
-    return set_error(MOEQ_ERR_MISALIGNED, "moe_decode_forward: x and w_router must be 16-byte aligned");
+    return set_error(MOEQ_ERR_UNSUPPORTED, "%s: gate and up must share a bit width", fn);
+  if (!(norm.xraw || x) || !w_router || !logits || !topk_idx || !topk_w || !out)
+    return set_error(MOEQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(norm.xraw ? norm.xraw : x) || !aligned16(w_router))
+    return set_error(MOEQ_ERR_MISALIGNED, "%s: x and w_router must be 16-byte aligned", fn);
   const WsLayout wl = ws_layout(H, I, E, S, k, T);
   if (!ws || ws_bytes < wl.total)
-    return set_error(MOEQ_ERR_WORKSPACE, "moe_decode_forward: workspace of %zu bytes, need %zu", ws_bytes, wl.total);
+    return set_error(MOEQ_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, ws_bytes, wl.total);
   // h: bf16 [T (k+S)][I], rows in assignment order
   uint16_t* hh = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.h);
   float* spart = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.shared_part);
+  if (norm.xraw) {
+    norm.nout = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.norm);
+    x = norm.nout;
+  }
+  const bool nm = norm.xraw != nullptr;
   switch (L->gate.bits) {
-    case 4: rc = decode_router_shared_b4(L, x, w_router, bias, T, logits, spart, stream); break;
-    case 6: rc = decode_router_shared_b6(L, x, w_router, bias, T, logits, spart, stream); break;
-    default: rc = decode_router_shared_b8(L, x, w_router, bias, T, logits, spart, stream); break;
+    case 4: rc = decode_router_shared_b4(L, x, w_router, bias, T, logits, spart, norm, stream); break;
+    case 6: rc = decode_router_shared_b6(L, x, w_router, bias, T, logits, spart, norm, stream); break;
+    default: rc = decode_router_shared_b8(L, x, w_router, bias, T, logits, spart, norm, stream); break;
   }
   if (rc != MOEQ_OK) return rc;
   switch (L->gate.bits) {
-    case 4: rc = decode_gateup_routed_b4(L, x, logits, spart, T, topk_idx, topk_w, hh, stream); break;
-    case 6: rc = decode_gateup_routed_b6(L, x, logits, spart, T, topk_idx, topk_w, hh, stream); break;
-    default: rc = decode_gateup_routed_b8(L, x, logits, spart, T, topk_idx, topk_w, hh, stream); break;
+    case 4: rc = decode_gateup_routed_b4(L, x, logits, spart, T, topk_idx, topk_w, hh, nm, stream); break;
+    case 6: rc = decode_gateup_routed_b6(L, x, logits, spart, T, topk_idx, topk_w, hh, nm, stream); break;
+    default: rc = decode_gateup_routed_b8(L, x, logits, spart, T, topk_idx, topk_w, hh, nm, stream); break;
   }
   if (rc != MOEQ_OK) return rc;
   switch (L->down.bits) {
@@ -127,4 +136,23 @@ extern "C" int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, co
     default: rc = decode_down_combine_b8(L, hh, T, topk_idx, topk_w, residual, out, stream); break;
   }
   return rc;
+}
+
+}  // namespace
+
+extern "C" int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, const uint16_t* w_router,
+                                  const float* bias, int T, const uint16_t* residual, float* logits,
+                                  int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  return decode_forward_impl("moe_decode_forward", L, x, w_router, bias, T, residual, logits, topk_idx, topk_w, out,
+                             ws, ws_bytes, decode_detail::NormArgs{nullptr, 0.0f, nullptr}, stream);
+}
+
+extern "C" int moe_decode_block(const moe_layer_desc* L, uint16_t* x, const uint16_t* w_router, const float* bias,
+                                int T, float eps, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  if (!x) return set_error(MOEQ_ERR_INVALID_ARG, "moe_decode_block: NULL pointer");
+  if (!(eps >= 0.0f)) return set_error(MOEQ_ERR_INVALID_ARG, "moe_decode_block: eps=%g", (double)eps);
+  return decode_forward_impl("moe_decode_block", L, nullptr, w_router, bias, T, x, logits, topk_idx, topk_w, x, ws,
+                             ws_bytes, decode_detail::NormArgs{x, eps, nullptr}, stream);
 }

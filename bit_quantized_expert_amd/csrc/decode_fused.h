@@ -74,6 +74,15 @@ struct FusedGrid {
   int groups;          // token pairs: ceil(T / 2)
 };
 
+// RMSNorm of the raw residual rows inside launch 1 (moe_decode_block): every
+// router block normalises the token rows itself, block 0 also stores them
+// for the later launches.  xraw == nullptr: the input is already normalised.
+struct NormArgs {
+  const uint16_t* xraw;   // [T][H] bf16
+  float eps;
+  uint16_t* nout;         // [T][H] bf16
+};
+
 MOEQ_DEV void select_token_any(const float* L, int E, int k, int rounds, int& idx, float& w) {
   const int ns = (E + 63) / 64;
   if (ns <= 1) select_token<1>(L, E, k, rounds, idx, w);
@@ -134,7 +143,8 @@ __global__ __launch_bounds__(256) void router_shared_kernel(const uint16_t* __re
                                                             const uint8_t* __restrict__ uq,
                                                             const uint32_t* __restrict__ usz,
                                                             const uint16_t* __restrict__ x, int I, FusedGrid fg,
-                                                            float* __restrict__ logits, float* __restrict__ spart) {
+                                                            float* __restrict__ logits, float* __restrict__ spart,
+                                                            NormArgs norm) {
   using Sh = SharedShape<BITS, NCH>;
   constexpr int H = NCH * 512;
   __shared__ Partials<Sh::W, 2> part;
@@ -142,6 +152,34 @@ __global__ __launch_bounds__(256) void router_shared_kernel(const uint16_t* __re
   const int b = (int)blockIdx.x;
   if (b < fg.router_blocks) {
     const int e = b * 4 + wave;
+    if (norm.xraw) {
+      // token by token: n = bf16(x / sqrt(mean(x^2) + eps)) as moe_rmsnorm
+      // forms it (the same sums in the same order), then the router rows
+      __shared__ __attribute__((aligned(16))) uint16_t nrow[H];
+      __shared__ float red[4];
+      for (int t = 0; t < fg.T; ++t) {
+        const uint16_t* xr = norm.xraw + (size_t)t * H;
+        float ss = 0.0f;
+        for (int i = threadIdx.x; i < H; i += 256) {
+          const float v = bf16_bits_to_f32(xr[i]);
+          ss = fmaf(v, v, ss);
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) red[wave] = ss;
+        __syncthreads();
+        const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+        const float r = 1.0f / sqrtf(tot / (float)H + norm.eps);
+        for (int i = threadIdx.x; i < H; i += 256) {
+          const uint16_t n = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(xr[i]) * r);
+          nrow[i] = n;
+          if (b == 0) norm.nout[(size_t)t * H + i] = n;
+        }
+        __syncthreads();
+        if (e < fg.E) router_row<NCH, 1>(nrow, wr, bias, 1, fg.E, e, logits + (size_t)t * fg.E);
+        __syncthreads();   // nrow and red are rewritten for the next token
+      }
+      return;
+    }
     if (e < fg.E) router_row<NCH>(x, wr, bias, fg.T, fg.E, e, logits);
     return;
   }
@@ -313,10 +351,11 @@ __global__ __launch_bounds__(64 * kFusedMaxSlots) void down_combine_kernel(const
 // Launchers per bit width (decode_b{4,6,8}.hip).
 #define MOEQ_DECODE_FUSED_LAUNCHERS(B)                                                                     \
   int decode_router_shared_b##B(const moe_layer_desc* L, const uint16_t* x, const uint16_t* wr,           \
-                                const float* bias, int T, float* logits, float* spart, hipStream_t s);     \
+                                const float* bias, int T, float* logits, float* spart,                     \
+                                decode_detail::NormArgs norm, hipStream_t s);                              \
   int decode_gateup_routed_b##B(const moe_layer_desc* L, const uint16_t* x, const float* logits,          \
                                 const float* spart, int T, int32_t* topk_idx, float* topk_w, uint16_t* hh, \
-                                hipStream_t s);                                                            \
+                                bool norm, hipStream_t s);                                                 \
   int decode_down_combine_b##B(const moe_layer_desc* L, const uint16_t* hh, int T, const int32_t* topk_idx, \
                                const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t s)
 
@@ -328,8 +367,10 @@ MOEQ_DECODE_FUSED_LAUNCHERS(8);
 #define MOEQ_SHARED_LATE_BLOCKS 256
 #endif
 
+// norm: moe_decode_block's launch 1 normalises the rows itself, so the
+// shared experts run as whole rows in launch 2 (reading the stored rows)
 template <int B, int NCH>
-decode_detail::FusedGrid fused_grid(const moe_layer_desc* L, int T) {
+decode_detail::FusedGrid fused_grid(const moe_layer_desc* L, int T, bool norm = false) {
   decode_detail::FusedGrid fg;
   fg.E = L->E;
   fg.S = L->S;
@@ -342,7 +383,7 @@ decode_detail::FusedGrid fused_grid(const moe_layer_desc* L, int T) {
   fg.router_blocks = ((L->E + 3) / 4 + 7) / 8 * 8;
   // shared experts: beside the router as K slices, unless the routed launch
   // leaves CUs idle anyway (small batches), where whole rows there are cheaper
-  fg.shared_late = L->S > 0 && T * L->k * fg.tiles < MOEQ_SHARED_LATE_BLOCKS;
+  fg.shared_late = L->S > 0 && (norm || T * L->k * fg.tiles < MOEQ_SHARED_LATE_BLOCKS);
   fg.shared_blocks = L->S > 0 && !fg.shared_late ? (L->S * fg.tiles * fg.Q + 7) / 8 * 8 * fg.groups : 0;
   fg.late_blocks = fg.shared_late ? (L->S * fg.tiles + 7) / 8 * 8 * fg.groups : 0;
   return fg;
@@ -362,22 +403,22 @@ int with_nch(int H, Fn&& fn) {
 
 template <int B>
 int launch_router_shared(const moe_layer_desc* L, const uint16_t* x, const uint16_t* wr, const float* bias, int T,
-                         float* logits, float* spart, hipStream_t s) {
+                         float* logits, float* spart, decode_detail::NormArgs norm, hipStream_t s) {
   return with_nch(L->H, [&](auto nch) {
     constexpr int NCH = decltype(nch)::value;
-    const decode_detail::FusedGrid fg = fused_grid<B, NCH>(L, T);
+    const decode_detail::FusedGrid fg = fused_grid<B, NCH>(L, T, norm.xraw != nullptr);
     decode_detail::router_shared_kernel<B, NCH><<<fg.router_blocks + fg.shared_blocks, 256, 0, s>>>(
-        wr, bias, L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->I, fg, logits, spart);
+        wr, bias, L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->I, fg, logits, spart, norm);
     return check_launch("moe_decode_forward (router + shared gate/up)");
   });
 }
 
 template <int B>
 int launch_gateup_routed(const moe_layer_desc* L, const uint16_t* x, const float* logits, const float* spart, int T,
-                         int32_t* topk_idx, float* topk_w, uint16_t* hh, hipStream_t s) {
+                         int32_t* topk_idx, float* topk_w, uint16_t* hh, bool norm, hipStream_t s) {
   return with_nch(L->H, [&](auto nch) {
     constexpr int NCH = decltype(nch)::value;
-    const decode_detail::FusedGrid fg = fused_grid<B, NCH>(L, T);
+    const decode_detail::FusedGrid fg = fused_grid<B, NCH>(L, T, norm);
     decode_detail::gateup_routed_kernel<B, NCH><<<T * L->k * fg.tiles + fg.late_blocks, 64 * decode_detail::FusedShape<B, NCH>::W,
                                                  0, s>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->I, fg,
                                                          logits, spart, topk_idx, topk_w, hh);
@@ -415,13 +456,14 @@ int launch_down_combine(const moe_layer_desc* L, const uint16_t* hh, int T, cons
 
 #define MOEQ_DEFINE_DECODE_FUSED(B)                                                                        \
   int decode_router_shared_b##B(const moe_layer_desc* L, const uint16_t* x, const uint16_t* wr,           \
-                                const float* bias, int T, float* logits, float* spart, hipStream_t s) {    \
-    return launch_router_shared<B>(L, x, wr, bias, T, logits, spart, s);                                   \
+                                const float* bias, int T, float* logits, float* spart,                     \
+                                decode_detail::NormArgs norm, hipStream_t s) {                             \
+    return launch_router_shared<B>(L, x, wr, bias, T, logits, spart, norm, s);                             \
   }                                                                                                        \
   int decode_gateup_routed_b##B(const moe_layer_desc* L, const uint16_t* x, const float* logits,          \
                                 const float* spart, int T, int32_t* topk_idx, float* topk_w, uint16_t* hh, \
-                                hipStream_t s) {                                                           \
-    return launch_gateup_routed<B>(L, x, logits, spart, T, topk_idx, topk_w, hh, s);                       \
+                                bool norm, hipStream_t s) {                                                \
+    return launch_gateup_routed<B>(L, x, logits, spart, T, topk_idx, topk_w, hh, norm, s);                 \
   }                                                                                                        \
   int decode_down_combine_b##B(const moe_layer_desc* L, const uint16_t* hh, int T, const int32_t* topk_idx, \
                                const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t s) { \

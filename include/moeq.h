@@ -294,6 +294,19 @@ int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, const uint16_
                        int32_t* topk_idx, float* topk_w, uint16_t* out,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* One block of a stacked decode step: x <- x + moe(RMSNorm(x)) in place, for
+ * a batch of T <= 64 token rows x (device bf16 [T][H]); the RMSNorm is
+ * moe_rmsnorm's (gamma = 1, eps), formed inside the router launch by every
+ * router block for itself (so the step is three launches, not four), the
+ * normalised rows kept in the workspace for the expert launches; the rest is
+ * moe_decode_forward with residual = out = x (shared experts, if any, as
+ * whole rows in the gate/up launch).  For S = 0 the result equals
+ * moe_rmsnorm followed by moe_decode_forward bit for bit.  Limits, logits,
+ * topk_idx, topk_w, workspace and errors as moe_decode_forward; eps >= 0. */
+int moe_decode_block(const moe_layer_desc* L, uint16_t* x, const uint16_t* w_router, const float* bias,
+                     int T, float eps, float* logits, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Prefill path (large T): the same y as moe_qgemv_decode, computed as a
  * grouped GEMM over expert-sorted tokens on the bf16 matrix cores (a prompt
  * touches nearly every expert: Qwen-tin page, "Memory layout and

@@ -53,6 +53,9 @@ def test_host_validation(bq):
     assert L.moe_quantize(ok, 4, 96, 4, ok, ok, None) == -2
     assert L.moe_quantize(ok, 4, 64, 4, ok, ok, None) == -2 and "multiple of 64" in _err(L)   # rows % 64
     assert L.moe_quantize(mis, 64, 64, 4, ok, ok, None) == -3
+    # decode block: its own checks first
+    assert L.moe_decode_block(ok, None, ok, None, 1, ctypes.c_float(1e-6), ok, ok, ok, ok, 0, None) == -1
+    assert L.moe_decode_block(ok, ok, ok, None, 1, ctypes.c_float(-1.0), ok, ok, ok, ok, 0, None) == -1
     # stacked decode: argument checks before any device query or launch
     assert L.moe_stack_table_bytes(0) == 0 and L.moe_stack_table_bytes(3) == 192
     assert L.moe_stack_table_write(None, None, 2, ok) == -1

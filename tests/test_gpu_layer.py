@@ -245,6 +245,43 @@ def test_stacked_blocks(bq):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name,T,layer_bits", [("stack48_h2048_e128_k8_mixed", 1, 6), ("stack48_h2048_e128_k8_mixed", 5, 8),
+                                              ("moe_h2048_e256_k8_s1_b4", 8, None)])
+def test_decode_block(bq, name, T, layer_bits):
+    """moe_decode_block (RMSNorm inside the router launch, in place) against
+    moe_rmsnorm + moe_decode_forward(residual = out = x): bit for bit
+    without shared experts; with one (run as whole rows in the gate/up launch
+    instead of K slices) within the decode bound; and the block output
+    against the oracle."""
+    w = synth.get_workload(name)
+    layer = gpu_layer(w, bits=layer_bits)
+    wr = bf16_tensor(synth.router_weight_bf16(w))
+    bias = synth.router_bias(w)
+    bt = None if bias is None else torch.from_numpy(bias).cuda()
+    ws = layer.workspace(T)
+    x0 = synth.activations_bf16(w, T, batch=21)
+    xa = bf16_tensor(x0)
+    _, la, ia, wa = bq.moe_decode_block(layer, xa, wr, bt, ws)
+    xb = bf16_tensor(x0)
+    n = bq.moe_rmsnorm(xb)
+    _, lb, ib, wb = bq.moe_decode_forward(layer, n, wr, bt, ws, residual=xb, out=xb)
+    torch.cuda.synchronize()
+    assert torch.equal(la, lb) and torch.equal(ia, ib) and torch.equal(wa, wb)
+    ga = oracle.bf16_to_f32(to_bits(xa)).astype(np.float64)
+    gb = oracle.bf16_to_f32(to_bits(xb)).astype(np.float64)
+    ol = oracle_layer(w, bits=layer_bits)
+    blk = oracle.moe_layer(ol, to_bits(n), logits=lb.cpu().numpy())
+    scale = np.max(np.abs(blk["out"]))
+    if w.S == 0:
+        assert np.array_equal(to_bits(xa), to_bits(xb))
+    else:
+        assert np.all(np.abs(ga - gb) <= 2.0 ** -7 * np.abs(gb) + DECODE_TOL * scale)
+    want = oracle.bf16_to_f32(oracle.residual_bf16(x0, blk["out"])).astype(np.float64)
+    assert np.all(np.abs(ga - want) <= 2.0 ** -7 * np.abs(want) + SPEC_TOL * scale)
+    del layer
+    torch.cuda.empty_cache()
+
+
 def test_stack_megakernel(bq):
     """The one-launch stacked decode (moe_stack_decode) over the stacked
     workload's first five blocks (6-, 4-, 4-, 4- and 8-bit), three tokens.
