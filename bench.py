@@ -616,7 +616,7 @@ def main():
     a = ap.parse_args()
 
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "bench.py runs on one GPU only; --gpus must be 1 "
                                    "(the multi-GPU sharding is described in the design notes, not built)"}))
         sys.exit(2)
 

@@ -1,6 +1,6 @@
 """Host-side checks of bench.py that need no GPU: every workload name parses,
 and no function refers to a module-level name that does not exist (the
-paths that only run on the GPU machine would otherwise fail there first)."""
+paths that only run with a GPU would otherwise fail only there)."""
 import ast
 import builtins
 import os
