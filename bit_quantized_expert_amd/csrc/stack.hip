@@ -488,7 +488,6 @@ extern "C" int moe_stack_table_write(const moe_layer_desc* layers, const uint16_
                                      void* table) {
   if (!layers || !w_router || !table || nlayers <= 0)
     return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack_table_write: NULL pointer or nlayers=%d", nlayers);
-  StackLayer* host = new StackLayer[nlayers];
   for (int l = 0; l < nlayers; ++l) {
     const moe_layer_desc* L = layers + l;
     int rc = validate_layer(L);
@@ -500,16 +499,21 @@ extern "C" int moe_stack_table_write(const moe_layer_desc* layers, const uint16_
     if (rc == MOEQ_OK && !w_router[l]) rc = set_error(MOEQ_ERR_INVALID_ARG, "moe_stack_table_write: router %d NULL", l);
     if (rc == MOEQ_OK && !aligned16(w_router[l]))
       rc = set_error(MOEQ_ERR_MISALIGNED, "moe_stack_table_write: router %d must be 16-byte aligned", l);
-    if (rc != MOEQ_OK) {
-      delete[] host;
-      return rc;
-    }
-    host[l] = StackLayer{L->gate.q, L->gate.sz, L->up.q, L->up.sz, L->down.q, L->down.sz, w_router[l],
-                         L->gate.bits, L->down.bits};
+    if (rc != MOEQ_OK) return rc;
   }
-  const hipError_t e = hipMemcpy(table, host, (size_t)nlayers * sizeof(StackLayer), hipMemcpyHostToDevice);
-  delete[] host;
-  if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "moe_stack_table_write: %s", hipGetErrorString(e));
+  // staged through a fixed host buffer, 64 layers at a time (no allocation)
+  StackLayer buf[64];
+  for (int l0 = 0; l0 < nlayers; l0 += 64) {
+    const int n = nlayers - l0 < 64 ? nlayers - l0 : 64;
+    for (int i = 0; i < n; ++i) {
+      const moe_layer_desc* L = layers + l0 + i;
+      buf[i] = StackLayer{L->gate.q, L->gate.sz, L->up.q, L->up.sz, L->down.q, L->down.sz, w_router[l0 + i],
+                          L->gate.bits, L->down.bits};
+    }
+    const hipError_t e = hipMemcpy(static_cast<char*>(table) + (size_t)l0 * sizeof(StackLayer), buf,
+                                   (size_t)n * sizeof(StackLayer), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "moe_stack_table_write: %s", hipGetErrorString(e));
+  }
   return MOEQ_OK;
 }
 
