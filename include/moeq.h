@@ -294,7 +294,8 @@ int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, const uint16_
                        int32_t* topk_idx, float* topk_w, uint16_t* out,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* One block of a stacked decode step: x <- x + moe(RMSNorm(x)) in place, for
+/* One block of a stacked decode step (fewer launches per block: Raon-1-mini,
+ * optimisation table): x <- x + moe(RMSNorm(x)) in place, for
  * a batch of T <= 64 token rows x (device bf16 [T][H]); the RMSNorm is
  * moe_rmsnorm's (gamma = 1, eps), formed inside the router launch by every
  * router block for itself (so the step is three launches, not four), the
