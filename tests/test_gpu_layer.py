@@ -380,6 +380,15 @@ def test_prefill_layer_sampled(bq, T):
     check_layer(bq, "moe_h2048_e128_k8_b6_zipf", T, prefill=True, sample=48)
 
 
+@pytest.mark.parametrize("T", [130, 600])
+def test_prefill_shared_expert(bq, T):
+    """Prefill with a shared expert (256 routed + 1 shared, 4-bit): the
+    shared expert takes every token (tiles of 128 plus a ragged one), the
+    routed ones few each."""
+    print(f"prefill 256-expert + shared T={T}", flush=True)
+    check_layer(bq, "moe_h2048_e256_k8_s1_b4", T, prefill=True, batch=7)
+
+
 def test_prefill_wide_sampled(bq):
     print("prefill 512-expert hot T=8192 (sampled)", flush=True)
     check_layer(bq, "moe_h4096_e512_k10_b4_hot", 8192, prefill=True, sample=24)
