@@ -322,6 +322,14 @@ def test_stack_megakernel(bq):
         err = rel_err(oracle.bf16_to_f32(prev), oracle.bf16_to_f32(xo))
         print(f"  stack megakernel token {step}: end-to-end rel err {err:.2e}", flush=True)
         assert err <= SPEC_TOL, (step, err)
+    # no blocks: nothing runs, x is left as it was
+    x0 = synth.activations_bf16(w, 1, batch=30)
+    xz = bf16_tensor(x0).reshape(-1)
+    sd.run(xz, nlayers=0)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(xz), x0.reshape(-1))
+    with pytest.raises(ValueError):
+        sd.run(xz, nlayers=len(bits) + 1)
     del sd, layers
     torch.cuda.empty_cache()
 

@@ -73,6 +73,16 @@ def test_quantize_hqq_l1_bitexact(bq, bits, shape):
     assert np.array_equal(got_sz, device_sz(_sz_from_oracle(s16, z16)))
 
 
+@pytest.mark.parametrize("iters,beta,kappa", [(1, 10.0, 1.01), (3, 2.0, 1.5), (50, 10.0, 1.01)])
+def test_quantize_hqq_l1_rounds_bitexact(bq, iters, beta, kappa):
+    """Other round counts and penalty schedules, p = 1: bit-exact."""
+    w = _weights(iters * 5, (2, 64, 256))
+    got_q, got_sz = _hqq_gpu(bq, w, 4, lp=1.0, beta=beta, kappa=kappa, iters=iters)
+    q, s16, z16 = oracle.hqq_refine(w.reshape(-1, 256), 4, lp=1.0, beta=beta, kappa=kappa, iters=iters)
+    assert np.array_equal(got_q, device_packed(q, 4))
+    assert np.array_equal(got_sz, device_sz(_sz_from_oracle(s16, z16)))
+
+
 @pytest.mark.parametrize("bits", [4, 6, 8])
 def test_quantize_hqq_no_rounds_is_minmax(bq, bits):
     w = _weights(bits * 13, (2, 64, 256))
