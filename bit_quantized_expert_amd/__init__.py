@@ -9,8 +9,10 @@ package without the built library raises -- there is no fallback.
 Functions carry the names of the C entry points (see ``include/moeq.h``):
 ``moe_quantize``, ``moe_quantize_hqq``, ``moe_kv_encode``, ``moe_kv_decode``, ``moe_unpack``, ``moe_route_topk``, ``moe_permute``,
 ``moe_route_permute_decode``, ``moe_qgemv_decode``, ``moe_qgemm_prefill``,
-``moe_combine``, ``moe_decode_forward``, ``moe_rmsnorm``,
-``moe_workspace_bytes``, ``moe_read_status``.
+``moe_combine``, ``moe_decode_forward``, ``moe_decode_block``, ``moe_rmsnorm``,
+``moe_workspace_bytes``, ``moe_read_status``, ``moe_pack``, ``moe_qweight_load``
+(plus ``StackDecoder`` for the stacked-decode calls and ``quantize_layer``,
+which quantises a whole layer on the device from fp32 host arrays).
 """
 from __future__ import annotations
 
@@ -65,8 +67,9 @@ def lib() -> ctypes.CDLL:
             "moe_kv_encode": (I, [P, L64, I, I, P, P, P]),
             "moe_stack_table_bytes": (SZ, [I]),
             "moe_stack_workspace_bytes": (SZ, [P]),
-            "moe_stack_table_write": (I, [P, P, I, P]),
-            "moe_stack_decode": (I, [P, P, I, ctypes.c_float, P, P, SZ, P]),
+            "moe_stack_table_write": (I, [P, P, I, P, SZ]),
+            "moe_stack_decode": (I, [P, P, SZ, I, ctypes.c_float, P, P, SZ, P]),
+            "moe_stack_read_status": (I, [P, SZ, P, P, P]),
             "moe_kv_decode": (I, [P, P, L64, I, I, P, P]),
             "moe_route_topk": (I, [P, P, P, I, I, I, I, P, P, P, P, SZ, P]),
             "moe_permute": (I, [P, I, I, I, I, P, P, P, P, P, P, SZ, P]),
@@ -78,6 +81,8 @@ def lib() -> ctypes.CDLL:
             "moe_combine": (I, [P, I, P, P, I, I, I, I, P, P]),
             "moe_rmsnorm": (I, [P, P, I, I, ctypes.c_float, P, P]),
             "moe_read_status": (I, [P, SZ, P, P]),
+            "moe_pack": (I, [P, L64, I, I, P]),
+            "moe_qweight_load": (I, [P, P, P, L64, I, I, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -141,6 +146,43 @@ def moe_quantize(w: torch.Tensor, bits: int, out: Optional[QWeight] = None, stre
     return out
 
 
+def moe_pack(codes, bits: int):
+    """Host codes [N, K] (uint8 numpy array, each < 2^bits) -> plain packed
+    rows [N, K*bits/8] (uint8 numpy array), by the library's host routine."""
+    import numpy as np
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    N, K = c.shape
+    out = np.empty((N, K * bits // 8), np.uint8)
+    _check(lib().moe_pack(c.ctypes.data_as(ctypes.c_void_p), N, K, bits, out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def moe_qweight_load(packed: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor, K: int, bits: int,
+                     out: Optional[QWeight] = None, stream=None) -> QWeight:
+    """Plain packed codes [..., N, K*bits/8] (device uint8) with fp16 scale and
+    zero [..., N, K/64] (device) -> the kernels' tiled QWeight."""
+    _dev(packed, torch.uint8, "packed")
+    _dev(scale, torch.float16, "scale")
+    _dev(zero, torch.float16, "zero")
+    rows = packed.numel() // (K * bits // 8)
+    if scale.numel() != rows * (K // GROUP) or zero.numel() != scale.numel():
+        raise ValueError("scale and zero must hold one value per row and group of 64")
+    if out is None:
+        q = torch.empty_like(packed)
+        sz = torch.empty(scale.shape, dtype=torch.int32, device=packed.device)
+        out = QWeight(q, sz, bits)
+    _check(lib().moe_qweight_load(_p(packed), _p(scale), _p(zero), rows, K, bits, _p(out.q), _p(out.sz),
+                                  _stream(stream)))
+    return out
+
+
+def bf16_from_bits(bits_u16, device="cuda") -> torch.Tensor:
+    """bf16 tensor on the device from a numpy array of bf16 bit patterns."""
+    import numpy as np
+    a = np.ascontiguousarray(bits_u16, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).to(device).view(torch.bfloat16)
+
+
 def moe_quantize_hqq(w: torch.Tensor, bits: int, lp: float = 0.7, beta: float = 10.0, kappa: float = 1.01,
                      iters: int = 20, out: Optional[QWeight] = None, stream=None) -> QWeight:
     """moe_quantize with HQQ's zero-point refinement of every group."""
@@ -192,7 +234,7 @@ class StackDecoder:
         descs = (_LayerDesc * n)(*[l.desc() for l in layers])
         wrs = (ctypes.c_void_p * n)(*[w.data_ptr() for w in w_routers])
         self.table = torch.empty(lib().moe_stack_table_bytes(n), dtype=torch.uint8, device=device)
-        _check(lib().moe_stack_table_write(descs, wrs, n, _p(self.table)))
+        _check(lib().moe_stack_table_write(descs, wrs, n, _p(self.table), self.table.numel()))
         self.n = n
         self.dims = layers[0].desc()
         nbytes = lib().moe_stack_workspace_bytes(ctypes.byref(self.dims))
@@ -205,9 +247,18 @@ class StackDecoder:
         n = self.n if nlayers is None else nlayers
         if not 0 <= n <= self.n:
             raise ValueError(f"nlayers={n}: the table holds {self.n} layers")
-        _check(lib().moe_stack_decode(ctypes.byref(self.dims), _p(self.table), n, eps, _p(x), _p(self.ws),
-                                      self.ws.numel(), _stream(stream)))
+        _check(lib().moe_stack_decode(ctypes.byref(self.dims), _p(self.table), self.table.numel(), n, eps, _p(x),
+                                      _p(self.ws), self.ws.numel(), _stream(stream)))
         return x
+
+    def read_status(self, stream=None) -> int:
+        """Synchronise and return the workspace's error word (0 = none since
+        the last read; bit 1: a grid barrier gave up; bit 2: table mismatch);
+        a non-zero word is cleared with the control words."""
+        v = ctypes.c_int(0)
+        _check(lib().moe_stack_read_status(_p(self.ws), self.ws.numel(), ctypes.byref(self.dims), ctypes.byref(v),
+                                           _stream(stream)))
+        return v.value
 
 
 def moe_unpack(q: torch.Tensor, K: int, bits: int, stream=None) -> torch.Tensor:
@@ -240,6 +291,33 @@ class QuantLayer:
     def workspace(self, T_max: int, device="cuda") -> torch.Tensor:
         # zero-filled: the library's control words start (and stay) at zero
         return torch.zeros(max(256, self.workspace_bytes(T_max)), dtype=torch.uint8, device=device)
+
+
+PROJECTIONS = ("gate", "up", "down")
+
+
+def quantize_layer(H: int, I: int, E: int, S: int, k: int, bits, draw, device="cuda", chunk: int = 64,
+                   stream=None) -> QuantLayer:
+    """Quantise a layer's expert weights on the device (moe_quantize), from
+    fp32 host arrays drawn ``chunk`` experts at a time: ``draw(proj, experts)``
+    returns [len(experts), N, K] float32 for proj in "gate", "up" (N = I,
+    K = H) and "down" (N = H, K = I).  ``bits``: one width, or a dict per
+    projection."""
+    n = E + S
+    projs = {}
+    for name in PROJECTIONS:
+        b = bits[name] if isinstance(bits, dict) else bits
+        N, K = (I, H) if name != "down" else (H, I)
+        q = torch.empty((n, N, K * b // 8), dtype=torch.uint8, device=device)
+        sz = torch.empty((n, N, K // GROUP), dtype=torch.int32, device=device)
+        for e0 in range(0, n, chunk):
+            es = list(range(e0, min(n, e0 + chunk)))
+            wd = torch.from_numpy(draw(name, es)).to(device)
+            moe_quantize(wd, b, out=QWeight(q[e0:e0 + len(es)], sz[e0:e0 + len(es)], b), stream=stream)
+            del wd
+        projs[name] = QWeight(q, sz, b)
+    torch.cuda.synchronize()
+    return QuantLayer(H, I, E, S, k, projs["gate"], projs["up"], projs["down"])
 
 
 def moe_workspace_bytes(layer: QuantLayer, T_max: int) -> int:

@@ -28,11 +28,22 @@
 //
 // Everything one block writes and another reads (logits, partial sums, h,
 // x, the barrier words) goes through device-scope atomic loads and stores,
-// which the hardware keeps coherent across the XCDs' separate L2 caches;
-// ordering inside a wavefront comes from waiting for its stores to complete
-// before it signals.  So no device-scope fence (an L2 write-back or
+// which the hardware keeps coherent across the XCDs' separate L2 caches.
+// A wavefront orders its stores before its signal by waiting for its
+// vector-memory counter to reach zero (s_waitcnt vmcnt(0): on gfx9 the
+// counter covers stores too, and a device-scope store counts as done once it
+// is visible device-wide) immediately before every arrival; the loads that
+// follow an arrival depend on the arrival's returned value, so they are
+// issued after it.  So no device-scope fence (an L2 write-back or
 // invalidate) is needed anywhere: the weights stay cached, and a barrier
 // costs one round of atomics.
+//
+// The table starts with a 64-byte header (layer count and H, I, E, k, S = 0)
+// that every block checks against the launch's dimensions before it touches
+// a layer; on a mismatch every block leaves at once (none has reached a
+// barrier) and the workspace's error word gets bit 2.  A barrier wait that
+// gives up (after about 2^26 sleeps) sets bit 1.  The error word is sticky
+// until moe_stack_read_status reads it.
 #include "decode_impl.h"
 
 using namespace moeq;
@@ -43,6 +54,14 @@ namespace {
 constexpr int kMaxH = 8192;      // LDS: n, bf16
 constexpr int kMaxKI = 16384;    // LDS: h of all slots, bf16
 constexpr int kMaxK = 16;
+
+struct StackHeader {  // 64 bytes before the layers
+  uint32_t magic, nlayers;
+  int H, I, E, k;
+  uint32_t pad[10];
+};
+static_assert(sizeof(StackHeader) == 64, "table header");
+constexpr uint32_t kStackMagic = 0x4B545351u;   // "QSTK"
 
 struct StackLayer {   // one block's weights (device pointers), 64 bytes
   const uint8_t* gq;
@@ -71,7 +90,7 @@ struct StackWs {
   int* gu_cnt;       // [k][I/64], 16 ints apart, zero between uses
   int* y_cnt;        // [H/64], 16 ints apart, zero between uses
   unsigned* bar;     // [0] arrivals (zero between barriers), [1] generation
-  int* err;          // set if a barrier wait gave up
+  int* err;          // bit 1: a barrier wait gave up; bit 2: table mismatch
 };
 
 // device-coherent accesses (see the header comment)
@@ -81,8 +100,12 @@ MOEQ_DEV uint32_t ld_u(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 MOEQ_DEV void st_u(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-// this wavefront's memory operations complete before what follows
-MOEQ_DEV void wave_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup"); }
+// Wait until every vector-memory operation this wavefront issued has
+// completed (s_waitcnt vmcnt(0), expcnt and lgkmcnt left free): its
+// device-scope stores are then visible to every XCD and its loads have
+// returned.  Issued right before each arrival at a counter.
+MOEQ_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// keeps the compiler from moving memory operations across this point
 MOEQ_DEV void wave_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup"); }
 
 // Grid-wide barrier of the co-resident blocks (cooperative launch), in two
@@ -90,13 +113,15 @@ MOEQ_DEV void wave_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgro
 // arrives at the count of group b % 8 (the blocks one XCD receives); the
 // last of a group clears that count and arrives at the top count; the last
 // of those clears it and advances the generation word of every group, on
-// which each group's blocks wait.  A block's first thread arrives once every
-// wavefront of the block has finished its stores (__syncthreads waits for
-// them).  A wait gives up after about 2^26 sleeps (seconds) and raises err,
-// so that every wavefront always reaches the end of the kernel.
+// which each group's blocks wait.  Every wavefront waits for its own stores
+// to complete before the block meets at __syncthreads, and the first thread
+// waits for its generation load and for each clearing store before its next
+// arrival.  A wait gives up after about 2^26 sleeps (seconds) and sets bit 1
+// of err, so that every wavefront always reaches the end of the kernel.
 //   bar[16 g]: count of group g; bar[128]: top count; bar[144 + 16 g]:
 //   generation of group g (words 64 bytes apart)
 MOEQ_DEV void grid_barrier(unsigned* bar, unsigned nblocks, int* err) {
+  wait_vmem();   // this wavefront's stores are visible device-wide
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned grp = blockIdx.x % 8u;
@@ -104,13 +129,16 @@ MOEQ_DEV void grid_barrier(unsigned* bar, unsigned nblocks, int* err) {
     const unsigned members = nblocks / 8u + (grp < nblocks % 8u ? 1u : 0u);
     unsigned* gen = bar + 144 + 16 * grp;
     const unsigned g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wave_acquire();   // the generation is read before arriving
+    wait_vmem();   // the generation is read before arriving
+    wave_acquire();
     if (__hip_atomic_fetch_add(bar + 16 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == members) {
       __hip_atomic_store(bar + 16 * grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wave_release();   // cleared before the group arrives above
+      wait_vmem();   // cleared before the group arrives above
+      wave_acquire();
       if (__hip_atomic_fetch_add(bar + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == ngroups) {
         __hip_atomic_store(bar + 128, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        wave_release();   // cleared before any generation moves
+        wait_vmem();   // cleared before any generation moves
+        wave_acquire();
         for (unsigned y = 0; y < ngroups; ++y)
           __hip_atomic_fetch_add(bar + 144 + 16 * y, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -119,7 +147,7 @@ MOEQ_DEV void grid_barrier(unsigned* bar, unsigned nblocks, int* err) {
     while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > (1u << 26)) {
-        __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
@@ -225,7 +253,8 @@ MOEQ_DEV void select_any(const float* logits, int E, int k, int* sel_idx, float*
 // Whether this wavefront is the last of total to arrive at a counter (its
 // stores complete before it arrives); the last one then sees everyone's.
 MOEQ_DEV bool last_arrival(int* cnt, int total) {
-  wave_release();
+  wait_vmem();
+  wave_acquire();
   int old = 0;
   if ((threadIdx.x & 63) == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
@@ -237,7 +266,7 @@ MOEQ_DEV bool last_arrival(int* cnt, int total) {
 // bf16 of this lane and of the next one as one word (for even lanes)
 MOEQ_DEV uint32_t pair_with_next(uint32_t b) { return b | (__shfl_down(b, 1) << 16); }
 
-__global__ __launch_bounds__(256) void stack_decode_kernel(const StackLayer* table, StackDims d, StackWs ws,
+__global__ __launch_bounds__(256) void stack_decode_kernel(const StackHeader* hdr, StackDims d, StackWs ws,
                                                            uint32_t* x2) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxH];
   __shared__ float xsum[kMaxH / 64];
@@ -252,6 +281,15 @@ __global__ __launch_bounds__(256) void stack_decode_kernel(const StackLayer* tab
   const int H = d.H, I = d.I, k = d.k;
   const int tI = I / 64, tH = H / 64;
   const unsigned nb = gridDim.x;
+  {
+    // every block reads the same header, so all leave or none does
+    const StackHeader h0 = *hdr;
+    if (h0.magic != kStackMagic || (int)h0.nlayers < d.L || h0.H != H || h0.I != I || h0.E != d.E || h0.k != k) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_fetch_or(ws.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+  }
+  const StackLayer* table = reinterpret_cast<const StackLayer*>(hdr + 1);
   for (int l = 0; l < d.L; ++l) {
     const StackLayer Ly = table[l];
     // ---- A: RMSNorm (every block), router rows (all wavefronts).  The
@@ -476,7 +514,9 @@ int stack_dims_ok(const moe_layer_desc* L) {
 
 }  // namespace
 
-extern "C" size_t moe_stack_table_bytes(int nlayers) { return nlayers > 0 ? (size_t)nlayers * sizeof(StackLayer) : 0; }
+extern "C" size_t moe_stack_table_bytes(int nlayers) {
+  return nlayers > 0 ? sizeof(StackHeader) + (size_t)nlayers * sizeof(StackLayer) : 0;
+}
 
 extern "C" size_t moe_stack_workspace_bytes(const moe_layer_desc* L) {
   StackLayout o;
@@ -485,9 +525,13 @@ extern "C" size_t moe_stack_workspace_bytes(const moe_layer_desc* L) {
 }
 
 extern "C" int moe_stack_table_write(const moe_layer_desc* layers, const uint16_t* const* w_router, int nlayers,
-                                     void* table) {
+                                     void* table, size_t table_bytes) {
   if (!layers || !w_router || !table || nlayers <= 0)
     return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack_table_write: NULL pointer or nlayers=%d", nlayers);
+  if (table_bytes < moe_stack_table_bytes(nlayers))
+    return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack_table_write: table of %zu bytes, %d layers need %zu", table_bytes,
+                     nlayers, moe_stack_table_bytes(nlayers));
+  if (!aligned16(table)) return set_error(MOEQ_ERR_MISALIGNED, "moe_stack_table_write: table must be 16-byte aligned");
   for (int l = 0; l < nlayers; ++l) {
     const moe_layer_desc* L = layers + l;
     int rc = validate_layer(L);
@@ -501,6 +545,16 @@ extern "C" int moe_stack_table_write(const moe_layer_desc* layers, const uint16_
       rc = set_error(MOEQ_ERR_MISALIGNED, "moe_stack_table_write: router %d must be 16-byte aligned", l);
     if (rc != MOEQ_OK) return rc;
   }
+  StackHeader hd{};
+  hd.magic = kStackMagic;
+  hd.nlayers = (uint32_t)nlayers;
+  hd.H = layers[0].H;
+  hd.I = layers[0].I;
+  hd.E = layers[0].E;
+  hd.k = layers[0].k;
+  hipError_t he = hipMemcpy(table, &hd, sizeof(hd), hipMemcpyHostToDevice);
+  if (he != hipSuccess) return set_error(MOEQ_ERR_HIP, "moe_stack_table_write: %s", hipGetErrorString(he));
+  char* body = static_cast<char*>(table) + sizeof(StackHeader);
   // staged through a fixed host buffer, 64 layers at a time (no allocation)
   StackLayer buf[64];
   for (int l0 = 0; l0 < nlayers; l0 += 64) {
@@ -510,18 +564,20 @@ extern "C" int moe_stack_table_write(const moe_layer_desc* layers, const uint16_
       buf[i] = StackLayer{L->gate.q, L->gate.sz, L->up.q, L->up.sz, L->down.q, L->down.sz, w_router[l0 + i],
                           L->gate.bits, L->down.bits};
     }
-    const hipError_t e = hipMemcpy(static_cast<char*>(table) + (size_t)l0 * sizeof(StackLayer), buf,
+    const hipError_t e = hipMemcpy(body + (size_t)l0 * sizeof(StackLayer), buf,
                                    (size_t)n * sizeof(StackLayer), hipMemcpyHostToDevice);
     if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "moe_stack_table_write: %s", hipGetErrorString(e));
   }
   return MOEQ_OK;
 }
 
-extern "C" int moe_stack_decode(const moe_layer_desc* dims, const void* table, int nlayers, float eps, uint16_t* x,
-                                void* ws, size_t ws_bytes, hipStream_t stream) {
+extern "C" int moe_stack_decode(const moe_layer_desc* dims, const void* table, size_t table_bytes, int nlayers,
+                                float eps, uint16_t* x, void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc = stack_dims_ok(dims);
   if (rc != MOEQ_OK) return rc;
   if (!table || !x || nlayers < 0) return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack_decode: NULL pointer or nlayers=%d", nlayers);
+  if (table_bytes < moe_stack_table_bytes(nlayers > 0 ? nlayers : 1))
+    return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack_decode: table of %zu bytes cannot hold %d layers", table_bytes, nlayers);
   if (!(eps >= 0.0f)) return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack_decode: eps=%g", (double)eps);
   if (!aligned16(x) || !aligned16(table)) return set_error(MOEQ_ERR_MISALIGNED, "moe_stack_decode: x and table must be 16-byte aligned");
   if (nlayers == 0) return MOEQ_OK;
@@ -535,11 +591,37 @@ extern "C" int moe_stack_decode(const moe_layer_desc* dims, const void* table, i
              reinterpret_cast<int*>(w + o.gu_cnt), reinterpret_cast<int*>(w + o.y_cnt),
              reinterpret_cast<unsigned*>(w + o.bar), reinterpret_cast<int*>(w + o.bar) + 280};
   StackDims sd{dims->H, dims->I, dims->E, dims->k, nlayers, o.P, o.PD, eps};
-  const StackLayer* tp = static_cast<const StackLayer*>(table);
+  const StackHeader* tp = static_cast<const StackHeader*>(table);
   uint32_t* x2 = reinterpret_cast<uint32_t*>(x);
   void* args[] = {&tp, &sd, &sw, &x2};
   const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(stack_decode_kernel), dim3(o.nb),
                                                   dim3(256), args, 0, stream);
   if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "moe_stack_decode: cooperative launch failed: %s", hipGetErrorString(e));
   return check_launch("moe_stack_decode");
+}
+
+extern "C" int moe_stack_read_status(void* ws, size_t ws_bytes, const moe_layer_desc* dims, int* err,
+                                     hipStream_t stream) {
+  if (!ws || !err) return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack_read_status: NULL workspace or output");
+  int rc = stack_dims_ok(dims);
+  if (rc != MOEQ_OK) return rc;
+  StackLayout o;
+  if ((rc = stack_layout(dims, &o)) != MOEQ_OK) return rc;
+  if (ws_bytes < o.total)
+    return set_error(MOEQ_ERR_WORKSPACE, "moe_stack_read_status: workspace of %zu bytes, need %zu", ws_bytes, o.total);
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  char* w = static_cast<char*>(ws);
+  int v = 0;
+  e = hipMemcpy(&v, w + o.bar + 280 * sizeof(int), sizeof(int), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "hipMemcpy: %s", hipGetErrorString(e));
+  if (v != 0) {
+    // a wait that gave up leaves counts behind: zero every control word
+    // (the counters, the barrier words and the error word) for the next call
+    e = hipMemset(w + o.gu_cnt, 0, o.total - o.gu_cnt);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "hipMemset: %s", hipGetErrorString(e));
+  }
+  *err = v;
+  return MOEQ_OK;
 }

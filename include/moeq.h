@@ -117,6 +117,31 @@ const char* moe_last_error(void);
 int moe_quantize(const float* w, long rows, int K, int bits,
                  uint8_t* q, uint32_t* sz, hipStream_t stream);
 
+/* Pack codes (host, one byte per code, codes [N][K], each < 2^bits) into the
+ * plain row form an offline quantiser stores (host, packed [N][K*bits/8]):
+ *   4-bit: byte i of a row = code 2i | code 2i+1 << 4 (two nibbles a byte);
+ *   6-bit: bytes 3i..3i+2 = the 24-bit little-endian word
+ *          code 4i | code 4i+1 << 6 | code 4i+2 << 12 | code 4i+3 << 18
+ *          (groups of four values in three bytes);
+ *   8-bit: one byte per code.
+ * HQQ weights are made once by a preprocessing stage before the hot path
+ * (Krasis update, "Latest updates"); this is their storage form.  K must be
+ * a multiple of 4; a code >= 2^bits is MOEQ_ERR_INVALID_ARG (nothing past
+ * the check is written).  Host memory only; no GPU work. */
+int moe_pack(const uint8_t* codes, long N, int K, int bits, uint8_t* packed);
+
+/* Lay weights in moe_pack's plain form (device packed [rows][K*bits/8]) with
+ * their fp16 scales and zeros (device scale [rows][K/64], zero [rows][K/64],
+ * group g = inputs 64g .. 64g+63 of a row) out into the layout of
+ * moe_qweight (device q, rows*K*bits/8 bytes, and sz, rows*K/64 words;
+ * 16-byte aligned).  The dequantised weight of the result is
+ * (code - zero) * scale exactly as given: this is how weights quantised
+ * elsewhere (HQQ assets, Krasis update, "Latest updates") enter the forward
+ * path.  rows and K multiples of 64; the inputs need no alignment beyond
+ * their element types.  Enqueued on stream; allocates nothing. */
+int moe_qweight_load(const uint8_t* packed, const uint16_t* scale, const uint16_t* zero, long rows, int K,
+                     int bits, uint8_t* q, uint32_t* sz, hipStream_t stream);
+
 /* moe_quantize followed by HQQ's zero-point refinement of every group, the
  * half-quadratic solver of Badri & Shaji ("Half-Quadratic Quantization of
  * Large Machine Learning Models", 2023) with the scale held (the pages name
@@ -142,19 +167,20 @@ int moe_quantize_hqq(const float* w, long rows, int K, int bits,
  * per-layer MoE megakernel instead of many small launches)
  * ------------------------------------------------------------------------ */
 
-/* Bytes of the device table moe_stack_table_write fills for nlayers layers
- * (64 per layer); 0 if nlayers <= 0. */
+/* Bytes of the device table moe_stack_table_write fills for nlayers layers:
+ * a 64-byte header (layer count, H, I, E, k) and 64 bytes per layer; 0 if
+ * nlayers <= 0. */
 size_t moe_stack_table_bytes(int nlayers);
 
 /* Write the device table of nlayers MoE layers (host array layers[], each
  * with its own weights and bit widths but the same H, I, E, k and S = 0;
  * gate and up of a layer share a bit width) and their bf16 router weights
  * (host array of device pointers w_router[l], [E][H], 16-byte aligned) into
- * table (device, moe_stack_table_bytes(nlayers) bytes, 16-byte aligned).
- * A setup call: it copies synchronously (hipMemcpy).  The weights must stay
- * allocated while the table is used. */
+ * table (device, table_bytes >= moe_stack_table_bytes(nlayers), 16-byte
+ * aligned).  A setup call: it copies synchronously (hipMemcpy).  The weights
+ * must stay allocated while the table is used. */
 int moe_stack_table_write(const moe_layer_desc* layers, const uint16_t* const* w_router, int nlayers,
-                          void* table);
+                          void* table, size_t table_bytes);
 
 /* Workspace bytes moe_stack_decode needs for layers of the dimensions of L
  * on the current device (it depends on the device's CU count); 0 if L is
@@ -162,17 +188,31 @@ int moe_stack_table_write(const moe_layer_desc* layers, const uint16_t* const* w
  * k*I <= 16384, k <= 16, k <= E <= 1024, S = 0).  Zero-fill it once. */
 size_t moe_stack_workspace_bytes(const moe_layer_desc* L);
 
-/* One batch-1 token through the first nlayers layers of table: for each
- * layer, n = RMSNorm(x) (as moe_rmsnorm, gamma = 1, eps), routed MoE of n
- * (top-k, renormalised weights, SwiGLU experts with h rounded to bf16, fp32
- * accumulation), x = bf16(x + bf16(moe)).  x: device bf16 [H], updated in
- * place.  dims: any layer's descriptor (only H, I, E, k, S are read).  One
- * cooperative launch whose blocks meet at grid-wide barriers three times per
- * layer; it fails (MOEQ_ERR_HIP) if the device cannot hold the grid at once.
+/* One batch-1 token through the first nlayers layers of table (the layer
+ * sequence of a model's decode step, each block RMSNorm -> MoE -> residual;
+ * Raon-1-mini, optimisation table: a persistent per-layer MoE megakernel
+ * instead of many small launches): for each layer, n = RMSNorm(x) (as
+ * moe_rmsnorm, gamma = 1, eps), routed MoE of n (top-k, renormalised
+ * weights, SwiGLU experts with h rounded to bf16, fp32 accumulation),
+ * x = bf16(x + bf16(moe)).  x: device bf16 [H], updated in place.  dims: any
+ * layer's descriptor (only H, I, E, k, S are read); table_bytes: the size
+ * of table.  One cooperative launch whose blocks meet at grid-wide barriers
+ * three times per layer; it fails (MOEQ_ERR_HIP) if the device cannot hold
+ * the grid at once.  The kernel checks the table's header against dims and
+ * nlayers and, on a mismatch, leaves x untouched and sets bit 2 of the
+ * workspace's error word; a grid barrier that waits for seconds gives up and
+ * sets bit 1 (x is then wrong).  Read the word with moe_stack_read_status.
  * The K sums are split across wavefronts, so results equal
  * moe_rmsnorm + moe_decode_forward to rounding, not bit for bit. */
-int moe_stack_decode(const moe_layer_desc* dims, const void* table, int nlayers, float eps, uint16_t* x,
-                     void* ws, size_t ws_bytes, hipStream_t stream);
+int moe_stack_decode(const moe_layer_desc* dims, const void* table, size_t table_bytes, int nlayers, float eps,
+                     uint16_t* x, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Synchronise `stream` and return in *err the error word of a
+ * moe_stack_decode workspace (0: no error since the last read; bit 1: a
+ * grid barrier gave up; bit 2: the table did not match).  A non-zero word is
+ * cleared together with the workspace's counters and barrier words, so the
+ * next call starts clean.  dims as for moe_stack_workspace_bytes. */
+int moe_stack_read_status(void* ws, size_t ws_bytes, const moe_layer_desc* dims, int* err, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Group-quantised KV cache (the same codec on cache rows; Krasis update,

@@ -12,8 +12,8 @@ PROJ = {"gate": synth.T_GATE, "up": synth.T_UP, "down": synth.T_DOWN}
 
 
 def bf16_tensor(bits_u16: np.ndarray, device="cuda"):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).to(device).view(torch.bfloat16)
+    import bit_quantized_expert_amd as bq
+    return bq.bf16_from_bits(bits_u16, device)
 
 
 def to_bits(t) -> np.ndarray:
@@ -21,29 +21,18 @@ def to_bits(t) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def synth_draw(w: synth.Workload, layer: int = 0):
+    """draw(proj, experts) of the seeded fp32 expert weights, for
+    bit_quantized_expert_amd.quantize_layer."""
+    return lambda name, es: synth.expert_weights_f32(w, layer, PROJ[name], es)
+
+
 def gpu_layer(w: synth.Workload, layer: int = 0, bits=None, device="cuda", chunk=64):
     """Quantise every expert's weights on the device (HIP path) from the
     seeded fp32 draws, streaming ``chunk`` experts at a time."""
-    import torch
     import bit_quantized_expert_amd as bq
-    bits = bits or w.bits
-    n = w.n_mats
-    projs = {}
-    for name, tid in PROJ.items():
-        N, K = (w.I, w.H) if name != "down" else (w.H, w.I)
-        q = torch.empty((n, N, K * bits // 8), dtype=torch.uint8, device=device)
-        sz = torch.empty((n, N, K // 64), dtype=torch.int32, device=device)
-        qw = bq.QWeight(q, sz, bits)
-        for e0 in range(0, n, chunk):
-            es = list(range(e0, min(n, e0 + chunk)))
-            host = synth.expert_weights_f32(w, layer, tid, es)
-            wd = torch.from_numpy(host).to(device)
-            part = bq.QWeight(q[e0:e0 + len(es)], sz[e0:e0 + len(es)], bits)
-            bq.moe_quantize(wd, bits, out=part)
-            del wd
-        projs[name] = qw
-    torch.cuda.synchronize()
-    return bq.QuantLayer(w.H, w.I, w.E, w.S, w.k, projs["gate"], projs["up"], projs["down"])
+    return bq.quantize_layer(w.H, w.I, w.E, w.S, w.k, bits or w.bits, synth_draw(w, layer), device=device,
+                             chunk=chunk)
 
 
 class LazyExperts:

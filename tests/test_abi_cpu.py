@@ -57,9 +57,10 @@ def test_host_validation(bq):
     assert L.moe_decode_block(ok, None, ok, None, 1, ctypes.c_float(1e-6), ok, ok, ok, ok, 0, None) == -1
     assert L.moe_decode_block(ok, ok, ok, None, 1, ctypes.c_float(-1.0), ok, ok, ok, ok, 0, None) == -1
     # stacked decode: argument checks before any device query or launch
-    assert L.moe_stack_table_bytes(0) == 0 and L.moe_stack_table_bytes(3) == 192
-    assert L.moe_stack_table_write(None, None, 2, ok) == -1
-    assert L.moe_stack_decode(None, ok, 1, ctypes.c_float(1e-6), ok, ok, 0, None) == -1
+    assert L.moe_stack_table_bytes(0) == 0 and L.moe_stack_table_bytes(3) == 64 + 192
+    assert L.moe_stack_table_write(None, None, 2, ok, 1 << 20) == -1
+    assert L.moe_stack_decode(None, ok, 1 << 20, 1, ctypes.c_float(1e-6), ok, ok, 0, None) == -1
+    assert L.moe_stack_read_status(None, 0, None, None, None) == -1
     # KV codec
     assert L.moe_kv_encode(None, 4, 64, 4, ok, ok, None) == -1
     assert L.moe_kv_encode(ok, 4, 64, 5, ok, ok, None) == -2 and "bits" in _err(L)
@@ -118,3 +119,40 @@ def test_workspace_grows_with_batch(bq):
     a, b = L.moe_workspace_bytes(ctypes.byref(d), 1), L.moe_workspace_bytes(ctypes.byref(d), 8192)
     assert 0 < a < b
     assert b >= 8192 * 10 * 768 * 4
+
+
+@pytest.mark.parametrize("bits", [4, 6, 8])
+def test_pack_matches_oracle(bq, bits):
+    """moe_pack (the library's host routine) writes the plain packed rows the
+    oracle's pack writes, byte for byte, on random codes and on every code
+    value at every position of a pack unit."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(bits)
+    codes = rng.integers(0, 1 << bits, size=(37, 192), dtype=np.uint8)
+    assert np.array_equal(bq.moe_pack(codes, bits), oracle.pack(codes, bits))
+    # each value at each of the 4 positions of a 4-code unit (covers both
+    # nibbles and all four 6-bit fields)
+    vals = np.arange(1 << bits, dtype=np.uint8)
+    unit = np.zeros((vals.size * 4, 4), np.uint8)
+    for p in range(4):
+        unit[p * vals.size:(p + 1) * vals.size, p] = vals
+    assert np.array_equal(bq.moe_pack(unit, bits), oracle.pack(unit, bits))
+
+
+def test_pack_rejects_bad_input(bq):
+    import numpy as np
+    L = bq.lib()
+    P = ctypes.c_void_p
+    bad = np.array([[0, 16, 1, 2]], np.uint8)
+    out = np.zeros(4, np.uint8)
+    assert L.moe_pack(bad.ctypes.data_as(P), 1, 4, 4, out.ctypes.data_as(P)) == -1 and "exceeds" in _err(L)
+    assert L.moe_pack(bad.ctypes.data_as(P), 1, 4, 5, out.ctypes.data_as(P)) == -2
+    assert L.moe_pack(bad.ctypes.data_as(P), 1, 3, 8, out.ctypes.data_as(P)) == -2
+    assert L.moe_pack(None, 1, 4, 8, out.ctypes.data_as(P)) == -1
+    ok = P(4096)
+    assert L.moe_qweight_load(ok, ok, ok, 64, 64, 5, ok, ok, None) == -2
+    assert L.moe_qweight_load(ok, ok, ok, 32, 64, 4, ok, ok, None) == -2
+    assert L.moe_qweight_load(ok, ok, ok, 64, 64, 4, P(4096 + 4), ok, None) == -3
+    assert L.moe_qweight_load(None, ok, ok, 64, 64, 4, ok, ok, None) == -1
+    assert L.moe_qweight_load(ok, ok, ok, 0, 64, 4, ok, ok, None) == 0     # nothing to do, no launch

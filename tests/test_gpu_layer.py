@@ -330,6 +330,7 @@ def test_stack_megakernel(bq):
     assert np.array_equal(to_bits(xz), x0.reshape(-1))
     with pytest.raises(ValueError):
         sd.run(xz, nlayers=len(bits) + 1)
+    assert sd.read_status() == 0     # no barrier gave up, the table matched
     del sd, layers
     torch.cuda.empty_cache()
 

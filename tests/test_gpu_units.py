@@ -53,6 +53,33 @@ def test_quantize_bitexact(bq, bits, shape):
     assert np.array_equal(got_sz, device_sz(_sz_from_oracle(s16, z16)))
 
 
+@pytest.mark.parametrize("bits", [4, 6, 8])
+@pytest.mark.parametrize("shape", [(3, 64, 512), (2, 128, 192), (1, 64, 64)])
+def test_qweight_load_bitexact(bq, bits, shape):
+    """Weights quantised elsewhere enter through moe_pack + moe_qweight_load:
+    the oracle's codes, packed by the library's host routine, with separate
+    fp16 scale and zero arrays, land byte for byte where moe_quantize puts
+    the same weights (and where the oracle's own model of the device layout
+    puts them)."""
+    w = _weights(bits * 11 + shape[1], shape)
+    K = shape[-1]
+    q, s16, z16 = oracle.quantize(w.reshape(-1, K), bits)
+    packed = bq.moe_pack(q, bits)
+    assert np.array_equal(packed, oracle.pack(q, bits))
+    qw = bq.moe_qweight_load(torch.from_numpy(packed).cuda(), torch.from_numpy(s16).cuda(),
+                             torch.from_numpy(z16).cuda(), K, bits)
+    ref = bq.moe_quantize(torch.from_numpy(w).cuda(), bits)
+    torch.cuda.synchronize()
+    got_q = qw.q.cpu().numpy().reshape(-1)
+    got_sz = qw.sz.cpu().numpy().view(np.uint32).reshape(-1)
+    assert np.array_equal(got_q, ref.q.cpu().numpy().reshape(-1))
+    assert np.array_equal(got_sz, ref.sz.cpu().numpy().view(np.uint32).reshape(-1))
+    assert np.array_equal(got_q, device_packed(q, bits))
+    assert np.array_equal(got_sz, device_sz(_sz_from_oracle(s16, z16)))
+    # and the decode kernels' unpacking reads back the oracle's codes
+    assert np.array_equal(bq.moe_unpack(qw.q, K, bits).cpu().numpy().reshape(-1, K), q)
+
+
 def _hqq_gpu(bq, w, bits, **kw):
     qw = bq.moe_quantize_hqq(torch.from_numpy(w).cuda(), bits, **kw)
     torch.cuda.synchronize()
