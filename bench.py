@@ -4,14 +4,21 @@
 A step is one pass of the whole layer -- router logits, top-k routing,
 permutation, the expert FFN (decode grouped GEMV or prefill grouped GEMM)
 and the weighted combine -- over one batch of synthetic tokens whose inputs
-and weights are already resident in HBM.  The default workload is decode
-with a batch of 8 tokens on the 256-expert + 1-shared-expert, 4-bit layer.
+and weights are already resident in HBM.
+
+The default line is the largest single-GPU workload: the 125B-class wide
+layer (hidden 4096, 512 experts, intermediate 768, top-10, 10 % hot experts,
+4-bit) at a prefill chunk of 8192 tokens, its roofline against the bf16
+matrix-core peak.  The same layer at one decode token and the 256-expert +
+shared decode layer at 8 tokens are measured in the same run and nested in
+the line ("decode").
 
 Cache-honest timing: successive steps use different copies of the layer's
 weights (R replicas at distinct addresses, R * layer size >> the 256 MB
 Infinity Cache) and different token batches, the way consecutive layers of
-a model would, so weight bytes come from HBM.  The steps are captured once
-in a HIP graph (one graph holds one step per replica) and replayed.
+a model would, so weight bytes come from HBM.  The steps are captured in HIP
+graphs (one graph holds one step per replica and batch, a second one the
+remainder) and replayed: exactly --steps steps are timed.
 
 Prints one JSON line (see the field list in the design notes).
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME:T]
@@ -37,7 +44,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "bit_quantized_expert_amd", "csrc")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
-DEFAULT_WORKLOAD = "moe_h2048_e256_k8_s1_b4:8"
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte where the two peaks meet
+DEFAULT_WORKLOAD = "moe_h4096_e512_k10_b4_hot:8192"
+# measured in the same run and nested in the default line
+NESTED_DECODE = ("moe_h4096_e512_k10_b4_hot:1", "moe_h2048_e256_k8_s1_b4:8")
+NESTED_STEPS, NESTED_WARMUP = 400, 50
 
 
 def parse_workload(s):
@@ -99,6 +110,17 @@ def copy_calibrate(mib):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
+def synth_draw(w, layer=0):
+    """draw(proj, experts) of the seeded fp32 expert weights (quantize_layer)."""
+    tid = {"gate": synth.T_GATE, "up": synth.T_UP, "down": synth.T_DOWN}
+    return lambda name, es: synth.expert_weights_f32(w, layer, tid[name], es)
+
+
+def synth_layer(bq, w, layer=0, bits=None, device="cuda"):
+    """The workload's layer quantised on the device from its seeded draws."""
+    return bq.quantize_layer(w.H, w.I, w.E, w.S, w.k, bits or w.bits, synth_draw(w, layer), device=device)
+
+
 class Step:
     """Preallocated buffers and the ctypes calls of one layer step.
 
@@ -106,7 +128,7 @@ class Step:
     (router; routing + gate/up; down + combine); the others as
     route/permute, the expert FFN call and the combine."""
 
-    def __init__(self, bq, layer, wr, bias, x, T, ws):
+    def __init__(self, bq, layer, wr, bias, x, T, ws, y=None, out=None):
         import torch
         self.bq, self.L, self.T = bq, layer, T
         self.desc = layer.desc()
@@ -125,8 +147,10 @@ class Step:
         self.prefill = T > bq.DECODE_MAX_T
         self.layer_fused = not self.prefill and bq.decode_forward_ok(layer, T)
         self.fused = not self.prefill and bq.fused_route_ok(T, H, E, k, S)
-        self.y = torch.empty((A, H), dtype=torch.bfloat16 if self.prefill else torch.float32, device=dev)
-        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        # steps run one after another on one stream, so they may share these
+        self.y = y if y is not None else torch.empty((A, H), dtype=torch.bfloat16 if self.prefill else torch.float32,
+                                                     device=dev)
+        self.out = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.residual = None
 
     def distinct_experts(self) -> int:
@@ -225,12 +249,11 @@ def build_stack(bq, w, device):
     """All blocks of the stacked workload, each with its own weights and bit
     width (quantised on the device)."""
     import torch
-    from tests.gpu_util import bf16_tensor, gpu_layer
     bits = synth.layer_bits(w)
     layers, wrs = [], []
     for l, b in enumerate(bits):
-        layers.append(gpu_layer(w, layer=l, bits=b, device=device))
-        wrs.append(bf16_tensor(synth.router_weight_bf16(w, layer=l), device=device))
+        layers.append(synth_layer(bq, w, layer=l, bits=b, device=device))
+        wrs.append(bq.bf16_from_bits(synth.router_weight_bf16(w, layer=l), device=device))
     torch.cuda.synchronize()
     return layers, wrs, bits
 
@@ -239,11 +262,10 @@ def main_stack(a, w, bq, dev):
     """Stacked decode: 256 consecutive batch-1 tokens through all blocks,
     one HIP graph per token step, timed end to end."""
     import torch
-    from tests.gpu_util import bf16_tensor
     t0 = time.time()
     layers, wrs, bits = build_stack(bq, w, dev)
     n_tok = w.steps
-    xs = torch.stack([bf16_tensor(synth.activations_bf16(w, 1, batch=b), device=dev) for b in range(n_tok)])
+    xs = torch.stack([bq.bf16_from_bits(synth.activations_bf16(w, 1, batch=b), device=dev) for b in range(n_tok)])
     x = torch.empty((1, w.H), dtype=torch.bfloat16, device=dev)
     ws = layers[0].workspace(1, device=dev)
     st = StackStep(bq, layers, wrs, x, ws)
@@ -373,12 +395,42 @@ def main_stack(a, w, bq, dev):
     print(json.dumps(res), flush=True)
 
 
+class OracleExperts:
+    """The oracle's experts of one layer: quantised by the oracle from the
+    seeded fp32 draws when first used (its load step, not timed)."""
+
+    def __init__(self, w, layer=0, bits=None):
+        self.w, self.layer, self.bits = w, layer, bits or w.bits
+        self.cache = {}
+
+    def load(self, experts, threads=None):
+        import oracle
+        from concurrent.futures import ThreadPoolExecutor
+        tid = {"gate": synth.T_GATE, "up": synth.T_UP, "down": synth.T_DOWN}
+        todo = [int(e) for e in experts if int(e) not in self.cache]
+
+        def one(e):
+            return e, {n: oracle.quantize(synth.expert_weight_f32(self.w, self.layer, t, e), self.bits)
+                       for n, t in tid.items()}
+        with ThreadPoolExecutor(threads or min(16, len(os.sched_getaffinity(0)))) as ex:
+            for e, d in ex.map(one, todo):
+                self.cache[e] = d
+
+    def __getitem__(self, e):
+        if e not in self.cache:
+            self.load([e], threads=1)
+        return self.cache[e]
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
+
+
 def cpu_baseline_stack(w, bits, budget_s):
     import oracle
-    from tests.gpu_util import LazyExperts
-    from threadpoolctl import threadpool_info
     n, t_total = 0, 0.0
-    experts = [LazyExperts(w, layer=l, bits=b) for l, b in enumerate(bits)]
+    experts = [OracleExperts(w, layer=l, bits=b) for l, b in enumerate(bits)]
     wrs = [synth.router_weight_bf16(w, layer=l) for l in range(len(bits))]
     while t_total < budget_s and n < 8:
         x = synth.activations_bf16(w, 1, batch=2000 + n)
@@ -393,8 +445,7 @@ def cpu_baseline_stack(w, bits, budget_s):
             x = oracle.residual_bf16(x, out)
             t_total += time.perf_counter() - t0
         n += 1
-    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-    return {"value": n / t_total, "unit": "tokens/s", "cores": max(blas + [1]), "kind": "oracle",
+    return {"value": n / t_total, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"{n} tokens through all {len(bits)} blocks ({t_total:.1f} s of oracle time; the per-block "
                       f"quantisation of the touched experts excluded)"}
 
@@ -403,8 +454,7 @@ def build_replicas(bq, w, R, device):
     """Quantise the layer once on the device, then copy it to R - 1 more
     places so consecutive steps never find their weights in a cache."""
     import torch
-    from tests.gpu_util import gpu_layer
-    base = gpu_layer(w, device=device)
+    base = synth_layer(bq, w, device=device)
     reps = [base]
     for _ in range(R - 1):
         cp = lambda qw: bq.QWeight(qw.q.clone(), qw.sz.clone(), qw.bits)
@@ -415,34 +465,39 @@ def build_replicas(bq, w, R, device):
 
 def cpu_baseline(w, T, budget_s=20.0):
     """The oracle as it stands, timed on this host's cores on a bounded
-    sample: whole-layer forwards of the same workload (routing, permutation,
-    dequantisation of the touched experts, FFN, combine), one batch at a
-    time until ~budget_s of CPU work.  Quantisation of the weights is the
-    oracle's load step and is not timed."""
+    sample of the same workload: whole-layer forwards (routing, permutation,
+    dequantisation of the touched experts, FFN, combine) of the workload's
+    token batches -- or, for prefill chunks, of consecutive 16-token slices
+    of the chunk -- until ~budget_s of timed CPU work.  Quantising the
+    touched experts is the oracle's load step and is not timed."""
     import oracle
-    from tests.gpu_util import LazyExperts
-    from threadpoolctl import threadpool_info
     wr = synth.router_weight_bf16(w)
     bias = synth.router_bias(w)
-    experts = LazyExperts(w)
-    n_tok, t_total, n_runs = 0, 0.0, 0
-    b = 0
+    experts = OracleExperts(w)
+    slice_T = min(T, 16)
+    n_tok, t_total, n_runs, b = 0, 0.0, 0, 0
+    chunk = None
     while t_total < budget_s and n_runs < 64:
-        x = synth.activations_bf16(w, T, batch=1000 + b)
+        if slice_T < T:      # slices of the first prefill chunk
+            if chunk is None:
+                chunk = synth.activations_bf16(w, T, batch=0)
+            x = chunk[(b * slice_T) % T:(b * slice_T) % T + slice_T]
+        else:
+            x = synth.activations_bf16(w, T, batch=1000 + b)
         L = oracle.router_logits(x, wr, bias)
-        for e in set(oracle.select_topk(L, w.k).reshape(-1).tolist()) | set(range(w.E, w.E + w.S)):
-            experts[e]            # quantise (load step, untimed)
+        experts.load(set(oracle.select_topk(L, w.k).reshape(-1).tolist()) | set(range(w.E, w.E + w.S)))
         layer = oracle.QuantLayer(w.H, w.I, w.E, w.k, w.S, experts)   # fresh dequant cache
         t0 = time.perf_counter()
         oracle.moe_layer(layer, x, wr, bias)
         t_total += time.perf_counter() - t0
-        n_tok += T
+        n_tok += x.shape[0]
         n_runs += 1
         b += 1
-    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-    return {"value": n_tok / t_total, "unit": "tokens/s", "cores": max(blas + [1]),
+    what = (f"{n_runs} consecutive {slice_T}-token slices of the first {T}-token chunk" if slice_T < T
+            else f"{n_runs} whole-layer forwards of {T} tokens")
+    return {"value": n_tok / t_total, "unit": "tokens/s", "cores": blas_threads(),
             "kind": "oracle",
-            "sample": f"{n_runs} whole-layer forwards of {T} tokens ({n_tok} tokens, {t_total:.1f} s); "
+            "sample": f"{what} ({n_tok} tokens, {t_total:.1f} s); "
                       f"dequantisation of the routed experts included, weight quantisation excluded; "
                       f"NumPy elementwise work single-threaded, BLAS threads as given in cores; "
                       f"host has {len(os.sched_getaffinity(0))} usable cores"}
@@ -455,18 +510,17 @@ def main_curve(a, w, bq, dev):
     T = 1 -- the price of verifying T - 1 speculated tokens with the target
     token in one call."""
     import torch
-    from tests.gpu_util import bf16_tensor
     layer_bytes = expert_bytes(w, w.bits) * w.n_mats
     R = a.replicas or max(2, min(16, math.ceil(2e9 / layer_bytes)))
     reps = build_replicas(bq, w, R, dev)
-    wr = bf16_tensor(synth.router_weight_bf16(w))
+    wr = bq.bf16_from_bits(synth.router_weight_bf16(w))
     bias = synth.router_bias(w)
     bias_t = None if bias is None else torch.from_numpy(bias).to(dev)
     s = torch.cuda.Stream()
     curve = []
     for T in range(1, a.curve_max + 1):
         NB = a.batches
-        xs = [bf16_tensor(synth.activations_bf16(w, T, batch=b)) for b in range(NB)]
+        xs = [bq.bf16_from_bits(synth.activations_bf16(w, T, batch=b)) for b in range(NB)]
         ws = [reps[0].workspace(T, device=dev) for _ in range(R)]
         G = max(R, NB)
         steps = [Step(bq, reps[i % R], wr, bias_t, xs[i % NB], T, ws[i % R]) for i in range(G)]
@@ -595,16 +649,216 @@ def main_kv(a, bq, dev):
     print(json.dumps(res), flush=True)
 
 
+def hot_share(w, steps, bq):
+    """Realised routing on the hot-expert workload: the share of top-k
+    selections and of routing weight that lands on the hot experts, and the
+    assignments per hot and per cold expert (mean), from every step's GPU
+    routing."""
+    import torch
+    hot = torch.from_numpy(synth.hot_experts(w)).to(steps[0].idx.device)
+    sel = wt = tot_w = n_sel = 0.0
+    counts = []
+    for st in steps:
+        m = torch.isin(st.idx.long(), hot)
+        sel += float(m.sum())
+        n_sel += m.numel()
+        wt += float((st.w * m).sum())
+        tot_w += float(st.w.sum())
+        counts.append(torch.bincount(st.idx.reshape(-1).long(), minlength=w.E).float())
+    c = torch.stack(counts).mean(0)
+    is_hot = torch.zeros(w.E, dtype=torch.bool, device=c.device)
+    is_hot[hot] = True
+    return {"hot_experts": int(hot.numel()), "selections": round(sel / n_sel, 4),
+            "routing_weight": round(wt / tot_w, 4),
+            "assignments_per_hot_expert": round(float(c[is_hot].mean()), 1),
+            "assignments_per_cold_expert": round(float(c[~is_hot].mean()), 2),
+            "cold_experts_at_most_32": round(float(((c <= 32) & ~is_hot).sum()), 1)}
+
+
+def measure(a, w, T, bq, dev, steps, warmup, cpu=True):
+    """Time exactly ``steps`` layer steps of workload w at T tokens (after
+    ``warmup`` untimed ones) and the dominant call's launches; returns the
+    result line as a dict."""
+    import torch
+    bits = w.bits
+    layer_bytes = expert_bytes(w, bits) * w.n_mats
+    R = a.replicas or max(2, min(16, math.ceil(2e9 / layer_bytes)))
+    t0 = time.time()
+    reps = build_replicas(bq, w, R, dev)
+    wr = bq.bf16_from_bits(synth.router_weight_bf16(w))
+    bias = synth.router_bias(w)
+    bias_t = None if bias is None else torch.from_numpy(bias).to(dev)
+    NB = a.batches
+    xs = [bq.bf16_from_bits(synth.activations_bf16(w, T, batch=b)) for b in range(NB)]
+    ws = [reps[0].workspace(T, device=dev) for _ in range(R)]
+    G = max(R, NB)    # steps per graph: every replica and batch once
+    A = T * (w.k + w.S)
+    prefill = T > bq.DECODE_MAX_T
+    y = torch.empty((A, w.H), dtype=torch.bfloat16 if prefill else torch.float32, device=dev)
+    out = torch.empty((T, w.H), dtype=torch.bfloat16, device=dev)
+    steps_l = [Step(bq, reps[i % R], wr, bias_t, xs[i % NB], T, ws[i % R], y=y, out=out) for i in range(G)]
+    print(f"# setup {time.time() - t0:.1f}s: {w.name} T={T} replicas={R} batches={NB} graph_steps={G}",
+          file=sys.stderr, flush=True)
+
+    s = torch.cuda.Stream()
+    sp = ctypes.c_void_p(s.cuda_stream)
+    with torch.cuda.stream(s):
+        for st in steps_l:          # eager warm pass (also loads code objects)
+            st.run(sp)
+    torch.cuda.synchronize()
+
+    # realised distinct experts per step -> algorithmic bytes
+    distinct = [st.distinct_experts() for st in steps_l]
+    n_dist = float(np.mean(distinct))
+    # the layer's algorithmic work: each distinct expert's weights once, the
+    # router rows, x in and the output out; flops of the experts and router
+    bytes_8d = n_dist * expert_bytes(w, bits) + w.E * w.H * 2 + T * w.H * 2 + T * w.H * 2
+    exp_flops = A * 6 * w.I * w.H
+    flops_8d = exp_flops + 2 * T * w.E * w.H
+
+    graphs = {}
+
+    def graph_of(n, part="run"):
+        if a.no_graph:
+            return None
+        key = (n, part)
+        if key not in graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for st in steps_l[:n]:
+                    getattr(st, part)(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            torch.cuda.synchronize()
+            graphs[key] = g
+        return graphs[key]
+
+    def run_steps(n):
+        """Exactly n steps: whole graphs of G steps, then one graph of the
+        remaining n % G steps (eager launches without graphs)."""
+        gfull = graph_of(G) if n >= G else None
+        grem = graph_of(n % G) if n % G else None
+        with torch.cuda.stream(s):
+            if a.no_graph:
+                for i in range(n):
+                    steps_l[i % G].run(sp)
+                return
+            for _ in range(n // G):
+                gfull.replay()
+            if grem is not None:
+                grem.replay()
+
+    run_steps(warmup)
+    if steps % G:
+        graph_of(steps % G)    # captured before the timed region
+    if steps >= G:
+        graph_of(G)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(s)
+    run_steps(steps)
+    ev1.record(s)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / steps
+
+    # dominant call: the expert FFN call (or the whole fused decode call),
+    # timed with events on its stream around replays of a graph that holds
+    # only that call for every step (the routing results it reads are those
+    # of the last full pass); eager launches when graphs are off
+    kg = graph_of(G, "timed")
+    with torch.cuda.stream(s):
+        if kg is not None:
+            kg.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nrep = max(2, min(50, steps // G))
+        e0.record(s)
+        for _ in range(nrep):
+            if kg is not None:
+                kg.replay()
+            else:
+                for st in steps_l:
+                    st.timed(sp)
+        e1.record(s)
+    torch.cuda.synchronize()
+    kern_ms = e0.elapsed_time(e1) / (nrep * G)
+
+    if prefill:
+        # The grouped GEMM: bound by the matrix cores when the layer's
+        # arithmetic intensity (its flops over its algorithmic bytes) is above
+        # the ridge of the two peaks, else by HBM.  The kernel's own bytes are
+        # the layer's less the router rows (another launch reads those); the
+        # h and y round trips are reported beside, not counted.
+        kern_bytes = bytes_8d - w.E * w.H * 2
+        tflops = exp_flops / (kern_ms * 1e-3) / 1e12
+        gbps = kern_bytes / (kern_ms * 1e-3) / 1e9
+        intensity = flops_8d / bytes_8d
+        common = {"traffic": measured_traffic(w.name, T),
+                  "kernel": "moe_qgemm_prefill (tile schedule, gate/up and down grouped GEMM kernels)",
+                  "alg_flops_per_launch": exp_flops, "alg_bytes_per_launch": round(kern_bytes),
+                  "h_y_round_trip_bytes": 2 * A * w.I * 2 + 2 * A * w.H * 2,
+                  "layer_intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": RIDGE,
+                  "kernel_us": round(kern_ms * 1e3, 3),
+                  "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4)}
+        if intensity >= RIDGE:
+            roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4), **common}
+        else:
+            roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbps / PEAK_HBM_GBS, 4), **common}
+    else:
+        fused = steps_l[0].layer_fused
+        # fused: the whole layer call (router rows, x and out included)
+        dec_bytes = bytes_8d if fused else n_dist * expert_bytes(w, bits) + T * w.H * 2
+        achieved = dec_bytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name, T),
+                "kernel": ("moe_decode_forward (router; routing + gate/up; down + combine)" if fused
+                           else "moe_qgemv_decode (gate/up + down grouped GEMV kernels)"),
+                "alg_bytes_per_launch": round(dec_bytes), "kernel_us": round(kern_ms * 1e3, 3)}
+
+    res = {
+        "metric": "MoE-layer tokens/s",
+        "value": round(T * steps / (total_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"u{bits} codes x bf16 -> fp32" if not prefill else f"u{bits} codes -> bf16 MFMA, fp32 acc",
+        "data": "synthetic (seeded N(0,0.02) weights quantised on the GPU; N(0,1) bf16 tokens)",
+        "config": {"workload": w.name, "phase": "prefill" if prefill else "decode", "tokens": T, "hidden": w.H,
+                   "intermediate": w.I, "experts": w.E, "top_k": w.k, "shared": w.S, "bits": bits,
+                   "weight_replicas": R, "token_batches": NB, "hip_graph": not a.no_graph,
+                   "distinct_experts_per_step": round(n_dist, 2), "layer_alg_bytes": round(bytes_8d),
+                   "layer_alg_flops": flops_8d,
+                   "layer_GBps": round(bytes_8d / (ms_per_step * 1e-3) / 1e9, 1),
+                   "layer_TFLOPs": round(flops_8d / (ms_per_step * 1e-3) / 1e12, 2)},
+        "roofline": roof,
+    }
+    if w.bias == "hot":
+        res["config"]["hot_share"] = hot_share(w, steps_l, bq)
+    if cpu and not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, T, a.cpu_budget)
+    del graphs, steps_l, reps, ws, xs, y, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    help=f"NAME:T (default {DEFAULT_WORKLOAD}, with {', '.join(NESTED_DECODE)} nested)")
     ap.add_argument("--replicas", type=int, default=0, help="weight copies (0: enough for >= 2 GB)")
     ap.add_argument("--batches", type=int, default=16)
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-nested", action="store_true", help="default line without the nested decode lines")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--kv", action="store_true", help="only time the KV-cache codec at a cache's size")
     ap.add_argument("--hqq", action="store_true",
@@ -619,168 +873,34 @@ def main():
         print(json.dumps({"error": "bench.py runs on one GPU only; --gpus must be 1 "
                                    "(the multi-GPU sharding is described in the design notes, not built)"}))
         sys.exit(2)
+    if a.steps < 1 or a.warmup < 0:
+        print(json.dumps({"error": "--steps must be >= 1 and --warmup >= 0"}))
+        sys.exit(2)
 
     if a.copy_calibrate:
         return copy_calibrate(a.copy_calibrate)
 
     import torch
     import bit_quantized_expert_amd as bq
-    from tests.gpu_util import bf16_tensor
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if a.kv:
         return main_kv(a, bq, dev)
-    w, T = parse_workload(a.workload)
+    w, T = parse_workload(a.workload or DEFAULT_WORKLOAD)
     if w.layers > 1:
         return main_stack(a, w, bq, dev)
     if a.curve_max:
         return main_curve(a, w, bq, dev)
     if a.hqq:
         return main_hqq(a, w, bq, dev)
-    bits = w.bits
-    layer_bytes = expert_bytes(w, bits) * w.n_mats
-    R = a.replicas or max(2, min(16, math.ceil(2e9 / layer_bytes)))
-    t0 = time.time()
-    reps = build_replicas(bq, w, R, dev)
-    wr = bf16_tensor(synth.router_weight_bf16(w))
-    bias = synth.router_bias(w)
-    bias_t = None if bias is None else torch.from_numpy(bias).to(dev)
-    NB = a.batches
-    xs = [bf16_tensor(synth.activations_bf16(w, T, batch=b)) for b in range(NB)]
-    ws = [reps[0].workspace(T, device=dev) for _ in range(R)]
-    G = max(R, NB)    # steps per graph: every replica and batch once
-    steps = [Step(bq, reps[i % R], wr, bias_t, xs[i % NB], T, ws[i % R]) for i in range(G)]
-    print(f"# setup {time.time() - t0:.1f}s: {w.name} T={T} replicas={R} batches={NB} graph_steps={G}",
-          file=sys.stderr, flush=True)
-
-    s = torch.cuda.Stream()
-    sp = ctypes.c_void_p(s.cuda_stream)
-    with torch.cuda.stream(s):
-        for st in steps:          # eager warm pass (also loads code objects)
-            st.run(sp)
-    torch.cuda.synchronize()
-
-    # realised distinct experts per step -> algorithmic bytes of the expert kernels
-    distinct = [st.distinct_experts() for st in steps]
-    alg_expert_bytes = float(np.mean(distinct)) * expert_bytes(w, bits) + T * w.H * 2
-    alg_layer_bytes = alg_expert_bytes + w.E * w.H * 2 + T * w.H * 2
-    flops = T * (w.k + w.S) * 6 * w.I * w.H + 2 * T * w.E * w.H
-
-    graph = None
-    if not a.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=s):
-            for st in steps:
-                st.run(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-        torch.cuda.synchronize()
-
-    def run_steps(n):
-        with torch.cuda.stream(s):
-            if graph is not None:
-                for _ in range(n // G):
-                    graph.replay()
-                for i in range(n % G):
-                    steps[i].run(sp)
-            else:
-                for i in range(n):
-                    steps[i % G].run(sp)
-
-    run_steps(a.warmup)
-    torch.cuda.synchronize()
-    K = max(G, (a.steps // G) * G)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(s)
-    run_steps(K)
-    ev1.record(s)
-    torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    ms_per_step = total_ms / K
-
-    # dominant kernel(s): the expert FFN call (or the whole fused decode
-    # call), timed with events on its stream around replays of a graph that
-    # holds only that part of every step (the routing results it reads are
-    # those of the last full pass); eager launches when graphs are off
-    kgraph = None
-    if graph is not None:
-        kgraph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(kgraph, stream=s):
-            for st in steps:
-                st.timed(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-        torch.cuda.synchronize()
-    with torch.cuda.stream(s):
-        if kgraph is not None:
-            kgraph.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(2, min(50, K // G))
-        e0.record(s)
-        for _ in range(reps):
-            if kgraph is not None:
-                kgraph.replay()
-            else:
-                for st in steps:
-                    st.timed(sp)
-        e1.record(s)
-    torch.cuda.synchronize()
-    kern_ms = e0.elapsed_time(e1) / (reps * G)
-
-    prefill = T > bq.DECODE_MAX_T
-    if prefill:
-        # The grouped GEMM is bound by the matrix cores or by HBM, whichever
-        # needs longer at peak: its flops (expert FFN only) against the bf16
-        # MFMA peak, its algorithmic bytes (each touched expert's weights
-        # once, x in, h out and back in, y out) against the HBM peak.
-        A = T * (w.k + w.S)
-        exp_flops = flops - 2 * T * w.E * w.H
-        pf_bytes = float(np.mean(distinct)) * expert_bytes(w, bits) + T * w.H * 2 + 2 * A * w.I * 2 + A * w.H * 2
-        t_mfma = exp_flops / (PEAK_BF16_TFLOPS * 1e12)
-        t_hbm = pf_bytes / (PEAK_HBM_GBS * 1e9)
-        tflops = exp_flops / (kern_ms * 1e-3) / 1e12
-        gbps = pf_bytes / (kern_ms * 1e-3) / 1e9
-        common = {"traffic": measured_traffic(w.name, T),
-                  "kernel": "moe_qgemm_prefill (gate/up + down grouped GEMM kernels)",
-                  "alg_flops_per_launch": exp_flops, "alg_bytes_per_launch": round(pf_bytes),
-                  "kernel_us": round(kern_ms * 1e3, 3),
-                  "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4), "hbm_frac": round(gbps / PEAK_HBM_GBS, 4)}
-        if t_mfma >= t_hbm:
-            roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4), **common}
-        else:
-            roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(gbps / PEAK_HBM_GBS, 4), **common}
-    else:
-        fused = steps[0].layer_fused
-        # fused: the whole layer call (router rows, x and out included)
-        dec_bytes = alg_layer_bytes if fused else alg_expert_bytes
-        achieved = dec_bytes / (kern_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name, T),
-                "kernel": ("moe_decode_forward (router; routing + gate/up; down + combine)" if fused
-                           else "moe_qgemv_decode (gate/up + down grouped GEMV kernels)"),
-                "alg_bytes_per_launch": round(dec_bytes), "kernel_us": round(kern_ms * 1e3, 3)}
-
-    res = {
-        "metric": "MoE-layer tokens/s",
-        "value": round(T * K / (total_ms * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": a.warmup,
-        "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": f"u{bits} codes x bf16 -> fp32" if not prefill else f"u{bits} codes -> bf16 MFMA, fp32 acc",
-        "data": "synthetic (seeded N(0,0.02) weights quantised on the GPU; N(0,1) bf16 tokens)",
-        "config": {"workload": w.name, "tokens": T, "hidden": w.H, "intermediate": w.I, "experts": w.E,
-                   "top_k": w.k, "shared": w.S, "bits": bits, "weight_replicas": R, "token_batches": NB,
-                   "hip_graph": graph is not None, "distinct_experts_per_step": round(float(np.mean(distinct)), 2),
-                   "layer_alg_bytes": round(alg_layer_bytes), "layer_GBps": round(alg_layer_bytes / (ms_per_step * 1e-3) / 1e9, 1)},
-        "roofline": roof,
-    }
-    if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, T, a.cpu_budget)
+    res = measure(a, w, T, bq, dev, a.steps, a.warmup)
+    if a.workload is None and not a.no_nested:
+        res["decode"] = []
+        for spec in NESTED_DECODE:
+            wd, Td = parse_workload(spec)
+            r = measure(a, wd, Td, bq, dev, NESTED_STEPS, NESTED_WARMUP, cpu=False)
+            res["decode"].append({k: r[k] for k in ("value", "unit", "steps", "ms_per_step", "config", "roofline")})
     print(json.dumps(res), flush=True)
 
 

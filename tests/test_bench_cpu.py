@@ -87,3 +87,21 @@ def test_bench_names_resolve():
     with open(os.path.join(ROOT, "bench.py")) as fh:
         tree = ast.parse(fh.read())
     assert _unbound_globals(tree) == set()
+
+
+def test_measured_path_imports_no_test_code():
+    """bench.py's GPU path builds its weights through the binding
+    (quantize_layer) and the seeded draws: nothing under tests/ is imported,
+    and the oracle only inside the CPU-baseline leg."""
+    with open(os.path.join(ROOT, "bench.py")) as fh:
+        tree = ast.parse(fh.read())
+    for node in ast.walk(tree):
+        if isinstance(node, (ast.Import, ast.ImportFrom)):
+            mods = [node.module] if isinstance(node, ast.ImportFrom) else [a.name for a in node.names]
+            assert not any(m and m.split(".")[0] == "tests" for m in mods)
+    allowed = {"cpu_baseline", "cpu_baseline_stack", "load"}   # OracleExperts.load
+    for node in ast.walk(tree):
+        if isinstance(node, ast.FunctionDef):
+            imports = [n for n in ast.walk(node) if isinstance(n, ast.Import)]
+            if any(a.name == "oracle" for n in imports for a in n.names):
+                assert node.name in allowed, node.name
