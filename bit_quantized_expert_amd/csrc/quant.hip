@@ -14,28 +14,60 @@ struct HqqParams {
   int iters;
 };
 
+// Sum of one double per lane over the wavefront (every lane gets it).  The
+// order of the additions is the butterfly's; in fp64 it moves the sum of a
+// group's 64 values by a few ulps at most, far below an fp16 step.
+MOEQ_DEV double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// fp64 -> fp16 bits, round to nearest even, in one rounding (no stop in
+// fp32 on the way), for finite |x| < 65520.
+MOEQ_DEV uint32_t f64_to_f16_bits(double x) {
+  const uint32_t sign = __builtin_signbit(x) ? 0x8000u : 0u;
+  const double a = fabs(x);
+  if (a < 0x1p-14) return sign | (uint32_t)rint(a * 0x1p24);   // subnormal (1024 is the smallest normal)
+  int e;
+  frexp(a, &e);                                 // a in [2^(e-1), 2^e)
+  double m = rint(ldexp(a, 11 - e));            // 11 significant bits: [1024, 2048]
+  int E = e - 1;
+  if (m == 2048.0) {
+    m = 1024.0;
+    ++E;
+  }
+  return sign | ((uint32_t)(E + 15) << 10) | ((uint32_t)m - 1024u);
+}
+
 // One round per iteration, for the group in this wavefront (lane l holds
 // value v of the group, sf its scale, z its current zero, an fp16 value):
-// the codes for z and their mean absolute error E; the group stops when E
-// is not below its best; else z is kept as the best and replaced by the
-// zero sub-problem's solution (rounded to fp16) for the shrunk residual.
-// No fused multiply-adds: every step is rounded as written.
+// the codes for z (fp32, as the quantiser) and the exact residual r (fp64);
+// the group stops when its mean absolute error is not below its best; else
+// z is kept as the best and replaced by the zero sub-problem's solution for
+// the shrunk residual, formed in fp64 and rounded once to fp16.  The shrink
+// is 0 wherever |r| is clearly below the round's threshold
+// beta^(-1/(2 - lp)) (there |r| - |r|^(lp - 1)/beta < 0), so the power is
+// only evaluated where it can matter.
 MOEQ_DEV float hqq_zero(float v, float sf, float z, float qmax, const HqqParams& hp) {
 #pragma clang fp contract(off)
-  float best = INFINITY, zb = z, beta = hp.beta;
-  const float pm1 = hp.lp - 1.0f;
+  double best = INFINITY, beta = (double)hp.beta;
+  float zb = z;
+  const double pm1 = (double)hp.lp - 1.0, vd = (double)v, sd = (double)sf;
   for (int it = 0; it < hp.iters; ++it) {
     const float qv = fminf(fmaxf(rintf(v / sf + z), 0.0f), qmax);
-    const float r = v - (qv - z) * sf;
-    const float E = wave_sum(fabsf(r)) * (1.0f / 64.0f);
-    if (!(E < best)) break;                          // the same value in every lane
+    const double r = vd - ((double)qv - (double)z) * sd;             // exact in fp64
+    const double a = fabs(r);
+    const double E = wave_sum_f64(a) / 64.0;
+    if (!(E < best)) break;                                           // the same value in every lane
     best = E;
     zb = z;
-    const float a = fabsf(r);
-    const float e = copysignf(fmaxf(a - powf(a, pm1) / beta, 0.0f), r);
-    const float zn = wave_sum(qv - (v - e) / sf) * (1.0f / 64.0f);
-    z = f16_bits_to_f32(f32_to_f16_bits(zn));
-    beta = beta * hp.kappa;
+    const double tau = pow(beta, -1.0 / (1.0 - pm1));                 // threshold of the shrink
+    double e = 0.0;
+    if (a >= tau * (1.0 - 1e-9)) e = copysign(fmax(a - pow(a, pm1) / beta, 0.0), r);
+    const double zn = wave_sum_f64((double)qv - (vd - e) / sd) / 64.0;
+    z = f16_bits_to_f32(f64_to_f16_bits(zn));
+    beta = beta * (double)hp.kappa;
   }
   return zb;
 }

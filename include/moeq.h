@@ -147,17 +147,21 @@ int moe_qweight_load(const uint8_t* packed, const uint16_t* scale, const uint16_
  * Large Machine Learning Models", 2023) with the scale held (the pages name
  * HQQ weights -- Krasis update, "Latest results (v1.0)" -- but no solver).
  * Per group, from the min-max zero z (an fp16 value), up to iters rounds of:
- *   q = clamp(rint(w / s16 + z), 0, 2^bits - 1);  r = w - (q - z) * s16;
- *   E = mean |r|; stop if E is not below the group's best, else keep z;
+ *   q = clamp(rint(w / s16 + z), 0, 2^bits - 1)      (fp32, as moe_quantize)
+ *   r = w - (q - z) * s16;  E = mean |r|;  stop if E is not below the
+ *   group's best, else keep z as its best;
  *   e = sign(r) * max(|r| - |r|^(lp - 1) / beta, 0);
  *   z = fp16(mean(q - (w - e) / s16));  beta = beta * kappa;
  * then the kept z and its codes are stored, so a group's mean absolute error
- * never exceeds the min-max one.  fp32, each step rounded as written (no
- * fused multiply-add); means are sums of adjacent pairs, then of adjacent
- * pair sums, ..., times 1/64.  Groups whose fp16 scale is zero keep the
- * min-max result.  lp in (0, 1] (0.7 and 1 are the usual choices), beta > 0,
- * kappa >= 1, 0 <= iters <= 1000 (0 gives moe_quantize's result); other
- * arguments, layout and errors as moe_quantize. */
+ * never exceeds the min-max one.  r is exact in fp64; E, e and the zero
+ * update are evaluated in fp64 (lp, beta and kappa taken as given, in fp32)
+ * and a mean is the fp64 sum over 64, rounded once to fp16 for z: the stored
+ * zero does not depend on the order of the additions.  The stopping test is
+ * per group (the objective is a sum over groups with disjoint variables).
+ * Groups whose fp16 scale is zero keep the min-max result.  lp in (0, 1]
+ * (0.7 and 1 are the usual choices), beta > 0, kappa >= 1, 0 <= iters <=
+ * 1000 (0 gives moe_quantize's result); other arguments, layout and errors
+ * as moe_quantize. */
 int moe_quantize_hqq(const float* w, long rows, int K, int bits,
                      float lp, float beta, float kappa, int iters,
                      uint8_t* q, uint32_t* sz, hipStream_t stream);

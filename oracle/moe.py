@@ -13,7 +13,7 @@ __all__ = [
     "bf16_to_f32", "f32_to_bf16", "quantize", "pack", "unpack", "dequant",
     "router_logits", "select_topk", "topk_weights", "assignment_experts",
     "permute", "expert_ffn", "combine", "QuantLayer", "moe_layer",
-    "rmsnorm_bf16", "residual_bf16", "silu", "shrink_lp", "tree_mean64", "hqq_refine",
+    "rmsnorm_bf16", "residual_bf16", "silu", "shrink_lp", "group_mean", "hqq_refine",
     "kv_encode", "kv_decode",
 ]
 
@@ -96,49 +96,58 @@ def quantize(w: np.ndarray, bits: int, group: int = GROUP):
 # group minimises the lp error (p < 1) of the reconstruction, split with an
 # auxiliary residual e and solved by alternating the two closed-form
 # sub-problems while the coupling weight beta grows by kappa each round.
-# Everything below is fp32 with IEEE division and ties-to-even rounding, as
-# the GPU quantiser computes it, so that both sides take every rounding
-# decision (a code, a zero rounded to fp16, stopping) from the same values.
+#
+# Precision.  The codes are those of the quantiser (fp32, as ``quantize``).
+# Everything else is real arithmetic carried in fp64: the residual
+# r = w - (q - z) s is exact in fp64 (w is fp32, q an integer, z and s fp16
+# values), the shrink and the zero sub-problem are evaluated in fp64, and a
+# group's means are its fp64 sum divided by 64.  A mean is stored as an fp16
+# zero, rounded once from fp64; the fp64 sum's rounding (a few fp64 ulps of
+# the sum, whatever the order of the additions) is 2^-40 of an fp16 step, so
+# the stored zero is the one the exact mean gives except where that mean
+# falls within such a distance of an fp16 rounding boundary.  The solver's
+# parameters are single-precision numbers (lp, beta, kappa as fp32).
 
 def shrink_lp(x: np.ndarray, beta, p) -> np.ndarray:
     """Proximal step of the lp penalty (p <= 1), generalised soft threshold:
-    sign(x) * max(|x| - |x|^(p-1) / beta, 0) in fp32.  At x = 0 and p < 1
+    sign(x) * max(|x| - |x|^(p-1) / beta, 0), in fp64.  At x = 0 and p < 1
     the threshold is infinite and the result 0."""
-    x = np.asarray(x, np.float32)
+    x = np.asarray(x, np.float64)
     a = np.abs(x)
     with np.errstate(divide="ignore"):
-        t = np.power(a, np.float32(p) - np.float32(1)) / np.float32(beta)
-    return np.copysign(np.maximum(a - t, np.float32(0)), x).astype(np.float32)
+        t = np.power(a, np.float64(p) - 1.0) / np.float64(beta)
+    return np.copysign(np.maximum(a - t, 0.0), x)
 
 
-def tree_mean64(x: np.ndarray) -> np.ndarray:
-    """Mean over the last axis (64 values) as the GPU forms it: fp32 sums of
-    adjacent pairs, then of adjacent pair sums, and so on (a balanced binary
-    tree over consecutive halves), times 1/64 (exact)."""
-    x = np.asarray(x, np.float32)
-    assert x.shape[-1] == 64
-    while x.shape[-1] > 1:
-        x = (x[..., 0::2] + x[..., 1::2]).astype(np.float32)
-    return (x[..., 0] * np.float32(1.0 / 64.0)).astype(np.float32)
+def group_mean(x: np.ndarray) -> np.ndarray:
+    """Mean over the last axis: the fp64 sum of the values divided by their
+    count (its rounding does not depend on the summation order beyond a few
+    fp64 ulps)."""
+    x = np.asarray(x, np.float64)
+    return x.sum(axis=-1) / x.shape[-1]
 
 
 def hqq_refine(w: np.ndarray, bits: int, lp: float = 0.7, beta: float = 10.0, kappa: float = 1.01,
-               iters: int = 20, group: int = GROUP):
+               iters: int = 20, group: int = GROUP, trace: bool = False):
     """Min-max quantisation (``quantize``) followed by HQQ's zero-point
     refinement, group by group with s fixed.  One round, from the group's
     current fp16 zero z:
-        q  = clip(rint(w / s + z), 0, 2^b - 1)          (codes for z)
+        q  = clip(rint(w / s + z), 0, 2^b - 1)          (codes for z, fp32)
         r  = w - (q - z) s;  E = mean |r|               (its error)
         stop if E is not below the group's best so far; else keep z as best
         e  = shrink_lp(r, beta, lp)                     (residual sub-problem)
         z  = fp16(mean(q - (w - e) / s))                (zero sub-problem)
         beta = beta * kappa
     The group keeps the zero of its lowest error and the codes for it, so its
-    mean absolute error never exceeds the min-max one.  Groups whose fp16
-    scale is zero keep the min-max result.  Returns q, s16, z16 as
-    ``quantize``."""
+    mean absolute error never exceeds the min-max one.  The stopping test is
+    taken per group: the objective is a sum over groups whose variables are
+    disjoint, so each group's test is the published whole-tensor test applied
+    to that group's own part of the objective.  Groups whose fp16 scale is
+    zero keep the min-max result.  Returns q, s16, z16 as ``quantize``; with
+    ``trace`` also a list, per round, of (z [N, K/64], E [N, K/64], active)
+    as the round found them."""
     if group != 64:
-        raise ValueError("the refinement reduces over groups of 64")
+        raise ValueError("the refinement runs on groups of 64")
     w = np.asarray(w, dtype=np.float32)
     N, K = w.shape
     q0, s16, z16 = quantize(w, bits, group)
@@ -146,27 +155,35 @@ def hqq_refine(w: np.ndarray, bits: int, lp: float = 0.7, beta: float = 10.0, ka
     wg = w.reshape(N, K // group, group)
     degenerate = ((wg.max(axis=2) - wg.min(axis=2)) / qmax).astype(np.float16) == np.float16(0)
     sf = s16.astype(np.float32)[..., None]
+    sd = sf.astype(np.float64)
+    wd = wg.astype(np.float64)
     z = z16.astype(np.float32)
     zb = z.copy()
-    best = np.full(z.shape, np.inf, np.float32)
+    best = np.full(z.shape, np.inf, np.float64)
     active = ~degenerate
-    b = np.float32(beta)
+    p = np.float64(np.float32(lp))
+    b = np.float64(np.float32(beta))
+    kap = np.float64(np.float32(kappa))
+    rounds = []
     for _ in range(iters):
         if not active.any():
             break
-        qv = np.clip(np.rint(wg / sf + z[..., None]), np.float32(0), qmax).astype(np.float32)
-        r = (wg - (qv - z[..., None]) * sf).astype(np.float32)
-        E = tree_mean64(np.abs(r))
+        qv = np.clip(np.rint(wg / sf + z[..., None]), np.float32(0), qmax)
+        r = wd - (qv.astype(np.float64) - z[..., None].astype(np.float64)) * sd
+        E = group_mean(np.abs(r))
+        if trace:
+            rounds.append((z.copy(), E.copy(), active.copy()))
         active = active & (E < best)
         best = np.where(active, E, best)
         zb = np.where(active, z, zb)
-        e = shrink_lp(r, b, lp)
-        znew = tree_mean64(qv - (wg - e) / sf)
+        e = shrink_lp(r, b, p)
+        znew = group_mean(qv.astype(np.float64) - (wd - e) / sd)
         z = np.where(active, znew.astype(np.float16).astype(np.float32), z)
-        b = np.float32(b * np.float32(kappa))
+        b = b * kap
     q = np.clip(np.rint(wg / sf + zb[..., None]), np.float32(0), qmax)
     q[degenerate] = 0
-    return q.astype(np.uint8).reshape(N, K), s16, zb.astype(np.float16)
+    out = (q.astype(np.uint8).reshape(N, K), s16, zb.astype(np.float16))
+    return out + (rounds,) if trace else out
 
 
 # --------------------------------------------------------------------------

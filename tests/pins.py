@@ -456,19 +456,46 @@ def pin_shrink_closed_form(o):
     x = np.array([4, 0.25, -16, 0.0625, 0], np.float32)
     assert np.array_equal(o.shrink_lp(x, 1.0, 0.5), np.array([3.5, 0, -15.75, 0, 0], np.float32))
     # large |x|: the threshold vanishes relative to x
-    assert o.shrink_lp(np.array([1e6], np.float32), 1e3, 0.7)[0] == np.float32(1e6) - np.float32(1e6 ** -0.3 / 1e3)
+    assert o.shrink_lp(np.array([1e6], np.float32), 1e3, 0.7)[0] == 1e6 - 1e6 ** -0.3 / 1e3
+    # fp64 throughout: a residual of 2^-30 with p = 1 and beta = 2^40 keeps 2^-30 - 2^-40
+    assert o.shrink_lp(np.array([2.0 ** -30]), 2.0 ** 40, 1.0)[0] == 2.0 ** -30 - 2.0 ** -40
 
 
-def pin_tree_mean(o):
-    """The mean over 64 values is a balanced pairwise tree: (2^24 + 1) + (1 -
-    2^24) = 2^24 + (1 - 2^24) = 1 (a left-to-right sum gives 0); integer
-    inputs give the exact mean."""
+def pin_group_mean(o):
+    """A group's mean is its fp64 sum over the count: exact on values an
+    fp32 sum loses (2^24 + 1 + 1 - 2^24 = 2, where a pairwise fp32 tree gives
+    1 and a left-to-right fp32 sum 0), the same in any order of the values,
+    and the exact mean of integers."""
     x = np.zeros(64, np.float32)
     x[:4] = [2.0 ** 24, 1, 1, -2.0 ** 24]
-    assert o.tree_mean64(x) == np.float32(1 / 64)
+    assert o.group_mean(x) == 2 / 64
     rng = np.random.default_rng(20)
-    y = rng.integers(0, 64, size=(50, 64)).astype(np.float32)
-    assert np.array_equal(o.tree_mean64(y), (y.astype(np.float64).sum(1) / 64).astype(np.float32))
+    y = (rng.standard_normal((50, 64)) * 100).astype(np.float32)
+    for _ in range(3):
+        perm = rng.permutation(64)
+        assert np.array_equal(o.group_mean(y).astype(np.float16), o.group_mean(y[:, perm]).astype(np.float16))
+    n = rng.integers(-1000, 1000, size=(50, 64))
+    assert np.array_equal(o.group_mean(n.astype(np.float32)), n.sum(1) / 64)
+
+
+def pin_hqq_golden(o):
+    """The refinement's trajectory on a group worked by hand
+    (tests/golden/hqq_trajectory.json): every round's zero and error, the
+    round it stops at (the zero stops moving once the fp16 step exceeds the
+    shrink threshold), the kept zero and its codes."""
+    with open(os.path.join(GOLDEN, "hqq_trajectory.json")) as fh:
+        g = json.load(fh)
+    w = np.array([1.0, 16.0] + [4.25] * 31 + [8.375] * 31, np.float32)[None, :]
+    codes = np.array([0, 15] + [3] * 31 + [7] * 31, np.uint8)[None, :]
+    for case in g["cases"]:
+        q, s16, z16, rounds = o.hqq_refine(w, g["group"]["bits"], lp=case["lp"], beta=case["beta"],
+                                          kappa=case["kappa"], iters=case["iters"], trace=True)
+        zs = [float(r[0][0, 0]) for r in rounds if r[2][0, 0]]
+        Es = [float(r[1][0, 0]) for r in rounds if r[2][0, 0]]
+        assert zs == case["z_rounds"], (zs, case["z_rounds"])
+        assert Es == case["E_rounds"], (Es, case["E_rounds"])
+        assert float(z16[0, 0]) == case["z_final"] and float(s16[0, 0]) == 1.0
+        assert np.array_equal(q, codes)
 
 
 def _group_mae(o, w, q, s16, z16):

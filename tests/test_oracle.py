@@ -64,8 +64,12 @@ def test_shrink_closed_form():
     pins.pin_shrink_closed_form(oracle)
 
 
-def test_tree_mean():
-    pins.pin_tree_mean(oracle)
+def test_group_mean():
+    pins.pin_group_mean(oracle)
+
+
+def test_hqq_golden():
+    pins.pin_hqq_golden(oracle)
 
 
 @pytest.mark.parametrize("bits", [4, 6, 8])

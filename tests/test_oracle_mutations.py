@@ -127,51 +127,63 @@ def _residual_no_block_rounding(x_bf16, moe_out):
 
 def _shrink_identity(x, beta, p):
     # mistake: the residual is not shrunk at all
-    return np.asarray(x, np.float32)
+    return np.asarray(x, np.float64)
 
 
-def _mean_left_to_right(x):
-    # mistake: a left-to-right fp32 sum instead of the pairwise tree
+def _mean_fp32_left_to_right(x):
+    # mistake: the group's mean summed left to right in fp32
     x = np.asarray(x, np.float32)
     acc = np.zeros(x.shape[:-1], np.float32)
     for i in range(x.shape[-1]):
         acc = (acc + x[..., i]).astype(np.float32)
-    return (acc * np.float32(1 / 64)).astype(np.float32)
+    return (acc / np.float32(x.shape[-1])).astype(np.float64)
 
 
-def _hqq_variant(sign=1.0, keep_best=True):
-    def refine(w, bits, lp=0.7, beta=10.0, kappa=1.01, iters=20, group=64):
+def _hqq_variant(sign=1.0, keep_best=True, max_rounds=None):
+    """The refinement with one plausible mistake planted (the rest as the
+    oracle states it)."""
+    def refine(w, bits, lp=0.7, beta=10.0, kappa=1.01, iters=20, group=64, trace=False):
         w = np.asarray(w, np.float32)
         N, K = w.shape
         q0, s16, z16 = _quantize(w, bits, group)
         qmax = np.float32(2 ** bits - 1)
         wg = w.reshape(N, K // group, group)
         sf = s16.astype(np.float32)[..., None]
+        sd, wd = sf.astype(np.float64), wg.astype(np.float64)
         z = z16.astype(np.float32)
-        zb, best, active, b = z.copy(), np.full(z.shape, np.inf, np.float32), np.ones(z.shape, bool), np.float32(beta)
-        for _ in range(iters):
-            qv = np.clip(np.rint(wg / sf + z[..., None]), 0, qmax).astype(np.float32)
-            r = (wg - (qv - z[..., None]) * sf).astype(np.float32)
-            E = om.tree_mean64(np.abs(r))
+        zb, best, active = z.copy(), np.full(z.shape, np.inf), np.ones(z.shape, bool)
+        b, p, kap = np.float64(np.float32(beta)), np.float64(np.float32(lp)), np.float64(np.float32(kappa))
+        rounds = []
+        n = iters if max_rounds is None else min(iters, max_rounds)
+        for _ in range(n):
+            if not active.any():
+                break
+            qv = np.clip(np.rint(wg / sf + z[..., None]), 0, qmax)
+            r = wd - (qv.astype(np.float64) - z[..., None]) * sd
+            E = om.group_mean(np.abs(r))
+            rounds.append((z.copy(), E.copy(), active.copy()))
             if keep_best:
                 active = active & (E < best)
                 best = np.where(active, E, best)
                 zb = np.where(active, z, zb)
-            e = om.shrink_lp(r, b, lp)
-            znew = om.tree_mean64(qv + np.float32(sign) * (-(wg - e) / sf))
+            e = om.shrink_lp(r, b, p)
+            znew = om.group_mean(qv + sign * (-(wd - e) / sd))
             z = np.where(active, znew.astype(np.float16).astype(np.float32), z)
             if not keep_best:
                 zb = z
-            b = np.float32(b * np.float32(kappa))
+            b = b * kap
         q = np.clip(np.rint(wg / sf + zb[..., None]), 0, qmax)
-        return q.astype(np.uint8).reshape(N, K), s16, zb.astype(np.float16)
+        out = (q.astype(np.uint8).reshape(N, K), s16, zb.astype(np.float16))
+        return out + (rounds,) if trace else out
     return refine
 
 
 _hqq_zero_sign_flipped = _hqq_variant(sign=-1.0)     # mistake: z = mean(q + (w - e) / s)
 _hqq_keeps_last = _hqq_variant(keep_best=False)      # mistake: the last zero, not the best one
+_hqq_round_cap = _hqq_variant(max_rounds=5)          # mistake: at most 5 rounds whatever iters says
 _hqq_zero_sign_flipped.__name__ = "_hqq_zero_sign_flipped"
 _hqq_keeps_last.__name__ = "_hqq_keeps_last"
+_hqq_round_cap.__name__ = "_hqq_round_cap"
 
 
 def _kv_decode_truncating(packed, s16, z16, bits, D):
@@ -195,9 +207,11 @@ MUTANTS = [
     ("rmsnorm_bf16", _rmsnorm_no_eps, [pins.pin_bf16_and_norm]),
     ("residual_bf16", _residual_no_block_rounding, [pins.pin_bf16_and_norm]),
     ("shrink_lp", _shrink_identity, [pins.pin_shrink_closed_form, lambda o: pins.pin_hqq_refine(o, 4)]),
-    ("tree_mean64", _mean_left_to_right, [pins.pin_tree_mean]),
-    ("hqq_refine", _hqq_zero_sign_flipped, [pins.pin_hqq_least_squares_round]),
-    ("hqq_refine", _hqq_keeps_last, [lambda o: pins.pin_hqq_refine(o, 6)]),
+    ("shrink_lp", _shrink_identity, [pins.pin_hqq_golden]),
+    ("group_mean", _mean_fp32_left_to_right, [pins.pin_group_mean]),
+    ("hqq_refine", _hqq_zero_sign_flipped, [pins.pin_hqq_least_squares_round, pins.pin_hqq_golden]),
+    ("hqq_refine", _hqq_keeps_last, [lambda o: pins.pin_hqq_refine(o, 6), pins.pin_hqq_golden]),
+    ("hqq_refine", _hqq_round_cap, [pins.pin_hqq_golden]),
     ("kv_decode", _kv_decode_truncating, [pins.pin_kv_codec]),
 ]
 
