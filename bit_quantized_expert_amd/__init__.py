@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "moe_qgemv_decode": (I, [P, P, I, P, P, P, P, P, SZ, P]),
             "moe_decode_forward": (I, [P, P, P, P, I, P, P, P, P, P, P, SZ, P]),
             "moe_decode_block": (I, [P, P, P, P, I, ctypes.c_float, P, P, P, P, SZ, P]),
+            "moe_decode_forward_noalloc": (I, [P, P, P, P, I, P, P, P, P, P, P]),
+            "moe_decode_forward_noalloc_max_scratch": (SZ, []),
             "moe_qgemm_prefill": (I, [P, P, I, P, P, P, P, P, SZ, P]),
             "moe_combine": (I, [P, I, P, P, I, I, I, I, P, P]),
             "moe_rmsnorm": (I, [P, P, I, I, ctypes.c_float, P, P]),
@@ -444,6 +446,31 @@ def moe_decode_forward(layer: QuantLayer, x: torch.Tensor, w_router: torch.Tenso
     d = layer.desc()
     _check(lib().moe_decode_forward(ctypes.byref(d), _p(x), _p(w_router), _p(bias), T, _p(residual), _p(logits),
                                     _p(idx), _p(w), _p(out), _p(ws), ws.numel(), _stream(stream)))
+    return out, logits, idx, w
+
+
+def moe_decode_forward_noalloc(layer: QuantLayer, x: torch.Tensor, w_router: torch.Tensor,
+                               bias: Optional[torch.Tensor], residual: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                               idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None, stream=None):
+    """moe_decode_forward on the library's static scratch (no workspace);
+    output tensors are allocated here unless given.  Returns (out, logits,
+    idx, w)."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(w_router, torch.bfloat16, "w_router")
+    T = x.shape[0]
+    dev = x.device
+    if logits is None:
+        logits = torch.empty((T, layer.E), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((T, layer.k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, layer.k), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, layer.H), dtype=torch.bfloat16, device=dev)
+    d = layer.desc()
+    _check(lib().moe_decode_forward_noalloc(ctypes.byref(d), _p(x), _p(w_router), _p(bias), T, _p(residual),
+                                            _p(logits), _p(idx), _p(w), _p(out), _stream(stream)))
     return out, logits, idx, w
 
 

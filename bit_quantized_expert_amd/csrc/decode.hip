@@ -4,7 +4,17 @@
 // decode_b{4,6,8}.hip.
 #include "decode_fused.h"
 
+#include <mutex>
+
 using namespace moeq;
+
+// Scratch of moe_decode_forward_noalloc: a fixed array in device memory that
+// every GPU holds one copy of from the time the library's code is loaded on
+// it until the process ends.  Host code never passes the array's name to a
+// kernel (in host code it only names the symbol): it passes the device
+// address hipGetSymbolAddress returns for the current device, kept below.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -155,4 +165,53 @@ extern "C" int moe_decode_block(const moe_layer_desc* L, uint16_t* x, const uint
   if (!(eps >= 0.0f)) return set_error(MOEQ_ERR_INVALID_ARG, "moe_decode_block: eps=%g", (double)eps);
   return decode_forward_impl("moe_decode_block", L, nullptr, w_router, bias, T, x, logits, topk_idx, topk_w, x, ws,
                              ws_bytes, decode_detail::NormArgs{x, eps, nullptr}, stream);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];   // scratch's device address, per device
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "moe_decode_forward_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_decode_forward_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(MOEQ_ERR_HIP, "moe_decode_forward_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOEQ_OK;
+}
+
+}  // namespace
+
+extern "C" size_t moe_decode_forward_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+extern "C" int moe_decode_forward_noalloc(const moe_layer_desc* L, const uint16_t* x, const uint16_t* w_router,
+                                          const float* bias, int T, const uint16_t* residual, float* logits,
+                                          int32_t* topk_idx, float* topk_w, uint16_t* out, hipStream_t stream) {
+  int rc = validate_layer(L);
+  if (rc != MOEQ_OK) return rc;
+  if (T < 0 || T > decode_detail::kFusedMaxT)
+    return set_error(MOEQ_ERR_INVALID_ARG, "moe_decode_forward_noalloc: T=%d (0 <= T <= %d)", T, decode_detail::kFusedMaxT);
+  const size_t need = ws_layout(L->H, L->I, L->E, L->S, L->k, T).total;
+  if (need > kNoAllocScratchBytes)
+    return set_error(MOEQ_ERR_WORKSPACE,
+                     "moe_decode_forward_noalloc: this layer at T=%d needs %zu bytes of scratch; the static scratch "
+                     "holds %zu (use moe_decode_forward with a workspace)", T, need, kNoAllocScratchBytes);
+  if (T == 0) return MOEQ_OK;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws)) != MOEQ_OK) return rc;
+  return decode_forward_impl("moe_decode_forward_noalloc", L, x, w_router, bias, T, residual, logits, topk_idx, topk_w,
+                             out, ws, kNoAllocScratchBytes, decode_detail::NormArgs{nullptr, 0.0f, nullptr}, stream);
 }

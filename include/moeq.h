@@ -338,6 +338,26 @@ int moe_decode_forward(const moe_layer_desc* L, const uint16_t* x, const uint16_
                        int32_t* topk_idx, float* topk_w, uint16_t* out,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_decode_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Its scratch (the h rows and the shared
+ * experts' partial sums) is a fixed array of
+ * moe_decode_forward_noalloc_max_scratch() bytes (8 MiB) in device memory
+ * that each GPU holds from the library's load until the process ends; the
+ * call allocates nothing.  Every call on one GPU uses that GPU's one array,
+ * so calls that overlap on one GPU (other streams, other threads) race and
+ * must be serialised by the caller.  Nothing in the array needs to start at
+ * zero: the kernels write all they read.  A layer and batch that need more
+ * scratch than the array holds (see moe_workspace_bytes(L, T)) are rejected
+ * with MOEQ_ERR_WORKSPACE; T <= 64.  Results, other limits and errors as
+ * moe_decode_forward. */
+int moe_decode_forward_noalloc(const moe_layer_desc* L, const uint16_t* x, const uint16_t* w_router,
+                               const float* bias, int T, const uint16_t* residual, float* logits,
+                               int32_t* topk_idx, float* topk_w, uint16_t* out, hipStream_t stream);
+
+/* Bytes of moe_decode_forward_noalloc's static scratch. */
+size_t moe_decode_forward_noalloc_max_scratch(void);
+
 /* One block of a stacked decode step (fewer launches per block: Raon-1-mini,
  * optimisation table): x <- x + moe(RMSNorm(x)) in place, for
  * a batch of T <= 64 token rows x (device bf16 [T][H]); the RMSNorm is
