@@ -569,7 +569,7 @@ def main_hqq(a, w, bq, dev):
     import torch
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
-    wt = torch.randn((w.n_mats, w.I, w.H), generator=g, device=dev, dtype=torch.float32) * 0.02
+    wt = torch.randn((w.n_mats, w.I, w.H), generator=g, device=dev, dtype=torch.float32) * a.hqq_std
     bits = w.bits
 
     def timed(fn, n):
@@ -606,7 +606,9 @@ def main_hqq(a, w, bq, dev):
                       "matrix": [w.n_mats, w.I, w.H], "ms_hqq": round(ms_h, 3), "ms_minmax": round(ms_mm, 3),
                       "minmax_GBps_fp32_in": round(n * 4 / (ms_mm * 1e-3) / 1e9, 1),
                       "mae_minmax": err_mm, "mae_hqq": err_h, "mae_drop": round(1 - err_h / err_mm, 4),
-                      "solver": {"lp": 0.7, "beta": 10.0, "kappa": 1.01, "iters": 20}, "data": "synthetic"}),
+                      "solver": {"lp": 0.7, "beta": 10.0, "kappa": 1.01, "iters": 20}, "weight_std": a.hqq_std,
+                      "zeros_moved": round(float(((outh.sz >> 16) != (out.sz >> 16)).float().mean()), 4),
+                      "data": "synthetic"}),
           flush=True)
 
 
@@ -863,6 +865,8 @@ def main():
     ap.add_argument("--kv", action="store_true", help="only time the KV-cache codec at a cache's size")
     ap.add_argument("--hqq", action="store_true",
                     help="only time the HQQ-refined quantisation of one projection of the workload")
+    ap.add_argument("--hqq-std", type=float, default=0.02,
+                    help="standard deviation of the weights --hqq quantises (0.02: the workloads' weights)")
     ap.add_argument("--curve-max", type=int, default=0, metavar="T",
                     help="only measure the decode layer at 1 .. T tokens per call (cost curve)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",

@@ -244,8 +244,11 @@ int moe_kv_decode(const uint8_t* q, const uint32_t* sz, long rows, int D, int bi
 
 /* Unpack codes q (rows*K*bits/8 bytes in the layout of moe_qweight, rows a
  * multiple of 64, device) into one byte per code, codes [rows][K] (device,
- * natural order).  It runs the same in-register unpacking the
- * decode kernels use, so it tests their view of the format bit for bit. */
+ * natural order): the inverse of the packing (two nibbles a byte at 4 bits,
+ * four values in three bytes at 6 bits; Krasis update, "Latest results
+ * (v1.0)": HQQ 4/6/8-bit weights).  It runs the same in-register unpacking
+ * the decode kernels use, so it tests their view of the format bit for
+ * bit. */
 int moe_unpack(const uint8_t* q, long rows, int K, int bits,
                uint8_t* codes, hipStream_t stream);
 
@@ -271,7 +274,10 @@ int moe_route_topk(const uint16_t* x, const uint16_t* w_router, const float* bia
                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Group the T*(k+S) assignments by expert: histogram, exclusive scan and a
- * stable scatter.  Outputs (device int32):
+ * stable scatter, so that each expert's tokens are contiguous for its GEMV
+ * or GEMM (a prefill chunk spreads over nearly every expert -- Qwen-tin,
+ * "Memory layout and performance" -- and each expert's weights are then
+ * read once per token tile).  Outputs (device int32):
  *   counts  [E+S]    assignments per expert,
  *   offsets [E+S+1]  exclusive prefix sum of counts,
  *   sorted  [T*(k+S)] assignment ids grouped by expert, ascending within one,
@@ -305,7 +311,9 @@ int moe_route_permute_decode(const uint16_t* x, const uint16_t* w_router, const 
 
 /* Decode path (small T): for every assignment a, y[a] = Wd h with
  * h = silu(Wg x_t) * (Wu x_t), t = a / (k+S), using expert sorted-order data
- * from moe_permute.  Only the experts in `active` are read, each once per
+ * from moe_permute.  Decode streams only the routed experts' weights, and
+ * that stream sets its speed (Raon-1-mini on an RTX 5070 Ti, result
+ * paragraph: decode at about two thirds of the card's bandwidth).  Only the experts in `active` are read, each once per
  * batch, as a grouped GEMV: codes are unpacked in registers and dot products
  * accumulated in fp32 with the group scale/zero applied per group in fp32;
  * h is rounded to bf16 between the two projections (as on the prefill path).
@@ -390,7 +398,10 @@ int moe_qgemm_prefill(const moe_layer_desc* L, const uint16_t* x, int T,
 #define MOEQ_Y_BF16 1
 /* Weighted combine: out[t] = sum_{j<k} topk_w[t][j] * y[t*(k+S)+j]
  *                          + sum_{j>=k} y[t*(k+S)+j],
- * summed in fp32 in ascending j.  If residual (device bf16 [T][H]) is
+ * summed in fp32 in ascending j: each token's output is its routed experts'
+ * outputs weighted by the renormalised routing weights (top-10 of 512
+ * experts: Qwen 3.8 Flash Next on an RTX 3060, introduction), plus the
+ * always-on shared experts with weight one.  If residual (device bf16 [T][H]) is
  * non-NULL, out[t] = bf16(residual[t] + bf16(sum)) instead of bf16(sum).
  * y is device fp32 or bf16 (y_dtype) [T*(k+S)][H]; out device bf16 [T][H]
  * (may alias residual). */
@@ -398,14 +409,20 @@ int moe_combine(const void* y, int y_dtype, const float* topk_w,
                 const uint16_t* residual, int T, int k, int S, int H,
                 uint16_t* out, hipStream_t stream);
 
-/* RMSNorm of bf16 rows: out[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps) * g),
+/* RMSNorm of bf16 rows, the normalisation in front of each MoE block of a
+ * stacked decode step (the per-layer work a persistent decode kernel runs
+ * between blocks: Raon-1-mini, optimisation table):
+ * out[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps) * g),
  * g = gamma (device bf16 [H]) or 1 if gamma is NULL; fp32 arithmetic.
  * x, out device bf16 [T][H]; may not alias. */
 int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, int T, int H, float eps,
                 uint16_t* out, hipStream_t stream);
 
 /* Synchronise `stream` and report the number of out-of-range expert ids the
- * last moe_permute on this workspace skipped. */
+ * last moe_permute on this workspace skipped: the routing step's ids must
+ * name one of the E routed experts (top-k over the router's E logits;
+ * Qwen 3.8 Flash Next on an RTX 3060, introduction), and the permutation
+ * counts any that do not instead of reading out of bounds. */
 int moe_read_status(const void* ws, size_t ws_bytes, int* n_bad_ids, hipStream_t stream);
 
 #ifdef __cplusplus
