@@ -1,6 +1,6 @@
 """Build libmoeq.so (the HIP kernels and their C ABI) for gfx950 with hipcc.
 
-    python bit_quantized_expert_amd/build.py [-j N] [--save-temps]
+    python bit_quantized_expert_amd/build.py [-j N] [--save-temps] [-D NAME[=VALUE] ...] [--out PATH]
 
 (Run it by path: importing the package itself needs the built library.)
 
@@ -67,14 +67,14 @@ def _check_no_scratch(src, out):
         raise RuntimeError(f"{src}: kernels use scratch memory (register spills): {bad}")
 
 
-def _compile(src, save_temps=False):
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+def _compile(src, save_temps=False, defines=(), build_dir=BUILD):
+    obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     if os.path.basename(src) in NO_SCRATCH:
         cmd.append("-Rpass-analysis=kernel-resource-usage")
     if save_temps:
         cmd.insert(1, "--save-temps")
-    r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=build_dir)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)   # host pass does not know the feature
     if r.returncode != 0:
@@ -87,26 +87,33 @@ def _compile(src, save_temps=False):
     return obj, out
 
 
-def build(jobs: int = 8, save_temps: bool = False, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, save_temps: bool = False, verbose: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile every source and link the library at ``out``; ``defines``
+    (NAME or NAME=VALUE) are passed to every compile, and a library built
+    with any goes to its own object folder."""
+    build_dir = BUILD if not defines else os.path.join(BUILD, "d_" + "_".join(
+        "".join(c if c.isalnum() else "-" for c in d) for d in defines))
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(lambda s: _compile(s, save_temps), sources()))
-    for obj, out in results:
-        if verbose and out.strip():
-            print(out)
-    tmp = LIB + ".tmp"
+        results = list(ex.map(lambda s: _compile(s, save_temps, defines, build_dir), sources()))
+    for obj, msg in results:
+        if verbose and msg.strip():
+            print(msg)
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", type=int, default=min(8, os.cpu_count() or 1))
     ap.add_argument("--save-temps", action="store_true")
+    ap.add_argument("-D", dest="defines", action="append", default=[], metavar="NAME[=VALUE]")
+    ap.add_argument("--out", default=LIB, help="library path (default: the package's libmoeq.so)")
     a = ap.parse_args()
-    print(build(a.j, a.save_temps, verbose=True))
+    print(build(a.j, a.save_temps, verbose=True, defines=a.defines, out=os.path.abspath(a.out)))
     sys.exit(0)

@@ -370,7 +370,10 @@ struct Mainloop {
   static constexpr int MT = BM / 32;   // M-tiles of the LDS tile; MTA of them hold rows
   static constexpr int NA = Stages<BITS>::NA, NB = Stages<BITS>::NB;
   static constexpr int ATILE = BM * 64 * 2;              // bytes of one token-row tile
-  static constexpr int LA = ADma<BM>::N, LB = BDma<BITS>::LOADS;
+  // token rows moved per slice: only those of the MTA M-tiles that hold rows
+  // (a tile of one or two tokens loads 32 rows, not BM)
+  using AD = ADma<32 * MTA>;
+  static constexpr int LA = AD::N, LB = BDma<BITS>::LOADS;
   // loads issued after those of slice s + 1 when slice s ends (each slice
   // issues token rows, then codes; see run())
   static constexpr int WAIT = (NA == 3 && NB == 3) ? LA + LB : (NA == 2 && NB == 3) ? LB : 0;
@@ -379,7 +382,7 @@ struct Mainloop {
   // MFMA step of this one, except at 6 bits where the unpacking needs the
   // registers (there they are dequantised when the slice starts)
   static constexpr bool EARLY_DQ = BITS != 6;
-  const ADma<BM>& ad;
+  const AD& ad;
   const BDma<BITS>& bd;
   int ns;
   f32x16_t (&acc)[MT][2];
@@ -387,7 +390,7 @@ struct Mainloop {
   int hh, wv;
   int aoff[4];    // byte offset of this lane's A operand (M-tile 0) at each step
 
-  MOEQ_DEV Mainloop(const ADma<BM>& ad_, const BDma<BITS>& bd_, int ns_, f32x16_t (&acc_)[MT][2], uint8_t* lds_)
+  MOEQ_DEV Mainloop(const AD& ad_, const BDma<BITS>& bd_, int ns_, f32x16_t (&acc_)[MT][2], uint8_t* lds_)
       : ad(ad_), bd(bd_), ns(ns_), acc(acc_), lds(lds_) {
     const int lane = threadIdx.x & 63;
     hh = lane >> 5;
@@ -571,14 +574,6 @@ __global__ __launch_bounds__(256, 2) void mfma_gateup_kernel(const uint8_t* __re
   const int rows = min(BM, counts[e] - mt * BM);
   const int lane = threadIdx.x & 63, hh = lane >> 5;
   const int wv = uniform(threadIdx.x >> 6);
-  ADma<BM> ad;
-  {
-    const uint16_t* rowp[ADma<BM>::N];
-#pragma unroll
-    for (int j = 0; j < ADma<BM>::N; ++j)
-      rowp[j] = x + (size_t)(sorted[base + min(ADma<BM>::row_of(j), rows - 1)] / kS) * H;
-    ad.init(rowp);
-  }
   BDma<BITS> bd;
   {
     const uint8_t* const q[2] = {gq, uq};
@@ -589,8 +584,17 @@ __global__ __launch_bounds__(256, 2) void mfma_gateup_kernel(const uint8_t* __re
   }
   with_mtiles(rows, [&](auto mta) {
     constexpr int MTA = decltype(mta)::value;
+    using ML = Mainloop<BITS, BM, MTA>;
+    typename ML::AD ad;
+    {
+      const uint16_t* rowp[ML::AD::N];
+#pragma unroll
+      for (int j = 0; j < ML::AD::N; ++j)
+        rowp[j] = x + (size_t)(sorted[base + min(ML::AD::row_of(j), rows - 1)] / kS) * H;
+      ad.init(rowp);
+    }
     f32x16_t acc[BM / 32][2];
-    Mainloop<BITS, BM, MTA>(ad, bd, H / 64, acc, lds).run();
+    ML(ad, bd, H / 64, acc, lds).run();
     // h tile -> LDS: lane (l % 32, half hh) holds column 32 wv + l % 32 of
     // rows 32 i + 8 (r / 4) + 4 hh + r % 4
 #pragma unroll
@@ -635,13 +639,6 @@ __global__ __launch_bounds__(256, 2) void mfma_down_kernel(const uint8_t* __rest
   const int rows = min(BM, counts[e] - mt * BM);
   const int lane = threadIdx.x & 63, hh = lane >> 5;
   const int wv = uniform(threadIdx.x >> 6);
-  ADma<BM> ad;
-  {
-    const uint16_t* rowp[ADma<BM>::N];
-#pragma unroll
-    for (int j = 0; j < ADma<BM>::N; ++j) rowp[j] = h + (size_t)(base + min(ADma<BM>::row_of(j), rows - 1)) * I;
-    ad.init(rowp);
-  }
   BDma<BITS> bd;
   {
     const uint8_t* const q[2] = {dq, dq};
@@ -652,8 +649,16 @@ __global__ __launch_bounds__(256, 2) void mfma_down_kernel(const uint8_t* __rest
   }
   with_mtiles(rows, [&](auto mta) {
     constexpr int MTA = decltype(mta)::value;
+    using ML = Mainloop<BITS, BM, MTA>;
+    typename ML::AD ad;
+    {
+      const uint16_t* rowp[ML::AD::N];
+#pragma unroll
+      for (int j = 0; j < ML::AD::N; ++j) rowp[j] = h + (size_t)(base + min(ML::AD::row_of(j), rows - 1)) * I;
+      ad.init(rowp);
+    }
     f32x16_t acc[BM / 32][2];
-    Mainloop<BITS, BM, MTA>(ad, bd, I / 64, acc, lds).run();
+    ML(ad, bd, I / 64, acc, lds).run();
 #pragma unroll
     for (int i = 0; i < MTA; ++i)
 #pragma unroll
