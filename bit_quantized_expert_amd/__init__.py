@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
         P, I, L64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_size_t
         sig = {
             "moe_workspace_bytes": (SZ, [P, I]),
+            "moe_workspace_h": (I, [P, I, P]),
             "moe_last_error": (ctypes.c_char_p, []),
             "moe_quantize": (I, [P, L64, I, I, P, P, P]),
             "moe_quantize_hqq": (I, [P, L64, I, I, ctypes.c_float, ctypes.c_float, ctypes.c_float, I, P, P, P]),
@@ -320,6 +321,16 @@ def quantize_layer(H: int, I: int, E: int, S: int, k: int, bits, draw, device="c
         projs[name] = QWeight(q, sz, b)
     torch.cuda.synchronize()
     return QuantLayer(H, I, E, S, k, projs["gate"], projs["up"], projs["down"])
+
+
+def workspace_h(layer: QuantLayer, ws: torch.Tensor, T: int, T_max: int) -> torch.Tensor:
+    """The intermediate h (bf16 [T*(k+S), I]) the last expert call left in
+    workspace ws (sized for T_max tokens), as a view."""
+    off = ctypes.c_size_t(0)
+    d = layer.desc()
+    _check(lib().moe_workspace_h(ctypes.byref(d), T_max, ctypes.byref(off)))
+    A = T * (layer.k + layer.S)
+    return ws[off.value:off.value + A * layer.I * 2].view(torch.bfloat16).view(A, layer.I)
 
 
 def moe_workspace_bytes(layer: QuantLayer, T_max: int) -> int:

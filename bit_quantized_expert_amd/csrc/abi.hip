@@ -88,6 +88,14 @@ extern "C" size_t moe_workspace_bytes(const moe_layer_desc* L, int T_max) {
 
 extern "C" const char* moe_last_error(void) { return g_err; }
 
+extern "C" int moe_workspace_h(const moe_layer_desc* L, int T_max, size_t* offset) {
+  int rc = validate_layer(L);
+  if (rc != MOEQ_OK) return rc;
+  if (T_max < 0 || !offset) return set_error(MOEQ_ERR_INVALID_ARG, "moe_workspace_h: T_max=%d or NULL offset", T_max);
+  *offset = ws_layout(L->H, L->I, L->E, L->S, L->k, T_max).h;
+  return MOEQ_OK;
+}
+
 extern "C" int moe_read_status(const void* ws, size_t ws_bytes, int* n_bad_ids, hipStream_t stream) {
   if (!ws || !n_bad_ids) return set_error(MOEQ_ERR_INVALID_ARG, "NULL workspace or output");
   if (ws_bytes < 256) return set_error(MOEQ_ERR_WORKSPACE, "workspace smaller than its status block");

@@ -205,29 +205,46 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 MOEQ_DEV float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(f16x2_t, v).x; }
 MOEQ_DEV float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(f16x2_t, v).y; }
 
+
 // Dequantisation of one group.  A code q is held as the fp16 value
 // v = 1024 + m q, m = 1, 4 or 16 (the code OR-ed into the mantissa at bit 0,
-// 2 or 4, wherever it lands without a shift), and
-//     w = (q - z) s = v (s / m) - (1024 / m + z) s,
-// one fma in fp32 with one rounding (v_fma_mix reads the fp16 half itself).
+// 2 or 4, wherever it lands without a shift).  v - 1024 = m q exactly (one
+// packed fp16 subtraction per pair), and
+//     w = (q - z) s = (m q) (s / m) - z s
+// is one fma in fp32 with one rounding: z s is a product of two fp16 values
+// (22 significant bits), exact in fp32, and (m q)(s / m) = q s is exact, so
+// w is fp32((q - z) s) rounded once, the plain dequantised weight.  It is
+// then rounded to bf16 for the matrix cores.
 struct GroupDq {
-  float s1, n1, sm, nm;   // (s / m, -(1024 / m + z) s) for m = 1 and m = M
+  float s1, sm, nzs;   // s / 1, s / M, -(z s)
   template <int M>
   MOEQ_DEV static GroupDq make(uint32_t sz) {
     const float s = f16_bits_to_f32(sz & 0xFFFFu), z = f16_bits_to_f32(sz >> 16);
     GroupDq g;
     g.s1 = s;
-    g.n1 = -(1024.0f + z) * s;
     g.sm = s * (1.0f / M);
-    g.nm = -(1024.0f / M + z) * s;
+    g.nzs = -(z * s);
     return g;
   }
 };
+
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+// (1024 + m q_lo, 1024 + m q_hi) -> (m q_lo, m q_hi), exact
+MOEQ_DEV f16x2v minus_1024(uint32_t p) {
+  return __builtin_bit_cast(f16x2v, p) - f16x2v{(_Float16)1024.0f, (_Float16)1024.0f};
+}
 
 MOEQ_DEV uint32_t bf16_pair(float lo, float hi) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   const bf2 v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32, round to nearest even
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// One pair of weights: codes (m_lo q_lo, m_hi q_hi) held as 1024 + m q in
+// the fp16 halves of p, scales s_lo = s / m_lo and s_hi = s / m_hi.
+MOEQ_DEV uint32_t dq_pair(uint32_t p, float s_lo, float s_hi, float nzs) {
+  const f16x2v t = minus_1024(p);
+  return bf16_pair(fmaf((float)t.x, s_lo, nzs), fmaf((float)t.y, s_hi, nzs));
 }
 
 // The 8 weights this lane supplies at MFMA step st, dequantised and rounded
@@ -240,11 +257,10 @@ MOEQ_DEV bf16x8_t dequant_step(const SliceCodes<BITS>& sc, const GroupDq& g, int
   if constexpr (BITS == 4) {
     // nibbles i and i + 4 of the dword hold codes 2i and 2i + 1
     const uint32_t d = sc.d[2 * j + sub], t = d >> 8;
-    r[0] = bf16_pair(fmaf(f16_lo(and_or(d, 0x000F000Fu, M)), g.s1, g.n1), fmaf(f16_hi(and_or(d, 0x000F000Fu, M)), g.s1, g.n1));
-    const uint32_t p1 = and_or(d, 0x00F000F0u, M), p3 = and_or(t, 0x00F000F0u, M), p2 = and_or(t, 0x000F000Fu, M);
-    r[1] = bf16_pair(fmaf(f16_lo(p1), g.sm, g.nm), fmaf(f16_hi(p1), g.sm, g.nm));
-    r[2] = bf16_pair(fmaf(f16_lo(p2), g.s1, g.n1), fmaf(f16_hi(p2), g.s1, g.n1));
-    r[3] = bf16_pair(fmaf(f16_lo(p3), g.sm, g.nm), fmaf(f16_hi(p3), g.sm, g.nm));
+    r[0] = dq_pair(and_or(d, 0x000F000Fu, M), g.s1, g.s1, g.nzs);
+    r[1] = dq_pair(and_or(d, 0x00F000F0u, M), g.sm, g.sm, g.nzs);
+    r[2] = dq_pair(and_or(t, 0x000F000Fu, M), g.s1, g.s1, g.nzs);
+    r[3] = dq_pair(and_or(t, 0x00F000F0u, M), g.sm, g.sm, g.nzs);
   } else if constexpr (BITS == 6) {
     // pair i of the chunk = codes (2i, 2i + 1) from fields 3 apart (18
     // bits): the low code at bit 0 (m = 1), the high one at bit 18 (bit 2
@@ -263,15 +279,14 @@ MOEQ_DEV bf16x8_t dequant_step(const SliceCodes<BITS>& sc, const GroupDq& g, int
       P[3] = and_or(d2 >> 8, 0x00FC003Fu, M);                                 // fields 12, 15
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = bf16_pair(fmaf(f16_lo(P[i]), g.s1, g.n1), fmaf(f16_hi(P[i]), g.sm, g.nm));
+    for (int i = 0; i < 4; ++i) r[i] = dq_pair(P[i], g.s1, g.sm, g.nzs);
   } else {
     // bytes (2i, 2i + 1) under the fp16 exponent byte 0x64
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t v = sc.d[4 * j + 2 * sub + i];
-      const uint32_t pa = __builtin_amdgcn_perm(M, v, 0x05010500u), pb = __builtin_amdgcn_perm(M, v, 0x05030502u);
-      r[2 * i] = bf16_pair(fmaf(f16_lo(pa), g.s1, g.n1), fmaf(f16_hi(pa), g.s1, g.n1));
-      r[2 * i + 1] = bf16_pair(fmaf(f16_lo(pb), g.s1, g.n1), fmaf(f16_hi(pb), g.s1, g.n1));
+      r[2 * i] = dq_pair(__builtin_amdgcn_perm(M, v, 0x05010500u), g.s1, g.s1, g.nzs);
+      r[2 * i + 1] = dq_pair(__builtin_amdgcn_perm(M, v, 0x05030502u), g.s1, g.s1, g.nzs);
     }
   }
   return __builtin_bit_cast(bf16x8_t, r);

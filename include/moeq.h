@@ -97,6 +97,16 @@ typedef struct moe_layer_desc {
  * the control words it relies on at zero between calls. */
 size_t moe_workspace_bytes(const moe_layer_desc* L, int T_max);
 
+/* Byte offset, in a workspace of moe_workspace_bytes(L, T_max) bytes, of the
+ * intermediate h = silu(Wg x) * (Wu x) the expert calls leave there: bf16
+ * [T*(k+S)][I], rows in expert-sorted order (the order of moe_permute's
+ * sorted) after moe_qgemv_decode and moe_qgemm_prefill, in assignment order
+ * after moe_decode_forward.  h is what the two projections of a SwiGLU expert
+ * hand each other (Raon-1-mini, optimisation table: the projections that share
+ * an input run together, the down projection waits for their result); the
+ * call exists to inspect it.  Valid until the next call on the workspace. */
+int moe_workspace_h(const moe_layer_desc* L, int T_max, size_t* offset);
+
 /* Description of the last error raised on this thread ("" if none). */
 const char* moe_last_error(void);
 

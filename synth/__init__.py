@@ -75,6 +75,9 @@ WORKLOADS = {w.name: w for w in [
     Workload("moe_h2048_e128_k8_b6_zipf", 3, 2048, 512, 128, 8, 0, 6, (512, 2048, 4096), "zipf"),
     # wide MoE, hidden 4096, 512 experts, intermediate 768, top-10, 10% hot experts
     Workload("moe_h4096_e512_k10_b4_hot", 4, 4096, 768, 512, 10, 0, 4, (1, 8192), "hot"),
+    # the same prefill chunks on the 256-expert + 1-shared shapes (the decode
+    # layer's), 6-bit, Zipf(1.1) router offsets
+    Workload("moe_h2048_e256_k8_s1_b6_zipf", 6, 2048, 512, 256, 8, 1, 6, (512, 2048, 4096), "zipf"),
     # 48 stacked blocks (RMSNorm -> 128-expert MoE -> residual), mixed 4/6/8-bit
     Workload("stack48_h2048_e128_k8_mixed", 5, 2048, 512, 128, 8, 0, 0, (1,), None,
              layers=48, bits_mix=(24, 14, 10), steps=256),

@@ -445,6 +445,29 @@ def pin_ffn_bf16_h(o, seed=9):
     assert not np.array_equal(got, exact)
 
 
+def pin_ffn_bf16_w(o, seed=10):
+    """w_bf16 rounds the dequantised fp32 weights to bf16 before the
+    products: torch's fp32 -> bf16 conversion of the same weights, with h
+    rounded as well, gives the same y; weights that are bf16 values already
+    (a power-of-two grid) are left as they are; otherwise the result moves
+    from the fp64 FFN."""
+    import torch
+    rng = np.random.default_rng(seed)
+    n, H, I = 6, 64, 48
+    x = rng.standard_normal((n, H))
+    wg, wu, wd = ((rng.standard_normal(sh) * 0.3).astype(np.float32) for sh in ((I, H), (I, H), (H, I)))
+    tb = lambda a: torch.tensor(a).to(torch.bfloat16).double()       # fp32 -> bf16, nearest even
+    xt = torch.tensor(x, dtype=torch.float64)
+    h = torch.nn.functional.silu(xt @ tb(wg).T) * (xt @ tb(wu).T)
+    hb = torch.tensor(o.bf16_to_f32(o.f32_to_bf16(h.numpy())), dtype=torch.float64)
+    ref = (hb @ tb(wd).T).numpy()
+    got = o.expert_ffn(x, wg, wu, wd, h_bf16=True, w_bf16=True)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+    assert not np.allclose(got, o.expert_ffn(x, wg, wu, wd, h_bf16=True), rtol=1e-6, atol=0)
+    grid = [((rng.integers(-8, 8, sh)) * 2.0 ** -5).astype(np.float32) for sh in ((I, H), (I, H), (H, I))]
+    assert np.array_equal(o.expert_ffn(x, *grid, w_bf16=True), o.expert_ffn(x, *grid))
+
+
 # --------------------------------------------------------------------------
 # HQQ zero-point refinement
 # --------------------------------------------------------------------------

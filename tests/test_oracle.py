@@ -60,6 +60,10 @@ def test_ffn_bf16_h():
     pins.pin_ffn_bf16_h(oracle)
 
 
+def test_ffn_bf16_w():
+    pins.pin_ffn_bf16_w(oracle)
+
+
 def test_shrink_closed_form():
     pins.pin_shrink_closed_form(oracle)
 

@@ -8,7 +8,7 @@ import oracle
 import oracle.moe as om
 from tests import pins
 
-_quantize, _pack, _permute = om.quantize, om.pack, om.permute
+_quantize, _pack, _permute, _expert_ffn = om.quantize, om.pack, om.permute, om.expert_ffn
 
 
 def _fails(fn, *a, **kw):
@@ -83,21 +83,21 @@ def _permute_unstable(idx, E, S=0):
     return counts, offsets, srt, inv
 
 
-def _ffn_silu_on_up(x, wg, wu, wd, h_bf16=False):
+def _ffn_silu_on_up(x, wg, wu, wd, h_bf16=False, w_bf16=False):
     x = np.asarray(x, np.float64)
     g = x @ np.asarray(wg, np.float64).T
     u = x @ np.asarray(wu, np.float64).T
     return (g * om.silu(u)) @ np.asarray(wd, np.float64).T
 
 
-def _ffn_transposed_down(x, wg, wu, wd, h_bf16=False):
+def _ffn_transposed_down(x, wg, wu, wd, h_bf16=False, w_bf16=False):
     x = np.asarray(x, np.float64)
     g = x @ np.asarray(wg, np.float64).T
     u = x @ np.asarray(wu, np.float64).T
     return (om.silu(g) * u) @ np.asarray(wd, np.float64).T[::-1]   # mistake: rows reversed
 
 
-def _ffn_rounds_up_not_h(x, wg, wu, wd, h_bf16=False):
+def _ffn_rounds_up_not_h(x, wg, wu, wd, h_bf16=False, w_bf16=False):
     # mistake: the bf16 rounding applied to the up projection instead of h
     x = np.asarray(x, np.float64)
     g = x @ np.asarray(wg, np.float64).T
@@ -105,6 +105,14 @@ def _ffn_rounds_up_not_h(x, wg, wu, wd, h_bf16=False):
     if h_bf16:
         u = om.bf16_to_f32(om.f32_to_bf16(u)).astype(np.float64)
     return (om.silu(g) * u) @ np.asarray(wd, np.float64).T
+
+
+def _ffn_w_truncated(x, wg, wu, wd, h_bf16=False, w_bf16=False):
+    # mistake: the bf16 weights truncated instead of rounded to nearest even
+    if w_bf16:
+        wg, wu, wd = (om.bf16_to_f32((np.asarray(m, np.float32).view(np.uint32) >> 16).astype(np.uint16))
+                      for m in (wg, wu, wd))
+    return _expert_ffn(x, wg, wu, wd, h_bf16)
 
 
 def _combine_drop_shared(y, w, S=0):
@@ -203,6 +211,7 @@ MUTANTS = [
     ("expert_ffn", _ffn_silu_on_up, [pins.pin_layer_bruteforce, pins.pin_layer_special_cases]),
     ("expert_ffn", _ffn_transposed_down, [pins.pin_layer_bruteforce, pins.pin_on_grid_layer]),
     ("expert_ffn", _ffn_rounds_up_not_h, [pins.pin_ffn_bf16_h]),
+    ("expert_ffn", _ffn_w_truncated, [pins.pin_ffn_bf16_w]),
     ("combine", _combine_drop_shared, [pins.pin_layer_bruteforce, pins.pin_layer_special_cases]),
     ("rmsnorm_bf16", _rmsnorm_no_eps, [pins.pin_bf16_and_norm]),
     ("residual_bf16", _residual_no_block_rounding, [pins.pin_bf16_and_norm]),
