@@ -48,6 +48,8 @@ WsLayout ws_layout(int H, int I, int E, int S, int k, int T_max) {
   off = align_up(off + (size_t)S * Tf * kSharedMaxSplit * 2 * I * sizeof(float), 256);
   w.norm = off;          // [T][H] bf16, decode batches
   off = align_up(off + (size_t)Tf * H * sizeof(uint16_t), 256);
+  w.gemv = off;
+  off = align_up(off + (size_t)(nexp + 1) * sizeof(int32_t), 256);
   w.total = off;
   return w;
 }

@@ -36,12 +36,21 @@ struct WsLayout {
   size_t sched;      // prefill: int32 tile schedule
   size_t shared_part;   // moe_decode_forward: fp32 partial gate/up sums of the shared experts
   size_t norm;          // moe_decode_block: the normalised token rows, bf16
+  size_t gemv;          // prefill: int32 [1 + E + S] experts taking the GEMV path (count, ids)
   size_t total;
 };
 constexpr int kPermBlock = 1024;          // assignments per permute block
 constexpr int kPrefillBM = 128;           // prefill token tile
 constexpr int kFusedMaxTokens = 64;       // moe_decode_forward batches
 constexpr int kSharedMaxSplit = 16;       // moe_decode_forward: K slices of a shared-expert row
+#ifndef MOEQ_PREFILL_GEMV_MAX
+#define MOEQ_PREFILL_GEMV_MAX 2
+#endif
+#ifndef MOEQ_PREFILL_GEMV_MIN
+#define MOEQ_PREFILL_GEMV_MIN 64
+#endif
+constexpr int kPrefillGemvMax = MOEQ_PREFILL_GEMV_MAX;   // prefill: experts with at most this many assignments take the GEMV path,
+constexpr int kPrefillGemvMin = MOEQ_PREFILL_GEMV_MIN;   // when a batch has at least this many of them
 int perm_blocks(long A);
 long prefill_max_tiles(long A, int nexp);
 WsLayout ws_layout(int H, int I, int E, int S, int k, int T_max);

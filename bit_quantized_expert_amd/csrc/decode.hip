@@ -18,39 +18,6 @@ static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
 
-// Block shape for K inputs at `bits`: W wavefronts split the CPR = K / codes
-// chunks of a row, CW = CPR / W each, a whole number of groups (at most 8).
-// The wavefront's run of CW chunks is a software pipeline whose register
-// footprint grows with CW, so the shape with the run closest to `want`
-// chunks (and not shorter than one group) is taken.
-bool pick_shape(int K, int bits, int want, int& W, int& CW) {
-  const int codes = bits == 4 ? 32 : 16, cpg = 64 / codes;
-  if (K % codes) return false;
-  const int cpr = K / codes;
-  bool found = false;
-  int best = 0;
-  for (const auto& s : decode_detail::kShapes) {
-    const int w = s[0], cw = s[1];
-    if (w * cw != cpr || cw % cpg || cw / cpg > 8) continue;
-    const int score = cw >= want ? cw - want : 2 * (want - cw);   // shorter runs cost more
-    if (!found || score < best) {
-      W = w;
-      CW = cw;
-      best = score;
-      found = true;
-    }
-  }
-  return found;
-}
-
-#ifndef MOEQ_GATEUP_RUN
-#define MOEQ_GATEUP_RUN 8
-#endif
-#ifndef MOEQ_DOWN_RUN
-#define MOEQ_DOWN_RUN 8
-#endif
-
-
 }  // namespace
 
 extern "C" int moe_qgemv_decode(const moe_layer_desc* L, const uint16_t* x, int T, const int32_t* offsets,

@@ -17,6 +17,20 @@
         L->down.q, L->down.sz, hh, L->H, L->I, dg, offsets, sorted, active, y);                        \
     launched = true;                                                                                   \
   }
+#define MOEQ_LAUNCH_GU_LIST(W_, CW_)                                                                   \
+  if constexpr (CW_ % Fmt<6>::CHUNKS_PER_GROUP == 0 && CW_ / Fmt<6>::CHUNKS_PER_GROUP <= 8)           \
+  if (W == W_ && CW == CW_) {                                                                          \
+    decode_detail::gateup_list_kernel<6, W_, CW_><<<grid, 64 * W_, 0, s>>>(                          \
+        L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, dg, offsets, sorted, active, hh);     \
+    launched = true;                                                                                   \
+  }
+#define MOEQ_LAUNCH_DN_LIST(W_, CW_)                                                                   \
+  if constexpr (CW_ % Fmt<6>::CHUNKS_PER_GROUP == 0 && CW_ / Fmt<6>::CHUNKS_PER_GROUP <= 8)           \
+  if (W == W_ && CW == CW_) {                                                                          \
+    decode_detail::down_list_kernel<6, W_, CW_><<<grid, 64 * W_, 0, s>>>(                            \
+        L->down.q, L->down.sz, hh, L->H, L->I, dg, offsets, sorted, active, y);                        \
+    launched = true;                                                                                   \
+  }
 namespace moeq {
 MOEQ_DEFINE_DECODE(6)
 MOEQ_DEFINE_DECODE_FUSED(6)

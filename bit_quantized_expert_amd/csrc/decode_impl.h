@@ -57,8 +57,8 @@ struct DecodeGrid {
 // Decodes blockIdx.x.  Returns false for a block without work; otherwise
 // sets the expert, the row tile and, for a shared-expert block, its token
 // pair (-1 for a routed block: all of the expert's tokens).
-MOEQ_DEV bool block_work(const DecodeGrid& dg, const int32_t* __restrict__ active, int& e, int& tile, int& pair) {
-  const int b = (int)blockIdx.x;
+MOEQ_DEV bool block_work(int b, const DecodeGrid& dg, const int32_t* __restrict__ active, int& e, int& tile,
+                         int& pair) {
   if (b < dg.shared_blocks) {
     const int span = 8 * dg.groups;
     const int l = (b / span) * 8 + (b % 8);   // (shared expert, row tile)
@@ -309,20 +309,16 @@ MOEQ_DEV void block_pass(const Stream<BITS, NM>& st, ChunkBuf<BITS, NM> (&buf)[C
 // sorted positions p (token t = sorted[p] / (k+S)); h is [A][I] bf16.
 // -------------------------------------------------------------------------
 template <int BITS, int W, int CW>
-__global__ __launch_bounds__(64 * W, 4) void gateup_rows_kernel(const uint8_t* __restrict__ gq,
-                                                                const uint32_t* __restrict__ gsz,
-                                                                const uint8_t* __restrict__ uq,
-                                                                const uint32_t* __restrict__ usz,
-                                                                const uint16_t* __restrict__ x, int H, int I,
-                                                                DecodeGrid dg, const int32_t* __restrict__ offsets,
-                                                                const int32_t* __restrict__ sorted,
-                                                                const int32_t* __restrict__ active,
-                                                                uint16_t* __restrict__ hh) {
+MOEQ_DEV void gateup_rows_unit(int b, Partials<W, 2>& part, const uint8_t* __restrict__ gq,
+                               const uint32_t* __restrict__ gsz, const uint8_t* __restrict__ uq,
+                               const uint32_t* __restrict__ usz, const uint16_t* __restrict__ x, int H, int I,
+                               const DecodeGrid& dg, const int32_t* __restrict__ offsets,
+                               const int32_t* __restrict__ sorted, const int32_t* __restrict__ active,
+                               uint16_t* __restrict__ hh) {
   using F = Fmt<BITS>;
   constexpr int D = CW < kDepth ? CW : kDepth;
-  __shared__ Partials<W, 2> part;
   int e, tile, pair;
-  if (!block_work(dg, active, e, tile, pair)) return;
+  if (!block_work(b, dg, active, e, tile, pair)) return;
   e = uniform(e);
   tile = uniform(tile);
   pair = uniform(pair);
@@ -369,23 +365,60 @@ __global__ __launch_bounds__(64 * W, 4) void gateup_rows_kernel(const uint8_t* _
   }
 }
 
+// One block per unit (decode batches).
+template <int BITS, int W, int CW>
+__global__ __launch_bounds__(64 * W, 4) void gateup_rows_kernel(const uint8_t* __restrict__ gq,
+                                                                const uint32_t* __restrict__ gsz,
+                                                                const uint8_t* __restrict__ uq,
+                                                                const uint32_t* __restrict__ usz,
+                                                                const uint16_t* __restrict__ x, int H, int I,
+                                                                DecodeGrid dg, const int32_t* __restrict__ offsets,
+                                                                const int32_t* __restrict__ sorted,
+                                                                const int32_t* __restrict__ active,
+                                                                uint16_t* __restrict__ hh) {
+  __shared__ Partials<W, 2> part;
+  gateup_rows_unit<BITS, W, CW>((int)blockIdx.x, part, gq, gsz, uq, usz, x, H, I, dg, offsets, sorted, active, hh);
+}
+
+// A grid smaller than the list: each block takes units blockIdx.x,
+// blockIdx.x + gridDim.x, ... up to the list's active[0] * tiles (routed
+// experts only), so an empty or short list costs one read per block.
+template <int BITS, int W, int CW>
+__global__ __launch_bounds__(64 * W, 4) void gateup_list_kernel(const uint8_t* __restrict__ gq,
+                                                                const uint32_t* __restrict__ gsz,
+                                                                const uint8_t* __restrict__ uq,
+                                                                const uint32_t* __restrict__ usz,
+                                                                const uint16_t* __restrict__ x, int H, int I,
+                                                                DecodeGrid dg, const int32_t* __restrict__ offsets,
+                                                                const int32_t* __restrict__ sorted,
+                                                                const int32_t* __restrict__ active,
+                                                                uint16_t* __restrict__ hh) {
+  __shared__ Partials<W, 2> part;
+  const int units = uniform(active[0]) * dg.tiles;
+  for (int b = (int)blockIdx.x; b < units; b += (int)gridDim.x) {
+    __syncthreads();   // the previous unit's partials have been read
+    gateup_rows_unit<BITS, W, CW>(b, part, gq, gsz, uq, usz, x, H, I, dg, offsets, sorted, active, hh);
+  }
+}
+
+MOEQ_DEV float y_value(float v, float*) { return v; }
+MOEQ_DEV uint16_t y_value(float v, uint16_t*) { return (uint16_t)f32_to_bf16_bits(v); }
+
 // -------------------------------------------------------------------------
 // down: y[a][n] = (Wd h_p)[n] for the expert's sorted positions p and their
-// assignments a = sorted[p]; y is [A][H] fp32.
+// assignments a = sorted[p]; y is [A][H], fp32 (YT = float) or bf16 (YT =
+// uint16_t, rounded to nearest even).
 // -------------------------------------------------------------------------
-template <int BITS, int W, int CW>
-__global__ __launch_bounds__(64 * W, 4) void down_rows_kernel(const uint8_t* __restrict__ dq,
-                                                              const uint32_t* __restrict__ dsz,
-                                                              const uint16_t* __restrict__ hh, int H, int I,
-                                                              DecodeGrid dg, const int32_t* __restrict__ offsets,
-                                                              const int32_t* __restrict__ sorted,
-                                                              const int32_t* __restrict__ active,
-                                                              float* __restrict__ y) {
+template <int BITS, int W, int CW, typename YT>
+MOEQ_DEV void down_rows_unit(int b, Partials<W, 1>& part, const uint8_t* __restrict__ dq,
+                             const uint32_t* __restrict__ dsz, const uint16_t* __restrict__ hh, int H, int I,
+                             const DecodeGrid& dg, const int32_t* __restrict__ offsets,
+                             const int32_t* __restrict__ sorted, const int32_t* __restrict__ active,
+                             YT* __restrict__ y) {
   using F = Fmt<BITS>;
   constexpr int D = CW < kDepth ? CW : kDepth;
-  __shared__ Partials<W, 1> part;
   int e, tile, pair;
-  if (!block_work(dg, active, e, tile, pair)) return;
+  if (!block_work(b, dg, active, e, tile, pair)) return;
   e = uniform(e);
   tile = uniform(tile);
   pair = uniform(pair);
@@ -411,7 +444,7 @@ __global__ __launch_bounds__(64 * W, 4) void down_rows_kernel(const uint8_t* __r
     const uint16_t* const xr[kMaxNT] = {hh + (size_t)p0 * I, hh + (size_t)(p0 + (nt > 1 ? 1 : 0)) * I};
     float tot[1];
     block_pass<BITS, 1, W, CW>(st, b, xr, nt, part, tot);
-    if (wave < nt) y[(size_t)sorted[p0 + wave] * H + row] = tot[0];
+    if (wave < nt) y[(size_t)sorted[p0 + wave] * H + row] = y_value(tot[0], y);
   };
   if (pb >= pe) return;
   pass(pb, buf);
@@ -425,6 +458,34 @@ __global__ __launch_bounds__(64 * W, 4) void down_rows_kernel(const uint8_t* __r
   }
 }
 
+template <int BITS, int W, int CW, typename YT>
+__global__ __launch_bounds__(64 * W, 4) void down_rows_kernel(const uint8_t* __restrict__ dq,
+                                                              const uint32_t* __restrict__ dsz,
+                                                              const uint16_t* __restrict__ hh, int H, int I,
+                                                              DecodeGrid dg, const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ sorted,
+                                                              const int32_t* __restrict__ active,
+                                                              YT* __restrict__ y) {
+  __shared__ Partials<W, 1> part;
+  down_rows_unit<BITS, W, CW, YT>((int)blockIdx.x, part, dq, dsz, hh, H, I, dg, offsets, sorted, active, y);
+}
+
+template <int BITS, int W, int CW, typename YT>
+__global__ __launch_bounds__(64 * W, 4) void down_list_kernel(const uint8_t* __restrict__ dq,
+                                                              const uint32_t* __restrict__ dsz,
+                                                              const uint16_t* __restrict__ hh, int H, int I,
+                                                              DecodeGrid dg, const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ sorted,
+                                                              const int32_t* __restrict__ active,
+                                                              YT* __restrict__ y) {
+  __shared__ Partials<W, 1> part;
+  const int units = uniform(active[0]) * dg.tiles;
+  for (int b = (int)blockIdx.x; b < units; b += (int)gridDim.x) {
+    __syncthreads();
+    down_rows_unit<BITS, W, CW, YT>(b, part, dq, dsz, hh, H, I, dg, offsets, sorted, active, y);
+  }
+}
+
 // (W, CW) shapes with a kernel: W wavefronts per block, CW chunks each.
 #define MOEQ_DECODE_SHAPES(X)                                                                            \
   X(2, 2) X(2, 4) X(2, 8) X(2, 16) X(4, 2) X(4, 4) X(4, 6) X(4, 8) X(4, 12) X(4, 16) X(8, 2) X(8, 4)      \
@@ -433,6 +494,38 @@ constexpr int kShapes[][2] = {{2, 2}, {2, 4}, {2, 8}, {2, 16}, {4, 2}, {4, 4}, {
                               {4, 16}, {8, 2}, {8, 4}, {8, 8}, {8, 16}, {16, 4}, {16, 8}, {16, 16}};
 
 }  // namespace decode_detail
+
+// Block shape for K inputs at `bits`: W wavefronts split the CPR = K / codes
+// chunks of a row, CW = CPR / W each, a whole number of groups (at most 8).
+// The wavefront's run of CW chunks is a software pipeline whose register
+// footprint grows with CW, so the shape with the run closest to `want`
+// chunks (and not shorter than one group) is taken.
+inline bool pick_shape(int K, int bits, int want, int& W, int& CW) {
+  const int codes = bits == 4 ? 32 : 16, cpg = 64 / codes;
+  if (K % codes) return false;
+  const int cpr = K / codes;
+  bool found = false;
+  int best = 0;
+  for (const auto& s : decode_detail::kShapes) {
+    const int w = s[0], cw = s[1];
+    if (w * cw != cpr || cw % cpg || cw / cpg > 8) continue;
+    const int score = cw >= want ? cw - want : 2 * (want - cw);   // shorter runs cost more
+    if (!found || score < best) {
+      W = w;
+      CW = cw;
+      best = score;
+      found = true;
+    }
+  }
+  return found;
+}
+
+#ifndef MOEQ_GATEUP_RUN
+#define MOEQ_GATEUP_RUN 8
+#endif
+#ifndef MOEQ_DOWN_RUN
+#define MOEQ_DOWN_RUN 8
+#endif
 
 // Grid of the decode kernels for N output rows per expert (see
 // decode_detail::DecodeGrid); returns the block count.
@@ -447,6 +540,19 @@ inline int decode_grid(const moe_layer_desc* L, int T, int N, decode_detail::Dec
   return dg.shared_blocks + (int)routed * dg.tiles;
 }
 
+// Grid of the list kernels over routed experts only (no shared blocks):
+// up to max_experts of them, N output rows each, at most 1024 blocks.
+inline int decode_list_grid(const moe_layer_desc* L, int max_experts, int N, decode_detail::DecodeGrid& dg) {
+  dg.E = L->E;
+  dg.S = 0;
+  dg.kS = L->k + L->S;
+  dg.tiles = N / 64;
+  dg.groups = 1;
+  dg.shared_blocks = 0;
+  const int units = max_experts * dg.tiles;
+  return units < 1024 ? units : 1024;
+}
+
 // Per-bit-width launchers (one translation unit each, decode_b{4,6,8}.hip).
 #define MOEQ_DECODE_LAUNCHERS(B)                                                                          \
   int decode_gateup_b##B(const moe_layer_desc* L, const uint16_t* x, const int32_t* offsets,              \
@@ -454,7 +560,12 @@ inline int decode_grid(const moe_layer_desc* L, int T, int N, decode_detail::Dec
                          hipStream_t s);                                                                  \
   int decode_down_b##B(const moe_layer_desc* L, const uint16_t* hh, const int32_t* offsets,               \
                        const int32_t* sorted, const int32_t* active, int T, int W, int CW, float* y,      \
-                       hipStream_t s)
+                       hipStream_t s);                                                                    \
+  int list_gateup_b##B(const moe_layer_desc* L, const uint16_t* x, const int32_t* offsets,                \
+                       const int32_t* sorted, const int32_t* list, int W, int CW, uint16_t* hh,           \
+                       hipStream_t s);                                                                    \
+  int list_down_b##B(const moe_layer_desc* L, const uint16_t* hh, const int32_t* offsets,                 \
+                     const int32_t* sorted, const int32_t* list, int W, int CW, uint16_t* y, hipStream_t s)
 
 MOEQ_DECODE_LAUNCHERS(4);
 MOEQ_DECODE_LAUNCHERS(6);
@@ -482,6 +593,26 @@ MOEQ_DECODE_LAUNCHERS(8);
     MOEQ_DECODE_SHAPES(MOEQ_LAUNCH_DN)                                                                    \
     if (!launched) return set_error(MOEQ_ERR_UNSUPPORTED, "decode: no down kernel for W=%d CW=%d", W, CW); \
     return check_launch("moe_qgemv_decode (down)");                                                       \
+  }                                                                                                       \
+  int list_gateup_b##B(const moe_layer_desc* L, const uint16_t* x, const int32_t* offsets,                \
+                       const int32_t* sorted, const int32_t* active, int W, int CW, uint16_t* hh,         \
+                       hipStream_t s) {                                                                   \
+    decode_detail::DecodeGrid dg;                                                                         \
+    const int grid = decode_list_grid(L, L->E, L->I, dg);                                                 \
+    bool launched = false;                                                                                \
+    MOEQ_DECODE_SHAPES(MOEQ_LAUNCH_GU_LIST)                                                               \
+    if (!launched) return set_error(MOEQ_ERR_UNSUPPORTED, "expert list: no gate/up kernel for W=%d CW=%d", W, CW); \
+    return check_launch("moe_qgemm_prefill (gate/up of the GEMV list)");                                  \
+  }                                                                                                       \
+  int list_down_b##B(const moe_layer_desc* L, const uint16_t* hh, const int32_t* offsets,                 \
+                     const int32_t* sorted, const int32_t* active, int W, int CW, uint16_t* y,            \
+                     hipStream_t s) {                                                                     \
+    decode_detail::DecodeGrid dg;                                                                         \
+    const int grid = decode_list_grid(L, L->E, L->H, dg);                                                 \
+    bool launched = false;                                                                                \
+    MOEQ_DECODE_SHAPES(MOEQ_LAUNCH_DN_LIST)                                                               \
+    if (!launched) return set_error(MOEQ_ERR_UNSUPPORTED, "expert list: no down kernel for W=%d CW=%d", W, CW); \
+    return check_launch("moe_qgemm_prefill (down of the GEMV list)");                                     \
   }
 
 }  // namespace moeq

@@ -9,11 +9,17 @@
 //     assignment order.
 // A schedule kernel turns the per-expert counts into the list of
 // (expert, token tile) work items on the device, so the host never reads the
-// routing back; blocks past the end of the list exit at once.
+// routing back; blocks past the end of the list exit at once.  Experts with
+// at most kPrefillGemvMax assignments (under a skewed router most of the
+// experts a chunk touches get a token or two) are left out of that list and
+// go to the decode GEMV kernels instead, which stream their weights once at
+// ~1 VALU per weight and token rather than a dequantised matrix-core slice
+// loop per token tile.
 // Prior art: a long prompt touches nearly all experts (Qwen-tin, "Memory
 // layout and performance"), so every expert's weights are streamed once per
 // token tile.
 #include "gemm_bf16.h"
+#include "decode_impl.h"
 
 #include <type_traits>
 
@@ -27,27 +33,49 @@ constexpr int BM = kPrefillBM;   // 128 tokens per tile
 // Work items are listed by the number of 32-row M-tiles they fill, most
 // first (full tiles, then partial ones from the largest down), so that
 // blocks dealt out last are the short ones and fill the tail of the launch.
+// gemv[0] = number of experts with 1 .. kPrefillGemvMax assignments, gemv[1
+// ..] their ids, ascending (the decode kernels' list of active experts).
 // One block of 256 threads; thread i takes a contiguous range of experts;
-// the four per-bucket counts are scanned together.
-__global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict__ counts, int nexp,
-                                                       int32_t* __restrict__ sched) {
+// the four per-bucket counts and the list count are scanned together.
+__global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict__ counts, int nexp, int nrouted,
+                                                       int32_t* __restrict__ sched, int32_t* __restrict__ gemv) {
   constexpr int NBK = BM / 32;   // buckets: 1 .. NBK M-tiles
   static_assert(NBK == 4, "four buckets");
   __shared__ int4 part[256];
+  __shared__ int partg[256];
   const int tid = threadIdx.x;
   const int per = (nexp + 255) / 256;
   const int e0 = min(nexp, tid * per), e1 = min(nexp, e0 + per);
   auto mtiles = [](int c, int m) { return (min(BM, c - m * BM) + 31) / 32; };
+  // routed experts only: the GEMV list kernels take routed ids; the list is
+  // used only when it holds at least kPrefillGemvMin experts (a shorter one
+  // costs more as its own launches than it saves on the matrix cores)
+  auto small = [nrouted](int e, int c) { return e < nrouted && c > 0 && c <= kPrefillGemvMax; };
+  int mg = 0;
+  for (int e = e0; e < e1; ++e) mg += small(e, counts[e]) ? 1 : 0;
+  int vg = mg;
+  partg[tid] = vg;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {   // inclusive scan of the list counts
+    const int ug = tid >= o ? partg[tid - o] : 0;
+    __syncthreads();
+    vg += ug;
+    partg[tid] = vg;
+    __syncthreads();
+  }
+  const bool use = partg[255] >= kPrefillGemvMin;
+  auto on_gemv = [&](int e, int c) { return use && small(e, c); };
   int mine[NBK + 1] = {0, 0, 0, 0, 0};
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e];
+    if (on_gemv(e, c)) continue;
     mine[4] += c / BM;   // full tiles
     if (c % BM) mine[mtiles(c, c / BM)] += 1;
   }
   int4 v = make_int4(mine[1], mine[2], mine[3], mine[4]);
   part[tid] = v;
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {   // inclusive Hillis-Steele scan of the four counts
+  for (int o = 1; o < 256; o <<= 1) {   // inclusive Hillis-Steele scan of the four bucket counts
     const int4 u = tid >= o ? part[tid - o] : make_int4(0, 0, 0, 0);
     __syncthreads();
     v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
@@ -55,6 +83,7 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict
     __syncthreads();
   }
   const int4 tot = part[255];
+  int pg = vg - mg;   // this thread's first slot in the GEMV list
   // bucket order 4, 3, 2, 1: exclusive start of this thread in each
   int pos[NBK + 1];
   pos[4] = v.w - mine[4];
@@ -63,13 +92,20 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict
   pos[1] = tot.w + tot.z + tot.y + v.x - mine[1];
   for (int e = e0; e < e1; ++e) {
     const int c = counts[e], nt = (c + BM - 1) / BM;
+    if (on_gemv(e, c)) {
+      gemv[1 + pg++] = e;
+      continue;
+    }
     for (int m = 0; m < nt; ++m) {
       const int p = pos[mtiles(c, m)]++;
       sched[2 + 2 * p] = e;
       sched[3 + 2 * p] = m;
     }
   }
-  if (tid == 0) sched[0] = tot.x + tot.y + tot.z + tot.w;
+  if (tid == 0) {
+    sched[0] = tot.x + tot.y + tot.z + tot.w;
+    gemv[0] = use ? partg[255] : 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -851,13 +887,19 @@ extern "C" int moe_qgemm_prefill(const moe_layer_desc* L, const uint16_t* x, int
   const WsLayout wl = ws_layout(L->H, L->I, L->E, L->S, L->k, T);
   if (!ws || ws_bytes < wl.total)
     return set_error(MOEQ_ERR_WORKSPACE, "moe_qgemm_prefill: workspace of %zu bytes, need %zu", ws_bytes, wl.total);
+  int w_gu, cw_gu, w_dn, cw_dn;
+  if (!pick_shape(L->H, L->gate.bits, MOEQ_GATEUP_RUN, w_gu, cw_gu) ||
+      !pick_shape(L->I, L->down.bits, MOEQ_DOWN_RUN, w_dn, cw_dn))
+    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_qgemm_prefill: no GEMV kernel for H=%d/I=%d at these bit widths",
+                     L->H, L->I);
   char* w = static_cast<char*>(ws);
   int32_t* sched = reinterpret_cast<int32_t*>(w + wl.sched);
+  int32_t* gemv = reinterpret_cast<int32_t*>(w + wl.gemv);
   uint16_t* h = reinterpret_cast<uint16_t*>(w + wl.h);
   const int nexp = L->E + L->S, kS = L->k + L->S;
   const long A = (long)T * kS;
   const long max_tiles = prefill_max_tiles(A, nexp);
-  schedule_kernel<<<1, 256, 0, stream>>>(counts, nexp, sched);
+  schedule_kernel<<<1, 256, 0, stream>>>(counts, nexp, L->E, sched, gemv);
   if ((rc = check_launch("moe_qgemm_prefill (schedule)")) != MOEQ_OK) return rc;
   const unsigned nw = (unsigned)((max_tiles + 7) / 8 * 8);   // work items, padded for the XCD mapping
   const unsigned g1 = nw * (unsigned)(L->I / 128), g2 = nw * (unsigned)(L->H / 256);
@@ -872,5 +914,18 @@ extern "C" int moe_qgemm_prefill(const moe_layer_desc* L, const uint16_t* x, int
     case 6: mfma_down_kernel<6, BM><<<g2, 256, 0, stream>>>(L->down.q, L->down.sz, h, L->H, L->I, counts, offsets, sorted, sched, y); break;
     default: mfma_down_kernel<8, BM><<<g2, 256, 0, stream>>>(L->down.q, L->down.sz, h, L->H, L->I, counts, offsets, sorted, sched, y); break;
   }
-  return check_launch("moe_qgemm_prefill (down)");
+  if ((rc = check_launch("moe_qgemm_prefill (down)")) != MOEQ_OK) return rc;
+  // the experts of the GEMV list (shared experts take every token: never on it)
+  switch (L->gate.bits) {
+    case 4: rc = list_gateup_b4(L, x, offsets, sorted, gemv, w_gu, cw_gu, h, stream); break;
+    case 6: rc = list_gateup_b6(L, x, offsets, sorted, gemv, w_gu, cw_gu, h, stream); break;
+    default: rc = list_gateup_b8(L, x, offsets, sorted, gemv, w_gu, cw_gu, h, stream); break;
+  }
+  if (rc != MOEQ_OK) return rc;
+  switch (L->down.bits) {
+    case 4: rc = list_down_b4(L, h, offsets, sorted, gemv, w_dn, cw_dn, y, stream); break;
+    case 6: rc = list_down_b6(L, h, offsets, sorted, gemv, w_dn, cw_dn, y, stream); break;
+    default: rc = list_down_b8(L, h, offsets, sorted, gemv, w_dn, cw_dn, y, stream); break;
+  }
+  return rc;
 }

@@ -20,6 +20,11 @@ import synth
 from tests import tolerance as tol
 
 PROJ = {"gate": synth.T_GATE, "up": synth.T_UP, "down": synth.T_DOWN}
+# moe_qgemm_prefill runs routed experts with at most PREFILL_GEMV_MAX
+# assignments in the batch through the GEMV (decode) arithmetic instead of the
+# matrix cores, when the batch has at least PREFILL_GEMV_MIN such experts
+PREFILL_GEMV_MAX = 2
+PREFILL_GEMV_MIN = 64
 
 
 def _threads():
@@ -39,9 +44,11 @@ class LayerReference:
     """
 
     def __init__(self, w: synth.Workload, x_bits, logits, path: str, layer: int = 0, bits=None,
-                 residual_bits=None, norm_eps=None, threads=None):
+                 residual_bits=None, norm_eps=None, threads=None, batch_counts=None):
         """norm_eps: x_bits is a residual stream; the block is
-        x + moe(RMSNorm(x)) (residual_bits must then be None)."""
+        x + moe(RMSNorm(x)) (residual_bits must then be None).  batch_counts:
+        assignments per expert in the whole GPU batch (when x holds a subset
+        of its tokens), which decides the prefill path per expert."""
         self.w = w
         T = x_bits.shape[0]
         x_dev = None
@@ -65,6 +72,9 @@ class LayerReference:
         self.hv = np.zeros((A, I), np.float32)
         self.dhv = np.zeros((A, I), np.float32)
         work = [e for e in range(E + S) if counts[e]]
+        bc = counts if batch_counts is None else np.asarray(batch_counts)
+        small = (bc[:E] > 0) & (bc[:E] <= PREFILL_GEMV_MAX)
+        on_gemv = small if small.sum() >= PREFILL_GEMV_MIN else np.zeros(E, bool)
 
         def one(e):
             lo, hi = offsets[e], offsets[e + 1]
@@ -73,7 +83,10 @@ class LayerReference:
             mats = expert_mats(w, layer, e, bits)
             dense = [oracle.dequant(*mats[p]) for p in ("gate", "up", "down")]
             y = oracle.expert_ffn(xe, *dense)
-            if path == "prefill":
+            if path == "prefill" and e < E and on_gemv[e]:
+                hv, dhv, yv, dyv = tol.decode_ffn(xe, mats, bits)
+                dyv = dyv + 2.0 ** -8 * (np.abs(yv) + dyv)          # y stored in bf16
+            elif path == "prefill":
                 hv, dhv, yv, dyv = tol.prefill_ffn(xe, mats)
             else:
                 hv, dhv, yv, dyv = tol.decode_ffn(xe, mats, bits, None if x_dev is None else x_dev[a // kS])
