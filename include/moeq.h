@@ -396,10 +396,11 @@ int moe_decode_block(const moe_layer_desc* L, uint16_t* x, const uint16_t* w_rou
  * performance").  Codes and scale/zero words are staged in LDS and
  * dequantised in registers into the MFMA operand: each weight is
  * fp32((q - z) s), rounded once to bf16; products accumulate in fp32; h is
- * rounded to bf16 between the two GEMMs.  Routed experts with at most two
- * assignments in the batch (the tail a skewed router leaves) are computed
- * by the GEMV kernels of moe_qgemv_decode instead (fp32 weights (q - z) s,
- * h rounded to bf16), which stream their weights once.  y is device bf16
+ * rounded to bf16 between the two GEMMs.  When the batch has at least 64
+ * routed experts with one or two assignments (the tail a skewed router
+ * leaves), those experts are computed by the GEMV kernels of
+ * moe_qgemv_decode instead (fp32 weights (q - z) s, h rounded to bf16),
+ * which stream their weights once.  y is device bf16
  * [T*(k+S)][H], rows in assignment order.
  * Needs I % 128 == 0 and H % 256 == 0 (MOEQ_ERR_UNSUPPORTED otherwise);
  * counts/offsets/sorted as produced by moe_permute. */
