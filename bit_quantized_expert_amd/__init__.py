@@ -256,8 +256,8 @@ class StackDecoder:
 
     def read_status(self, stream=None) -> int:
         """Synchronise and return the workspace's error word (0 = none since
-        the last read; bit 1: a grid barrier gave up; bit 2: table mismatch);
-        a non-zero word is cleared with the control words."""
+        the last read; bit 1: a wait gave up; bit 2: table mismatch) and
+        clear it."""
         v = ctypes.c_int(0)
         _check(lib().moe_stack_read_status(_p(self.ws), self.ws.numel(), ctypes.byref(self.dims), ctypes.byref(v),
                                            _stream(stream)))

@@ -1,49 +1,47 @@
 // Stacked decode in one launch: a batch-1 token through L MoE blocks
 // (RMSNorm -> router -> top-k -> gate/up -> down -> weighted combine ->
-// residual), each block's phases separated by grid-wide barriers, the
-// blocks' weights streamed by every CU of the chip.  The pages' decode lever
-// is exactly this: small per-step kernel launches left most of the bandwidth
-// unused, a persistent per-layer MoE megakernel recovered it (Raon-1-mini,
-// optimisation table and result paragraph).
+// residual), the blocks' weights streamed by every CU of the chip.  The
+// pages' decode lever is exactly this: small per-step kernel launches left
+// most of the bandwidth unused, a persistent per-layer MoE megakernel
+// recovered it (Raon-1-mini, optimisation table and result paragraph).
 //
-// A layer, for the residual stream x (bf16 [H], in global memory):
-//   A  every block: n = RMSNorm(x) into LDS (and its 64-group sums);
-//      router rows spread over all wavefronts: logits[e] = n . Wr[e]
-//   -- grid barrier --
-//   B  every block: top-k of the logits (first wavefront), into LDS;
-//      gate/up units (slot j, 64-row tile of I, K slice p of H) spread over
-//      all wavefronts: partial gate and up sums per row; the unit that
-//      completes a (slot, tile) adds its P partials in slice order and
-//      writes h = bf16(silu(g) u)
-//   -- grid barrier --
-//   C  every block: h of all slots into LDS (and its group sums);
-//      down units (64-row tile of H, slot j, K slice p of I): partial rows;
-//      the unit that completes a tile adds the partials (slices, then slots
-//      in ascending order, weighted) and writes x = bf16(x + bf16(sum))
-//   -- grid barrier --
+// A layer, for the residual stream x (bf16 [H]):
+//   A  every block: n = RMSNorm(x) into LDS (and its 64-group sums); router
+//      rows spread over the first wavefronts: logits[e] = n . Wr[e]
+//   B  every block: top-k of the logits into LDS; gate/up units (slot j,
+//      64-row tile of I, K slice p of H) over all wavefronts: partial gate
+//      and up sums per row.  Wavefront r then adds the P partials of
+//      (slot, tile) r in slice order and writes h = bf16(silu(g) u)
+//   C  down units (64-row tile of H, slot j, K slice p of I) over all
+//      wavefronts, each on its own slice of h: partial rows.  Wavefront t
+//      then adds the partials of x tile t (slices, then slots in ascending
+//      order, weighted) and writes x = bf16(x + bf16(sum))
 // The dot products are the decode GEMV's (format.h): codes become bf16
 // (128 + q, or q at 8 bits) pairs, v_dot2_f32_bf16 with the activations'
 // pairs (read from LDS, the same address on every lane), and the group's
 // scale and zero enter once per group in fp32.
 //
-// Everything one block writes and another reads (logits, partial sums, h,
-// x, the barrier words) goes through device-scope atomic loads and stores,
-// which the hardware keeps coherent across the XCDs' separate L2 caches.
-// A wavefront orders its stores before its signal by waiting for its
-// vector-memory counter to reach zero (s_waitcnt vmcnt(0): on gfx9 the
-// counter covers stores too, and a device-scope store counts as done once it
-// is visible device-wide) immediately before every arrival; the loads that
-// follow an arrival depend on the arrival's returned value, so they are
-// issued after it.  So no device-scope fence (an L2 write-back or
-// invalidate) is needed anywhere: the weights stay cached, and a barrier
-// costs one round of atomics.
+// No barrier and no counter: every value one wavefront hands to another
+// (logits, partial sums, h, x between layers) is stored as a 64-bit word,
+// the 32-bit value beside a 32-bit tag (call number * 1024 + layer), with a
+// device-scope atomic store, which lands whole and is coherent across the
+// XCDs' separate L2 caches.  A consumer loads the words it needs with
+// device-scope atomic loads and loads again those whose tag is older than
+// the one it waits for.  A producer thus never waits for its stores to
+// complete, and a hand-over costs one store and one load.  A word with a
+// newer tag than awaited is taken as well: only a wavefront whose result no
+// one uses can fall that far behind (a value of layer l + 1 exists only
+// after every unit of layer l has finished).  A small kernel launched before
+// each call advances the call number.  The router rows are loaded before x
+// arrives.
 //
-// The table starts with a 64-byte header (layer count and H, I, E, k, S = 0)
-// that every block checks against the launch's dimensions before it touches
-// a layer; on a mismatch every block leaves at once (none has reached a
-// barrier) and the workspace's error word gets bit 2.  A barrier wait that
-// gives up (after about 2^26 sleeps) sets bit 1.  The error word is sticky
-// until moe_stack_read_status reads it.
+// The table starts with a 64-byte header (layer count and H, I, E, k) that
+// every block checks against the launch's dimensions before it touches a
+// layer; on a mismatch every block leaves at once and the workspace's error
+// word gets bit 2.  A wait that gives up (after 2^18 polls, a fraction of a
+// second) sets bit 1 and goes on with what it read, so that every wavefront reaches
+// the end of the kernel.  The error word is sticky until
+// moe_stack_read_status reads it.
 #include "decode_impl.h"
 
 using namespace moeq;
@@ -52,8 +50,12 @@ using decode_detail::load_chunk_g;
 namespace {
 
 constexpr int kMaxH = 8192;      // LDS: n, bf16
-constexpr int kMaxKI = 16384;    // LDS: h of all slots, bf16
+constexpr int kMaxI = 4096;      // LDS: a down unit's slice of h, bf16, per wavefront
 constexpr int kMaxK = 16;
+constexpr int kMaxLayers = 1024; // tags: call * 1024 + layer
+constexpr int kDW = 16;          // dwords of one group's codes in one lane (8-bit: 4 chunks of 4)
+constexpr int kRedRows = 4 * kMaxI / 128;   // rows of 64 floats a block reduces in its h-slice LDS
+constexpr unsigned kSpinLimit = 1u << 18;
 
 struct StackHeader {  // 64 bytes before the layers
   uint32_t magic, nlayers;
@@ -82,152 +84,191 @@ struct StackDims {
   float eps;
 };
 
+// Tagged words: value in the low half, tag in the high half.
 struct StackWs {
-  float* logits;     // [E]
-  float* gu_part;    // [k][I/64][P][2][64]
-  uint32_t* h;       // [k][I/2]: bf16 pairs
-  float* y_part;     // [H/64][k][PD][64]
-  int* gu_cnt;       // [k][I/64], 16 ints apart, zero between uses
-  int* y_cnt;        // [H/64], 16 ints apart, zero between uses
-  unsigned* bar;     // [0] arrivals (zero between barriers), [1] generation
-  int* err;          // bit 1: a barrier wait gave up; bit 2: table mismatch
+  uint64_t* logits;    // [E] fp32
+  uint64_t* gu_part;   // [k * I/64][P][2][64] fp32 partial gate, up sums
+  uint64_t* h;         // [k][I/2] bf16 pairs
+  uint64_t* y_part;    // [H/64][k][PD][64] fp32 partial down sums
+  uint64_t* x;         // [H/2] bf16 pairs: x between layers
+  uint32_t* epoch;     // call number
+  int* err;            // bit 1: a wait gave up; bit 2: table mismatch
+  uint64_t* tl;        // event times per (layer, wavefront), or null
 };
 
-// device-coherent accesses (see the header comment)
-MOEQ_DEV float ld_f(const float* p) { return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-MOEQ_DEV void st_f(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 MOEQ_DEV uint32_t ld_u(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 MOEQ_DEV void st_u(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-// Wait until every vector-memory operation this wavefront issued has
-// completed (s_waitcnt vmcnt(0), expcnt and lgkmcnt left free): its
-// device-scope stores are then visible to every XCD and its loads have
-// returned.  Issued right before each arrival at a counter.
-MOEQ_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// keeps the compiler from moving memory operations across this point
-MOEQ_DEV void wave_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup"); }
-
-// Grid-wide barrier of the co-resident blocks (cooperative launch), in two
-// levels so that no word is hit by more than a group's blocks: block b
-// arrives at the count of group b % 8 (the blocks one XCD receives); the
-// last of a group clears that count and arrives at the top count; the last
-// of those clears it and advances the generation word of every group, on
-// which each group's blocks wait.  Every wavefront waits for its own stores
-// to complete before the block meets at __syncthreads, and the first thread
-// waits for its generation load and for each clearing store before its next
-// arrival.  A wait gives up after about 2^26 sleeps (seconds) and sets bit 1
-// of err, so that every wavefront always reaches the end of the kernel.
-//   bar[16 g]: count of group g; bar[128]: top count; bar[144 + 16 g]:
-//   generation of group g (words 64 bytes apart)
-MOEQ_DEV void grid_barrier(unsigned* bar, unsigned nblocks, int* err) {
-  wait_vmem();   // this wavefront's stores are visible device-wide
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned grp = blockIdx.x % 8u;
-    const unsigned ngroups = nblocks < 8u ? nblocks : 8u;
-    const unsigned members = nblocks / 8u + (grp < nblocks % 8u ? 1u : 0u);
-    unsigned* gen = bar + 144 + 16 * grp;
-    const unsigned g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_vmem();   // the generation is read before arriving
-    wave_acquire();
-    if (__hip_atomic_fetch_add(bar + 16 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == members) {
-      __hip_atomic_store(bar + 16 * grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wait_vmem();   // cleared before the group arrives above
-      wave_acquire();
-      if (__hip_atomic_fetch_add(bar + 128, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == ngroups) {
-        __hip_atomic_store(bar + 128, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        wait_vmem();   // cleared before any generation moves
-        wave_acquire();
-        for (unsigned y = 0; y < ngroups; ++y)
-          __hip_atomic_fetch_add(bar + 144 + 16 * y, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    unsigned spins = 0;
-    while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > (1u << 26)) {
-        __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-    wave_acquire();
-  }
-  __syncthreads();
+MOEQ_DEV uint64_t ld_t(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A workspace base pointer as a value the compiler takes as new in every
+// layer, held in scalar registers: addresses built from it stay scalar base
+// plus lane offset and are not computed ahead for all layers (which would
+// hold a vector address per load for the whole kernel).
+template <class T>
+MOEQ_DEV T* fresh_base(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  // each half through uint32_t: readfirstlane returns int, which would
+  // sign-extend a low half with bit 31 set into the high half
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  uint64_t a = ((uint64_t)hi << 32) | lo;
+  asm volatile("" : "+s"(a));
+  return reinterpret_cast<T*>(a);
+}
+MOEQ_DEV void st_t(uint64_t* p, uint32_t v, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+MOEQ_DEV bool fresh(uint64_t w, uint32_t tag) { return (int32_t)((uint32_t)(w >> 32) - tag) >= 0; }
+MOEQ_DEV float val_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
-// Loads v(i) for i < n (n <= 64) all at once into b, so that they are in
-// flight together.
-template <class Fn>
-MOEQ_DEV void load_all(int n, float (&b)[64], Fn&& v) {
+// Loads word addr(i) for i < n (n <= M, may differ per lane) into b, all in
+// flight together, then loads again every word with a tag older than `tag`
+// until none is left (the whole wavefront decides together).
+template <int M, class Addr>
+MOEQ_DEV void poll(int n, uint64_t (&b)[M], Addr&& addr, uint32_t tag, int* err) {
+  // (every element is assigned: a conditionally assigned one would let the
+  // compiler carry an older value across loops)
 #pragma unroll
-  for (int i = 0; i < 64; ++i) b[i] = i < n ? v(i) : 0.0f;
+  for (int i = 0; i < M; ++i) b[i] = i < n ? ld_t(addr(i)) : 0;
+  for (unsigned spins = 0;; ++spins) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+      if (i < n && !fresh(b[i], tag)) ok = false;
+    if (__all(ok)) return;
+    // give up after kSpinLimit polls, or after 1024 once another wait has
+    // given up (so that a failed call ends in well under a second)
+    if (spins == kSpinLimit || ((spins & 1023) == 1023 && (ld_u(reinterpret_cast<const uint32_t*>(err)) & 1))) {
+      if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+      if (i < n && !fresh(b[i], tag)) b[i] = ld_t(addr(i));
+  }
 }
+
+// Orders this wavefront's LDS writes before its following LDS reads (other
+// lanes read what a lane wrote).
+MOEQ_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+MOEQ_DEV void event(const StackWs& ws, int l, int gw, int nw, int i) {
+  if (ws.tl && (threadIdx.x & 63) == 0) ws.tl[((size_t)l * nw + gw) * 8 + i] = wall_clock64();
+}
+
+// The codes and scale/zero words of up to two groups of NM matrices for one
+// lane (row), loaded together.
+template <int NM>
+struct Batch {
+  uint32_t d[NM][2][kDW];
+  uint32_t w[NM][2];
+};
 
 template <int BITS, int NM>
-MOEQ_DEV void unit_dot(const uint8_t* const (&q)[NM], const uint32_t* const (&sz)[NM], size_t row, int K, int g0,
-                       int G, const uint16_t* xl, const float* xsl, float (&out)[NM]) {
+MOEQ_DEV void batch_load(Batch<NM>& B, const uint8_t* const (&q)[NM], const uint32_t* const (&sz)[NM], size_t row,
+                         int K, int g, int ng) {
   using F = Fmt<BITS>;
   constexpr int CPG = F::CHUNKS_PER_GROUP;
   const size_t cpr = (size_t)(K / F::CODES), gpr = (size_t)(K / 64);
 #pragma unroll
-  for (int m = 0; m < NM; ++m) out[m] = 0.0f;
-  for (int g = g0; g < g0 + G; g += 2) {
-    const int ng = min(2, g0 + G - g);
-    uint32_t d[NM][2 * CPG][F::DW];
-    uint32_t w[NM][2];
+  for (int gg = 0; gg < 2; ++gg) {
 #pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
+    for (int m = 0; m < NM; ++m) {
+#pragma unroll
+      for (int i = CPG * F::DW; i < kDW; ++i) B.d[m][gg][i] = 0;   // every element assigned
       if (gg < ng) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
+        for (int c = 0; c < CPG; ++c) {
+          uint32_t t[F::DW];
+          load_chunk_g<BITS>((gbytes)(q[m] + chunk_offset<BITS>(row, (size_t)(g + gg) * CPG + c, cpr)), t);
 #pragma unroll
-          for (int c = 0; c < CPG; ++c)
-            load_chunk_g<BITS>((gbytes)(q[m] + chunk_offset<BITS>(row, (size_t)(g + gg) * CPG + c, cpr)),
-                               d[m][gg * CPG + c]);
-          w[m][gg] = sz[m][sz_index(row, (size_t)(g + gg), gpr)];
+          for (int i = 0; i < F::DW; ++i) B.d[m][gg][c * F::DW + i] = t[i];
         }
-      }
-    }
+        B.w[m][gg] = sz[m][sz_index(row, (size_t)(g + gg), gpr)];
+      } else {
 #pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      if (gg < ng) {
-        const float x_sum = xsl[g + gg];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-          for (int c = 0; c < CPG; ++c) {
-            uint32_t P[F::PAIRS];
-            chunk_pairs<BITS>(d[m][gg * CPG + c], P);
-            const uint4* xp = reinterpret_cast<const uint4*>(xl + (size_t)(g + gg) * 64 + c * F::CODES);
-#pragma unroll
-            for (int p = 0; p < F::PAIRS; p += 4) {
-              const uint4 X = xp[p / 4];
-              a0 = dot2_bf16(P[p], X.x, a0);
-              a1 = dot2_bf16(P[p + 1], X.y, a1);
-              a0 = dot2_bf16(P[p + 2], X.z, a0);
-              a1 = dot2_bf16(P[p + 3], X.w, a1);
-            }
-          }
-          const float s = f16_bits_to_f32(w[m][gg] & 0xFFFFu);
-          const float zc = f16_bits_to_f32(w[m][gg] >> 16) + F::OFFSET;
-          out[m] = fmaf(s, (a0 + a1) - zc * x_sum, out[m]);
-        }
+        for (int i = 0; i < CPG * F::DW; ++i) B.d[m][gg][i] = 0;
+        B.w[m][gg] = 0;
       }
     }
   }
 }
 
-template <int NM>
-MOEQ_DEV void unit_dot_bits(int bits, const uint8_t* const (&q)[NM], const uint32_t* const (&sz)[NM], size_t row,
-                            int K, int g0, int G, const uint16_t* xl, const float* xsl, float (&out)[NM]) {
-  switch (bits) {
-    case 4: unit_dot<4, NM>(q, sz, row, K, g0, G, xl, xsl, out); break;
-    case 6: unit_dot<6, NM>(q, sz, row, K, g0, G, xl, xsl, out); break;
-    default: unit_dot<8, NM>(q, sz, row, K, g0, G, xl, xsl, out); break;
+// out[m] += the batch's groups' contributions, group after group; xl, xsl:
+// the activations (LDS, bf16) and group sums of the batch's first group.
+template <int BITS, int NM>
+MOEQ_DEV void batch_dot(const Batch<NM>& B, int ng, const uint16_t* xl, const float* xsl, float (&out)[NM]) {
+  using F = Fmt<BITS>;
+  constexpr int CPG = F::CHUNKS_PER_GROUP;
+#pragma unroll
+  for (int gg = 0; gg < 2; ++gg) {
+    if (gg < ng) {
+      const float x_sum = xsl[gg];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPG; ++c) {
+          uint32_t t[F::DW], P[F::PAIRS];
+#pragma unroll
+          for (int i = 0; i < F::DW; ++i) t[i] = B.d[m][gg][c * F::DW + i];
+          chunk_pairs<BITS>(t, P);
+          const uint4* xp = reinterpret_cast<const uint4*>(xl + gg * 64 + c * F::CODES);
+#pragma unroll
+          for (int p = 0; p < F::PAIRS; p += 4) {
+            const uint4 X = xp[p / 4];
+            a0 = dot2_bf16(P[p], X.x, a0);
+            a1 = dot2_bf16(P[p + 1], X.y, a1);
+            a0 = dot2_bf16(P[p + 2], X.z, a0);
+            a1 = dot2_bf16(P[p + 3], X.w, a1);
+          }
+        }
+        const float s = f16_bits_to_f32(B.w[m][gg] & 0xFFFFu);
+        const float zc = f16_bits_to_f32(B.w[m][gg] >> 16) + F::OFFSET;
+        out[m] = fmaf(s, (a0 + a1) - zc * x_sum, out[m]);
+      }
+    }
   }
 }
+
+// One unit: rows `row` of NM matrices over groups g0 .. g0 + G - 1 of K;
+// xl, xsl hold the activations from group g0 on.  `first` holds the first
+// batch already when loaded is true.
+template <int BITS, int NM>
+MOEQ_DEV void unit_run(Batch<NM>& first, bool loaded, const uint8_t* const (&q)[NM],
+                       const uint32_t* const (&sz)[NM], size_t row, int K, int g0, int G, const uint16_t* xl,
+                       const float* xsl, float (&out)[NM]) {
+#pragma unroll
+  for (int m = 0; m < NM; ++m) out[m] = 0.0f;
+  if (!loaded) batch_load<BITS, NM>(first, q, sz, row, K, g0, min(2, G));
+  batch_dot<BITS, NM>(first, min(2, G), xl, xsl, out);
+  for (int g = 2; g < G; g += 2) {
+    Batch<NM> B;
+    const int ng = min(2, G - g);
+    batch_load<BITS, NM>(B, q, sz, row, K, g0 + g, ng);
+    batch_dot<BITS, NM>(B, ng, xl + g * 64, xsl + g, out);
+  }
+}
+
+template <int NM>
+MOEQ_DEV void unit_bits(int bits, Batch<NM>& first, bool loaded, const uint8_t* const (&q)[NM],
+                        const uint32_t* const (&sz)[NM], size_t row, int K, int g0, int G, const uint16_t* xl,
+                        const float* xsl, float (&out)[NM]) {
+  switch (bits) {
+    case 4: unit_run<4, NM>(first, loaded, q, sz, row, K, g0, G, xl, xsl, out); break;
+    case 6: unit_run<6, NM>(first, loaded, q, sz, row, K, g0, G, xl, xsl, out); break;
+    default: unit_run<8, NM>(first, loaded, q, sz, row, K, g0, G, xl, xsl, out); break;
+  }
+}
+
 
 // Top-k of E logits (first wavefront of the block) into LDS.
 template <int NS>
@@ -250,75 +291,93 @@ MOEQ_DEV void select_any(const float* logits, int E, int k, int* sel_idx, float*
   else select_into<16>(logits, E, k, sel_idx, sel_w);
 }
 
-// Whether this wavefront is the last of total to arrive at a counter (its
-// stores complete before it arrives); the last one then sees everyone's.
-MOEQ_DEV bool last_arrival(int* cnt, int total) {
-  wait_vmem();
-  wave_acquire();
-  int old = 0;
-  if ((threadIdx.x & 63) == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0);
-  if (old != total - 1) return false;
-  wave_acquire();
-  return true;
-}
-
 // bf16 of this lane and of the next one as one word (for even lanes)
 MOEQ_DEV uint32_t pair_with_next(uint32_t b) { return b | (__shfl_down(b, 1) << 16); }
 
-__global__ __launch_bounds__(256) void stack_decode_kernel(const StackHeader* hdr, StackDims d, StackWs ws,
-                                                           uint32_t* x2) {
+__global__ __launch_bounds__(256) void stack_epoch_kernel(uint32_t* epoch) {
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader* hdr, StackDims d, StackWs ws0,
+                                                              uint32_t* x2_0) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxH];
   __shared__ float xsum[kMaxH / 64];
-  __shared__ __attribute__((aligned(16))) uint16_t hs[kMaxKI];
-  __shared__ float hsum[kMaxKI / 64];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[4][kMaxI];
+  __shared__ float hsum[4][kMaxI / 64];
   __shared__ float lg[1024];
   __shared__ int sel_idx[kMaxK];
   __shared__ float sel_w[kMaxK];
   __shared__ float red[4];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int gw = (int)blockIdx.x * 4 + wave, nw = (int)gridDim.x * 4;
-  const int H = d.H, I = d.I, k = d.k;
-  const int tI = I / 64, tH = H / 64;
-  const unsigned nb = gridDim.x;
   {
     // every block reads the same header, so all leave or none does
     const StackHeader h0 = *hdr;
-    if (h0.magic != kStackMagic || (int)h0.nlayers < d.L || h0.H != H || h0.I != I || h0.E != d.E || h0.k != k) {
-      if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_fetch_or(ws.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (h0.magic != kStackMagic || (int)h0.nlayers < d.L || h0.H != d.H || h0.I != d.I || h0.E != d.E || h0.k != d.k) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_fetch_or(ws0.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
   }
   const StackLayer* table = reinterpret_cast<const StackLayer*>(hdr + 1);
+  const uint32_t base = ld_u(ws0.epoch) << 10;
   for (int l = 0; l < d.L; ++l) {
+    // the dimensions as values the compiler takes as new in every layer, so
+    // that what derives from them is computed where it is used rather than
+    // ahead of the loop for all layers (where it would occupy registers)
+    int H = d.H, I = d.I, k = d.k, E = d.E, P = d.P, PD = d.PD, wave = (int)threadIdx.x >> 6;
+    asm volatile("" : "+s"(H), "+s"(I), "+s"(k), "+s"(E), "+s"(P), "+s"(PD));
+    wave = uniform(wave);
+    const int lane = threadIdx.x & 63;
+    const int gw = (int)blockIdx.x * 4 + wave, nw = (int)gridDim.x * 4;
+    const int tI = I / 64, tH = H / 64, G = tH / P, GD = tI / PD;
+    const int n_gu = k * tI * P, n_dn = tH * k * PD;
     const StackLayer Ly = table[l];
-    // ---- A: RMSNorm (every block), router rows (all wavefronts).  The
-    // first router row's weights (they do not depend on x) are loaded first.
+    const uint32_t tag = base + (uint32_t)l;
+    StackWs ws = ws0;
+    ws.logits = fresh_base(ws0.logits);
+    ws.gu_part = fresh_base(ws0.gu_part);
+    ws.h = fresh_base(ws0.h);
+    ws.y_part = fresh_base(ws0.y_part);
+    ws.x = fresh_base(ws0.x);
+    uint32_t* x2 = fresh_base(x2_0);
+    // ---- A: RMSNorm (every block), router rows.  The first router row's
+    // weights (they do not depend on x) are loaded before x.
     constexpr int kRouterChunks = 4;   // H <= 2048 fully; the rest of longer rows after x
     uint4 wfirst[kRouterChunks];
-    if (gw < d.E) {
+#pragma unroll
+    for (int c = 0; c < kRouterChunks; ++c) wfirst[c] = make_uint4(0, 0, 0, 0);
+    if (gw < E) {
       const uint16_t* wrow = Ly.wr + (size_t)gw * H;
 #pragma unroll
       for (int c = 0; c < kRouterChunks; ++c)
         if (c * 512 < H) wfirst[c] = *reinterpret_cast<const uint4*>(wrow + c * 512 + lane * 8);
     }
-    float ss = 0.0f;
-    for (int i0 = threadIdx.x; i0 < H / 2; i0 += 256 * 4) {
-      uint32_t v[4];
+    {
+      // x as H/2 bf16 pairs, H/512 of them per thread, 4 at a time
+      const int nx = H / 512;
+      float ss = 0.0f;
+      for (int u0 = 0; u0 < nx; u0 += 4) {
+        uint64_t xb[4];
+        const int nu = min(4, nx - u0);
+        if (l == 0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = i0 + 256 * u < H / 2 ? ld_u(x2 + i0 + 256 * u) : 0u;
+          for (int u = 0; u < 4; ++u) xb[u] = u < nu ? ld_u(x2 + threadIdx.x + 256 * (u0 + u)) : 0;
+        } else {
+          poll(nu, xb, [&](int u) { return ws.x + threadIdx.x + 256 * (u0 + u); }, tag - 1, ws.err);
+        }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (i0 + 256 * u < H / 2) {
-          const float a = bf16_bits_to_f32(v[u] & 0xFFFFu), b = bf16_bits_to_f32(v[u] >> 16);
-          reinterpret_cast<uint32_t*>(xs)[i0 + 256 * u] = v[u];
-          ss = fmaf(a, a, ss);
-          ss = fmaf(b, b, ss);
+        for (int u = 0; u < 4; ++u) {
+          if (u < nu) {
+            const uint32_t v = (uint32_t)xb[u];
+            const float a = bf16_bits_to_f32(v & 0xFFFFu), b = bf16_bits_to_f32(v >> 16);
+            reinterpret_cast<uint32_t*>(xs)[threadIdx.x + 256 * (u0 + u)] = v;
+            ss = fmaf(a, a, ss);
+            ss = fmaf(b, b, ss);
+          }
         }
       }
+      ss = wave_sum(ss);
+      if (lane == 0) red[wave] = ss;
     }
-    ss = wave_sum(ss);
-    if (lane == 0) red[wave] = ss;
+    event(ws, l, gw, nw, 0);
     __syncthreads();
     const float tot = (red[0] + red[1]) + (red[2] + red[3]);
     const float r = 1.0f / sqrtf(tot / (float)H + d.eps);
@@ -328,7 +387,7 @@ __global__ __launch_bounds__(256) void stack_decode_kernel(const StackHeader* hd
       const float s = wave_sum(bf16_bits_to_f32(xs[g * 64 + lane]));
       if (lane == 0) xsum[g] = s;
     }
-    for (int e = gw; e < d.E; e += nw) {
+    for (int e = gw; e < E; e += nw) {
       const uint16_t* wrow = Ly.wr + (size_t)e * H;
       float acc = 0.0f;
 #pragma unroll
@@ -351,101 +410,134 @@ __global__ __launch_bounds__(256) void stack_decode_kernel(const StackHeader* hd
         acc = dot2_bf16(wv.w, nv.w, acc);
       }
       acc = wave_sum(acc);
-      if (lane == 0) st_f(ws.logits + e, acc);
+      if (lane == 0) st_t(ws.logits + e, __float_as_uint(acc), tag);
     }
-    grid_barrier(ws.bar, nb, ws.err);
     // ---- B: top-k (every block), gate/up units (all wavefronts)
-    for (int e = threadIdx.x; e < d.E; e += 256) lg[e] = ld_f(ws.logits + e);
-    __syncthreads();
-    if (wave == 0) select_any(lg, d.E, k, sel_idx, sel_w);
-    __syncthreads();
     {
-      const int P = d.P, G = tH / P;
-      const int nunits = k * tI * P;
-      for (int u = gw; u < nunits; u += nw) {
-        const int j = u / (tI * P), t = (u / P) % tI, p = u % P;
-        const size_t row = (size_t)min(max(sel_idx[j], 0), d.E - 1) * I + (size_t)t * 64 + lane;
-        const uint8_t* const q[2] = {Ly.gq, Ly.uq};
-        const uint32_t* const sz[2] = {Ly.gsz, Ly.usz};
-        float o[2];
-        unit_dot_bits<2>(Ly.gbits, q, sz, row, H, p * G, G, xs, xsum, o);
-        float* part = ws.gu_part + (size_t)(j * tI + t) * P * 128;
-        st_f(part + p * 128 + lane, o[0]);
-        st_f(part + p * 128 + 64 + lane, o[1]);
-        if (last_arrival(ws.gu_cnt + 16 * (j * tI + t), P)) {
-          float gs = 0.0f, us = 0.0f;
-          for (int p0 = 0; p0 < P; p0 += 32) {   // slices in order, 32 at a time (64 loads in flight)
-            float b[64];
-            const int np = min(32, P - p0);
-            load_all(2 * np, b, [&](int i) { return ld_f(part + (p0 + (i >> 1)) * 128 + (i & 1) * 64 + lane); });
+      uint64_t lb[4];   // E <= 1024: at most 4 logits per thread
+      const int nl = (E - (int)threadIdx.x + 255) / 256;
+      poll(nl, lb, [&](int i) { return ws.logits + threadIdx.x + 256 * i; }, tag, ws.err);
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
-              if (i < np) { gs += b[2 * i]; us += b[2 * i + 1]; }
-          }
-          const uint32_t hw = pair_with_next(f32_to_bf16_bits(silu_f32(gs) * us));
-          if (!(lane & 1)) st_u(ws.h + ((size_t)j * I + t * 64 + lane) / 2, hw);
-          if (lane == 0) __hip_atomic_store(ws.gu_cnt + 16 * (j * tI + t), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < 4; ++i)
+        if (i < nl) lg[threadIdx.x + 256 * i] = val_f(lb[i]);
+    }
+    __syncthreads();
+    event(ws, l, gw, nw, 1);
+    if (wave == 0) select_any(lg, E, k, sel_idx, sel_w);
+    __syncthreads();
+    for (int u = gw; u < n_gu; u += nw) {
+      const int j = u / (tI * P), t = (u / P) % tI, p = u % P;
+      const size_t row = (size_t)min(max(sel_idx[j], 0), E - 1) * I + (size_t)t * 64 + lane;
+      const uint8_t* const q[2] = {Ly.gq, Ly.uq};
+      const uint32_t* const sz[2] = {Ly.gsz, Ly.usz};
+      float o[2];
+      Batch<2> B;
+      unit_bits<2>(Ly.gbits, B, false, q, sz, row, H, p * G, G, xs + p * G * 64, xsum + p * G, o);
+      uint64_t* part = ws.gu_part + ((size_t)(j * tI + t) * P + p) * 128;
+      st_t(part + lane, __float_as_uint(o[0]), tag);
+      st_t(part + 64 + lane, __float_as_uint(o[1]), tag);
+    }
+    const uint8_t* const dq[1] = {Ly.dq};
+    const uint32_t* const dsz[1] = {Ly.dsz};
+    event(ws, l, gw, nw, 2);
+    // (slot, tile) rt is reduced by block rt: its four wavefronts load the
+    // P partials into LDS, the first adds them in slice order
+    float* rl = reinterpret_cast<float*>(&hs[0][0]);
+    for (int rt = blockIdx.x; rt < k * tI; rt += gridDim.x) {
+      __syncthreads();   // rl is free
+      const uint64_t* part = ws.gu_part + (size_t)rt * P * 128;
+      for (int p0 = wave * 8; p0 < P; p0 += 32) {   // slices p0 .. p0 + 7 of this wavefront
+        uint64_t b[16];
+        const int np = min(8, P - p0);
+        poll(2 * np, b, [&](int i) { return part + (size_t)(p0 + (i >> 1)) * 128 + (i & 1) * 64 + lane; }, tag, ws.err);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (i < 2 * np) rl[(2 * p0 + i) * 64 + lane] = val_f(b[i]);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        float gs = 0.0f, us = 0.0f;
+        for (int p = 0; p < P; ++p) {
+          gs += rl[(2 * p) * 64 + lane];
+          us += rl[(2 * p + 1) * 64 + lane];
+        }
+        const uint32_t hw = pair_with_next(f32_to_bf16_bits(silu_f32(gs) * us));
+        if (!(lane & 1)) st_t(ws.h + ((size_t)rt * 64 + lane) / 2, hw, tag);
+      }
+    }
+    __syncthreads();   // rl has been read before the h slices overwrite it
+    event(ws, l, gw, nw, 3);
+    // ---- C: down units (all wavefronts), each on its own slice of h
+    uint16_t* hw_l = hs[wave];
+    float* hsum_w = hsum[wave];
+    for (int u = gw; u < n_dn; u += nw) {
+      const int t = u / (k * PD), j = (u / PD) % k, p = u % PD;
+      // h of slot j, groups p GD .. p GD + GD - 1: GD 32 words, 64 at a time
+      const uint64_t* hp = ws.h + ((size_t)j * I + (size_t)p * GD * 64) / 2;
+      for (int w0 = 0; w0 < GD * 32; w0 += 64) {
+        uint64_t b[1];
+        poll(w0 + lane < GD * 32 ? 1 : 0, b, [&](int) { return hp + w0 + lane; }, tag, ws.err);
+        if (w0 + lane < GD * 32) reinterpret_cast<uint32_t*>(hw_l)[w0 + lane] = (uint32_t)b[0];
+      }
+      wave_lds_sync();
+      for (int g = 0; g < GD; ++g) {
+        const float s = wave_sum(bf16_bits_to_f32(hw_l[g * 64 + lane]));
+        if (lane == 0) hsum_w[g] = s;
+      }
+      wave_lds_sync();
+      if (u == gw) event(ws, l, gw, nw, 4);
+      const size_t row = (size_t)min(max(sel_idx[j], 0), E - 1) * H + (size_t)t * 64 + lane;
+      float o[1];
+      Batch<1> B;
+      unit_bits<1>(Ly.dbits, B, false, dq, dsz, row, I, p * GD, GD, hw_l, hsum_w, o);
+      st_t(ws.y_part + ((size_t)(t * k + j) * PD + p) * 64 + lane, __float_as_uint(o[0]), tag);
+      wave_lds_sync();   // the slice has been read before the next unit's h lands
+    }
+    event(ws, l, gw, nw, 5);
+    const bool last = l + 1 == d.L;
+    // x tile t is reduced by block t: its four wavefronts load the k PD
+    // partials (slot-major) into LDS, the first adds them: slots in
+    // ascending order, each the sum of its slices in order
+    for (int t = blockIdx.x; t < tH; t += gridDim.x) {
+      __syncthreads();   // rl is free (the down units have read their h)
+      const uint64_t* part = ws.y_part + (size_t)t * k * PD * 64;
+      const int n = k * PD;
+      for (int i0 = wave * 16; i0 < n; i0 += 64) {
+        uint64_t b[16];
+        const int ni = min(16, n - i0);
+        poll(ni, b, [&](int i) { return part + (size_t)(i0 + i) * 64 + lane; }, tag, ws.err);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (i < ni) rl[(i0 + i) * 64 + lane] = val_f(b[i]);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const int xi = (t * 64 + (lane & ~1)) / 2;
+        uint32_t xw;
+        if (l == 0) {
+          xw = ld_u(x2 + xi);
+        } else {
+          uint64_t b[1];
+          poll(1, b, [&](int) { return ws.x + xi; }, tag - 1, ws.err);
+          xw = (uint32_t)b[0];
+        }
+        float acc = 0.0f;
+        for (int j = 0; j < k; ++j) {
+          float yj = 0.0f;
+          for (int p = 0; p < PD; ++p) yj += rl[(j * PD + p) * 64 + lane];
+          acc = fmaf(sel_w[j], yj, acc);
+        }
+        const float xo = bf16_bits_to_f32((lane & 1) ? (xw >> 16) : (xw & 0xFFFFu));
+        const float yb = bf16_bits_to_f32(f32_to_bf16_bits(acc));
+        const uint32_t nx2 = pair_with_next(f32_to_bf16_bits(xo + yb));
+        if (!(lane & 1)) {
+          if (last) st_u(x2 + (t * 64 + lane) / 2, nx2);
+          else st_t(ws.x + (t * 64 + lane) / 2, nx2, tag);
         }
       }
     }
-    grid_barrier(ws.bar, nb, ws.err);
-    // ---- C: h into LDS (every block), down units (all wavefronts)
-    for (int i0 = threadIdx.x; i0 < k * I / 2; i0 += 256 * 8) {
-      uint32_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = i0 + 256 * u < k * I / 2 ? ld_u(ws.h + i0 + 256 * u) : 0u;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (i0 + 256 * u < k * I / 2) reinterpret_cast<uint32_t*>(hs)[i0 + 256 * u] = v[u];
-    }
     __syncthreads();
-    for (int g = wave; g < k * tI; g += 4) {
-      const float s = wave_sum(bf16_bits_to_f32(hs[g * 64 + lane]));
-      if (lane == 0) hsum[g] = s;
-    }
-    __syncthreads();
-    {
-      const int PD = d.PD, G = tI / PD;
-      const int nunits = tH * k * PD;
-      for (int u = gw; u < nunits; u += nw) {
-        const int t = u / (k * PD), j = (u / PD) % k, p = u % PD;
-        const size_t row = (size_t)min(max(sel_idx[j], 0), d.E - 1) * H + (size_t)t * 64 + lane;
-        const uint8_t* const q[1] = {Ly.dq};
-        const uint32_t* const sz[1] = {Ly.dsz};
-        float o[1];
-        unit_dot_bits<1>(Ly.dbits, q, sz, row, I, p * G, G, hs + (size_t)j * I, hsum + j * tI, o);
-        float* part = ws.y_part + (size_t)t * k * PD * 64;
-        st_f(part + (j * PD + p) * 64 + lane, o[0]);
-        if (last_arrival(ws.y_cnt + 16 * t, k * PD)) {
-          // slots in ascending order, each the sum of its slices in order;
-          // the partials (slot-major) are loaded 64 at a time
-          float acc = 0.0f, yj = 0.0f;
-          const int n = k * PD;
-          for (int i0 = 0; i0 < n; i0 += 64) {
-            float b[64];
-            load_all(min(64, n - i0), b, [&](int i) { return ld_f(part + (i0 + i) * 64 + lane); });
-#pragma unroll
-            for (int i = 0; i < 64; ++i) {
-              if (i0 + i < n) {
-                yj += b[i];
-                if ((i0 + i) % PD == PD - 1) {
-                  acc = fmaf(sel_w[(i0 + i) / PD], yj, acc);
-                  yj = 0.0f;
-                }
-              }
-            }
-          }
-          // x rows t*64 .. t*64 + 63 as 32 pairs
-          const uint32_t xw = ld_u(x2 + (t * 64 + (lane & ~1)) / 2);
-          const float xo = bf16_bits_to_f32((lane & 1) ? (xw >> 16) : (xw & 0xFFFFu));
-          const float yb = bf16_bits_to_f32(f32_to_bf16_bits(acc));
-          const uint32_t nw2 = pair_with_next(f32_to_bf16_bits(xo + yb));
-          if (!(lane & 1)) st_u(x2 + (t * 64 + lane) / 2, nw2);
-          if (lane == 0) __hip_atomic_store(ws.y_cnt + 16 * t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    }
-    grid_barrier(ws.bar, nb, ws.err);
+    event(ws, l, gw, nw, 6);
   }
 }
 
@@ -468,33 +560,43 @@ int device_blocks(int* nb) {
 #define MOEQ_STACK_MIN_GROUPS 1
 #endif
 constexpr int kMinGroups = MOEQ_STACK_MIN_GROUPS;
-int slices(int n, int units, int waves) {
+int slices(int n, int units, int waves, int cap) {
   int p = 1;
-  while (n % (2 * p) == 0 && n / (2 * p) >= kMinGroups && units * 2 * p <= waves) p *= 2;
+  while (n % (2 * p) == 0 && n / (2 * p) >= kMinGroups && units * 2 * p <= waves && 2 * p <= cap) p *= 2;
   return p;
 }
 
 struct StackLayout {
-  size_t logits, gu_part, h, y_part, gu_cnt, y_cnt, bar, total;
+  size_t logits, gu_part, h, y_part, x, ctl, tl, total;
   int P, PD, nb;
 };
 
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 
+// With MOEQ_STACK_TIMELINE defined, the workspace ends with the event times
+// of every (layer, wavefront) of a call of up to that many layers.
+#ifdef MOEQ_STACK_TIMELINE
+constexpr int kTimelineLayers = MOEQ_STACK_TIMELINE;
+#else
+constexpr int kTimelineLayers = 0;
+#endif
+
 int stack_layout(const moe_layer_desc* L, StackLayout* o) {
   int rc = device_blocks(&o->nb);
   if (rc != MOEQ_OK) return rc;
   const int tI = L->I / 64, tH = L->H / 64, waves = 4 * o->nb;
-  o->P = slices(tH, L->k * tI, waves);
-  o->PD = slices(tI, tH * L->k, waves);
+  // a reduction's partials fit the LDS of the h slices: 2 P rows of 64
+  // floats for gate/up, k PD rows for down
+  o->P = slices(tH, L->k * tI, waves, kRedRows / 2);
+  o->PD = slices(tI, tH * L->k, waves, kRedRows / L->k);
   size_t off = 0;
-  o->logits = off;  off = up256(off + (size_t)L->E * 4);
-  o->gu_part = off; off = up256(off + (size_t)L->k * tI * o->P * 128 * 4);
-  o->h = off;       off = up256(off + (size_t)L->k * L->I * 2);
-  o->y_part = off;  off = up256(off + (size_t)tH * L->k * o->PD * 64 * 4);
-  o->gu_cnt = off;  off = up256(off + (size_t)L->k * tI * 64);   // counters 64 bytes apart
-  o->y_cnt = off;   off = up256(off + (size_t)tH * 64);
-  o->bar = off;     off = up256(off + 288 * 4);   // barrier words (see grid_barrier), then the error flag
+  o->logits = off;  off = up256(off + (size_t)L->E * 8);
+  o->gu_part = off; off = up256(off + (size_t)L->k * tI * o->P * 128 * 8);
+  o->h = off;       off = up256(off + (size_t)L->k * L->I / 2 * 8);
+  o->y_part = off;  off = up256(off + (size_t)tH * L->k * o->PD * 64 * 8);
+  o->x = off;       off = up256(off + (size_t)L->H / 2 * 8);
+  o->ctl = off;     off = up256(off + 256);   // call number, error word
+  o->tl = off;      off = up256(off + (size_t)kTimelineLayers * waves * 8 * 8);
   o->total = off;
   return MOEQ_OK;
 }
@@ -505,8 +607,8 @@ int stack_dims_ok(const moe_layer_desc* L) {
     return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack: H=%d I=%d E=%d k=%d S=%d", L->H, L->I, L->E, L->k, L->S);
   if (L->S != 0) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack: shared experts (S=%d) not supported", L->S);
   if (L->H % 512 || L->H > kMaxH) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack: H=%d not a multiple of 512 up to %d", L->H, kMaxH);
-  if (L->I % 64 || L->k * L->I > kMaxKI)
-    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack: I=%d not a multiple of 64 or k*I above %d", L->I, kMaxKI);
+  if (L->I % 64 || L->I > kMaxI)
+    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack: I=%d not a multiple of 64 up to %d", L->I, kMaxI);
   if (L->k > kMaxK || L->k > L->E || L->E > 1024)
     return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack: k=%d E=%d (k <= 16, k <= E <= 1024)", L->k, L->E);
   return MOEQ_OK;
@@ -580,17 +682,21 @@ extern "C" int moe_stack_decode(const moe_layer_desc* dims, const void* table, s
     return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack_decode: table of %zu bytes cannot hold %d layers", table_bytes, nlayers);
   if (!(eps >= 0.0f)) return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack_decode: eps=%g", (double)eps);
   if (!aligned16(x) || !aligned16(table)) return set_error(MOEQ_ERR_MISALIGNED, "moe_stack_decode: x and table must be 16-byte aligned");
+  if (nlayers > kMaxLayers) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack_decode: nlayers=%d above %d", nlayers, kMaxLayers);
   if (nlayers == 0) return MOEQ_OK;
   StackLayout o;
   if ((rc = stack_layout(dims, &o)) != MOEQ_OK) return rc;
   if (!ws || ws_bytes < o.total)
     return set_error(MOEQ_ERR_WORKSPACE, "moe_stack_decode: workspace of %zu bytes, need %zu", ws_bytes, o.total);
   char* w = static_cast<char*>(ws);
-  StackWs sw{reinterpret_cast<float*>(w + o.logits), reinterpret_cast<float*>(w + o.gu_part),
-             reinterpret_cast<uint32_t*>(w + o.h), reinterpret_cast<float*>(w + o.y_part),
-             reinterpret_cast<int*>(w + o.gu_cnt), reinterpret_cast<int*>(w + o.y_cnt),
-             reinterpret_cast<unsigned*>(w + o.bar), reinterpret_cast<int*>(w + o.bar) + 280};
+  uint64_t* tl = nlayers <= kTimelineLayers ? reinterpret_cast<uint64_t*>(w + o.tl) : nullptr;
+  StackWs sw{reinterpret_cast<uint64_t*>(w + o.logits), reinterpret_cast<uint64_t*>(w + o.gu_part),
+             reinterpret_cast<uint64_t*>(w + o.h), reinterpret_cast<uint64_t*>(w + o.y_part),
+             reinterpret_cast<uint64_t*>(w + o.x), reinterpret_cast<uint32_t*>(w + o.ctl),
+             reinterpret_cast<int*>(w + o.ctl) + 16, tl};
   StackDims sd{dims->H, dims->I, dims->E, dims->k, nlayers, o.P, o.PD, eps};
+  stack_epoch_kernel<<<1, 64, 0, stream>>>(sw.epoch);
+  if ((rc = check_launch("moe_stack_decode (call number)")) != MOEQ_OK) return rc;
   const StackHeader* tp = static_cast<const StackHeader*>(table);
   uint32_t* x2 = reinterpret_cast<uint32_t*>(x);
   void* args[] = {&tp, &sd, &sw, &x2};
@@ -613,14 +719,14 @@ extern "C" int moe_stack_read_status(void* ws, size_t ws_bytes, const moe_layer_
   if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
   char* w = static_cast<char*>(ws);
   int v = 0;
-  e = hipMemcpy(&v, w + o.bar + 280 * sizeof(int), sizeof(int), hipMemcpyDeviceToHost);
+  e = hipMemcpy(&v, w + o.ctl + 16 * sizeof(int), sizeof(int), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "hipMemcpy: %s", hipGetErrorString(e));
   if (v != 0) {
-    // a wait that gave up leaves counts behind: zero every control word
-    // (the counters, the barrier words and the error word) for the next call
-    e = hipMemset(w + o.gu_cnt, 0, o.total - o.gu_cnt);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "hipMemset: %s", hipGetErrorString(e));
+    // the word is sticky until read; the tagged words need no reset (a
+    // later call waits for its own tags)
+    const int zero = 0;
+    e = hipMemcpy(w + o.ctl + 16 * sizeof(int), &zero, sizeof(int), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "hipMemcpy: %s", hipGetErrorString(e));
   }
   *err = v;
   return MOEQ_OK;

@@ -198,8 +198,8 @@ int moe_stack_table_write(const moe_layer_desc* layers, const uint16_t* const* w
 
 /* Workspace bytes moe_stack_decode needs for layers of the dimensions of L
  * on the current device (it depends on the device's CU count); 0 if L is
- * not supported (H a multiple of 512 up to 8192, I a multiple of 64 with
- * k*I <= 16384, k <= 16, k <= E <= 1024, S = 0).  Zero-fill it once. */
+ * not supported (H a multiple of 512 up to 8192, I a multiple of 64 up to
+ * 4096, k <= 16, k <= E <= 1024, S = 0).  Zero-fill it once. */
 size_t moe_stack_workspace_bytes(const moe_layer_desc* L);
 
 /* One batch-1 token through the first nlayers layers of table (the layer
@@ -210,12 +210,16 @@ size_t moe_stack_workspace_bytes(const moe_layer_desc* L);
  * weights, SwiGLU experts with h rounded to bf16, fp32 accumulation),
  * x = bf16(x + bf16(moe)).  x: device bf16 [H], updated in place.  dims: any
  * layer's descriptor (only H, I, E, k, S are read); table_bytes: the size
- * of table.  One cooperative launch whose blocks meet at grid-wide barriers
- * three times per layer; it fails (MOEQ_ERR_HIP) if the device cannot hold
- * the grid at once.  The kernel checks the table's header against dims and
- * nlayers and, on a mismatch, leaves x untouched and sets bit 2 of the
- * workspace's error word; a grid barrier that waits for seconds gives up and
- * sets bit 1 (x is then wrong).  Read the word with moe_stack_read_status.
+ * of table; nlayers <= 1024.  A one-thread kernel that advances the
+ * workspace's call number, then one cooperative launch whose wavefronts
+ * hand values to each other through tagged words in the workspace (no
+ * barriers); it fails (MOEQ_ERR_HIP) if the device cannot hold the grid at
+ * once.  The kernel checks the table's header against dims and nlayers and,
+ * on a mismatch, leaves x untouched and sets bit 2 of the workspace's error
+ * word; a wait that polls for a fraction of a second gives up and sets bit 1
+ * (x is then wrong).  Read the word with moe_stack_read_status.  Calls that
+ * share a workspace must not overlap; a workspace serves one set of
+ * dimensions.
  * The K sums are split across wavefronts, so results equal
  * moe_rmsnorm + moe_decode_forward to rounding, not bit for bit. */
 int moe_stack_decode(const moe_layer_desc* dims, const void* table, size_t table_bytes, int nlayers, float eps,
@@ -223,9 +227,9 @@ int moe_stack_decode(const moe_layer_desc* dims, const void* table, size_t table
 
 /* Synchronise `stream` and return in *err the error word of a
  * moe_stack_decode workspace (0: no error since the last read; bit 1: a
- * grid barrier gave up; bit 2: the table did not match).  A non-zero word is
- * cleared together with the workspace's counters and barrier words, so the
- * next call starts clean.  dims as for moe_stack_workspace_bytes. */
+ * wait gave up; bit 2: the table did not match) and clear it.  The next call
+ * needs no other reset: it waits for words tagged with its own call number.
+ * dims as for moe_stack_workspace_bytes. */
 int moe_stack_read_status(void* ws, size_t ws_bytes, const moe_layer_desc* dims, int* err, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
