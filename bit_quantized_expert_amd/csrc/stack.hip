@@ -6,16 +6,24 @@
 // recovered it (Raon-1-mini, optimisation table and result paragraph).
 //
 // A layer, for the residual stream x (bf16 [H]):
-//   A  every block: n = RMSNorm(x) into LDS (and its 64-group sums); router
-//      rows spread over the first wavefronts: logits[e] = n . Wr[e]
+//   A  every block: n = RMSNorm(x) into LDS (and its 64-group sums), from x
+//      held in registers; router rows over the first wavefronts:
+//      logits[e] = n . Wr[e]
 //   B  every block: top-k of the logits into LDS; gate/up units (slot j,
 //      64-row tile of I, K slice p of H) over all wavefronts: partial gate
-//      and up sums per row.  Wavefront r then adds the P partials of
-//      (slot, tile) r in slice order and writes h = bf16(silu(g) u)
+//      and up sums per row.  The workgroup that owns (slot, tile) rt adds
+//      its P partials in slice order (gate in its first wavefront, up in the
+//      second, in registers) and writes h = bf16(silu(g) u)
 //   C  down units (64-row tile of H, slot j, K slice p of I) over all
-//      wavefronts, each on its own slice of h: partial rows.  Wavefront t
-//      then adds the partials of x tile t (slices, then slots in ascending
+//      wavefronts, each on its own slice of h, its first unit's weights
+//      loaded before the gate/up reduction: partial rows.  The workgroup
+//      that owns x tile t adds the partials (each wavefront whole slots,
+//      slices in order; then the first wavefront the slots in ascending
 //      order, weighted) and writes x = bf16(x + bf16(sum))
+// The router, the gate/up reductions and the x reductions sit on different
+// workgroups.  Logits, h and x are written once per XCD (eight copies) and
+// each workgroup reads the copy of its XCD, so that the pollers of one value
+// spread over eight times as many lines.
 // The dot products are the decode GEMV's (format.h): codes become bf16
 // (128 + q, or q at 8 bits) pairs, v_dot2_f32_bf16 with the activations'
 // pairs (read from LDS, the same address on every lane), and the group's
@@ -39,10 +47,12 @@
 // every block checks against the launch's dimensions before it touches a
 // layer; on a mismatch every block leaves at once and the workspace's error
 // word gets bit 2.  A wait that gives up (after 2^18 polls, a fraction of a
-// second) sets bit 1 and goes on with what it read, so that every wavefront reaches
-// the end of the kernel.  The error word is sticky until
+// second) sets bit 1 and goes on with what it read, so that every wavefront
+// reaches the end of the kernel.  The error word is sticky until
 // moe_stack_read_status reads it.
 #include "decode_impl.h"
+
+#include <type_traits>
 
 using namespace moeq;
 using decode_detail::load_chunk_g;
@@ -54,8 +64,16 @@ constexpr int kMaxI = 4096;      // LDS: a down unit's slice of h, bf16, per wav
 constexpr int kMaxK = 16;
 constexpr int kMaxLayers = 1024; // tags: call * 1024 + layer
 constexpr int kDW = 16;          // dwords of one group's codes in one lane (8-bit: 4 chunks of 4)
-constexpr int kRedRows = 4 * kMaxI / 128;   // rows of 64 floats a block reduces in its h-slice LDS
 constexpr unsigned kSpinLimit = 1u << 18;
+// Copies of the values every workgroup reads (logits, h, x): one per XCD, so
+// that the pollers of one value spread over that many lines.
+#ifndef MOEQ_STACK_REPLICAS
+#define MOEQ_STACK_REPLICAS 8
+#endif
+constexpr int kRep = MOEQ_STACK_REPLICAS;
+#ifndef MOEQ_STACK_SLEEP
+#define MOEQ_STACK_SLEEP 1
+#endif
 
 struct StackHeader {  // 64 bytes before the layers
   uint32_t magic, nlayers;
@@ -86,11 +104,11 @@ struct StackDims {
 
 // Tagged words: value in the low half, tag in the high half.
 struct StackWs {
-  uint64_t* logits;    // [E] fp32
+  uint64_t* logits;    // [kRep][E] fp32
   uint64_t* gu_part;   // [k * I/64][P][2][64] fp32 partial gate, up sums
-  uint64_t* h;         // [k][I/2] bf16 pairs
+  uint64_t* h;         // [kRep][k][I/2] bf16 pairs
   uint64_t* y_part;    // [H/64][k][PD][64] fp32 partial down sums
-  uint64_t* x;         // [H/2] bf16 pairs: x between layers
+  uint64_t* x;         // [kRep][H/2] bf16 pairs: x between layers
   uint32_t* epoch;     // call number
   int* err;            // bit 1: a wait gave up; bit 2: table mismatch
   uint64_t* tl;        // event times per (layer, wavefront), or null
@@ -145,7 +163,7 @@ MOEQ_DEV void poll(int n, uint64_t (&b)[M], Addr&& addr, uint32_t tag, int* err)
       if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(MOEQ_STACK_SLEEP);
 #pragma unroll
     for (int i = 0; i < M; ++i)
       if (i < n && !fresh(b[i], tag)) b[i] = ld_t(addr(i));
@@ -161,7 +179,7 @@ MOEQ_DEV void wave_lds_sync() {
 }
 
 MOEQ_DEV void event(const StackWs& ws, int l, int gw, int nw, int i) {
-  if (ws.tl && (threadIdx.x & 63) == 0) ws.tl[((size_t)l * nw + gw) * 8 + i] = wall_clock64();
+  if (ws.tl && (threadIdx.x & 63) == 0) ws.tl[((size_t)l * nw + gw) * 16 + i] = wall_clock64();
 }
 
 // The codes and scale/zero words of up to two groups of NM matrices for one
@@ -270,7 +288,8 @@ MOEQ_DEV void unit_bits(int bits, Batch<NM>& first, bool loaded, const uint8_t* 
 }
 
 
-// Top-k of E logits (first wavefront of the block) into LDS.
+// Top-k of E logits (first wavefront of the block) into LDS: select_token's
+// choices and weights.
 template <int NS>
 MOEQ_DEV void select_into(const float* logits, int E, int k, int* sel_idx, float* sel_w) {
   int idx;
@@ -304,6 +323,7 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
   __shared__ float xsum[kMaxH / 64];
   __shared__ __attribute__((aligned(16))) uint16_t hs[4][kMaxI];
   __shared__ float hsum[4][kMaxI / 64];
+  __shared__ __attribute__((aligned(16))) uint16_t xr[kMaxH];   // x itself (the residual)
   __shared__ float lg[1024];
   __shared__ int sel_idx[kMaxK];
   __shared__ float sel_w[kMaxK];
@@ -331,6 +351,7 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
     const int n_gu = k * tI * P, n_dn = tH * k * PD;
     const StackLayer Ly = table[l];
     const uint32_t tag = base + (uint32_t)l;
+    const int rep = (int)blockIdx.x % kRep;   // the copy this workgroup reads
     StackWs ws = ws0;
     ws.logits = fresh_base(ws0.logits);
     ws.gu_part = fresh_base(ws0.gu_part);
@@ -350,28 +371,38 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
       for (int c = 0; c < kRouterChunks; ++c)
         if (c * 512 < H) wfirst[c] = *reinterpret_cast<const uint4*>(wrow + c * 512 + lane * 8);
     }
+    // x as H/2 bf16 pairs, H/512 of them per thread (kept in registers), 4
+    // at a time
+    const int nx = H / 512;
+    uint32_t xv[kMaxH / 512];
     {
-      // x as H/2 bf16 pairs, H/512 of them per thread, 4 at a time
-      const int nx = H / 512;
+      const uint64_t* xrep = ws.x + (size_t)rep * (H / 2);
       float ss = 0.0f;
-      for (int u0 = 0; u0 < nx; u0 += 4) {
-        uint64_t xb[4];
-        const int nu = min(4, nx - u0);
-        if (l == 0) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) xb[u] = u < nu ? ld_u(x2 + threadIdx.x + 256 * (u0 + u)) : 0;
-        } else {
-          poll(nu, xb, [&](int u) { return ws.x + threadIdx.x + 256 * (u0 + u); }, tag - 1, ws.err);
-        }
+      for (int u0 = 0; u0 < kMaxH / 512; u0 += 4) {
+        if (u0 < nx) {
+          uint64_t xb[4];
+          const int nu = min(4, nx - u0);
+          if (l == 0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (u < nu) {
-            const uint32_t v = (uint32_t)xb[u];
-            const float a = bf16_bits_to_f32(v & 0xFFFFu), b = bf16_bits_to_f32(v >> 16);
-            reinterpret_cast<uint32_t*>(xs)[threadIdx.x + 256 * (u0 + u)] = v;
-            ss = fmaf(a, a, ss);
-            ss = fmaf(b, b, ss);
+            for (int u = 0; u < 4; ++u) xb[u] = u < nu ? ld_u(x2 + threadIdx.x + 256 * (u0 + u)) : 0;
+          } else {
+            poll(nu, xb, [&](int u) { return xrep + threadIdx.x + 256 * (u0 + u); }, tag - 1, ws.err);
           }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t v = (uint32_t)xb[u];
+            xv[u0 + u] = v;
+            if (u < nu) {
+              const float a = bf16_bits_to_f32(v & 0xFFFFu), b = bf16_bits_to_f32(v >> 16);
+              reinterpret_cast<uint32_t*>(xr)[threadIdx.x + 256 * (u0 + u)] = v;
+              ss = fmaf(a, a, ss);
+              ss = fmaf(b, b, ss);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) xv[u0 + u] = 0;
         }
       }
       ss = wave_sum(ss);
@@ -379,14 +410,25 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
     }
     event(ws, l, gw, nw, 0);
     __syncthreads();
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-    const float r = 1.0f / sqrtf(tot / (float)H + d.eps);
-    for (int i = threadIdx.x; i < H; i += 256) xs[i] = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(xs[i]) * r);
-    __syncthreads();
-    for (int g = wave; g < tH; g += 4) {
-      const float s = wave_sum(bf16_bits_to_f32(xs[g * 64 + lane]));
-      if (lane == 0) xsum[g] = s;
+    {
+      // n = bf16(x r) from the registers; the 32 pairs of a 64-group sit in
+      // one half of a wavefront (pair index tid + 256 u), so its sum is a
+      // 32-lane sum
+      const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+      const float r = 1.0f / sqrtf(tot / (float)H + d.eps);
+#pragma unroll
+      for (int u = 0; u < kMaxH / 512; ++u) {
+        if (u < nx) {
+          const uint32_t na = f32_to_bf16_bits(bf16_bits_to_f32(xv[u] & 0xFFFFu) * r);
+          const uint32_t nb2 = f32_to_bf16_bits(bf16_bits_to_f32(xv[u] >> 16) * r);
+          reinterpret_cast<uint32_t*>(xs)[threadIdx.x + 256 * u] = na | (nb2 << 16);
+          const float gsum = group_sum(bf16_bits_to_f32(na) + bf16_bits_to_f32(nb2), 32);
+          if ((lane & 31) == 0) xsum[2 * wave + 8 * u + (lane >> 5)] = gsum;
+        }
+      }
     }
+    __syncthreads();
+    event(ws, l, gw, nw, 7);
     for (int e = gw; e < E; e += nw) {
       const uint16_t* wrow = Ly.wr + (size_t)e * H;
       float acc = 0.0f;
@@ -410,13 +452,15 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
         acc = dot2_bf16(wv.w, nv.w, acc);
       }
       acc = wave_sum(acc);
-      if (lane == 0) st_t(ws.logits + e, __float_as_uint(acc), tag);
+      if (lane < kRep) st_t(ws.logits + (size_t)lane * E + e, __float_as_uint(acc), tag);
     }
+    event(ws, l, gw, nw, 8);
     // ---- B: top-k (every block), gate/up units (all wavefronts)
     {
       uint64_t lb[4];   // E <= 1024: at most 4 logits per thread
       const int nl = (E - (int)threadIdx.x + 255) / 256;
-      poll(nl, lb, [&](int i) { return ws.logits + threadIdx.x + 256 * i; }, tag, ws.err);
+      const uint64_t* lr = ws.logits + (size_t)rep * E;
+      poll(nl, lb, [&](int i) { return lr + threadIdx.x + 256 * i; }, tag, ws.err);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (i < nl) lg[threadIdx.x + 256 * i] = val_f(lb[i]);
@@ -425,6 +469,7 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
     event(ws, l, gw, nw, 1);
     if (wave == 0) select_any(lg, E, k, sel_idx, sel_w);
     __syncthreads();
+    event(ws, l, gw, nw, 9);
     for (int u = gw; u < n_gu; u += nw) {
       const int j = u / (tI * P), t = (u / P) % tI, p = u % P;
       const size_t row = (size_t)min(max(sel_idx[j], 0), E - 1) * I + (size_t)t * 64 + lane;
@@ -437,102 +482,132 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
       st_t(part + lane, __float_as_uint(o[0]), tag);
       st_t(part + 64 + lane, __float_as_uint(o[1]), tag);
     }
-    const uint8_t* const dq[1] = {Ly.dq};
-    const uint32_t* const dsz[1] = {Ly.dsz};
     event(ws, l, gw, nw, 2);
-    // (slot, tile) rt is reduced by block rt: its four wavefronts load the
-    // P partials into LDS, the first adds them in slice order
+    // Workgroups that reduce: the router's are the first ceil(E/4); x tile t
+    // is reduced by workgroup R0 + t, (slot, tile) rt of gate/up by R0 + tH +
+    // rt (mod the grid), so that no workgroup holds two roles in a row.
+    const int nb = (int)gridDim.x, R0 = (E + 3) / 4;
+    auto first_of = [&](int r0) { return (((int)blockIdx.x - r0) % nb + nb) % nb; };
     float* rl = reinterpret_cast<float*>(&hs[0][0]);
-    for (int rt = blockIdx.x; rt < k * tI; rt += gridDim.x) {
-      __syncthreads();   // rl is free
-      const uint64_t* part = ws.gu_part + (size_t)rt * P * 128;
-      for (int p0 = wave * 8; p0 < P; p0 += 32) {   // slices p0 .. p0 + 7 of this wavefront
-        uint64_t b[16];
-        const int np = min(8, P - p0);
-        poll(2 * np, b, [&](int i) { return part + (size_t)(p0 + (i >> 1)) * 128 + (i & 1) * 64 + lane; }, tag, ws.err);
+    // The rest of the block, for down weights of DB bits: the first down
+    // unit's weights are loaded before the gate/up reduction, so that they
+    // arrive while h is made.
+    auto rest = [&](auto db) {
+      constexpr int DB = decltype(db)::value;
+      const uint8_t* const dq[1] = {Ly.dq};
+      const uint32_t* const dsz[1] = {Ly.dsz};
+      Batch<1> dpre;
+      if (gw < n_dn) {
+        const int t = gw / (k * PD), j = (gw / PD) % k, p = gw % PD;
+        const size_t row = (size_t)min(max(sel_idx[j], 0), E - 1) * H + (size_t)t * 64 + lane;
+        batch_load<DB, 1>(dpre, dq, dsz, row, I, p * GD, min(2, GD));
+      }
+      // (slot, tile) rt: wavefront 0 adds the gate partials of its P slices,
+      // wavefront 1 the up partials, each in slice order in registers; the up
+      // sums reach wavefront 0 through LDS
+      for (int rt = first_of(R0 + tH); rt < k * tI; rt += nb) {
+        __syncthreads();   // rl is free
+        event(ws, l, gw, nw, 12);
+        const uint64_t* part = ws.gu_part + (size_t)rt * P * 128 + wave * 64;
+        float sum = 0.0f;
+        if (wave < 2) {
+          for (int p0 = 0; p0 < P; p0 += 32) {
+            uint64_t b[32];
+            const int np = min(32, P - p0);
+            poll(np, b, [&](int i) { return part + (size_t)(p0 + i) * 128 + lane; }, tag, ws.err);
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (i < 2 * np) rl[(2 * p0 + i) * 64 + lane] = val_f(b[i]);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        float gs = 0.0f, us = 0.0f;
-        for (int p = 0; p < P; ++p) {
-          gs += rl[(2 * p) * 64 + lane];
-          us += rl[(2 * p + 1) * 64 + lane];
+            for (int i = 0; i < 32; ++i)
+              if (i < np) sum += val_f(b[i]);
+          }
+          if (wave == 1) rl[lane] = sum;
         }
-        const uint32_t hw = pair_with_next(f32_to_bf16_bits(silu_f32(gs) * us));
-        if (!(lane & 1)) st_t(ws.h + ((size_t)rt * 64 + lane) / 2, hw, tag);
+        event(ws, l, gw, nw, 13);
+        __syncthreads();
+        if (wave == 0) {
+          const uint32_t hw = pair_with_next(f32_to_bf16_bits(silu_f32(sum) * rl[lane]));
+          if (!(lane & 1))
+#pragma unroll
+            for (int c = 0; c < kRep; ++c) st_t(ws.h + (size_t)c * (k * I / 2) + ((size_t)rt * 64 + lane) / 2, hw, tag);
+        }
       }
-    }
-    __syncthreads();   // rl has been read before the h slices overwrite it
-    event(ws, l, gw, nw, 3);
-    // ---- C: down units (all wavefronts), each on its own slice of h
-    uint16_t* hw_l = hs[wave];
-    float* hsum_w = hsum[wave];
-    for (int u = gw; u < n_dn; u += nw) {
-      const int t = u / (k * PD), j = (u / PD) % k, p = u % PD;
-      // h of slot j, groups p GD .. p GD + GD - 1: GD 32 words, 64 at a time
-      const uint64_t* hp = ws.h + ((size_t)j * I + (size_t)p * GD * 64) / 2;
-      for (int w0 = 0; w0 < GD * 32; w0 += 64) {
-        uint64_t b[1];
-        poll(w0 + lane < GD * 32 ? 1 : 0, b, [&](int) { return hp + w0 + lane; }, tag, ws.err);
-        if (w0 + lane < GD * 32) reinterpret_cast<uint32_t*>(hw_l)[w0 + lane] = (uint32_t)b[0];
+      __syncthreads();   // rl has been read before the h slices overwrite it
+      event(ws, l, gw, nw, 3);
+      // ---- C: down units (all wavefronts), each on its own slice of h
+      uint16_t* hw_l = hs[wave];
+      float* hsum_w = hsum[wave];
+      for (int u = gw; u < n_dn; u += nw) {
+        const int t = u / (k * PD), j = (u / PD) % k, p = u % PD;
+        // h of slot j, groups p GD .. p GD + GD - 1: GD 32 words, 64 at a time
+        const uint64_t* hp = ws.h + (size_t)rep * (k * I / 2) + ((size_t)j * I + (size_t)p * GD * 64) / 2;
+        for (int w0 = 0; w0 < GD * 32; w0 += 64) {
+          uint64_t b[1];
+          poll(w0 + lane < GD * 32 ? 1 : 0, b, [&](int) { return hp + w0 + lane; }, tag, ws.err);
+          if (w0 + lane < GD * 32) reinterpret_cast<uint32_t*>(hw_l)[w0 + lane] = (uint32_t)b[0];
+        }
+        wave_lds_sync();
+        for (int g = 0; g < GD; ++g) {
+          const float s = wave_sum(bf16_bits_to_f32(hw_l[g * 64 + lane]));
+          if (lane == 0) hsum_w[g] = s;
+        }
+        wave_lds_sync();
+        if (u == gw) event(ws, l, gw, nw, 4);
+        const size_t row = (size_t)min(max(sel_idx[j], 0), E - 1) * H + (size_t)t * 64 + lane;
+        float o[1];
+        if (u == gw) {
+          unit_run<DB, 1>(dpre, true, dq, dsz, row, I, p * GD, GD, hw_l, hsum_w, o);
+        } else {
+          Batch<1> B;
+          unit_run<DB, 1>(B, false, dq, dsz, row, I, p * GD, GD, hw_l, hsum_w, o);
+        }
+        st_t(ws.y_part + ((size_t)(t * k + j) * PD + p) * 64 + lane, __float_as_uint(o[0]), tag);
+        wave_lds_sync();   // the slice has been read before the next unit's h lands
       }
-      wave_lds_sync();
-      for (int g = 0; g < GD; ++g) {
-        const float s = wave_sum(bf16_bits_to_f32(hw_l[g * 64 + lane]));
-        if (lane == 0) hsum_w[g] = s;
-      }
-      wave_lds_sync();
-      if (u == gw) event(ws, l, gw, nw, 4);
-      const size_t row = (size_t)min(max(sel_idx[j], 0), E - 1) * H + (size_t)t * 64 + lane;
-      float o[1];
-      Batch<1> B;
-      unit_bits<1>(Ly.dbits, B, false, dq, dsz, row, I, p * GD, GD, hw_l, hsum_w, o);
-      st_t(ws.y_part + ((size_t)(t * k + j) * PD + p) * 64 + lane, __float_as_uint(o[0]), tag);
-      wave_lds_sync();   // the slice has been read before the next unit's h lands
+    };
+    switch (Ly.dbits) {
+      case 4: rest(std::integral_constant<int, 4>{}); break;
+      case 6: rest(std::integral_constant<int, 6>{}); break;
+      default: rest(std::integral_constant<int, 8>{}); break;
     }
     event(ws, l, gw, nw, 5);
     const bool last = l + 1 == d.L;
     // x tile t is reduced by block t: its four wavefronts load the k PD
     // partials (slot-major) into LDS, the first adds them: slots in
     // ascending order, each the sum of its slices in order
-    for (int t = blockIdx.x; t < tH; t += gridDim.x) {
-      __syncthreads();   // rl is free (the down units have read their h)
+    for (int t = first_of(R0); t < tH; t += nb) {
+      __syncthreads();   // rl is free
+      event(ws, l, gw, nw, 10);
+      // wavefront w: slots w, w + 4, ..., each the sum of its PD slices in
+      // order (partials slot-major), into LDS; wavefront 0 then adds the
+      // slots in ascending order, weighted
       const uint64_t* part = ws.y_part + (size_t)t * k * PD * 64;
-      const int n = k * PD;
-      for (int i0 = wave * 16; i0 < n; i0 += 64) {
-        uint64_t b[16];
-        const int ni = min(16, n - i0);
-        poll(ni, b, [&](int i) { return part + (size_t)(i0 + i) * 64 + lane; }, tag, ws.err);
+      for (int j = wave; j < k; j += 4) {
+        float yj = 0.0f;
+        for (int p0 = 0; p0 < PD; p0 += 16) {
+          uint64_t b[16];
+          const int np = min(16, PD - p0);
+          poll(np, b, [&](int i) { return part + (size_t)(j * PD + p0 + i) * 64 + lane; }, tag, ws.err);
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (i < ni) rl[(i0 + i) * 64 + lane] = val_f(b[i]);
+          for (int i = 0; i < 16; ++i)
+            if (i < np) yj += val_f(b[i]);
+        }
+        rl[j * 64 + lane] = yj;
       }
+      event(ws, l, gw, nw, 11);
       __syncthreads();
       if (wave == 0) {
-        const int xi = (t * 64 + (lane & ~1)) / 2;
-        uint32_t xw;
-        if (l == 0) {
-          xw = ld_u(x2 + xi);
-        } else {
-          uint64_t b[1];
-          poll(1, b, [&](int) { return ws.x + xi; }, tag - 1, ws.err);
-          xw = (uint32_t)b[0];
-        }
+        const uint32_t xw = reinterpret_cast<const uint32_t*>(xr)[(t * 64 + (lane & ~1)) / 2];
         float acc = 0.0f;
-        for (int j = 0; j < k; ++j) {
-          float yj = 0.0f;
-          for (int p = 0; p < PD; ++p) yj += rl[(j * PD + p) * 64 + lane];
-          acc = fmaf(sel_w[j], yj, acc);
-        }
+        for (int j = 0; j < k; ++j) acc = fmaf(sel_w[j], rl[j * 64 + lane], acc);
         const float xo = bf16_bits_to_f32((lane & 1) ? (xw >> 16) : (xw & 0xFFFFu));
         const float yb = bf16_bits_to_f32(f32_to_bf16_bits(acc));
         const uint32_t nx2 = pair_with_next(f32_to_bf16_bits(xo + yb));
         if (!(lane & 1)) {
-          if (last) st_u(x2 + (t * 64 + lane) / 2, nx2);
-          else st_t(ws.x + (t * 64 + lane) / 2, nx2, tag);
+          if (last) {
+            st_u(x2 + (t * 64 + lane) / 2, nx2);
+          } else {
+#pragma unroll
+            for (int c = 0; c < kRep; ++c) st_t(ws.x + (size_t)c * (H / 2) + (t * 64 + lane) / 2, nx2, tag);
+          }
         }
       }
     }
@@ -560,9 +635,9 @@ int device_blocks(int* nb) {
 #define MOEQ_STACK_MIN_GROUPS 1
 #endif
 constexpr int kMinGroups = MOEQ_STACK_MIN_GROUPS;
-int slices(int n, int units, int waves, int cap) {
+int slices(int n, int units, int waves) {
   int p = 1;
-  while (n % (2 * p) == 0 && n / (2 * p) >= kMinGroups && units * 2 * p <= waves && 2 * p <= cap) p *= 2;
+  while (n % (2 * p) == 0 && n / (2 * p) >= kMinGroups && units * 2 * p <= waves) p *= 2;
   return p;
 }
 
@@ -585,18 +660,16 @@ int stack_layout(const moe_layer_desc* L, StackLayout* o) {
   int rc = device_blocks(&o->nb);
   if (rc != MOEQ_OK) return rc;
   const int tI = L->I / 64, tH = L->H / 64, waves = 4 * o->nb;
-  // a reduction's partials fit the LDS of the h slices: 2 P rows of 64
-  // floats for gate/up, k PD rows for down
-  o->P = slices(tH, L->k * tI, waves, kRedRows / 2);
-  o->PD = slices(tI, tH * L->k, waves, kRedRows / L->k);
+  o->P = slices(tH, L->k * tI, waves);
+  o->PD = slices(tI, tH * L->k, waves);
   size_t off = 0;
-  o->logits = off;  off = up256(off + (size_t)L->E * 8);
+  o->logits = off;  off = up256(off + (size_t)kRep * L->E * 8);
   o->gu_part = off; off = up256(off + (size_t)L->k * tI * o->P * 128 * 8);
-  o->h = off;       off = up256(off + (size_t)L->k * L->I / 2 * 8);
+  o->h = off;       off = up256(off + (size_t)kRep * L->k * L->I / 2 * 8);
   o->y_part = off;  off = up256(off + (size_t)tH * L->k * o->PD * 64 * 8);
-  o->x = off;       off = up256(off + (size_t)L->H / 2 * 8);
+  o->x = off;       off = up256(off + (size_t)kRep * L->H / 2 * 8);
   o->ctl = off;     off = up256(off + 256);   // call number, error word
-  o->tl = off;      off = up256(off + (size_t)kTimelineLayers * waves * 8 * 8);
+  o->tl = off;      off = up256(off + (size_t)kTimelineLayers * waves * 16 * 8);
   o->total = off;
   return MOEQ_OK;
 }
