@@ -360,6 +360,36 @@ def test_stack_megakernel(bq):
     del one, whole
 
 
+def test_stack_table_mismatch(bq):
+    """A table whose header holds fewer layers than the call asks for: every
+    workgroup leaves before touching a layer, x is left as it was, and the
+    workspace's error word reads 2 (table mismatch) once, then 0.  A call
+    with a matching table afterwards runs and reports nothing."""
+    import ctypes
+    w, bits, layers, wrs = stack_layers(bq)
+    L = bq.lib()
+    sd = bq.StackDecoder(layers[:2], wrs[:2])
+    big = torch.zeros(L.moe_stack_table_bytes(4), dtype=torch.uint8, device="cuda")
+    descs = (bq._LayerDesc * 2)(*[l.desc() for l in layers[:2]])
+    ptrs = (ctypes.c_void_p * 2)(*[t.data_ptr() for t in wrs[:2]])
+    assert L.moe_stack_table_write(descs, ptrs, 2, bq._p(big), big.numel()) == 0
+    x0 = synth.activations_bf16(w, 1, batch=31)
+    x = bf16_tensor(x0).reshape(-1)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = L.moe_stack_decode(ctypes.byref(sd.dims), bq._p(big), big.numel(), 3, ctypes.c_float(1e-6), bq._p(x),
+                            bq._p(sd.ws), sd.ws.numel(), stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(x), x0.reshape(-1))
+    assert sd.read_status() == 2
+    assert sd.read_status() == 0
+    sd.run(x)
+    torch.cuda.synchronize()
+    assert sd.read_status() == 0
+    assert not np.array_equal(to_bits(x), x0.reshape(-1))
+    del sd, big
+
+
 def wrs_np(w, l):
     return synth.router_weight_bf16(w, layer=l)
 
