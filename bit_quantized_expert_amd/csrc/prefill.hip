@@ -571,13 +571,20 @@ struct Mainloop {
 // Block -> (work item, feature tile): the feature tiles of one work item (one
 // expert's token tile) land on one XCD (blocks are dealt to the 8 XCDs
 // round-robin) back to back, so the token rows they all read come from that
-// XCD's L2 after the first.  The grid is (work items rounded up to a
-// multiple of 8) x nft.
-MOEQ_DEV void block_tile(int nft, int& w, int& ft) {
+// XCD's L2 after the first; and runs of xrun consecutive work items (the
+// token tiles of one expert sit next to each other in the schedule) go to
+// the same XCD, so that its L2 serves their common weight rows.  The grid is
+// (work items rounded up to a multiple of 8 xrun) x nft.
+MOEQ_DEV void block_tile(int nft, int xrun, int& w, int& ft) {
   const int b = (int)blockIdx.x, r = b % 8, slot = b / 8;
-  w = (slot / nft) * 8 + r;
+  const int n = slot / nft;   // this XCD's n-th work item
+  w = (n / xrun) * 8 * xrun + r * xrun + n % xrun;
   ft = slot % nft;
 }
+
+// Runs of 8 work items per XCD once a batch fills at least this many
+// 128-token tiles (fewer items would leave the XCDs' last runs uneven).
+constexpr int kXcdRunMinTiles = 64;
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
@@ -612,13 +619,13 @@ __global__ __launch_bounds__(256, 2) void mfma_gateup_kernel(const uint8_t* __re
                                                              const int32_t* __restrict__ counts,
                                                              const int32_t* __restrict__ offsets,
                                                              const int32_t* __restrict__ sorted,
-                                                             const int32_t* __restrict__ sched,
+                                                             const int32_t* __restrict__ sched, int xrun,
                                                              uint16_t* __restrict__ h) {
   static_assert(BM == 128, "tile");
   using Out = OutTile<128>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[cmax(lds_bytes<BITS, BM>(), Out::BYTES)];
   int wi, ft;
-  block_tile(I / 128, wi, ft);
+  block_tile(I / 128, xrun, wi, ft);
   if (wi >= sched[0]) return;
   const int e = sched[2 + 2 * wi], mt = sched[3 + 2 * wi];
   const int base = offsets[e] + mt * BM;
@@ -677,13 +684,13 @@ __global__ __launch_bounds__(256, 2) void mfma_down_kernel(const uint8_t* __rest
                                                            const int32_t* __restrict__ counts,
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ sorted,
-                                                           const int32_t* __restrict__ sched,
+                                                           const int32_t* __restrict__ sched, int xrun,
                                                            uint16_t* __restrict__ y) {
   static_assert(BM == 128, "tile");
   using Out = OutTile<256>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[cmax(lds_bytes<BITS, BM>(), Out::BYTES)];
   int wi, ft;
-  block_tile(H / 256, wi, ft);
+  block_tile(H / 256, xrun, wi, ft);
   if (wi >= sched[0]) return;
   const int e = sched[2 + 2 * wi], mt = sched[3 + 2 * wi];
   const int base = offsets[e] + mt * BM;
@@ -901,18 +908,19 @@ extern "C" int moe_qgemm_prefill(const moe_layer_desc* L, const uint16_t* x, int
   const long max_tiles = prefill_max_tiles(A, nexp);
   schedule_kernel<<<1, 256, 0, stream>>>(counts, nexp, L->E, sched, gemv);
   if ((rc = check_launch("moe_qgemm_prefill (schedule)")) != MOEQ_OK) return rc;
-  const unsigned nw = (unsigned)((max_tiles + 7) / 8 * 8);   // work items, padded for the XCD mapping
+  const int xrun = A / BM >= kXcdRunMinTiles ? 8 : 1;
+  const unsigned nw = (unsigned)((max_tiles + 8 * xrun - 1) / (8 * xrun) * (8 * xrun));   // work items, padded for the XCD mapping
   const unsigned g1 = nw * (unsigned)(L->I / 128), g2 = nw * (unsigned)(L->H / 256);
   switch (L->gate.bits) {
-    case 4: mfma_gateup_kernel<4, BM><<<g1, 256, 0, stream>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, kS, counts, offsets, sorted, sched, h); break;
-    case 6: mfma_gateup_kernel<6, BM><<<g1, 256, 0, stream>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, kS, counts, offsets, sorted, sched, h); break;
-    default: mfma_gateup_kernel<8, BM><<<g1, 256, 0, stream>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, kS, counts, offsets, sorted, sched, h); break;
+    case 4: mfma_gateup_kernel<4, BM><<<g1, 256, 0, stream>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, kS, counts, offsets, sorted, sched, xrun, h); break;
+    case 6: mfma_gateup_kernel<6, BM><<<g1, 256, 0, stream>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, kS, counts, offsets, sorted, sched, xrun, h); break;
+    default: mfma_gateup_kernel<8, BM><<<g1, 256, 0, stream>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->H, L->I, kS, counts, offsets, sorted, sched, xrun, h); break;
   }
   if ((rc = check_launch("moe_qgemm_prefill (gate/up)")) != MOEQ_OK) return rc;
   switch (L->down.bits) {
-    case 4: mfma_down_kernel<4, BM><<<g2, 256, 0, stream>>>(L->down.q, L->down.sz, h, L->H, L->I, counts, offsets, sorted, sched, y); break;
-    case 6: mfma_down_kernel<6, BM><<<g2, 256, 0, stream>>>(L->down.q, L->down.sz, h, L->H, L->I, counts, offsets, sorted, sched, y); break;
-    default: mfma_down_kernel<8, BM><<<g2, 256, 0, stream>>>(L->down.q, L->down.sz, h, L->H, L->I, counts, offsets, sorted, sched, y); break;
+    case 4: mfma_down_kernel<4, BM><<<g2, 256, 0, stream>>>(L->down.q, L->down.sz, h, L->H, L->I, counts, offsets, sorted, sched, xrun, y); break;
+    case 6: mfma_down_kernel<6, BM><<<g2, 256, 0, stream>>>(L->down.q, L->down.sz, h, L->H, L->I, counts, offsets, sorted, sched, xrun, y); break;
+    default: mfma_down_kernel<8, BM><<<g2, 256, 0, stream>>>(L->down.q, L->down.sz, h, L->H, L->I, counts, offsets, sorted, sched, xrun, y); break;
   }
   if ((rc = check_launch("moe_qgemm_prefill (down)")) != MOEQ_OK) return rc;
   // the experts of the GEMV list (shared experts take every token: never on it)
