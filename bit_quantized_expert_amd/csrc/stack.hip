@@ -6,28 +6,34 @@
 // recovered it (Raon-1-mini, optimisation table and result paragraph).
 //
 // A layer, for the residual stream x (bf16 [H]):
-//   A  every block: n = RMSNorm(x) into LDS (and its 64-group sums), from x
-//      held in registers; router rows over the first wavefronts:
+//   A  every workgroup: n = RMSNorm(x) into LDS (and its 64-group sums),
+//      from x held in registers; router rows over the first wavefronts:
 //      logits[e] = n . Wr[e]
-//   B  every block: top-k of the logits into LDS; gate/up units (slot j,
-//      64-row tile of I, K slice p of H) over all wavefronts: partial gate
-//      and up sums per row.  The workgroup that owns (slot, tile) rt adds
-//      its P partials in slice order (gate in its first wavefront, up in the
-//      second, in registers) and writes h = bf16(silu(g) u)
-//   C  down units (64-row tile of H, slot j, K slice p of I) over all
-//      wavefronts, each on its own slice of h, its first unit's weights
-//      loaded before the gate/up reduction: partial rows.  The workgroup
-//      that owns x tile t adds the partials (each wavefront whole slots,
-//      slices in order; then the first wavefront the slots in ascending
-//      order, weighted) and writes x = bf16(x + bf16(sum))
-// The router, the gate/up reductions and the x reductions sit on different
-// workgroups.  Logits, h and x are written once per XCD (eight copies) and
-// each workgroup reads the copy of its XCD, so that the pollers of one value
+//   B  every workgroup: top-k of the logits into LDS.  Gate/up: workgroup u
+//      computes eight whole rows (all of K) of one slot's gate and up
+//      projections, lane l taking row l % 8 and 64-groups l / 8 + 8 w + 32 i
+//      (w: its wavefront); the 32 group lanes of a row are added in the
+//      wavefront (butterfly) and the four wavefronts in LDS, in a fixed
+//      order, and h = bf16(silu(g) u) of the eight rows goes out
+//   C  down: workgroup t takes eight rows of x, all k slots and all of I
+//      (lane l: row l % 8, (slot, 64-group) items l / 8 + 8 w + 32 i), every
+//      item weighted by its slot's routing weight, adds them the same way
+//      and writes x = bf16(x + bf16(sum)).  Its weights are loaded right
+//      after the top-k, before its gate/up rows, and are in registers when h
+//      arrives.
+// Eight rows of one 64-row tile hold, chunk after chunk, whole 128-byte
+// lines (4- and 8-bit), so these units read only whole lines, and the only
+// values that cross workgroups are x, the logits and h: three hand-offs a
+// layer.  The router, the gate/up units and the down units sit on different
+// workgroups where the grid allows, so that the router's workgroups load
+// the next layer's router rows while the down units run.
+// Logits, h and x are written once per XCD (eight copies) and each
+// workgroup reads the copy of its XCD, so that the pollers of one value
 // spread over eight times as many lines.
 // The dot products are the decode GEMV's (format.h): codes become bf16
 // (128 + q, or q at 8 bits) pairs, v_dot2_f32_bf16 with the activations'
-// pairs (read from LDS, the same address on every lane), and the group's
-// scale and zero enter once per group in fp32.
+// pairs (read from LDS), and the group's scale and zero enter once per group
+// in fp32.
 //
 // No barrier and no counter: every value one wavefront hands to another
 // (logits, partial sums, h, x between layers) is stored as a 64-bit word,
@@ -39,7 +45,8 @@
 // complete, and a hand-over costs one store and one load.  A word with a
 // newer tag than awaited is taken as well: only a wavefront whose result no
 // one uses can fall that far behind (a value of layer l + 1 exists only
-// after every unit of layer l has finished).  A small kernel launched before
+// after every down unit of layer l has finished, and each of those has read
+// every h word and needed every gate/up unit, which read every logit).  A small kernel launched before
 // each call advances the call number.  The router rows are loaded before x
 // arrives.
 //
@@ -60,7 +67,7 @@ using decode_detail::load_chunk_g;
 namespace {
 
 constexpr int kMaxH = 8192;      // LDS: n, bf16
-constexpr int kMaxI = 4096;      // LDS: a down unit's slice of h, bf16, per wavefront
+constexpr int kMaxKI = 16384;    // LDS: h of every slot, bf16 (k * I)
 constexpr int kMaxK = 16;
 constexpr int kMaxLayers = 1024; // tags: call * 1024 + layer
 constexpr int kDW = 16;          // dwords of one group's codes in one lane (8-bit: 4 chunks of 4)
@@ -71,6 +78,9 @@ constexpr unsigned kSpinLimit = 1u << 18;
 #define MOEQ_STACK_REPLICAS 8
 #endif
 constexpr int kRep = MOEQ_STACK_REPLICAS;
+#ifndef MOEQ_STACK_DN_EARLY
+#define MOEQ_STACK_DN_EARLY 0
+#endif
 #ifndef MOEQ_STACK_SLEEP
 #define MOEQ_STACK_SLEEP 1
 #endif
@@ -97,29 +107,38 @@ static_assert(sizeof(StackLayer) == 64, "table entry");
 
 struct StackDims {
   int H, I, E, k, L;
-  int P;    // K slices of a gate/up row (over H)
-  int PD;   // K slices of a down row (over I)
   float eps;
 };
 
 // Tagged words: value in the low half, tag in the high half.
 struct StackWs {
   uint64_t* logits;    // [kRep][E] fp32
-  uint64_t* gu_part;   // [k * I/64][P][2][64] fp32 partial gate, up sums
   uint64_t* h;         // [kRep][k][I/2] bf16 pairs
-  uint64_t* y_part;    // [H/64][k][PD][64] fp32 partial down sums
   uint64_t* x;         // [kRep][H/2] bf16 pairs: x between layers
   uint32_t* epoch;     // call number
   int* err;            // bit 1: a wait gave up; bit 2: table mismatch
   uint64_t* tl;        // event times per (layer, wavefront), or null
 };
 
-MOEQ_DEV uint32_t ld_u(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The hand-off accesses go through global-address-space pointers, so that
+// they compile to global (not flat) loads and stores: flat accesses also
+// count as LDS accesses and would make every LDS wait wait for them.
+typedef __attribute__((address_space(1))) uint32_t gu32;
+typedef __attribute__((address_space(1))) uint64_t gu64;
+// 16 bytes through a global pointer as a uint4
+MOEQ_DEV uint4 ld_g16(const void* p) {
+  typedef const __attribute__((address_space(1))) moeq_u32x4* g4;
+  const moeq_u32x4 v = *(g4)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
-MOEQ_DEV void st_u(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+MOEQ_DEV uint32_t ld_u(const uint32_t* p) {
+  return __hip_atomic_load((gu32*)(const_cast<uint32_t*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+MOEQ_DEV void st_u(uint32_t* p, uint32_t v) {
+  __hip_atomic_store((gu32*)(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 MOEQ_DEV uint64_t ld_t(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((gu64*)(const_cast<uint64_t*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // A workspace base pointer as a value the compiler takes as new in every
 // layer, held in scalar registers: addresses built from it stay scalar base
@@ -137,7 +156,7 @@ MOEQ_DEV T* fresh_base(T* p) {
   return reinterpret_cast<T*>(a);
 }
 MOEQ_DEV void st_t(uint64_t* p, uint32_t v, uint32_t tag) {
-  __hip_atomic_store(p, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((gu64*)(p), ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 MOEQ_DEV bool fresh(uint64_t w, uint32_t tag) { return (int32_t)((uint32_t)(w >> 32) - tag) >= 0; }
 MOEQ_DEV float val_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
@@ -170,123 +189,86 @@ MOEQ_DEV void poll(int n, uint64_t (&b)[M], Addr&& addr, uint32_t tag, int* err)
   }
 }
 
-// Orders this wavefront's LDS writes before its following LDS reads (other
-// lanes read what a lane wrote).
-MOEQ_DEV void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 MOEQ_DEV void event(const StackWs& ws, int l, int gw, int nw, int i) {
   if (ws.tl && (threadIdx.x & 63) == 0) ws.tl[((size_t)l * nw + gw) * 16 + i] = wall_clock64();
 }
 
-// The codes and scale/zero words of up to two groups of NM matrices for one
-// lane (row), loaded together.
-template <int NM>
-struct Batch {
-  uint32_t d[NM][2][kDW];
-  uint32_t w[NM][2];
+// One 64-group of one row of a matrix, for one lane: its codes (CPG
+// chunks) and the group's scale/zero word.
+struct Grp {
+  uint32_t d[kDW];
+  uint32_t w;
 };
 
-template <int BITS, int NM>
-MOEQ_DEV void batch_load(Batch<NM>& B, const uint8_t* const (&q)[NM], const uint32_t* const (&sz)[NM], size_t row,
-                         int K, int g, int ng) {
-  using F = Fmt<BITS>;
-  constexpr int CPG = F::CHUNKS_PER_GROUP;
-  const size_t cpr = (size_t)(K / F::CODES), gpr = (size_t)(K / 64);
-#pragma unroll
-  for (int gg = 0; gg < 2; ++gg) {
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-#pragma unroll
-      for (int i = CPG * F::DW; i < kDW; ++i) B.d[m][gg][i] = 0;   // every element assigned
-      if (gg < ng) {
-#pragma unroll
-        for (int c = 0; c < CPG; ++c) {
-          uint32_t t[F::DW];
-          load_chunk_g<BITS>((gbytes)(q[m] + chunk_offset<BITS>(row, (size_t)(g + gg) * CPG + c, cpr)), t);
-#pragma unroll
-          for (int i = 0; i < F::DW; ++i) B.d[m][gg][c * F::DW + i] = t[i];
-        }
-        B.w[m][gg] = sz[m][sz_index(row, (size_t)(g + gg), gpr)];
-      } else {
-#pragma unroll
-        for (int i = 0; i < CPG * F::DW; ++i) B.d[m][gg][i] = 0;
-        B.w[m][gg] = 0;
-      }
-    }
-  }
-}
-
-// out[m] += the batch's groups' contributions, group after group; xl, xsl:
-// the activations (LDS, bf16) and group sums of the batch's first group.
-template <int BITS, int NM>
-MOEQ_DEV void batch_dot(const Batch<NM>& B, int ng, const uint16_t* xl, const float* xsl, float (&out)[NM]) {
+// Loads group g of row `row` (K columns) when `on`, else zeros (every element
+// assigned, so that no older value is carried across loops).
+template <int BITS>
+MOEQ_DEV void grp_load(Grp& G, const uint8_t* q, const uint32_t* sz, size_t row, int K, int g, bool on) {
   using F = Fmt<BITS>;
   constexpr int CPG = F::CHUNKS_PER_GROUP;
 #pragma unroll
-  for (int gg = 0; gg < 2; ++gg) {
-    if (gg < ng) {
-      const float x_sum = xsl[gg];
+  for (int i = 0; i < kDW; ++i) G.d[i] = 0;
+  G.w = 0;
+  if (on) {
+    const size_t cpr = (size_t)(K / F::CODES), gpr = (size_t)(K / 64);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        float a0 = 0.0f, a1 = 0.0f;
+    for (int c = 0; c < CPG; ++c) {
+      uint32_t t[F::DW];
+      load_chunk_g<BITS>((gbytes)(q + chunk_offset<BITS>(row, (size_t)g * CPG + c, cpr)), t);
 #pragma unroll
-        for (int c = 0; c < CPG; ++c) {
-          uint32_t t[F::DW], P[F::PAIRS];
+      for (int i = 0; i < F::DW; ++i) G.d[c * F::DW + i] = t[i];
+    }
+    G.w = load_word_g((gbytes)(sz + sz_index(row, (size_t)g, gpr)));
+  }
+}
+
+// The group's dot product with the activations xl (LDS, bf16, 64 of them)
+// whose sum is xsum: s (sum of code x activation - (z + offset) xsum).
+template <int BITS>
+MOEQ_DEV float grp_dot(const Grp& G, const uint16_t* xl, float xsum) {
+  using F = Fmt<BITS>;
+  constexpr int CPG = F::CHUNKS_PER_GROUP;
+  float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-          for (int i = 0; i < F::DW; ++i) t[i] = B.d[m][gg][c * F::DW + i];
-          chunk_pairs<BITS>(t, P);
-          const uint4* xp = reinterpret_cast<const uint4*>(xl + gg * 64 + c * F::CODES);
+  for (int c = 0; c < CPG; ++c) {
+    uint32_t t[F::DW], P[F::PAIRS];
 #pragma unroll
-          for (int p = 0; p < F::PAIRS; p += 4) {
-            const uint4 X = xp[p / 4];
-            a0 = dot2_bf16(P[p], X.x, a0);
-            a1 = dot2_bf16(P[p + 1], X.y, a1);
-            a0 = dot2_bf16(P[p + 2], X.z, a0);
-            a1 = dot2_bf16(P[p + 3], X.w, a1);
-          }
-        }
-        const float s = f16_bits_to_f32(B.w[m][gg] & 0xFFFFu);
-        const float zc = f16_bits_to_f32(B.w[m][gg] >> 16) + F::OFFSET;
-        out[m] = fmaf(s, (a0 + a1) - zc * x_sum, out[m]);
-      }
+    for (int i = 0; i < F::DW; ++i) t[i] = G.d[c * F::DW + i];
+    chunk_pairs<BITS>(t, P);
+    const uint4* xp = reinterpret_cast<const uint4*>(xl + c * F::CODES);
+#pragma unroll
+    for (int p = 0; p < F::PAIRS; p += 4) {
+      const uint4 X = xp[p / 4];
+      a0 = dot2_bf16(P[p], X.x, a0);
+      a1 = dot2_bf16(P[p + 1], X.y, a1);
+      a0 = dot2_bf16(P[p + 2], X.z, a0);
+      a1 = dot2_bf16(P[p + 3], X.w, a1);
     }
   }
+  const float s = f16_bits_to_f32(G.w & 0xFFFFu);
+  const float zc = f16_bits_to_f32(G.w >> 16) + F::OFFSET;
+  return s * ((a0 + a1) - zc * xsum);
 }
 
-// One unit: rows `row` of NM matrices over groups g0 .. g0 + G - 1 of K;
-// xl, xsl hold the activations from group g0 on.  `first` holds the first
-// batch already when loaded is true.
-template <int BITS, int NM>
-MOEQ_DEV void unit_run(Batch<NM>& first, bool loaded, const uint8_t* const (&q)[NM],
-                       const uint32_t* const (&sz)[NM], size_t row, int K, int g0, int G, const uint16_t* xl,
-                       const float* xsl, float (&out)[NM]) {
-#pragma unroll
-  for (int m = 0; m < NM; ++m) out[m] = 0.0f;
-  if (!loaded) batch_load<BITS, NM>(first, q, sz, row, K, g0, min(2, G));
-  batch_dot<BITS, NM>(first, min(2, G), xl, xsl, out);
-  for (int g = 2; g < G; g += 2) {
-    Batch<NM> B;
-    const int ng = min(2, G - g);
-    batch_load<BITS, NM>(B, q, sz, row, K, g0 + g, ng);
-    batch_dot<BITS, NM>(B, ng, xl + g * 64, xsl + g, out);
-  }
+// Unit of the i-th of n workgroups that take units (workgroup b runs on XCD
+// b mod 8, and i = b - a multiple of 8): with n a multiple of 64, each XCD
+// takes runs of eight consecutive units, the eight 8-row units of one
+// 64-row tile, so that all the 128-byte lines of a tile's chunks are read
+// through one L2, one unit right after the other.
+MOEQ_DEV int xcd_unit(int i, int n) {
+  if (n % 64) return i;
+  const int x = i % 8, s = i / 8;
+  return ((s / 8) * 8 + x) * 8 + s % 8;
 }
 
-template <int NM>
-MOEQ_DEV void unit_bits(int bits, Batch<NM>& first, bool loaded, const uint8_t* const (&q)[NM],
-                        const uint32_t* const (&sz)[NM], size_t row, int K, int g0, int G, const uint16_t* xl,
-                        const float* xsl, float (&out)[NM]) {
-  switch (bits) {
-    case 4: unit_run<4, NM>(first, loaded, q, sz, row, K, g0, G, xl, xsl, out); break;
-    case 6: unit_run<6, NM>(first, loaded, q, sz, row, K, g0, G, xl, xsl, out); break;
-    default: unit_run<8, NM>(first, loaded, q, sz, row, K, g0, G, xl, xsl, out); break;
-  }
+// Sum over the eight lanes of a wavefront that share lane % 8 (a butterfly:
+// every one of them ends with the same value).
+MOEQ_DEV float sum_stride8(float v) {
+  v += __shfl_xor(v, 8);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
 }
-
 
 // Top-k of E logits (first wavefront of the block) into LDS: select_token's
 // choices and weights.
@@ -321,13 +303,14 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
                                                               uint32_t* x2_0) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxH];
   __shared__ float xsum[kMaxH / 64];
-  __shared__ __attribute__((aligned(16))) uint16_t hs[4][kMaxI];
-  __shared__ float hsum[4][kMaxI / 64];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[kMaxKI];
+  __shared__ float hsum[kMaxKI / 64];
   __shared__ __attribute__((aligned(16))) uint16_t xr[kMaxH];   // x itself (the residual)
   __shared__ float lg[1024];
   __shared__ int sel_idx[kMaxK];
   __shared__ float sel_w[kMaxK];
   __shared__ float red[4];
+  __shared__ float rsum[64];
   {
     // every block reads the same header, so all leave or none does
     const StackHeader h0 = *hdr;
@@ -342,21 +325,17 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
     // the dimensions as values the compiler takes as new in every layer, so
     // that what derives from them is computed where it is used rather than
     // ahead of the loop for all layers (where it would occupy registers)
-    int H = d.H, I = d.I, k = d.k, E = d.E, P = d.P, PD = d.PD, wave = (int)threadIdx.x >> 6;
-    asm volatile("" : "+s"(H), "+s"(I), "+s"(k), "+s"(E), "+s"(P), "+s"(PD));
+    int H = d.H, I = d.I, k = d.k, E = d.E, wave = (int)threadIdx.x >> 6;
+    asm volatile("" : "+s"(H), "+s"(I), "+s"(k), "+s"(E));
     wave = uniform(wave);
     const int lane = threadIdx.x & 63;
     const int gw = (int)blockIdx.x * 4 + wave, nw = (int)gridDim.x * 4;
-    const int tI = I / 64, tH = H / 64, G = tH / P, GD = tI / PD;
-    const int n_gu = k * tI * P, n_dn = tH * k * PD;
     const StackLayer Ly = table[l];
     const uint32_t tag = base + (uint32_t)l;
     const int rep = (int)blockIdx.x % kRep;   // the copy this workgroup reads
     StackWs ws = ws0;
     ws.logits = fresh_base(ws0.logits);
-    ws.gu_part = fresh_base(ws0.gu_part);
     ws.h = fresh_base(ws0.h);
-    ws.y_part = fresh_base(ws0.y_part);
     ws.x = fresh_base(ws0.x);
     uint32_t* x2 = fresh_base(x2_0);
     // ---- A: RMSNorm (every block), router rows.  The first router row's
@@ -369,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
       const uint16_t* wrow = Ly.wr + (size_t)gw * H;
 #pragma unroll
       for (int c = 0; c < kRouterChunks; ++c)
-        if (c * 512 < H) wfirst[c] = *reinterpret_cast<const uint4*>(wrow + c * 512 + lane * 8);
+        if (c * 512 < H) wfirst[c] = ld_g16(wrow + c * 512 + lane * 8);
     }
     // x as H/2 bf16 pairs, H/512 of them per thread (kept in registers), 4
     // at a time
@@ -435,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
 #pragma unroll
       for (int c = 0; c < kRouterChunks; ++c) {
         if (c * 512 < H) {
-          const uint4 wv = e == gw ? wfirst[c] : *reinterpret_cast<const uint4*>(wrow + c * 512 + lane * 8);
+          const uint4 wv = e == gw ? wfirst[c] : ld_g16(wrow + c * 512 + lane * 8);
           const uint4 nv = *reinterpret_cast<const uint4*>(xs + c * 512 + lane * 8);
           acc = dot2_bf16(wv.x, nv.x, acc);
           acc = dot2_bf16(wv.y, nv.y, acc);
@@ -444,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
         }
       }
       for (int c = kRouterChunks * 512 + lane * 8; c < H; c += 512) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(wrow + c);
+        const uint4 wv = ld_g16(wrow + c);
         const uint4 nv = *reinterpret_cast<const uint4*>(xs + c);
         acc = dot2_bf16(wv.x, nv.x, acc);
         acc = dot2_bf16(wv.y, nv.y, acc);
@@ -455,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
       if (lane < kRep) st_t(ws.logits + (size_t)lane * E + e, __float_as_uint(acc), tag);
     }
     event(ws, l, gw, nw, 8);
-    // ---- B: top-k (every block), gate/up units (all wavefronts)
+    // ---- B: top-k (every workgroup)
     {
       uint64_t lb[4];   // E <= 1024: at most 4 logits per thread
       const int nl = (E - (int)threadIdx.x + 255) / 256;
@@ -470,146 +449,184 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
     if (wave == 0) select_any(lg, E, k, sel_idx, sel_w);
     __syncthreads();
     event(ws, l, gw, nw, 9);
-    for (int u = gw; u < n_gu; u += nw) {
-      const int j = u / (tI * P), t = (u / P) % tI, p = u % P;
-      const size_t row = (size_t)min(max(sel_idx[j], 0), E - 1) * I + (size_t)t * 64 + lane;
-      const uint8_t* const q[2] = {Ly.gq, Ly.uq};
-      const uint32_t* const sz[2] = {Ly.gsz, Ly.usz};
-      float o[2];
-      Batch<2> B;
-      unit_bits<2>(Ly.gbits, B, false, q, sz, row, H, p * G, G, xs + p * G * 64, xsum + p * G, o);
-      uint64_t* part = ws.gu_part + ((size_t)(j * tI + t) * P + p) * 128;
-      st_t(part + lane, __float_as_uint(o[0]), tag);
-      st_t(part + 64 + lane, __float_as_uint(o[1]), tag);
-    }
-    event(ws, l, gw, nw, 2);
-    // Workgroups that reduce: the router's are the first ceil(E/4); x tile t
-    // is reduced by workgroup R0 + t, (slot, tile) rt of gate/up by R0 + tH +
-    // rt (mod the grid), so that no workgroup holds two roles in a row.
-    const int nb = (int)gridDim.x, R0 = (E + 3) / 4;
-    auto first_of = [&](int r0) { return (((int)blockIdx.x - r0) % nb + nb) % nb; };
-    float* rl = reinterpret_cast<float*>(&hs[0][0]);
-    // The rest of the block, for down weights of DB bits: the first down
-    // unit's weights are loaded before the gate/up reduction, so that they
-    // arrive while h is made.
-    auto rest = [&](auto db) {
-      constexpr int DB = decltype(db)::value;
-      const uint8_t* const dq[1] = {Ly.dq};
-      const uint32_t* const dsz[1] = {Ly.dsz};
-      Batch<1> dpre;
-      if (gw < n_dn) {
-        const int t = gw / (k * PD), j = (gw / PD) % k, p = gw % PD;
-        const size_t row = (size_t)min(max(sel_idx[j], 0), E - 1) * H + (size_t)t * 64 + lane;
-        batch_load<DB, 1>(dpre, dq, dsz, row, I, p * GD, min(2, GD));
-      }
-      // (slot, tile) rt: wavefront 0 adds the gate partials of its P slices,
-      // wavefront 1 the up partials, each in slice order in registers; the up
-      // sums reach wavefront 0 through LDS
-      for (int rt = first_of(R0 + tH); rt < k * tI; rt += nb) {
-        __syncthreads();   // rl is free
-        event(ws, l, gw, nw, 12);
-        const uint64_t* part = ws.gu_part + (size_t)rt * P * 128 + wave * 64;
-        float sum = 0.0f;
-        if (wave < 2) {
-          for (int p0 = 0; p0 < P; p0 += 32) {
-            uint64_t b[32];
-            const int np = min(32, P - p0);
-            poll(np, b, [&](int i) { return part + (size_t)(p0 + i) * 128 + lane; }, tag, ws.err);
+    // Units: gate/up unit u (slot u / (I/8), rows 8 (u % (I/8)) ..) over all
+    // workgroups; down unit t (rows 8 t .. 8 t + 7 of x) over the last
+    // workgroups, so that with more workgroups than down units the router's
+    // workgroups (the first ones) have none; both in xcd_unit's order.
+    const int nb = (int)gridDim.x;
+    const int r8 = lane & 7, ql = (lane >> 3) + 8 * wave;   // row of the eight; group lane 0 .. 31
+    const int nG = H / 64, nGL = (nG + 31) / 32;            // groups of a gate/up row; per lane
+    const int nGI = I / 64, nIt = k * nGI, nIL = (nIt + 31) / 32;   // down items of a row; per lane
+    const int nU = k * (I / 8), nD = H / 8;
+    const int nDw = min(nD, nb), D0 = nb - nDw;   // workgroups D0 .. nb - 1 take the down units
+    const int t0 = (int)blockIdx.x >= D0 ? xcd_unit((int)blockIdx.x - D0, nDw) : nD;   // first down unit
+    const bool last = l + 1 == d.L;
+    auto expert_of = [&](int j) { return (size_t)min(max(sel_idx[j], 0), E - 1); };
+    auto experts = [&](auto gb, auto db) {
+      constexpr int GB = decltype(gb)::value, DB = decltype(db)::value;
+      // the first down unit's first two items (this lane's)
+      Grp dn[2];
+      auto load_dn = [&]() {
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
-              if (i < np) sum += val_f(b[i]);
-          }
-          if (wave == 1) rl[lane] = sum;
+        for (int i = 0; i < 2; ++i) {
+          const int idx = ql + 32 * i;
+          const bool on = t0 < nD && i < nIL && idx < nIt;
+          const int j = on ? idx / nGI : 0, g = on ? idx % nGI : 0;
+          grp_load<DB>(dn[i], Ly.dq, Ly.dsz, expert_of(j) * H + (size_t)t0 * 8 + r8, I, g, on);
         }
-        event(ws, l, gw, nw, 13);
+      };
+      // gate/up unit u; FIRST: load dn after its first rows
+      auto gu_unit = [&](int u, auto first) {
+        const int j = u / (I / 8), r0 = (u % (I / 8)) * 8;
+        const size_t row = expert_of(j) * I + r0 + r8;
+        float ag = 0.0f, au = 0.0f;
+        Grp G[2][2];
+        auto load = [&](int i0) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int g = ql + 32 * (i0 + i);
+            const bool on = i0 + i < nGL && g < nG;
+            grp_load<GB>(G[i][0], Ly.gq, Ly.gsz, row, H, g, on);
+            grp_load<GB>(G[i][1], Ly.uq, Ly.usz, row, H, g, on);
+          }
+        };
+        auto dot = [&](int i0) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int g = ql + 32 * (i0 + i);
+            if (i0 + i < nGL && g < nG) {
+              ag += grp_dot<GB>(G[i][0], xs + g * 64, xsum[g]);
+              au += grp_dot<GB>(G[i][1], xs + g * 64, xsum[g]);
+            }
+          }
+        };
+        load(0);
+        if constexpr (MOEQ_STACK_DN_EARLY && decltype(first)::value) load_dn();
+        dot(0);
+        for (int i0 = 2; i0 < nGL; i0 += 2) {
+          load(i0);
+          dot(i0);
+        }
+        event(ws, l, gw, nw, 12);
+        ag = sum_stride8(ag);
+        au = sum_stride8(au);
+        __syncthreads();   // rsum is free
+        if (lane < 8) {
+          rsum[wave * 16 + lane] = ag;
+          rsum[wave * 16 + 8 + lane] = au;
+        }
         __syncthreads();
         if (wave == 0) {
-          const uint32_t hw = pair_with_next(f32_to_bf16_bits(silu_f32(sum) * rl[lane]));
-          if (!(lane & 1))
+          const float gs = ((rsum[r8] + rsum[16 + r8]) + rsum[32 + r8]) + rsum[48 + r8];
+          const float us = ((rsum[8 + r8] + rsum[24 + r8]) + rsum[40 + r8]) + rsum[56 + r8];
+          const uint32_t hw = pair_with_next(f32_to_bf16_bits(silu_f32(gs) * us));
+          if (lane < 8 && !(lane & 1))
 #pragma unroll
-            for (int c = 0; c < kRep; ++c) st_t(ws.h + (size_t)c * (k * I / 2) + ((size_t)rt * 64 + lane) / 2, hw, tag);
+            for (int c = 0; c < kRep; ++c) st_t(ws.h + (size_t)c * (k * I / 2) + ((size_t)j * I + r0 + lane) / 2, hw, tag);
+        }
+      };
+      {
+        const int u0 = xcd_unit((int)blockIdx.x, nb);
+        if (u0 < nU) {
+          gu_unit(u0, std::true_type{});
+          for (int u = u0 + nb; u < nU; u += nb) gu_unit(u, std::false_type{});
+        } else if (MOEQ_STACK_DN_EARLY) {
+          load_dn();
         }
       }
-      __syncthreads();   // rl has been read before the h slices overwrite it
-      event(ws, l, gw, nw, 3);
-      // ---- C: down units (all wavefronts), each on its own slice of h
-      uint16_t* hw_l = hs[wave];
-      float* hsum_w = hsum[wave];
-      for (int u = gw; u < n_dn; u += nw) {
-        const int t = u / (k * PD), j = (u / PD) % k, p = u % PD;
-        // h of slot j, groups p GD .. p GD + GD - 1: GD 32 words, 64 at a time
-        const uint64_t* hp = ws.h + (size_t)rep * (k * I / 2) + ((size_t)j * I + (size_t)p * GD * 64) / 2;
-        for (int w0 = 0; w0 < GD * 32; w0 += 64) {
-          uint64_t b[1];
-          poll(w0 + lane < GD * 32 ? 1 : 0, b, [&](int) { return hp + w0 + lane; }, tag, ws.err);
-          if (w0 + lane < GD * 32) reinterpret_cast<uint32_t*>(hw_l)[w0 + lane] = (uint32_t)b[0];
-        }
-        wave_lds_sync();
-        for (int g = 0; g < GD; ++g) {
-          const float s = wave_sum(bf16_bits_to_f32(hw_l[g * 64 + lane]));
-          if (lane == 0) hsum_w[g] = s;
-        }
-        wave_lds_sync();
-        if (u == gw) event(ws, l, gw, nw, 4);
-        const size_t row = (size_t)min(max(sel_idx[j], 0), E - 1) * H + (size_t)t * 64 + lane;
-        float o[1];
-        if (u == gw) {
-          unit_run<DB, 1>(dpre, true, dq, dsz, row, I, p * GD, GD, hw_l, hsum_w, o);
-        } else {
-          Batch<1> B;
-          unit_run<DB, 1>(B, false, dq, dsz, row, I, p * GD, GD, hw_l, hsum_w, o);
-        }
-        st_t(ws.y_part + ((size_t)(t * k + j) * PD + p) * 64 + lane, __float_as_uint(o[0]), tag);
-        wave_lds_sync();   // the slice has been read before the next unit's h lands
-      }
-    };
-    switch (Ly.dbits) {
-      case 4: rest(std::integral_constant<int, 4>{}); break;
-      case 6: rest(std::integral_constant<int, 6>{}); break;
-      default: rest(std::integral_constant<int, 8>{}); break;
-    }
-    event(ws, l, gw, nw, 5);
-    const bool last = l + 1 == d.L;
-    // x tile t is reduced by block t: its four wavefronts load the k PD
-    // partials (slot-major) into LDS, the first adds them: slots in
-    // ascending order, each the sum of its slices in order
-    for (int t = first_of(R0); t < tH; t += nb) {
-      __syncthreads();   // rl is free
-      event(ws, l, gw, nw, 10);
-      // wavefront w: slots w, w + 4, ..., each the sum of its PD slices in
-      // order (partials slot-major), into LDS; wavefront 0 then adds the
-      // slots in ascending order, weighted
-      const uint64_t* part = ws.y_part + (size_t)t * k * PD * 64;
-      for (int j = wave; j < k; j += 4) {
-        float yj = 0.0f;
-        for (int p0 = 0; p0 < PD; p0 += 16) {
-          uint64_t b[16];
-          const int np = min(16, PD - p0);
-          poll(np, b, [&](int i) { return part + (size_t)(j * PD + p0 + i) * 64 + lane; }, tag, ws.err);
+      // without MOEQ_STACK_DN_EARLY the down weights are loaded here, after
+      // the gate/up rows: they then arrive during the h hand-off instead of
+      // sharing the bandwidth with the gate/up rows, which h waits for
+      if (!MOEQ_STACK_DN_EARLY) load_dn();
+      event(ws, l, gw, nw, 2);
+      if (t0 >= nD) return;
+      // ---- C: h of every slot from this XCD's copy into LDS, with its
+      // 64-group sums (a group is 32 words, held by 32 consecutive threads)
+      {
+        const uint64_t* hrep = ws.h + (size_t)rep * (k * I / 2);
+        uint32_t* hs32 = reinterpret_cast<uint32_t*>(hs);
+        const int nhw = k * I / 2;
+        for (int w0 = 0; w0 < nhw; w0 += 256 * 8) {
+          uint64_t hb[8];
+          const int rem = nhw - w0 - (int)threadIdx.x;
+          const int nh = rem <= 0 ? 0 : min(8, (rem + 255) / 256);
+          poll(nh, hb, [&](int i) { return hrep + w0 + threadIdx.x + 256 * i; }, tag, ws.err);
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (i < np) yj += val_f(b[i]);
-        }
-        rl[j * 64 + lane] = yj;
-      }
-      event(ws, l, gw, nw, 11);
-      __syncthreads();
-      if (wave == 0) {
-        const uint32_t xw = reinterpret_cast<const uint32_t*>(xr)[(t * 64 + (lane & ~1)) / 2];
-        float acc = 0.0f;
-        for (int j = 0; j < k; ++j) acc = fmaf(sel_w[j], rl[j * 64 + lane], acc);
-        const float xo = bf16_bits_to_f32((lane & 1) ? (xw >> 16) : (xw & 0xFFFFu));
-        const float yb = bf16_bits_to_f32(f32_to_bf16_bits(acc));
-        const uint32_t nx2 = pair_with_next(f32_to_bf16_bits(xo + yb));
-        if (!(lane & 1)) {
-          if (last) {
-            st_u(x2 + (t * 64 + lane) / 2, nx2);
-          } else {
-#pragma unroll
-            for (int c = 0; c < kRep; ++c) st_t(ws.x + (size_t)c * (H / 2) + (t * 64 + lane) / 2, nx2, tag);
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t v = (uint32_t)hb[i];
+            const int wi = w0 + (int)threadIdx.x + 256 * i;
+            if (i < nh) hs32[wi] = v;
+            const float gsum = group_sum(i < nh ? bf16_bits_to_f32(v & 0xFFFFu) + bf16_bits_to_f32(v >> 16) : 0.0f, 32);
+            if (i < nh && (lane & 31) == 0) hsum[wi / 32] = gsum;
           }
         }
       }
+      __syncthreads();
+      event(ws, l, gw, nw, 4);
+      // down unit t; PRE: the items of its first two group lanes are in dn
+      auto down_unit = [&](int t, auto pre) {
+        auto load = [&](int i0) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int idx = ql + 32 * (i0 + i);
+            const bool on = i0 + i < nIL && idx < nIt;
+            const int j = on ? idx / nGI : 0, g = on ? idx % nGI : 0;
+            grp_load<DB>(dn[i], Ly.dq, Ly.dsz, expert_of(j) * H + (size_t)t * 8 + r8, I, g, on);
+          }
+        };
+        float acc = 0.0f;
+        auto dot = [&](int i0) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int idx = ql + 32 * (i0 + i);
+            if (i0 + i < nIL && idx < nIt) {
+              const int j = idx / nGI, g = idx % nGI;
+              acc = fmaf(sel_w[j], grp_dot<DB>(dn[i], hs + j * I + g * 64, hsum[j * nGI + g]), acc);
+            }
+          }
+        };
+        if constexpr (!decltype(pre)::value) load(0);
+        dot(0);
+        for (int i0 = 2; i0 < nIL; i0 += 2) {
+          load(i0);
+          dot(i0);
+        }
+        event(ws, l, gw, nw, 10);
+        acc = sum_stride8(acc);
+        __syncthreads();   // rsum is free
+        if (lane < 8) rsum[wave * 8 + lane] = acc;
+        __syncthreads();
+        event(ws, l, gw, nw, 11);
+        if (wave == 0) {
+          const float y = ((rsum[r8] + rsum[8 + r8]) + rsum[16 + r8]) + rsum[24 + r8];
+          const float xo = bf16_bits_to_f32(xr[t * 8 + r8]);
+          const float yb = bf16_bits_to_f32(f32_to_bf16_bits(y));
+          const uint32_t nx2 = pair_with_next(f32_to_bf16_bits(xo + yb));
+          if (lane < 8 && !(lane & 1)) {
+            if (last) {
+              st_u(x2 + (t * 8 + lane) / 2, nx2);
+            } else {
+#pragma unroll
+              for (int c = 0; c < kRep; ++c) st_t(ws.x + (size_t)c * (H / 2) + (t * 8 + lane) / 2, nx2, tag);
+            }
+          }
+        }
+      };
+      down_unit(t0, std::true_type{});
+      for (int t = t0 + nDw; t < nD; t += nDw) down_unit(t, std::false_type{});
+      event(ws, l, gw, nw, 5);
+    };
+    auto by_down = [&](auto gb) {
+      switch (Ly.dbits) {
+        case 4: experts(gb, std::integral_constant<int, 4>{}); break;
+        case 6: experts(gb, std::integral_constant<int, 6>{}); break;
+        default: experts(gb, std::integral_constant<int, 8>{}); break;
+      }
+    };
+    switch (Ly.gbits) {
+      case 4: by_down(std::integral_constant<int, 4>{}); break;
+      case 6: by_down(std::integral_constant<int, 6>{}); break;
+      default: by_down(std::integral_constant<int, 8>{}); break;
     }
     __syncthreads();
     event(ws, l, gw, nw, 6);
@@ -629,21 +646,9 @@ int device_blocks(int* nb) {
   return MOEQ_OK;
 }
 
-// K slices of a row of n groups: the largest power of two p dividing n with
-// units * p <= waves and at least kMinGroups groups per slice (at least 1).
-#ifndef MOEQ_STACK_MIN_GROUPS
-#define MOEQ_STACK_MIN_GROUPS 1
-#endif
-constexpr int kMinGroups = MOEQ_STACK_MIN_GROUPS;
-int slices(int n, int units, int waves) {
-  int p = 1;
-  while (n % (2 * p) == 0 && n / (2 * p) >= kMinGroups && units * 2 * p <= waves) p *= 2;
-  return p;
-}
-
 struct StackLayout {
-  size_t logits, gu_part, h, y_part, x, ctl, tl, total;
-  int P, PD, nb;
+  size_t logits, h, x, ctl, tl, total;
+  int nb;
 };
 
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
@@ -659,14 +664,10 @@ constexpr int kTimelineLayers = 0;
 int stack_layout(const moe_layer_desc* L, StackLayout* o) {
   int rc = device_blocks(&o->nb);
   if (rc != MOEQ_OK) return rc;
-  const int tI = L->I / 64, tH = L->H / 64, waves = 4 * o->nb;
-  o->P = slices(tH, L->k * tI, waves);
-  o->PD = slices(tI, tH * L->k, waves);
+  const int waves = 4 * o->nb;
   size_t off = 0;
   o->logits = off;  off = up256(off + (size_t)kRep * L->E * 8);
-  o->gu_part = off; off = up256(off + (size_t)L->k * tI * o->P * 128 * 8);
   o->h = off;       off = up256(off + (size_t)kRep * L->k * L->I / 2 * 8);
-  o->y_part = off;  off = up256(off + (size_t)tH * L->k * o->PD * 64 * 8);
   o->x = off;       off = up256(off + (size_t)kRep * L->H / 2 * 8);
   o->ctl = off;     off = up256(off + 256);   // call number, error word
   o->tl = off;      off = up256(off + (size_t)kTimelineLayers * waves * 16 * 8);
@@ -680,8 +681,9 @@ int stack_dims_ok(const moe_layer_desc* L) {
     return set_error(MOEQ_ERR_INVALID_ARG, "moe_stack: H=%d I=%d E=%d k=%d S=%d", L->H, L->I, L->E, L->k, L->S);
   if (L->S != 0) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack: shared experts (S=%d) not supported", L->S);
   if (L->H % 512 || L->H > kMaxH) return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack: H=%d not a multiple of 512 up to %d", L->H, kMaxH);
-  if (L->I % 64 || L->I > kMaxI)
-    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack: I=%d not a multiple of 64 up to %d", L->I, kMaxI);
+  if (L->I % 64 || (long)L->k * L->I > kMaxKI)
+    return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack: I=%d not a multiple of 64, or k*I=%ld above %d", L->I,
+                     (long)L->k * L->I, kMaxKI);
   if (L->k > kMaxK || L->k > L->E || L->E > 1024)
     return set_error(MOEQ_ERR_UNSUPPORTED, "moe_stack: k=%d E=%d (k <= 16, k <= E <= 1024)", L->k, L->E);
   return MOEQ_OK;
@@ -763,11 +765,10 @@ extern "C" int moe_stack_decode(const moe_layer_desc* dims, const void* table, s
     return set_error(MOEQ_ERR_WORKSPACE, "moe_stack_decode: workspace of %zu bytes, need %zu", ws_bytes, o.total);
   char* w = static_cast<char*>(ws);
   uint64_t* tl = nlayers <= kTimelineLayers ? reinterpret_cast<uint64_t*>(w + o.tl) : nullptr;
-  StackWs sw{reinterpret_cast<uint64_t*>(w + o.logits), reinterpret_cast<uint64_t*>(w + o.gu_part),
-             reinterpret_cast<uint64_t*>(w + o.h), reinterpret_cast<uint64_t*>(w + o.y_part),
+  StackWs sw{reinterpret_cast<uint64_t*>(w + o.logits), reinterpret_cast<uint64_t*>(w + o.h),
              reinterpret_cast<uint64_t*>(w + o.x), reinterpret_cast<uint32_t*>(w + o.ctl),
              reinterpret_cast<int*>(w + o.ctl) + 16, tl};
-  StackDims sd{dims->H, dims->I, dims->E, dims->k, nlayers, o.P, o.PD, eps};
+  StackDims sd{dims->H, dims->I, dims->E, dims->k, nlayers, eps};
   stack_epoch_kernel<<<1, 64, 0, stream>>>(sw.epoch);
   if ((rc = check_launch("moe_stack_decode (call number)")) != MOEQ_OK) return rc;
   const StackHeader* tp = static_cast<const StackHeader*>(table);

@@ -198,8 +198,8 @@ int moe_stack_table_write(const moe_layer_desc* layers, const uint16_t* const* w
 
 /* Workspace bytes moe_stack_decode needs for layers of the dimensions of L
  * on the current device (it depends on the device's CU count); 0 if L is
- * not supported (H a multiple of 512 up to 8192, I a multiple of 64 up to
- * 4096, k <= 16, k <= E <= 1024, S = 0).  Zero-fill it once. */
+ * not supported (H a multiple of 512 up to 8192, I a multiple of 64 with
+ * k * I <= 16384, k <= 16, k <= E <= 1024, S = 0).  Zero-fill it once. */
 size_t moe_stack_workspace_bytes(const moe_layer_desc* L);
 
 /* One batch-1 token through the first nlayers layers of table (the layer
@@ -220,8 +220,10 @@ size_t moe_stack_workspace_bytes(const moe_layer_desc* L);
  * (x is then wrong).  Read the word with moe_stack_read_status.  Calls that
  * share a workspace must not overlap; a workspace serves one set of
  * dimensions.
- * The K sums are split across wavefronts, so results equal
- * moe_rmsnorm + moe_decode_forward to rounding, not bit for bit. */
+ * Each row's K sum is split over the lanes and wavefronts of one
+ * workgroup and the down rows take their k slots' weighted sums together,
+ * in a fixed order, so results equal moe_rmsnorm + moe_decode_forward to
+ * rounding, not bit for bit, and are the same from run to run. */
 int moe_stack_decode(const moe_layer_desc* dims, const void* table, size_t table_bytes, int nlayers, float eps,
                      uint16_t* x, void* ws, size_t ws_bytes, hipStream_t stream);
 
