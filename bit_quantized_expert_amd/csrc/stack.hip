@@ -78,8 +78,8 @@ constexpr unsigned kSpinLimit = 1u << 18;
 #define MOEQ_STACK_REPLICAS 8
 #endif
 constexpr int kRep = MOEQ_STACK_REPLICAS;
-#ifndef MOEQ_STACK_DN_EARLY
-#define MOEQ_STACK_DN_EARLY 0
+#ifndef MOEQ_STACK_GENERIC_ONLY
+#define MOEQ_STACK_GENERIC_ONLY 0
 #endif
 #ifndef MOEQ_STACK_SLEEP
 #define MOEQ_STACK_SLEEP 1
@@ -299,6 +299,10 @@ __global__ __launch_bounds__(256) void stack_epoch_kernel(uint32_t* epoch) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// CH, CI, CK, CE: H, I, k, E fixed at compile time (0: taken from d at run
+// time); the stacked workload's shape has an instantiation of its own, in
+// which the unit and item indices need no run-time divisions.
+template <int CH, int CI, int CK, int CE>
 __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader* hdr, StackDims d, StackWs ws0,
                                                               uint32_t* x2_0) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxH];
@@ -325,8 +329,11 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
     // the dimensions as values the compiler takes as new in every layer, so
     // that what derives from them is computed where it is used rather than
     // ahead of the loop for all layers (where it would occupy registers)
-    int H = d.H, I = d.I, k = d.k, E = d.E, wave = (int)threadIdx.x >> 6;
-    asm volatile("" : "+s"(H), "+s"(I), "+s"(k), "+s"(E));
+    int H = CH ? CH : d.H, I = CI ? CI : d.I, k = CK ? CK : d.k, E = CE ? CE : d.E, wave = (int)threadIdx.x >> 6;
+    if constexpr (!CH) asm volatile("" : "+s"(H));
+    if constexpr (!CI) asm volatile("" : "+s"(I));
+    if constexpr (!CK) asm volatile("" : "+s"(k));
+    if constexpr (!CE) asm volatile("" : "+s"(E));
     wave = uniform(wave);
     const int lane = threadIdx.x & 63;
     const int gw = (int)blockIdx.x * 4 + wave, nw = (int)gridDim.x * 4;
@@ -475,8 +482,8 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
           grp_load<DB>(dn[i], Ly.dq, Ly.dsz, expert_of(j) * H + (size_t)t0 * 8 + r8, I, g, on);
         }
       };
-      // gate/up unit u; FIRST: load dn after its first rows
-      auto gu_unit = [&](int u, auto first) {
+      // gate/up unit u
+      auto gu_unit = [&](int u) {
         const int j = u / (I / 8), r0 = (u % (I / 8)) * 8;
         const size_t row = expert_of(j) * I + r0 + r8;
         float ag = 0.0f, au = 0.0f;
@@ -501,7 +508,6 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
           }
         };
         load(0);
-        if constexpr (MOEQ_STACK_DN_EARLY && decltype(first)::value) load_dn();
         dot(0);
         for (int i0 = 2; i0 < nGL; i0 += 2) {
           load(i0);
@@ -525,19 +531,13 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
             for (int c = 0; c < kRep; ++c) st_t(ws.h + (size_t)c * (k * I / 2) + ((size_t)j * I + r0 + lane) / 2, hw, tag);
         }
       };
-      {
-        const int u0 = xcd_unit((int)blockIdx.x, nb);
-        if (u0 < nU) {
-          gu_unit(u0, std::true_type{});
-          for (int u = u0 + nb; u < nU; u += nb) gu_unit(u, std::false_type{});
-        } else if (MOEQ_STACK_DN_EARLY) {
-          load_dn();
-        }
-      }
-      // without MOEQ_STACK_DN_EARLY the down weights are loaded here, after
-      // the gate/up rows: they then arrive during the h hand-off instead of
-      // sharing the bandwidth with the gate/up rows, which h waits for
-      if (!MOEQ_STACK_DN_EARLY) load_dn();
+      for (int u = xcd_unit((int)blockIdx.x, nb); u < nU; u += nb) gu_unit(u);
+      // the down weights after the gate/up rows: they then arrive during the
+      // h hand-off instead of sharing the bandwidth with the gate/up rows,
+      // which h waits for (issued before the gate/up rows or before their
+      // reduction, they cost 4 % a token)
+      event(ws, l, gw, nw, 3);
+      load_dn();
       event(ws, l, gw, nw, 2);
       if (t0 >= nD) return;
       // ---- C: h of every slot from this XCD's copy into LDS, with its
@@ -633,11 +633,20 @@ __global__ __launch_bounds__(256, 2) void stack_decode_kernel(const StackHeader*
   }
 }
 
-int device_blocks(int* nb) {
+using StackKernel = void (*)(const StackHeader*, StackDims, StackWs, uint32_t*);
+
+StackKernel stack_kernel_for(const moe_layer_desc* L) {
+#if !MOEQ_STACK_GENERIC_ONLY
+  if (L->H == 2048 && L->I == 512 && L->k == 8 && L->E == 128) return stack_decode_kernel<2048, 512, 8, 128>;
+#endif
+  return stack_decode_kernel<0, 0, 0, 0>;
+}
+
+int device_blocks(StackKernel kern, int* nb) {
   int dev = 0, cus = 0, per = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return set_error(MOEQ_ERR_HIP, "moe_stack: device query failed");
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, stack_decode_kernel, 256, 0) != hipSuccess || per < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(kern), 256, 0) != hipSuccess || per < 1)
     return set_error(MOEQ_ERR_HIP, "moe_stack: occupancy query failed");
 #ifndef MOEQ_STACK_BLOCKS_PER_CU
 #define MOEQ_STACK_BLOCKS_PER_CU 2
@@ -662,7 +671,7 @@ constexpr int kTimelineLayers = 0;
 #endif
 
 int stack_layout(const moe_layer_desc* L, StackLayout* o) {
-  int rc = device_blocks(&o->nb);
+  int rc = device_blocks(stack_kernel_for(L), &o->nb);
   if (rc != MOEQ_OK) return rc;
   const int waves = 4 * o->nb;
   size_t off = 0;
@@ -774,7 +783,7 @@ extern "C" int moe_stack_decode(const moe_layer_desc* dims, const void* table, s
   const StackHeader* tp = static_cast<const StackHeader*>(table);
   uint32_t* x2 = reinterpret_cast<uint32_t*>(x);
   void* args[] = {&tp, &sd, &sw, &x2};
-  const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(stack_decode_kernel), dim3(o.nb),
+  const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(stack_kernel_for(dims)), dim3(o.nb),
                                                   dim3(256), args, 0, stream);
   if (e != hipSuccess) return set_error(MOEQ_ERR_HIP, "moe_stack_decode: cooperative launch failed: %s", hipGetErrorString(e));
   return check_launch("moe_stack_decode");
