@@ -29,6 +29,7 @@
 #pragma once
 #include "decode_impl.h"
 #include "router.h"
+#include "rows8.h"
 
 namespace moeq {
 namespace decode_detail {
@@ -346,6 +347,215 @@ __global__ __launch_bounds__(64 * kFusedMaxSlots) void down_combine_kernel(const
   }
 }
 
+// -------------------------------------------------------------------------
+// Small batches (T <= kRows8MaxT): launches 2 and 3 as whole-row units of
+// eight rows (rows8.h), so that one token's work spreads over every CU
+// instead of one block per 64-row tile streaming whole rows of H or I.
+//  2'. block (token t, slot j, eight rows of I): wavefront 0 makes the first
+//      j + 1 choices of token t (shared slots j >= k: expert E + j - k), the
+//      block computes the eight rows' gate and up sums over all of H and
+//      stores h = bf16(silu(g) u) of them;
+//  3'. block (token t, eight rows of H): every (slot, 64-group of I) item of
+//      the eight rows, times its slot's routing weight (1 for shared slots),
+//      summed over the block in a fixed order; out = bf16(y), with the
+//      residual added as moe_combine adds it.
+// The shared experts are slots of launch 2' (launch 1 is the router only).
+// -------------------------------------------------------------------------
+#ifndef MOEQ_ROWS8_MAX_T
+#define MOEQ_ROWS8_MAX_T 2
+#endif
+constexpr int kRows8MaxT = MOEQ_ROWS8_MAX_T;
+
+// n bf16 values from src into LDS dst (8 per thread and pass) with their
+// 64-group sums into gsum (8 threads per group), n a multiple of 64.
+MOEQ_DEV void stage_rows(const uint16_t* __restrict__ src, int n, uint16_t* dst, float* gsum) {
+  for (int i0 = 0; i0 < n; i0 += 256 * 8) {
+    const int i = i0 + (int)threadIdx.x * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (i < n) v = *reinterpret_cast<const uint4*>(src + i);
+    float s = 0.0f;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s += bf16_bits_to_f32(w[c] & 0xFFFFu) + bf16_bits_to_f32(w[c] >> 16);
+    s = group_sum(s, 8);
+    if (i < n) {
+      *reinterpret_cast<uint4*>(dst + i) = v;
+      if ((threadIdx.x & 7) == 0) gsum[i / 64] = s;
+    }
+  }
+}
+
+// stage_rows split in two for n <= 2048 N: issue() loads this thread's
+// values, finish() sums and stores them (work can go between the two)
+template <int N>
+struct RowStage {
+  uint4 v[N];
+  MOEQ_DEV void issue(const uint16_t* __restrict__ src, int n) {
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      const int i = p * 2048 + (int)threadIdx.x * 8;
+      v[p] = i < n ? *reinterpret_cast<const uint4*>(src + i) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  MOEQ_DEV void finish(int n, uint16_t* dst, float* gsum) const {
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+      const int i = p * 2048 + (int)threadIdx.x * 8;
+      const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+      float s = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s += bf16_bits_to_f32(w[c] & 0xFFFFu) + bf16_bits_to_f32(w[c] >> 16);
+      s = group_sum(s, 8);
+      if (i < n) {
+        *reinterpret_cast<uint4*>(dst + i) = v[p];
+        if ((threadIdx.x & 7) == 0) gsum[i / 64] = s;
+      }
+    }
+  }
+};
+
+template <int BITS, int NCH>
+__global__ __launch_bounds__(256, 2) void gateup_rows8_kernel(const uint8_t* __restrict__ gq,
+                                                             const uint32_t* __restrict__ gsz,
+                                                             const uint8_t* __restrict__ uq,
+                                                             const uint32_t* __restrict__ usz,
+                                                             const uint16_t* __restrict__ x, int I, FusedGrid fg,
+                                                             const float* __restrict__ logits,
+                                                             int32_t* __restrict__ topk_idx,
+                                                             float* __restrict__ topk_w, uint16_t* __restrict__ hh) {
+  constexpr int H = NCH * 512, NG = H / 64, NGL = (NG + 31) / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[H];
+  __shared__ float xsum[NG];
+  __shared__ float rsum[64];
+  __shared__ int chosen;
+  const int lane = threadIdx.x & 63, wave = uniform((int)threadIdx.x >> 6);
+  const int r8 = lane & 7, ql = (lane >> 3) + 8 * wave;
+  const int per = I / 8;
+  const int u = xcd_unit((int)blockIdx.x, fg.T * fg.kS * per);
+  const int a = u / per, t = a / fg.kS, j = a % fg.kS, r0 = (u % per) * 8;
+  // the token's row is loaded while wavefront 0 selects
+  RowStage<(H + 2047) / 2048> xst;
+  xst.issue(x + (size_t)t * H, H);
+  if (j < fg.k) {
+    if (wave == 0) {
+      const bool writer = j == 0 && r0 == 0;
+      int bi;
+      float w;
+      select_token_any(logits + (size_t)t * fg.E, fg.E, fg.k, writer ? fg.k : j + 1, bi, w);
+      if (writer && lane < fg.k) {
+        topk_idx[(size_t)t * fg.k + lane] = bi;
+        topk_w[(size_t)t * fg.k + lane] = w;
+      }
+      if (lane == 0) chosen = __builtin_amdgcn_readlane(bi, j);
+    }
+  } else if (threadIdx.x == 0) {
+    chosen = fg.E + (j - fg.k);
+  }
+  xst.finish(H, xs, xsum);
+  __syncthreads();
+  const size_t row = (size_t)uniform(chosen) * I + r0 + r8;
+  Grp G[NGL][2];
+#pragma unroll
+  for (int i = 0; i < NGL; ++i) {
+    const int g = ql + 32 * i;
+    grp_load<BITS>(G[i][0], gq, gsz, row, H, g, g < NG);
+    grp_load<BITS>(G[i][1], uq, usz, row, H, g, g < NG);
+  }
+  float ag = 0.0f, au = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NGL; ++i) {
+    const int g = ql + 32 * i;
+    if (g < NG) {
+      ag += grp_dot<BITS>(G[i][0], xs + g * 64, xsum[g]);
+      au += grp_dot<BITS>(G[i][1], xs + g * 64, xsum[g]);
+    }
+  }
+  ag = sum_stride8(ag);
+  au = sum_stride8(au);
+  if (lane < 8) {
+    rsum[wave * 16 + lane] = ag;
+    rsum[wave * 16 + 8 + lane] = au;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < 8) {
+    const float gs = ((rsum[lane] + rsum[16 + lane]) + rsum[32 + lane]) + rsum[48 + lane];
+    const float us = ((rsum[8 + lane] + rsum[24 + lane]) + rsum[40 + lane]) + rsum[56 + lane];
+    hh[(size_t)a * I + r0 + lane] = (uint16_t)f32_to_bf16_bits(silu_f32(gs) * us);
+  }
+}
+
+// NGI: 64-groups of I
+template <int BITS, int NGI>
+__global__ __launch_bounds__(256, 2) void down_rows8_kernel(const uint8_t* __restrict__ dq,
+                                                           const uint32_t* __restrict__ dsz,
+                                                           const uint16_t* __restrict__ hh, int H, FusedGrid fg,
+                                                           const int32_t* __restrict__ topk_idx,
+                                                           const float* __restrict__ topk_w,
+                                                           const uint16_t* __restrict__ residual,
+                                                           uint16_t* __restrict__ out) {
+  constexpr int I = NGI * 64;
+  constexpr int NIL = (kFusedMaxSlots * NGI + 31) / 32;   // items per lane at most
+  __shared__ __attribute__((aligned(16))) uint16_t hs[kFusedMaxSlots * I];
+  __shared__ float hsum[kFusedMaxSlots * NGI];
+  __shared__ float rsum[32];
+  const int lane = threadIdx.x & 63, wave = uniform((int)threadIdx.x >> 6);
+  const int r8 = lane & 7, ql = (lane >> 3) + 8 * wave;
+  const int per = H / 8;
+  const int u = xcd_unit((int)blockIdx.x, fg.T * per);
+  const int t = u / per, r0 = (u % per) * 8;
+  const int nIt = fg.kS * NGI;
+  // the items' experts and weights, then their weights' codes; the token's
+  // h rows meanwhile
+  int ej[NIL];
+  float wj[NIL];
+#pragma unroll
+  for (int i = 0; i < NIL; ++i) {
+    const int idx = ql + 32 * i, j = idx / NGI;
+    const bool on = idx < nIt;
+    ej[i] = !on ? 0 : j < fg.k ? topk_idx[(size_t)t * fg.k + j] : fg.E + (j - fg.k);
+    wj[i] = !on ? 0.0f : j < fg.k ? topk_w[(size_t)t * fg.k + j] : 1.0f;
+  }
+  constexpr int B = NIL < 4 ? NIL : 4;   // items in registers at once
+  Grp D[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    const int idx = ql + 32 * i;
+    grp_load<BITS>(D[i], dq, dsz, (size_t)ej[i] * H + r0 + r8, I, idx % NGI, idx < nIt);
+  }
+  stage_rows(hh + (size_t)t * fg.kS * I, fg.kS * I, hs, hsum);
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int i0 = 0; i0 < NIL; i0 += B) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int idx = ql + 32 * (i0 + i);
+        if (i0 + i < NIL)
+          grp_load<BITS>(D[i], dq, dsz, (size_t)ej[min(i0 + i, NIL - 1)] * H + r0 + r8, I, idx % NGI, idx < nIt);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int idx = ql + 32 * (i0 + i);
+      if (i0 + i < NIL && idx < nIt) {
+        const int j = idx / NGI, g = idx % NGI;
+        acc = fmaf(wj[min(i0 + i, NIL - 1)], grp_dot<BITS>(D[i], hs + j * I + g * 64, hsum[j * NGI + g]), acc);
+      }
+    }
+  }
+  acc = sum_stride8(acc);
+  if (lane < 8) rsum[wave * 8 + lane] = acc;
+  __syncthreads();
+  if (wave == 0 && lane < 8) {
+    const float y = ((rsum[lane] + rsum[8 + lane]) + rsum[16 + lane]) + rsum[24 + lane];
+    const size_t o = (size_t)t * H + r0 + lane;
+    uint32_t ob = f32_to_bf16_bits(y);
+    if (residual) ob = f32_to_bf16_bits(bf16_bits_to_f32(residual[o]) + bf16_bits_to_f32(ob));
+    out[o] = (uint16_t)ob;
+  }
+}
+
 }  // namespace decode_detail
 
 // Launchers per bit width (decode_b{4,6,8}.hip).
@@ -383,7 +593,7 @@ decode_detail::FusedGrid fused_grid(const moe_layer_desc* L, int T, bool norm = 
   fg.router_blocks = ((L->E + 3) / 4 + 7) / 8 * 8;
   // shared experts: beside the router as K slices, unless the routed launch
   // leaves CUs idle anyway (small batches), where whole rows there are cheaper
-  fg.shared_late = L->S > 0 && (norm || T * L->k * fg.tiles < MOEQ_SHARED_LATE_BLOCKS);
+  fg.shared_late = L->S > 0 && (norm || T <= decode_detail::kRows8MaxT || T * L->k * fg.tiles < MOEQ_SHARED_LATE_BLOCKS);
   fg.shared_blocks = L->S > 0 && !fg.shared_late ? (L->S * fg.tiles * fg.Q + 7) / 8 * 8 * fg.groups : 0;
   fg.late_blocks = fg.shared_late ? (L->S * fg.tiles + 7) / 8 * 8 * fg.groups : 0;
   return fg;
@@ -419,6 +629,11 @@ int launch_gateup_routed(const moe_layer_desc* L, const uint16_t* x, const float
   return with_nch(L->H, [&](auto nch) {
     constexpr int NCH = decltype(nch)::value;
     const decode_detail::FusedGrid fg = fused_grid<B, NCH>(L, T, norm);
+    if (T <= decode_detail::kRows8MaxT) {
+      decode_detail::gateup_rows8_kernel<B, NCH><<<T * fg.kS * (L->I / 8), 256, 0, s>>>(
+          L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->I, fg, logits, topk_idx, topk_w, hh);
+      return check_launch("moe_decode_forward (selection + gate/up rows)");
+    }
     decode_detail::gateup_routed_kernel<B, NCH><<<T * L->k * fg.tiles + fg.late_blocks, 64 * decode_detail::FusedShape<B, NCH>::W,
                                                  0, s>>>(L->gate.q, L->gate.sz, L->up.q, L->up.sz, x, L->I, fg,
                                                          logits, spart, topk_idx, topk_w, hh);
@@ -434,9 +649,14 @@ int launch_down_combine(const moe_layer_desc* L, const uint16_t* hh, int T, cons
                         const float* topk_w, const uint16_t* residual, uint16_t* out, hipStream_t s) {
   const decode_detail::FusedGrid fg = fused_grid<B, 1>(L, T);
   const int grid = T * (L->H / 64), threads = 64 * fg.kS;
+  const bool rows8 = T <= decode_detail::kRows8MaxT;
   auto go = [&](auto ng) {
-    decode_detail::down_combine_kernel<B, decltype(ng)::value><<<grid, threads, 0, s>>>(
-        L->down.q, L->down.sz, hh, L->H, L->I, fg, topk_idx, topk_w, residual, out);
+    if (rows8)
+      decode_detail::down_rows8_kernel<B, decltype(ng)::value><<<T * (L->H / 8), 256, 0, s>>>(
+          L->down.q, L->down.sz, hh, L->H, fg, topk_idx, topk_w, residual, out);
+    else
+      decode_detail::down_combine_kernel<B, decltype(ng)::value><<<grid, threads, 0, s>>>(
+          L->down.q, L->down.sz, hh, L->H, L->I, fg, topk_idx, topk_w, residual, out);
   };
   switch (L->I / 64) {
     case 4: go(std::integral_constant<int, 4>()); break;
