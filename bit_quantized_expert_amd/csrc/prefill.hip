@@ -519,6 +519,10 @@ struct Mainloop {
   // MFMAs of slice s run).  Past the last slice r reads the repeated last
   // slice, which goes unused.
   MOEQ_DEV void slice(int s, Ready& r) {
+    // the wave's issue priority is raised while it feeds the matrix cores
+    // and lowered for the loads and the barrier, so that of the two waves
+    // on a SIMD the one with MFMAs to issue goes first (1-3 % faster)
+    __builtin_amdgcn_s_setprio(1);
     const uint8_t* A = reinterpret_cast<const uint8_t*>(a_tile(s % NA));
     if constexpr (!EARLY_DQ) dequant_first(r);
     const SliceCodes<BITS> cur[2] = {r.cur[0], r.cur[1]};
@@ -565,6 +569,7 @@ struct Mainloop {
       w1 = n1;
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   }
 };
 
