@@ -35,7 +35,10 @@
 namespace moeq {
 namespace decode_detail {
 
-constexpr int kDepth = 4;   // chunks whose loads are in flight per wavefront
+#ifndef MOEQ_DEPTH
+#define MOEQ_DEPTH 4
+#endif
+constexpr int kDepth = MOEQ_DEPTH;   // chunks whose loads are in flight per wavefront
 constexpr int kMaxNT = 2;   // tokens per pass
 
 // Block -> work mapping shared by both kernels.  The grid has two parts:
@@ -526,6 +529,16 @@ inline bool pick_shape(int K, int bits, int want, int& W, int& CW) {
 #ifndef MOEQ_DOWN_RUN
 #define MOEQ_DOWN_RUN 8
 #endif
+// run lengths and grid size of the prefill's GEMV list (cold experts)
+#ifndef MOEQ_LIST_GATEUP_RUN
+#define MOEQ_LIST_GATEUP_RUN MOEQ_GATEUP_RUN
+#endif
+#ifndef MOEQ_LIST_DOWN_RUN
+#define MOEQ_LIST_DOWN_RUN MOEQ_DOWN_RUN
+#endif
+#ifndef MOEQ_LIST_GRID
+#define MOEQ_LIST_GRID 1024
+#endif
 
 // Grid of the decode kernels for N output rows per expert (see
 // decode_detail::DecodeGrid); returns the block count.
@@ -550,7 +563,7 @@ inline int decode_list_grid(const moe_layer_desc* L, int max_experts, int N, dec
   dg.groups = 1;
   dg.shared_blocks = 0;
   const int units = max_experts * dg.tiles;
-  return units < 1024 ? units : 1024;
+  return units < MOEQ_LIST_GRID ? units : MOEQ_LIST_GRID;
 }
 
 // Per-bit-width launchers (one translation unit each, decode_b{4,6,8}.hip).

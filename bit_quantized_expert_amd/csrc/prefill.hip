@@ -792,31 +792,40 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict
   }
 }
 
-// Router logits for large batches and expert counts: 128 x 128 output
-// tiles, both operands staged through double-buffered LDS tiles in
-// K-slices of 64; wavefront (wm, wn) owns the 64 x 64 sub-tile (wm, wn).
+// Router logits for large batches and expert counts: 128 x BN output tiles
+// (BN 128, or 64 where 128-wide tiles would leave CUs with one block), both
+// operands staged through double-buffered LDS tiles in K-slices of 64;
+// wavefront (wm, wn) owns a (128 / WM) x 64 sub-tile.  Every output element
+// is summed over the K-slices in ascending order whatever BN is.
+template <int BN>
 __global__ __launch_bounds__(256) void gemm_nt_tiled_kernel(const uint16_t* __restrict__ A,
                                                             const uint16_t* __restrict__ B,
                                                             const float* __restrict__ bias, int M, int N, int K,
                                                             float* __restrict__ C) {
+  constexpr int WN = BN / 64, WM = 4 / WN, MI = 128 / WM / 32;
   __shared__ __attribute__((aligned(16))) uint16_t As[2][128 * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][128 * kLds];
-  const int m0 = blockIdx.x * 128, n0 = blockIdx.y * 128;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1, hh = lane >> 5;
-  const uint16_t* arow[4];
-  const uint16_t* brow[4];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kLds];
+  const int m0 = blockIdx.x * 128, n0 = blockIdx.y * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN, hh = lane >> 5;
+  const uint16_t* arow[ATile<128>::N];
+  const uint16_t* brow[ATile<BN>::N];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < ATile<128>::N; ++j) {
     const int r = (threadIdx.x >> 3) + 32 * j;
     arow[j] = m0 + r < M ? A + (size_t)(m0 + r) * K : nullptr;
+  }
+#pragma unroll
+  for (int j = 0; j < ATile<BN>::N; ++j) {
+    const int r = (threadIdx.x >> 3) + 32 * j;
     brow[j] = n0 + r < N ? B + (size_t)(n0 + r) * K : nullptr;
   }
-  f32x16_t acc[2][2];
+  f32x16_t acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { acc[i][0][r] = 0.0f; acc[i][1][r] = 0.0f; }
-  ATile<128> sa, sb;
+  ATile<128> sa;
+  ATile<BN> sb;
   sa.load(arow, 0);
   sb.load(brow, 0);
   sa.store(As[0]);
@@ -828,18 +837,17 @@ __global__ __launch_bounds__(256) void gemm_nt_tiled_kernel(const uint16_t* __re
       sa.load(arow, (s + 1) * 64);
       sb.load(brow, (s + 1) * 64);
     }
-    const uint16_t* a_s = As[s & 1] + (64 * wm + (lane & 31)) * kLds + 8 * hh;
+    const uint16_t* a_s = As[s & 1] + (32 * MI * wm + (lane & 31)) * kLds + 8 * hh;
     const uint16_t* b_s = Bs[s & 1] + (64 * wn + (lane & 31)) * kLds + 8 * hh;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      bf16x8_t a[2], b[2];
+      bf16x8_t a[MI], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = *reinterpret_cast<const bf16x8_t*>(a_s + 32 * i * kLds + 16 * t);
-        b[i] = *reinterpret_cast<const bf16x8_t*>(b_s + 32 * i * kLds + 16 * t);
-      }
+      for (int i = 0; i < MI; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(a_s + 32 * i * kLds + 16 * t);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) b[i] = *reinterpret_cast<const bf16x8_t*>(b_s + 32 * i * kLds + 16 * t);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
@@ -854,10 +862,10 @@ __global__ __launch_bounds__(256) void gemm_nt_tiled_kernel(const uint16_t* __re
     if (n >= N) continue;
     const float bn = bias ? bias[n] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int m = m0 + 32 * MI * wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (m < M) C[(size_t)m * N + n] = acc[i][j][r] + bn;
       }
   }
@@ -871,8 +879,16 @@ int gemm_bf16_nt(const uint16_t* A, const uint16_t* B, const float* bias, int M,
   if (M == 0 || N == 0) return MOEQ_OK;
   const long tiles128 = (long)((M + 127) / 128) * ((N + 127) / 128);
   if (tiles128 >= 128) {   // enough large tiles to fill the chip
-    dim3 grid((M + 127) / 128, (N + 127) / 128);
-    gemm_nt_tiled_kernel<<<grid, 256, 0, stream>>>(A, B, bias, M, N, K, C);
+#ifndef MOEQ_ROUTER_BN64_BELOW
+#define MOEQ_ROUTER_BN64_BELOW 512
+#endif
+    if (tiles128 < MOEQ_ROUTER_BN64_BELOW) {   // 64-wide tiles: two blocks per CU
+      dim3 grid((M + 127) / 128, (N + 63) / 64);
+      gemm_nt_tiled_kernel<64><<<grid, 256, 0, stream>>>(A, B, bias, M, N, K, C);
+    } else {
+      dim3 grid((M + 127) / 128, (N + 127) / 128);
+      gemm_nt_tiled_kernel<128><<<grid, 256, 0, stream>>>(A, B, bias, M, N, K, C);
+    }
   } else {
     dim3 grid((M + 31) / 32, (N + 31) / 32);
     gemm_nt_kernel<<<grid, 256, 0, stream>>>(A, B, bias, M, N, K, C);
@@ -900,8 +916,8 @@ extern "C" int moe_qgemm_prefill(const moe_layer_desc* L, const uint16_t* x, int
   if (!ws || ws_bytes < wl.total)
     return set_error(MOEQ_ERR_WORKSPACE, "moe_qgemm_prefill: workspace of %zu bytes, need %zu", ws_bytes, wl.total);
   int w_gu, cw_gu, w_dn, cw_dn;
-  if (!pick_shape(L->H, L->gate.bits, MOEQ_GATEUP_RUN, w_gu, cw_gu) ||
-      !pick_shape(L->I, L->down.bits, MOEQ_DOWN_RUN, w_dn, cw_dn))
+  if (!pick_shape(L->H, L->gate.bits, MOEQ_LIST_GATEUP_RUN, w_gu, cw_gu) ||
+      !pick_shape(L->I, L->down.bits, MOEQ_LIST_DOWN_RUN, w_dn, cw_dn))
     return set_error(MOEQ_ERR_UNSUPPORTED, "moe_qgemm_prefill: no GEMV kernel for H=%d/I=%d at these bit widths",
                      L->H, L->I);
   char* w = static_cast<char*>(ws);
