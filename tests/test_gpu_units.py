@@ -262,6 +262,22 @@ def test_router_logits(bq, T, wl):
     assert np.array_equal(idx.cpu().numpy(), oracle.select_topk(got, w.k))
 
 
+@pytest.mark.parametrize("T,E,H", [(8192, 512, 4096), (8192, 1024, 2048), (5000, 400, 512)])
+def test_router_logits_tiled(bq, T, E, H):
+    """The tiled router GEMM at large batches: 128 x 64 tiles (8192 tokens x
+    512 experts: 256 tiles of 128 x 128, one block a CU), 128 x 128 tiles
+    (8192 x 1024: 512 of them) and ragged edges in both M and N (5000 x
+    400: 40 x 7 tiles of 128 x 64), every logit against the oracle's fp64 dot products."""
+    rng = np.random.default_rng(T * 7 + E)
+    x = synth.f32_to_bf16_bits_input(rng.standard_normal((T, H), dtype=np.float32))
+    wr = synth.f32_to_bf16_bits_input(rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.02))
+    logits, idx, _ = bq.moe_route_topk(bf16_tensor(x), bf16_tensor(wr), None, E, 8)
+    ref = oracle.router_logits(x, wr, None)
+    got = logits.cpu().numpy()
+    assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
+    assert np.array_equal(idx.cpu().numpy(), oracle.select_topk(got, 8))
+
+
 @pytest.mark.parametrize("T,k,E,S", [(0, 8, 128, 0), (1, 8, 128, 0), (16, 8, 128, 0), (8, 8, 256, 1),
                                      (113, 8, 128, 1), (128, 8, 128, 0), (4096, 8, 128, 0), (8192, 10, 512, 0),
                                      (300, 4, 4000, 1), (2000, 2, 3, 0)])
