@@ -231,7 +231,9 @@ MOEQ_DEV int wave_max_i32(int v) {
 // On return lane j < k holds choice j in idx and its weight in w (other
 // lanes: -1 and 0).  Needs k <= min(E, 64).  With rounds < k only the
 // first `rounds` choices are made (lanes j < rounds), and w is not valid.
-template <int NS>
+// EXACT_EXP: the weights' exponentials by expf instead of the hardware
+// exp2 (moe_route_topk's weights).
+template <int NS, bool EXACT_EXP = false>
 MOEQ_DEV void select_token(const float* __restrict__ L, int E, int k, int rounds, int& idx, float& w) {
   const int lane = threadIdx.x & 63;
   int key[NS];
@@ -258,7 +260,7 @@ MOEQ_DEV void select_token(const float* __restrict__ L, int E, int k, int rounds
     }
     const float bv = key_value(M);
     if (j == 0) top0 = bv;
-    const float ex = __expf(bv - top0);
+    const float ex = EXACT_EXP ? expf(bv - top0) : __expf(bv - top0);
     wsum += ex;
     if (lane == j) {
       myw = ex;

@@ -138,13 +138,20 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int nblk, int nexp, 
                                                              int32_t* __restrict__ active, int* __restrict__ status) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int tmp[16];
+  // the block counts 16 at a time, all loaded before the running sum
   for (int e = threadIdx.x; e < nexp; e += kB) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      int32_t* p = hist + (size_t)b * nexp + e;
-      const int v = *p;
-      *p = run;
-      run += v;
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = b0 + i < nblk ? hist[(size_t)(b0 + i) * nexp + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (b0 + i < nblk) {
+          hist[(size_t)(b0 + i) * nexp + e] = run;
+          run += v[i];
+        }
+      }
     }
     cnt[e] = run;
   }

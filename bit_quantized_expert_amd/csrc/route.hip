@@ -112,6 +112,25 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   for (int j = lane; j < k; j += 64) w_row[j] = w_row[j] / wsum;   // entries this lane wrote
 }
 
+// The same selection with lane l holding experts NS l .. NS l + NS - 1
+// (select_token: one ballot a round instead of one a slot), for k <= 64 and
+// E <= 1024; the same choices, and the weights formed the same way (expf,
+// summed in choice order, one division each).
+template <int NS>
+__global__ __launch_bounds__(256) void topk_keys_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                        int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int idx;
+  float w;
+  select_token<NS, true>(logits + (size_t)t * E, E, k, k, idx, w);
+  if (lane < k) {
+    idx_out[(size_t)t * k + lane] = idx;
+    w_out[(size_t)t * k + lane] = w;
+  }
+}
+
 }  // namespace
 
 extern "C" int moe_route_topk(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H,
@@ -146,6 +165,14 @@ extern "C" int moe_route_topk(const uint16_t* x, const uint16_t* w_router, const
   }
   const unsigned grid = (unsigned)((T + 3) / 4);
   const int ns = (E + 63) / 64;
+  if (k <= 64 && ns <= 16) {
+    if (ns <= 1) topk_keys_kernel<1><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+    else if (ns <= 2) topk_keys_kernel<2><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+    else if (ns <= 4) topk_keys_kernel<4><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+    else if (ns <= 8) topk_keys_kernel<8><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+    else topk_keys_kernel<16><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
+    return check_launch("moe_route_topk (top-k)");
+  }
   if (ns <= 1) topk_kernel<1><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
   else if (ns <= 2) topk_kernel<2><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
   else if (ns <= 4) topk_kernel<4><<<grid, 256, 0, stream>>>(logits, T, E, k, topk_idx, topk_w);
