@@ -332,17 +332,17 @@ template <int BITS>
 MOEQ_DEV GroupDq group_dq(uint32_t sz) { return GroupDq::make<BITS == 4 ? 16 : (BITS == 6 ? 4 : 1)>(sz); }
 
 // A (token rows) staging: BM rows x 64 bf16 per slice through registers
-// into one of two LDS tiles; rows past the tile's valid count are zeros.
+// into one of two LDS tiles.
 template <int BM>
 struct ATile {
   static constexpr int N = BM * 8 / 256;   // 16-byte pieces per thread
   moeq_u32x4 v[N];
-  // rows[j]: token row tid / 8 + 32 j of the tile, or null past the end
+  // rows[j]: row tid / 8 + 32 j of the tile (every pointer valid: rows past
+  // the operand's end repeat its last row, whose products are not stored),
+  // so that the loads are unconditional and the compiler counts them exactly
   MOEQ_DEV void load(const uint16_t* const (&rows)[N], int k0) {
 #pragma unroll
-    for (int j = 0; j < N; ++j)
-      v[j] = rows[j] ? *reinterpret_cast<const moeq_u32x4*>(rows[j] + k0 + (threadIdx.x & 7) * 8)
-                     : moeq_u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < N; ++j) v[j] = *reinterpret_cast<const moeq_u32x4*>(rows[j] + k0 + (threadIdx.x & 7) * 8);
   }
   MOEQ_DEV void store(uint16_t* lds) const {
 #pragma unroll
@@ -796,7 +796,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict
 // (BN 128, or 64 where 128-wide tiles would leave CUs with one block), both
 // operands staged through double-buffered LDS tiles in K-slices of 64;
 // wavefront (wm, wn) owns a (128 / WM) x 64 sub-tile.  Every output element
-// is summed over the K-slices in ascending order whatever BN is.
+// is summed over the K-slices in ascending order whatever BN is.  Rows past
+// M or N read row M - 1 or N - 1 and are not stored.
 template <int BN>
 __global__ __launch_bounds__(256) void gemm_nt_tiled_kernel(const uint16_t* __restrict__ A,
                                                             const uint16_t* __restrict__ B,
@@ -812,31 +813,37 @@ __global__ __launch_bounds__(256) void gemm_nt_tiled_kernel(const uint16_t* __re
 #pragma unroll
   for (int j = 0; j < ATile<128>::N; ++j) {
     const int r = (threadIdx.x >> 3) + 32 * j;
-    arow[j] = m0 + r < M ? A + (size_t)(m0 + r) * K : nullptr;
+    arow[j] = A + (size_t)min(m0 + r, M - 1) * K;
   }
 #pragma unroll
   for (int j = 0; j < ATile<BN>::N; ++j) {
     const int r = (threadIdx.x >> 3) + 32 * j;
-    brow[j] = n0 + r < N ? B + (size_t)(n0 + r) * K : nullptr;
+    brow[j] = B + (size_t)min(n0 + r, N - 1) * K;
   }
   f32x16_t acc[MI][2];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { acc[i][0][r] = 0.0f; acc[i][1][r] = 0.0f; }
-  ATile<128> sa;
-  ATile<BN> sb;
-  sa.load(arow, 0);
-  sb.load(brow, 0);
-  sa.store(As[0]);
-  sb.store(Bs[0]);
+  // K-slices reach registers two slices ahead of their LDS store: at the
+  // start of slice s, LDS[s & 1] holds slice s, ra/rb[(s + 1) & 1] slice
+  // s + 1 and ra/rb[s & 1] slice s + 2 (loads in flight or arrived).  Past
+  // the end the last slice is loaded and stored again (never read), so that
+  // every load and store is unconditional and the compiler's counts of the
+  // loads in flight are exact: a slice's stores wait only for its own loads.
+  ATile<128> ra[2];
+  ATile<BN> rb[2];
   const int ns = K / 64;
-  for (int s = 0; s < ns; ++s) {
+  ra[0].load(arow, 0);
+  rb[0].load(brow, 0);
+  ra[0].store(As[0]);
+  rb[0].store(Bs[0]);
+  ra[1].load(arow, min(1, ns - 1) * 64);
+  rb[1].load(brow, min(1, ns - 1) * 64);
+  ra[0].load(arow, min(2, ns - 1) * 64);
+  rb[0].load(brow, min(2, ns - 1) * 64);
+  auto step = [&](int s, ATile<128>& na, ATile<BN>& nb) {   // na, nb: slice s + 1
     __syncthreads();
-    if (s + 1 < ns) {
-      sa.load(arow, (s + 1) * 64);
-      sb.load(brow, (s + 1) * 64);
-    }
     const uint16_t* a_s = As[s & 1] + (32 * MI * wm + (lane & 31)) * kLds + 8 * hh;
     const uint16_t* b_s = Bs[s & 1] + (64 * wn + (lane & 31)) * kLds + 8 * hh;
 #pragma unroll
@@ -851,11 +858,18 @@ __global__ __launch_bounds__(256) void gemm_nt_tiled_kernel(const uint16_t* __re
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (s + 1 < ns) {
-      sa.store(As[(s + 1) & 1]);
-      sb.store(Bs[(s + 1) & 1]);
-    }
+    na.store(As[(s + 1) & 1]);
+    nb.store(Bs[(s + 1) & 1]);
+    const int nx = min(s + 3, ns - 1);
+    na.load(arow, nx * 64);
+    nb.load(brow, nx * 64);
+  };
+  int s = 0;
+  for (; s + 1 < ns; s += 2) {
+    step(s, ra[1], rb[1]);
+    step(s + 1, ra[0], rb[0]);
   }
+  if (s < ns) step(s, ra[1], rb[1]);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = n0 + 64 * wn + 32 * j + (lane & 31);
