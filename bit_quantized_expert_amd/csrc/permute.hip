@@ -191,6 +191,41 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(const int32_t* __
   inverse[a] = p;
 }
 
+// The same scatter for up to 1024 experts with parts of one wavefront: the
+// direct count runs over at most 63 earlier ids instead of 255, and the 15
+// earlier parts' counts (at most 64 each) are packed four to a 32-bit LDS
+// word.  The ranks, and so the output, are the same.
+constexpr int kPartW = 64;
+constexpr int kScatterWMaxExperts = 1024;
+__global__ __launch_bounds__(1024) void permute_scatter_w_kernel(const int32_t* __restrict__ idx, long A, int k,
+                                                                  int kS, int E, int nexp,
+                                                                  const int32_t* __restrict__ hist,
+                                                                  const int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ sorted,
+                                                                  int32_t* __restrict__ inverse) {
+  constexpr int NP = kB / kPartW - 1;   // the last part's counts are never needed
+  constexpr int NW = kScatterWMaxExperts / 4;
+  __shared__ int sid[kB];
+  __shared__ uint32_t pc[NP][NW];
+  const long a = (long)blockIdx.x * kB + threadIdx.x;
+  const int id = a < A ? assignment_expert(idx, a, k, kS, E) : -2;
+  const int part = threadIdx.x / kPartW;
+  for (int i = threadIdx.x; i < NP * NW; i += kB) pc[i / NW][i % NW] = 0u;
+  sid[threadIdx.x] = id;
+  __syncthreads();
+  if (id >= 0 && part < NP) atomicAdd(&pc[part][id >> 2], 1u << (8 * (id & 3)));
+  __syncthreads();
+  if (a >= A) return;
+  if (id < 0) { inverse[a] = -1; return; }
+  int rank = 0;
+  for (int q = 0; q < part; ++q) rank += (int)((pc[q][id >> 2] >> (8 * (id & 3))) & 0xFFu);
+  const int p0 = part * kPartW;
+  for (int j = p0; j < (int)threadIdx.x; ++j) rank += (sid[j] == id);
+  const int p = offsets[id] + hist[(size_t)blockIdx.x * nexp + id] + rank;
+  sorted[p] = (int32_t)a;
+  inverse[a] = p;
+}
+
 }  // namespace
 
 extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int S, int32_t* counts, int32_t* offsets,
@@ -219,6 +254,9 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int S, 
   if (rc != MOEQ_OK) return rc;
   permute_scan_kernel<<<1, kB, 0, stream>>>(nblk, nexp, A, hist, counts, offsets, active, status);
   if ((rc = check_launch("moe_permute (scan)")) != MOEQ_OK) return rc;
-  permute_scatter_kernel<<<nblk, kB, 0, stream>>>(topk_idx, A, k, kS, E, nexp, hist, offsets, sorted, inverse);
+  if (nexp <= kScatterWMaxExperts)
+    permute_scatter_w_kernel<<<nblk, kB, 0, stream>>>(topk_idx, A, k, kS, E, nexp, hist, offsets, sorted, inverse);
+  else
+    permute_scatter_kernel<<<nblk, kB, 0, stream>>>(topk_idx, A, k, kS, E, nexp, hist, offsets, sorted, inverse);
   return check_launch("moe_permute (scatter)");
 }
