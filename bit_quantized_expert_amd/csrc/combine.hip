@@ -7,26 +7,7 @@ using namespace moeq;
 namespace {
 
 // One thread per 8 consecutive outputs of one token; slots summed in
-// ascending order in fp32.  The rows of four slots are loaded before any of
-// them is added, so a thread keeps four 16-byte loads in flight (the kernel
-// is bound by HBM latency with one); the order of the additions is unchanged.
-template <bool F32>
-__device__ __forceinline__ void combine_load(const void* yv, size_t off, float (&v)[8]) {
-  if constexpr (F32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(yv) + off);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(yv) + off);
-    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      v[2 * c] = bf16_bits_to_f32(d[c] & 0xFFFFu);
-      v[2 * c + 1] = bf16_bits_to_f32(d[c] >> 16);
-    }
-  }
-}
-
+// ascending order in fp32.
 template <bool F32>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ yv, const float* __restrict__ w,
                                                       const uint16_t* __restrict__ residual, int T, int k, int S,
@@ -39,24 +20,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-  const size_t base = (size_t)t * kS * H + n;
-  int j = 0;
-  for (; j + 4 <= kS; j += 4) {
-    float v[4][8], wt[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      combine_load<F32>(yv, base + (size_t)(j + u) * H, v[u]);
-      wt[u] = j + u < k ? w[(size_t)t * k + j + u] : 1.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] = fmaf(wt[u], v[u][c], acc[c]);
-  }
-  for (; j < kS; ++j) {
-    float v[8];
-    combine_load<F32>(yv, base + (size_t)j * H, v);
+  for (int j = 0; j < kS; ++j) {
     const float wt = j < k ? w[(size_t)t * k + j] : 1.0f;
+    const size_t row = (size_t)t * kS + j;
+    float v[8];
+    if constexpr (F32) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(yv) + row * H + n);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(yv) + row * H + n);
+      const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v[2 * c] = bf16_bits_to_f32(d[c] & 0xFFFFu);
+        v[2 * c + 1] = bf16_bits_to_f32(d[c] >> 16);
+      }
+    }
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = fmaf(wt, v[c], acc[c]);
   }
