@@ -105,3 +105,15 @@ def test_measured_path_imports_no_test_code():
             imports = [n for n in ast.walk(node) if isinstance(n, ast.Import)]
             if any(a.name == "oracle" for n in imports for a in n.names):
                 assert node.name in allowed, node.name
+
+
+def test_counter_summaries_match_sources():
+    """The HBM counter summaries bench.py reads for its default line (the
+    8192-token prefill chunk and the two nested decode lines) were taken on
+    the kernel sources as they stand, so the line reports their traffic;
+    a kernel change without new counters would turn it into null."""
+    for workload, T in (("moe_h4096_e512_k10_b4_hot", 8192), ("moe_h4096_e512_k10_b4_hot", 1),
+                        ("moe_h2048_e256_k8_s1_b4", 8)):
+        got = bench.measured_traffic(workload, T)
+        assert got is not None, f"profiles/pmc_{workload}_T{T}.txt is missing or was taken on other sources"
+        assert got > 0
